@@ -1,0 +1,6 @@
+"""Float64 CPU oracle (test infrastructure only; never used by the product path)."""
+
+from .sla_oracle import (  # noqa: F401
+    BLOCK, OracleResult, block_counts, classify, compressed_scores, forward,
+    linear_branch, num_blocks, phi, router_pool, sparse_branch, token_mask, token_rows,
+)
