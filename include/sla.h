@@ -1,0 +1,150 @@
+/*
+ * sla.h - C ABI of the MI355X (gfx950) forward pass of SLA / SLA2
+ * sparse-linear attention.
+ *
+ * The method (SLA paper summary on aipaper.cc, section 4, Eq. 1-3 and Fig. 4;
+ * SLA2 article on mcffsbgs.com, the learned-router and mixing paragraphs):
+ * for every (batch, head), queries and keys are cut into 64-token blocks; a
+ * router projects Q and K with two learned d x d matrices and mean-pools each
+ * block; the compressed map Pc = softmax(pool(Q) pool(K)^T / sqrt(d)) ranks,
+ * per query block, the key blocks into critical (top kh), negligible
+ * (bottom kl) and marginal (the rest); critical blocks get exact block-sparse
+ * softmax attention O_s, marginal blocks get linear attention
+ * O_l = phi(Q_i) H_i / (phi(Q_i) Z_i) with H_i, Z_i the sums of
+ * phi(K_j)^T V_j and rowsum(phi(K_j)^T) over marginal j (phi = softmax over
+ * the features), negligible blocks are skipped, and
+ * O = alpha_h * O_s + (1 - alpha_h) * O_l.
+ *
+ * Conventions shared by every entry point:
+ *  - Q, K, V, O are [B, H, N, d] contiguous, row-major, 16-byte aligned
+ *    device buffers of `dtype`. Self-attention: queries and keys share N.
+ *  - Nb = ceil(N / 64). The last block may be ragged; its missing tokens
+ *    take no part in pooling, attention or sums, and are never written.
+ *  - Block mask values: 1 critical, 0 marginal, -1 negligible (Eq. 2 of the
+ *    SLA paper summary). Layout [B, H, Nb, Nb] int8, row = query block.
+ *  - Counts per query-block row: n_h = 0 if kh == 0, else
+ *    max(1, floor(kh*Nb + 1e-9)); n_l = floor(kl*Nb + 1e-9); n_h + n_l <= Nb.
+ *    Ranking order: larger compressed logit first, lower block index first
+ *    among equal logits; critical = head n_h, negligible = tail n_l.
+ *    Logits are formed and ranked in float64.
+ *  - All device work is enqueued on `stream` (a hipStream_t, NULL = the
+ *    default stream); calls return after enqueue and never synchronise.
+ *  - The library allocates no device memory and keeps no state between calls:
+ *    the caller owns every buffer, including the workspace sized by
+ *    sla_workspace_bytes(). Calls are reentrant if their workspaces differ.
+ *  - Argument errors are reported before anything is enqueued, with outputs
+ *    untouched. No C++ exception crosses this interface.
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLA_OK = 0,
+  SLA_ERR_ARG = -1,          /* bad pointer, size, fraction, alignment        */
+  SLA_ERR_UNSUPPORTED = -2,  /* valid request outside what is built           */
+  SLA_ERR_WORKSPACE = -3,    /* workspace missing, misaligned or too small    */
+  SLA_ERR_HIP = -4           /* a HIP runtime call or a launch failed         */
+} sla_status;
+
+typedef enum { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype;
+
+typedef enum {
+  SLA_QUANT_NONE = 0,
+  /* 8-bit sparse branch (SLA2 article, quantisation-aware paragraph): Q and
+   * K as int8 and V as fp8 e4m3, each with one absmax scale per 64-token
+   * block; P as fp8 e4m3 with one scale per row of every key tile.
+   * Requires dtype == SLA_BF16. The linear branch stays bf16. */
+  SLA_QUANT_I8QK_F8PV = 1
+} sla_quant;
+
+typedef struct {
+  int32_t B, H, N, d;         /* d in {64, 128}                                  */
+  int32_t dtype;              /* sla_dtype of Q, K, V, O                         */
+  int32_t quant;              /* sla_quant                                       */
+  int32_t proj_head_stride;   /* 0: proj_q/proj_k are one [d, d] matrix for all  */
+                              /* heads; d*d: they are [H, d, d]                  */
+  int32_t reserved;           /* must be 0                                       */
+  double  kh, kl;             /* critical / negligible fractions in [0, 1]       */
+} sla_problem;
+
+/* Debug outputs of sla_forward_debug. Every pointer is a device buffer or NULL.
+ * pooled_q, pooled_k: [B, H, Nb, d] float64, the router-projected block means
+ *                     (Eq. 1's pool(Q), pool(K));
+ * logits:             [B, H, Nb, Nb] float64, pool(Q) pool(K)^T / sqrt(d);
+ * o_s, o_l:           [B, H, N, d] float32, the sparse and linear branch outputs
+ *                     before the mix. pooled_q/pooled_k/logits are only written
+ *                     when the mask is computed (mask_in == NULL). */
+typedef struct {
+  double* pooled_q;
+  double* pooled_k;
+  double* logits;
+  float*  o_s;
+  float*  o_l;
+} sla_debug;
+
+/* Block counts of a problem (host only, no device work).
+ * Out: *nb = Nb, *n_h and *n_l as defined above (each pointer may be NULL).
+ * Returns SLA_OK, or SLA_ERR_ARG for a NULL problem, non-positive sizes,
+ * fractions outside [0, 1] or n_h + n_l > Nb. */
+int sla_block_counts(const sla_problem* p, int32_t* nb, int32_t* n_h, int32_t* n_l);
+
+/* Device workspace that sla_forward needs for `p` (host only, no device work).
+ * Out: *bytes. The workspace must be 256-byte aligned. Returns SLA_OK or the
+ * validation error sla_forward would return for `p`. */
+int sla_workspace_bytes(const sla_problem* p, size_t* bytes);
+
+/* The SLA2 forward pass.
+ *  Q, K, V   device, dtype, [B, H, N, d].
+ *  proj_q,   device float32 router matrices indexed [in, out], one [d, d] or
+ *  proj_k    [H, d, d] (see proj_head_stride); may be NULL when mask_in is given.
+ *  alpha     device float32 [H], the per-head mixing ratio.
+ *  mask_in   NULL, or a device int8 [B, H, Nb, Nb] block mask with values in
+ *            {1, 0, -1} that replaces the router, pooling and classification;
+ *            any such mask is valid and rows may hold any number of each class.
+ *  O         device, dtype, [B, H, N, d] output.
+ *  mask_out  device int8 [B, H, Nb, Nb]: the computed block mask. May be NULL
+ *            only when mask_in is given (then nothing is written there).
+ *  workspace device scratch of at least sla_workspace_bytes(p) bytes.
+ * An empty critical set gives O_s = 0 for that query block, an empty marginal
+ * set gives O_l = 0. Returns SLA_OK once all work is enqueued; SLA_ERR_ARG,
+ * SLA_ERR_UNSUPPORTED or SLA_ERR_WORKSPACE before any enqueue; SLA_ERR_HIP if
+ * a launch fails (sla_last_error() has the HIP message). Device faults surface
+ * at the caller's next synchronisation of `stream`. */
+int sla_forward(const sla_problem* p,
+                const void* Q, const void* K, const void* V,
+                const float* proj_q, const float* proj_k, const float* alpha,
+                const int8_t* mask_in,
+                void* O, int8_t* mask_out,
+                void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* sla_forward plus the debug outputs of `dbg` (which may be NULL). */
+int sla_forward_debug(const sla_problem* p,
+                      const void* Q, const void* K, const void* V,
+                      const float* proj_q, const float* proj_k, const float* alpha,
+                      const int8_t* mask_in,
+                      void* O, int8_t* mask_out,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream, const sla_debug* dbg);
+
+/* Static text of a status code. */
+const char* sla_status_str(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* sla_last_error(void);
+
+/* Interface version: (major << 16) | minor. */
+int sla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H */

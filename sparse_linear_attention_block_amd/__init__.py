@@ -1,0 +1,16 @@
+"""MI355X (gfx950) forward pass of SLA / SLA2 sparse-linear attention.
+
+Five hand-written HIP kernels behind the C ABI of include/sla.h:
+router projection + block mean pooling, compressed scores + three-way block
+classification, per-key-block linear state h_j / z_j, the marginal-block
+sums (one MFMA product per head), and block-sparse online-softmax attention
+over the critical blocks with the linear-branch output and the SLA2 mix
+fused into its epilogue. This package is the argument-marshalling binding.
+"""
+
+from ._binding import (  # noqa: F401
+    LIB_PATH, SLAError, block_counts, forward, load_library, make_problem, workspace_bytes,
+)
+
+__all__ = ["forward", "block_counts", "workspace_bytes", "load_library", "make_problem",
+           "SLAError", "LIB_PATH"]

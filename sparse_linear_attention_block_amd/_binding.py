@@ -1,0 +1,177 @@
+"""ctypes binding of libsla.so (argument marshalling only).
+
+Every step of the forward pass runs in the HIP kernels behind the C ABI of
+include/sla.h; PyTorch only supplies device memory and the current stream.
+There is no fallback: without the built library every call raises.
+"""
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
+
+SLA_OK, SLA_ERR_ARG, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_HIP = 0, -1, -2, -3, -4
+SLA_F32, SLA_BF16 = 0, 1
+SLA_QUANT_NONE, SLA_QUANT_I8QK_F8PV = 0, 1
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("quant", ctypes.c_int32),
+                ("proj_head_stride", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("kh", ctypes.c_double), ("kl", ctypes.c_double)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("pooled_q", ctypes.c_void_p), ("pooled_k", ctypes.c_void_p),
+                ("logits", ctypes.c_void_p), ("o_s", ctypes.c_void_p), ("o_l", ctypes.c_void_p)]
+
+
+class SLAError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(text)
+        self.status = status
+
+
+_lib = None
+
+_FWD_ARGS = [ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libsla.so once; raises ImportError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m sparse_linear_attention_block_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.sla_block_counts.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.sla_block_counts.restype = ctypes.c_int
+    lib.sla_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
+    lib.sla_workspace_bytes.restype = ctypes.c_int
+    lib.sla_forward.argtypes = _FWD_ARGS
+    lib.sla_forward.restype = ctypes.c_int
+    lib.sla_forward_debug.argtypes = _FWD_ARGS + [ctypes.POINTER(Debug)]
+    lib.sla_forward_debug.restype = ctypes.c_int
+    lib.sla_status_str.argtypes = [ctypes.c_int]
+    lib.sla_status_str.restype = ctypes.c_char_p
+    lib.sla_last_error.argtypes = []
+    lib.sla_last_error.restype = ctypes.c_char_p
+    lib.sla_version.argtypes = []
+    lib.sla_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != SLA_OK:
+        lib = load_library()
+        raise SLAError(rc, f"{lib.sla_status_str(rc).decode()}: {lib.sla_last_error().decode()}")
+
+
+def make_problem(B: int, H: int, N: int, d: int, dtype: str, kh: float, kl: float,
+                 quant: bool = False, proj_head_stride: int = 0) -> Problem:
+    return Problem(B, H, N, d, SLA_BF16 if dtype in ("bf16", torch.bfloat16) else SLA_F32,
+                   SLA_QUANT_I8QK_F8PV if quant else SLA_QUANT_NONE, proj_head_stride, 0,
+                   float(kh), float(kl))
+
+
+def block_counts(N: int, kh: float, kl: float, *, B: int = 1, H: int = 1, d: int = 128,
+                 dtype: str = "bf16"):
+    """(Nb, n_h, n_l) as the library computes them (host only)."""
+    lib = load_library()
+    p = make_problem(B, H, N, d, dtype, kh, kl)
+    nb, nh, nl = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.sla_block_counts(ctypes.byref(p), ctypes.byref(nb), ctypes.byref(nh), ctypes.byref(nl)))
+    return nb.value, nh.value, nl.value
+
+
+def workspace_bytes(p: Problem) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t()
+    _check(lib.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            proj_q: Optional[torch.Tensor], proj_k: Optional[torch.Tensor], alpha: torch.Tensor,
+            kh: float, kl: float, mask_in: Optional[torch.Tensor] = None, *,
+            quant: bool = False, out: Optional[torch.Tensor] = None,
+            mask_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            debug: bool = False):
+    """SLA2 forward on the GPU: returns (O, mask) or (O, mask, debug dict).
+
+    q, k, v: [B, H, N, d] contiguous bf16 or float32 device tensors.
+    proj_q, proj_k: float32 [d, d] or [H, d, d] (may be None with mask_in).
+    alpha: float32 [H]. mask_in: optional int8 [B, H, Nb, Nb] in {1, 0, -1}.
+    """
+    lib = load_library()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    Nb = (N + 63) // 64
+    dev = q.device
+    hs = 0
+    if proj_q is not None:
+        if proj_q.dtype != torch.float32 or proj_k is None or proj_k.shape != proj_q.shape:
+            raise ValueError("proj_q and proj_k must be float32 tensors of one shape")
+        proj_q, proj_k = proj_q.contiguous(), proj_k.contiguous()
+        hs = d * d if proj_q.dim() == 3 else 0
+    if alpha.dtype != torch.float32 or alpha.numel() != H:
+        raise ValueError("alpha must be float32 with H entries")
+    alpha = alpha.contiguous()
+    if mask_in is not None:
+        if mask_in.dtype != torch.int8 or tuple(mask_in.shape) != (B, H, Nb, Nb):
+            raise ValueError("mask_in must be int8 [B, H, Nb, Nb]")
+        mask_in = mask_in.contiguous()
+    p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", kh, kl,
+                     quant, hs)
+    need = workspace_bytes(p)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if mask_in is None and mask_out is None:
+        mask_out = torch.empty((B, H, Nb, Nb), dtype=torch.int8, device=dev)
+    dbg = None
+    dbg_t = {}
+    if debug:
+        if mask_in is None:
+            dbg_t["pooled_q"] = torch.empty((B, H, Nb, d), dtype=torch.float64, device=dev)
+            dbg_t["pooled_k"] = torch.empty((B, H, Nb, d), dtype=torch.float64, device=dev)
+            dbg_t["logits"] = torch.empty((B, H, Nb, Nb), dtype=torch.float64, device=dev)
+        dbg_t["o_s"] = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+        dbg_t["o_l"] = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+        dbg = Debug(*[_ptr(dbg_t.get(n)) for n in ("pooled_q", "pooled_k", "logits", "o_s", "o_l")])
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        args = [ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q), _ptr(proj_k),
+                _ptr(alpha), _ptr(mask_in), _ptr(out), _ptr(mask_out), _ptr(workspace),
+                ctypes.c_size_t(workspace.numel() * workspace.element_size()), stream]
+        if debug:
+            rc = lib.sla_forward_debug(*args, ctypes.byref(dbg))
+        else:
+            rc = lib.sla_forward(*args)
+    _check(rc)
+    mask = mask_out if mask_out is not None else mask_in
+    if debug:
+        return out, mask, dbg_t
+    return out, mask

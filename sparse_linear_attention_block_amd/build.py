@@ -1,0 +1,60 @@
+"""Builds libsla.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+Usage: python -m sparse_linear_attention_block_amd.build [-v]
+Every call compiles from source; objects go to _build/ at the repository root.
+"""
+
+import concurrent.futures
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libsla.so")
+ARCH = os.environ.get("SLA_OFFLOAD_ARCH", "gfx950")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CFLAGS = [
+    "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
+    # packed fp32 ops stay off: the compiler must not form v_pk_* f32 math
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        futs = [ex.submit(_run, [HIPCC, *CFLAGS, "-c", s, "-o", o], verbose)
+                for s, o in zip(srcs, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,75 @@
+// Device helpers shared by the gfx950 kernels: bf16 <-> f32, MFMA wrappers,
+// wave reductions. Wave size is 64 on CDNA4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sla {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
+typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
+
+__device__ __forceinline__ float bf2f(uint32_t u16) { return __uint_as_float(u16 << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 with round-to-nearest-even (the native gfx950 conversion)
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// D += A * B with A: 16x32, B: 32x16 bf16, D: 16x16 f32.
+// Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and
+// D[4*(l/16) + r][l%16] in register r. Any permutation of the 32 k slots is
+// allowed as long as A and B use the same one.
+__device__ __forceinline__ f32x4 mfma_bf16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// D += A * B with A: 16x64, B: 64x16 int8, D: 16x16 int32; lane l holds 16
+// consecutive k of row/column l%16 at k offset 16*(l/16).
+__device__ __forceinline__ i32x4 mfma_i8(const uint4& a, const uint4& b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// D += A * B with A: 16x128, B: 128x16 fp8 e4m3 (OCP), D: 16x16 f32; lane l
+// holds 32 k of row/column l%16 (unit block scales).
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ float wave_max16(float v) {  // over the 16 lanes of a row group
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+__device__ __forceinline__ float wave_sum16(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+// over lanes l, l^16, l^32, l^48 (the four k groups of one MFMA column)
+__device__ __forceinline__ float group4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+}  // namespace sla

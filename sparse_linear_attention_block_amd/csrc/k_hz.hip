@@ -1,0 +1,293 @@
+// K3: per-key-block linear-attention state.
+//
+// SLA explainer (intelliparadigm.com), section 1.2 "key implementation trick":
+// h_j = phi(K_j)^T V_j (d x d) and z_j = rowsum(phi(K_j)^T) (d) are formed once
+// per key block so that a query block only has to add them up (SLA paper
+// summary, Eq. 3). phi is the softmax over the d features of each key token
+// (SLA explainer, section 3.2; SLA paper summary, Table 2).
+//
+// bf16 path, one workgroup per 4 consecutive key blocks of one (batch, head):
+//  1. each block's K and V rows stream in with 16-byte loads (two tokens per
+//     lane), phi(K) is formed in float32 (row max / sum through LDS) and
+//     rounded to bf16, and phi(K)^T and V^T are written to LDS with the
+//     token index contiguous, two tokens per 32-bit word;
+//  2. MFMA 16x16x32 (bf16 in, f32 accumulate) forms h_j^T[c][r] =
+//     sum_t V[t][c] phi(K)[t][r] for the 4 blocks at once, so every lane holds
+//     the same (c, r) of the 4 blocks and writes them as one 8-byte word: the
+//     output layout hx[bh][j/4][c*d + r][j%4] gives the linear-branch GEMM
+//     its k operand (4 consecutive key blocks) contiguous;
+//  3. z_j[r] (from the same bf16 phi values) goes to column d*d + r;
+//  4. the V^T tile of each block is copied to vt[bh][j][c][t] for the sparse
+//     kernel, whose P.V product needs the token index contiguous.
+// Tokens past N and blocks past Nb are zero in LDS, so they add nothing.
+//
+// f32 path: one workgroup per key block, plain FMA loops, hx[bh][j][c*d + r].
+#include "sla_internal.h"
+#include "dev_common.h"
+
+namespace sla {
+namespace {
+
+template <int D>
+struct HzCfg {
+  static constexpr int TS = 72;            // LDS row stride in tokens (144 B, 16-B aligned)
+  static constexpr int CHUNKS = D / 8;     // 16-byte chunks per token row
+  static constexpr int CPT = CHUNKS / 8;   // chunks per thread (8 chunk groups)
+  static constexpr int NN = D * D + D;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
+                                                 const uint16_t* __restrict__ V,
+                                                 uint16_t* __restrict__ hx,
+                                                 uint16_t* __restrict__ vt, int N, int Nb,
+                                                 int Nb4) {
+  using C = HzCfg<D>;
+  constexpr int TS = C::TS, CPT = C::CPT, NN = C::NN;
+  __shared__ __attribute__((aligned(16))) uint16_t kT[4][D][TS];
+  __shared__ __attribute__((aligned(16))) uint16_t vT[4][D][TS];
+  __shared__ float red[8][64];
+  __shared__ float tstat[64];
+
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.y;
+  const int jq = blockIdx.x;        // group of 4 key blocks
+  const int tp = tid & 31;          // token pair
+  const int cg = tid >> 5;          // chunk group 0..7
+  const uint16_t* Kb = K + (size_t)bh * N * D;
+  const uint16_t* Vb = V + (size_t)bh * N * D;
+
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = 4 * jq + jj;
+    uint4 kr[2][CPT], vr[2][CPT];
+    bool valid[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = j * kBlock + 2 * tp + u;
+      valid[u] = (j < Nb) && (t < N);
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int ch = cg * CPT + q;
+        if (valid[u]) {
+          kr[u][q] = *reinterpret_cast<const uint4*>(Kb + (size_t)t * D + ch * 8);
+          vr[u][q] = *reinterpret_cast<const uint4*>(Vb + (size_t)t * D + ch * 8);
+        } else {
+          kr[u][q] = make_uint4(0, 0, 0, 0);
+          vr[u][q] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+    // phi(K) row statistics: max then sum of exp over the D features
+    float x[2][CPT * 8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const uint32_t w[4] = {kr[u][q].x, kr[u][q].y, kr[u][q].z, kr[u][q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[u][q * 8 + 2 * e] = bf_lo(w[e]);
+          x[u][q * 8 + 2 * e + 1] = bf_hi(w[e]);
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < CPT * 8; ++e) m = fmaxf(m, x[u][e]);
+      red[cg][2 * tp + u] = m;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float m = red[0][tid];
+#pragma unroll
+      for (int g = 1; g < 8; ++g) m = fmaxf(m, red[g][tid]);
+      tstat[tid] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float m = tstat[2 * tp + u];
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPT * 8; ++e) {
+        x[u][e] = __expf(x[u][e] - m);
+        s += x[u][e];
+      }
+      red[cg][2 * tp + u] = s;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float s = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) s += red[g][tid];
+      tstat[tid] = 1.0f / s;
+    }
+    __syncthreads();
+    const float inv0 = valid[0] ? tstat[2 * tp] : 0.f;
+    const float inv1 = valid[1] ? tstat[2 * tp + 1] : 0.f;
+    // transposed stores: word (token 2tp, token 2tp+1) of each feature
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int f0 = (cg * CPT + q) * 8;
+      const uint32_t v0[4] = {vr[0][q].x, vr[0][q].y, vr[0][q].z, vr[0][q].w};
+      const uint32_t v1[4] = {vr[1][q].x, vr[1][q].y, vr[1][q].z, vr[1][q].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t kw = pack_bf2(x[0][q * 8 + e] * inv0, x[1][q * 8 + e] * inv1);
+        *reinterpret_cast<uint32_t*>(&kT[jj][f0 + e][2 * tp]) = kw;
+        const uint32_t a = (e & 1) ? (v0[e >> 1] >> 16) : (v0[e >> 1] & 0xffffu);
+        const uint32_t b = (e & 1) ? (v1[e >> 1] >> 16) : (v1[e >> 1] & 0xffffu);
+        *reinterpret_cast<uint32_t*>(&vT[jj][f0 + e][2 * tp]) = a | (b << 16);
+      }
+    }
+    // red/tstat are reused by the next block only after this barrier
+    __syncthreads();
+  }
+
+  // ---- h_j^T[c][r] for the 4 blocks, MFMA 16x16x32
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  constexpr int CT = D / 16;            // c tiles
+  constexpr int CT_PER_WAVE = CT / 4;   // 2 for D=128, 1 for D=64
+  uint16_t* hxg = hx + ((size_t)bh * Nb4 + jq) * NN * 4;
+  for (int cti = 0; cti < CT_PER_WAVE; ++cti) {
+    const int ct = wave * CT_PER_WAVE + cti;
+    uint4 a[4][2];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        a[jj][u] = *reinterpret_cast<const uint4*>(&vT[jj][16 * ct + l16][32 * u + 8 * g]);
+    for (int rh = 0; rh < D / 64; ++rh) {
+      f32x4 acc[4][4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[rt][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * (4 * rh + rt) + l16;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint4 b = *reinterpret_cast<const uint4*>(&kT[jj][r][32 * u + 8 * g]);
+            acc[rt][jj] = mfma_bf16(a[jj][u], b, acc[rt][jj]);
+          }
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * (4 * rh + rt) + l16;
+#pragma unroll
+        for (int reg = 0; reg < 4; ++reg) {
+          const int c = 16 * ct + 4 * g + reg;
+          uint2 w;
+          w.x = pack_bf2(acc[rt][0][reg], acc[rt][1][reg]);
+          w.y = pack_bf2(acc[rt][2][reg], acc[rt][3][reg]);
+          *reinterpret_cast<uint2*>(hxg + ((size_t)c * D + r) * 4) = w;
+        }
+      }
+    }
+  }
+  // ---- z_j[r] = sum_t phi(K)[t][r] over the same bf16 values
+  if (tid < D) {
+    float z[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float s = 0.f;
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&kT[jj][tid][8 * t8]);
+        s += bf_lo(w.x) + bf_hi(w.x) + bf_lo(w.y) + bf_hi(w.y) + bf_lo(w.z) + bf_hi(w.z) +
+             bf_lo(w.w) + bf_hi(w.w);
+      }
+      z[jj] = s;
+    }
+    uint2 w;
+    w.x = pack_bf2(z[0], z[1]);
+    w.y = pack_bf2(z[2], z[3]);
+    *reinterpret_cast<uint2*>(hxg + ((size_t)D * D + tid) * 4) = w;
+  }
+  // ---- V^T tiles for the sparse kernel
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = 4 * jq + jj;
+    if (j >= Nb) break;
+    uint16_t* dst = vt + ((size_t)bh * Nb + j) * D * kBlock;
+    for (int x = tid; x < D * 8; x += 256) {
+      const int c = x >> 3, ch = x & 7;
+      *reinterpret_cast<uint4*>(dst + c * kBlock + ch * 8) =
+          *reinterpret_cast<const uint4*>(&vT[jj][c][ch * 8]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- f32 path
+__global__ __launch_bounds__(256) void k_hz_f32(const float* __restrict__ K,
+                                                const float* __restrict__ V,
+                                                float* __restrict__ hx, int N, int d, int Nb) {
+  extern __shared__ float sm[];
+  float* phk = sm;               // [64][d]
+  float* vs = sm + kBlock * d;   // [64][d]
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.y, j = blockIdx.x;
+  const int NN = d * d + d;
+  const float* Kb = K + ((size_t)bh * N + (size_t)j * kBlock) * d;
+  const float* Vb = V + ((size_t)bh * N + (size_t)j * kBlock) * d;
+  const int nt = min(kBlock, N - j * kBlock);
+  for (int x = tid; x < kBlock * d; x += 256) {
+    const int t = x / d;
+    phk[x] = t < nt ? Kb[x] : 0.f;
+    vs[x] = t < nt ? Vb[x] : 0.f;
+  }
+  __syncthreads();
+  if (tid < kBlock) {
+    float* row = phk + tid * d;
+    if (tid < nt) {
+      float m = -INFINITY;
+      for (int c = 0; c < d; ++c) m = fmaxf(m, row[c]);
+      float s = 0.f;
+      for (int c = 0; c < d; ++c) {
+        row[c] = expf(row[c] - m);
+        s += row[c];
+      }
+      const float inv = 1.0f / s;
+      for (int c = 0; c < d; ++c) row[c] *= inv;
+    }
+  }
+  __syncthreads();
+  float* out = hx + ((size_t)bh * Nb + j) * NN;
+  for (int x = tid; x < d * d; x += 256) {
+    const int c = x / d, r = x % d;
+    float s = 0.f;
+    for (int t = 0; t < kBlock; ++t) s = fmaf(vs[t * d + c], phk[t * d + r], s);
+    out[x] = s;  // x = c*d + r
+  }
+  for (int r = tid; r < d; r += 256) {
+    float s = 0.f;
+    for (int t = 0; t < kBlock; ++t) s += phk[t * d + r];
+    out[d * d + r] = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w, hipStream_t s) {
+  if (D.bf16) {
+    dim3 grid(D.Nbp / 4, D.BH);
+    if (D.d == 128)
+      hipLaunchKernelGGL(k_hz_bf16<128>, grid, dim3(256), 0, s, (const uint16_t*)K,
+                         (const uint16_t*)V, (uint16_t*)w.hx, w.vt, D.N, D.Nb, D.Nbp / 4);
+    else
+      hipLaunchKernelGGL(k_hz_bf16<64>, grid, dim3(256), 0, s, (const uint16_t*)K,
+                         (const uint16_t*)V, (uint16_t*)w.hx, w.vt, D.N, D.Nb, D.Nbp / 4);
+  } else {
+    dim3 grid(D.Nb, D.BH);
+    const size_t lds = 2 * kBlock * D.d * sizeof(float);
+    hipLaunchKernelGGL(k_hz_f32, grid, dim3(256), lds, s, (const float*)K, (const float*)V,
+                       (float*)w.hx, D.N, D.d, D.Nb);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sla

@@ -1,0 +1,225 @@
+// Host side of the C ABI declared in include/sla.h: argument validation,
+// block counts, workspace carving and the launch order of the five kernels on
+// the caller's stream. No device memory is allocated here and no call
+// synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sla_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validates the problem and derives its sizes; SLA_OK or an error code.
+int make_dims(const sla_problem* p, sla::Dims* D) {
+  if (!p) return fail(SLA_ERR_ARG, "problem is NULL");
+  if (p->B < 1 || p->H < 1 || p->N < 1)
+    return fail(SLA_ERR_ARG, "B, H and N must be >= 1 (got %d, %d, %d)", p->B, p->H, p->N);
+  if (p->dtype != SLA_F32 && p->dtype != SLA_BF16)
+    return fail(SLA_ERR_ARG, "unknown dtype %d", p->dtype);
+  if (p->quant != SLA_QUANT_NONE && p->quant != SLA_QUANT_I8QK_F8PV)
+    return fail(SLA_ERR_ARG, "unknown quant mode %d", p->quant);
+  if (p->reserved != 0) return fail(SLA_ERR_ARG, "reserved field must be 0");
+  if (!(p->kh >= 0.0 && p->kh <= 1.0) || !(p->kl >= 0.0 && p->kl <= 1.0))
+    return fail(SLA_ERR_ARG, "kh and kl must lie in [0, 1] (got %g, %g)", p->kh, p->kl);
+  if (p->d != 64 && p->d != 128) return fail(SLA_ERR_UNSUPPORTED, "head dim %d not built", p->d);
+  if (p->proj_head_stride != 0 && p->proj_head_stride != p->d * p->d)
+    return fail(SLA_ERR_ARG, "proj_head_stride must be 0 or d*d");
+  if ((long long)p->B * p->H > 65535)
+    return fail(SLA_ERR_UNSUPPORTED, "B*H = %lld exceeds 65535", (long long)p->B * p->H);
+  const int Nb = (p->N + sla::kBlock - 1) / sla::kBlock;
+  if (Nb > sla::kMaxNb) return fail(SLA_ERR_UNSUPPORTED, "N = %d exceeds %d tokens", p->N, sla::kMaxNb * sla::kBlock);
+  int n_h = p->kh <= 0.0 ? 0 : (int)floor(p->kh * Nb + 1e-9);
+  if (p->kh > 0.0 && n_h < 1) n_h = 1;
+  if (n_h > Nb) n_h = Nb;
+  const int n_l = (int)floor(p->kl * Nb + 1e-9);
+  if (n_h + n_l > Nb)
+    return fail(SLA_ERR_ARG, "kh and kl select %d + %d > %d blocks per row", n_h, n_l, Nb);
+  if (p->quant == SLA_QUANT_I8QK_F8PV && p->dtype != SLA_BF16)
+    return fail(SLA_ERR_UNSUPPORTED, "the 8-bit sparse branch needs bf16 inputs");
+  if (p->quant == SLA_QUANT_I8QK_F8PV)
+    return fail(SLA_ERR_UNSUPPORTED, "the 8-bit sparse branch is not built");
+  D->B = p->B;
+  D->H = p->H;
+  D->N = p->N;
+  D->d = p->d;
+  D->BH = p->B * p->H;
+  D->Nb = Nb;
+  D->n_h = n_h;
+  D->n_l = n_l;
+  D->Nbp = (Nb + 31) / 32 * 32;
+  D->NN = p->d * p->d + p->d;
+  D->bf16 = p->dtype == SLA_BF16;
+  D->quant = p->quant == SLA_QUANT_I8QK_F8PV;
+  return SLA_OK;
+}
+
+}  // namespace
+
+namespace sla {
+
+size_t carve(const Dims& D, void* base, Work* w) {
+  size_t off = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = b ? (void*)(b + off) : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  const size_t BH = (size_t)D.BH;
+  Work x = {};
+  x.pooled_q = (double*)take(BH * D.Nb * D.d * sizeof(double));
+  x.pooled_k = (double*)take(BH * D.Nb * D.d * sizeof(double));
+  if (D.bf16) {
+    x.hx = take(BH * (D.Nbp / 4) * D.NN * 4 * sizeof(uint16_t));
+    x.Hx = take(BH * D.Nb * D.NN * sizeof(uint16_t));
+    x.vt = (uint16_t*)take(BH * D.Nb * D.d * kBlock * sizeof(uint16_t));
+  } else {
+    x.hx = take(BH * D.Nb * D.NN * sizeof(float));
+    x.Hx = take(BH * D.Nb * D.NN * sizeof(float));
+  }
+  if (D.quant) {
+    x.q8 = (int8_t*)take(BH * D.N * D.d);
+    x.k8 = (int8_t*)take(BH * D.N * D.d);
+    x.qs = (float*)take(BH * D.Nb * sizeof(float));
+    x.ks = (float*)take(BH * D.Nb * sizeof(float));
+    x.v8t = (uint8_t*)take(BH * D.Nb * D.d * kBlock);
+    x.vs = (float*)take(BH * D.Nb * sizeof(float));
+  }
+  if (w) *w = x;
+  return off;
+}
+
+}  // namespace sla
+
+extern "C" {
+
+int sla_version(void) { return (1 << 16) | 0; }
+
+const char* sla_status_str(int status) {
+  switch (status) {
+    case SLA_OK: return "SLA_OK";
+    case SLA_ERR_ARG: return "SLA_ERR_ARG: invalid argument";
+    case SLA_ERR_UNSUPPORTED: return "SLA_ERR_UNSUPPORTED: valid request outside what is built";
+    case SLA_ERR_WORKSPACE: return "SLA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case SLA_ERR_HIP: return "SLA_ERR_HIP: HIP runtime error";
+    default: return "unknown sla status";
+  }
+}
+
+const char* sla_last_error(void) { return g_err; }
+
+int sla_block_counts(const sla_problem* p, int32_t* nb, int32_t* n_h, int32_t* n_l) {
+  sla::Dims D;
+  sla_problem q;
+  if (!p) return fail(SLA_ERR_ARG, "problem is NULL");
+  // counts do not depend on what is built: validate with a buildable stand-in
+  q = *p;
+  q.quant = SLA_QUANT_NONE;
+  if (q.d != 64 && q.d != 128) q.d = 64;
+  q.proj_head_stride = 0;
+  const int rc = make_dims(&q, &D);
+  if (rc != SLA_OK) return rc;
+  if (nb) *nb = D.Nb;
+  if (n_h) *n_h = D.n_h;
+  if (n_l) *n_l = D.n_l;
+  g_err[0] = 0;
+  return SLA_OK;
+}
+
+int sla_workspace_bytes(const sla_problem* p, size_t* bytes) {
+  sla::Dims D;
+  const int rc = make_dims(p, &D);
+  if (rc != SLA_OK) return rc;
+  if (!bytes) return fail(SLA_ERR_ARG, "bytes is NULL");
+  *bytes = sla::carve(D, nullptr, nullptr);
+  g_err[0] = 0;
+  return SLA_OK;
+}
+
+int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const void* V,
+                      const float* proj_q, const float* proj_k, const float* alpha,
+                      const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
+                      size_t workspace_bytes, void* stream, const sla_debug* dbg) {
+  sla::Dims D;
+  int rc = make_dims(p, &D);
+  if (rc != SLA_OK) return rc;
+  if (!Q || !K || !V || !alpha || !O) return fail(SLA_ERR_ARG, "Q, K, V, alpha and O must not be NULL");
+  if (!mask_in && (!proj_q || !proj_k))
+    return fail(SLA_ERR_ARG, "proj_q and proj_k are required when mask_in is NULL");
+  if (!mask_in && !mask_out) return fail(SLA_ERR_ARG, "mask_out may be NULL only when mask_in is given");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return fail(SLA_ERR_ARG, "Q, K, V and O must be 16-byte aligned");
+  if ((proj_q && !aligned(proj_q, 4)) || (proj_k && !aligned(proj_k, 4)) || !aligned(alpha, 4))
+    return fail(SLA_ERR_ARG, "proj_q, proj_k and alpha must be 4-byte aligned");
+  if (dbg && ((dbg->pooled_q && !aligned(dbg->pooled_q, 8)) || (dbg->pooled_k && !aligned(dbg->pooled_k, 8)) ||
+              (dbg->logits && !aligned(dbg->logits, 8)) || (dbg->o_s && !aligned(dbg->o_s, 16)) ||
+              (dbg->o_l && !aligned(dbg->o_l, 16))))
+    return fail(SLA_ERR_ARG, "debug buffers must be aligned (8 bytes float64, 16 bytes float32)");
+  const size_t need = sla::carve(D, nullptr, nullptr);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    return fail(SLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu at %p)",
+                need, workspace_bytes, workspace);
+  sla::Work w;
+  sla::carve(D, workspace, &w);
+  hipStream_t s = (hipStream_t)stream;
+  const int proj_hs = p->proj_head_stride;
+  (void)hipGetLastError();  // a stale error from earlier work is not ours to report
+
+#define SLA_LAUNCH(call, what)                                                            \
+  do {                                                                                    \
+    hipError_t e_ = (call);                                                               \
+    if (e_ != hipSuccess) return fail(SLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e_)); \
+  } while (0)
+
+  const int8_t* mask = mask_in;
+  if (!mask_in) {
+    SLA_LAUNCH(sla::launch_pool_proj(D, Q, K, proj_q, proj_k, proj_hs, w.pooled_q, w.pooled_k, s),
+               "pool/proj kernel");
+    SLA_LAUNCH(sla::launch_select(D, w.pooled_q, w.pooled_k, mask_out, dbg ? dbg->logits : nullptr, s),
+               "score/select kernel");
+    if (dbg && dbg->pooled_q)
+      SLA_LAUNCH(hipMemcpyAsync(dbg->pooled_q, w.pooled_q, (size_t)D.BH * D.Nb * D.d * sizeof(double),
+                                hipMemcpyDeviceToDevice, s), "debug copy");
+    if (dbg && dbg->pooled_k)
+      SLA_LAUNCH(hipMemcpyAsync(dbg->pooled_k, w.pooled_k, (size_t)D.BH * D.Nb * D.d * sizeof(double),
+                                hipMemcpyDeviceToDevice, s), "debug copy");
+    mask = mask_out;
+  }
+  SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
+  SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
+  float* dos = dbg ? dbg->o_s : nullptr;
+  float* dol = dbg ? dbg->o_l : nullptr;
+  if (D.bf16)
+    SLA_LAUNCH(sla::launch_sparse(D, Q, K, mask, alpha, w, O, dos, dol, s), "sparse kernel");
+  else
+    SLA_LAUNCH(sla::launch_sparse_f32(D, Q, K, V, mask, alpha, w, O, dos, dol, s), "sparse kernel");
+#undef SLA_LAUNCH
+  g_err[0] = 0;
+  return SLA_OK;
+}
+
+int sla_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                const float* proj_q, const float* proj_k, const float* alpha,
+                const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return sla_forward_debug(p, Q, K, V, proj_q, proj_k, alpha, mask_in, O, mask_out, workspace,
+                           workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal declarations shared by the host dispatcher and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sla.h"
+
+namespace sla {
+
+constexpr int kBlock = 64;        // tokens per query / key block
+constexpr int kMaxNb = 4096;      // largest block count the selection kernel handles
+
+// Sizes derived from an sla_problem.
+struct Dims {
+  int B, H, N, d, BH, Nb;
+  int n_h, n_l;
+  int Nbp;          // Nb rounded up to a multiple of 32 (K extent of the linear GEMM)
+  int NN;           // d*d + d: one h_j (stored transposed, c-major) followed by z_j
+  bool bf16;
+  bool quant;
+};
+
+// Device workspace regions, carved from the caller's buffer.
+struct Work {
+  double* pooled_q;   // [BH, Nb, d]
+  double* pooled_k;   // [BH, Nb, d]
+  void* hx;           // bf16: [BH, Nbp/4, NN, 4] (four key blocks interleaved per column)
+                      // f32:  [BH, Nb, NN]
+  void* Hx;           // [BH, Nb, NN] per query block: H_i^T (c-major) then Z_i; bf16 or f32
+  uint16_t* vt;       // bf16 only: [BH, Nb, d, 64] V^T of every key block (zero past N)
+  int8_t* q8;         // quant only: [BH, N, d] int8 Q
+  int8_t* k8;         // quant only: [BH, N, d] int8 K
+  float* qs;          // quant only: [BH, Nb] per-block scales of Q
+  float* ks;          // quant only: [BH, Nb] per-block scales of K
+  uint8_t* v8t;       // quant only: [BH, Nb, d, 64] fp8 e4m3 V^T
+  float* vs;          // quant only: [BH, Nb] per-block scales of V
+};
+
+size_t carve(const Dims& D, void* base, Work* w);  // returns bytes needed (base may be NULL)
+
+// ---- launchers (each enqueues one or more kernels on `s`, returns hipError_t)
+hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const float* proj_q,
+                            const float* proj_k, int proj_hs, double* pq, double* pk,
+                            hipStream_t s);
+hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8_t* mask,
+                         double* dbg_logits, hipStream_t s);
+hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w, hipStream_t s);
+hipError_t launch_linear(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
+hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const int8_t* mask,
+                         const float* alpha, const Work& w, void* O, float* dbg_os,
+                         float* dbg_ol, hipStream_t s);
+hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,
+                             const int8_t* mask, const float* alpha, const Work& w, void* O,
+                             float* dbg_os, float* dbg_ol, hipStream_t s);
+hipError_t launch_quant_qk(const Dims& D, const void* Q, const void* K, const Work& w,
+                           hipStream_t s);
+
+}  // namespace sla

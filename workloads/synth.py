@@ -5,7 +5,7 @@ these inputs stand in for them with the same shapes and a calibrated structure):
 
 * tokens are laid out in raster order n = (t*Hg + y)*Wg + x over the latent grid;
 * p_n is a 3-axis sin/cos position embedding: the d channels are split into
-  (d - 2*(d//3), d//3, d//3) for (t, y, x); an axis with m channels uses the
+  (d - 4*(d//6), 2*(d//6), 2*(d//6)) for (t, y, x); an axis with m channels uses the
   frequencies w_k = 10000^(-2k/m), k < m/2, and emits sin(pos*w_k) then
   cos(pos*w_k), so |p_n|^2 = d/2;
 * q_n = A_q p_n + 0.5*eps and k_n = A_k p_n + 0.5*eps' with independent
@@ -44,8 +44,8 @@ def _rng(seed: int, stream: int, b: int = 0, h: int = 0) -> np.random.Generator:
 def sincos_posemb(grid, d: int, N: Optional[int] = None) -> np.ndarray:
     """[N, d] float64 3-axis sin/cos embedding of a (t, h, w) grid in raster order."""
     T, Hg, Wg = grid
-    dh = d // 3
-    dw = d // 3
+    dh = 2 * (d // 6)
+    dw = 2 * (d // 6)
     dt = d - dh - dw
     n = np.arange(T * Hg * Wg if N is None else N)
     t = n // (Hg * Wg)
