@@ -80,13 +80,19 @@ typedef struct {
  * logits:             [B, H, Nb, Nb] float64, pool(Q) pool(K)^T / sqrt(d);
  * o_s, o_l:           [B, H, N, d] float32, the sparse and linear branch outputs
  *                     before the mix. pooled_q/pooled_k/logits are only written
- *                     when the mask is computed (mask_in == NULL). */
+ *                     when the mask is computed (mask_in == NULL).
+ * events:             caller-owned hipEvent_t handles (or NULL), recorded on
+ *                     `stream`: events[0] before the pooling kernel and
+ *                     events[k] after kernel k = 1 pooling, 2 scores/selection,
+ *                     3 h/z, 4 marginal sums, 5 sparse attention + mix. With
+ *                     mask_in, events 0-2 are recorded back to back. */
 typedef struct {
   double* pooled_q;
   double* pooled_k;
   double* logits;
   float*  o_s;
   float*  o_l;
+  void*   events[6];
 } sla_debug;
 
 /* Block counts of a problem (host only, no device work).

@@ -9,8 +9,9 @@ fused into its epilogue. This package is the argument-marshalling binding.
 """
 
 from ._binding import (  # noqa: F401
-    LIB_PATH, SLAError, block_counts, forward, load_library, make_problem, workspace_bytes,
+    LIB_PATH, HipEvents, Plan, SLAError, block_counts, forward, load_library, make_problem,
+    workspace_bytes,
 )
 
-__all__ = ["forward", "block_counts", "workspace_bytes", "load_library", "make_problem",
-           "SLAError", "LIB_PATH"]
+__all__ = ["forward", "Plan", "HipEvents", "block_counts", "workspace_bytes", "load_library",
+           "make_problem", "SLAError", "LIB_PATH"]

@@ -27,7 +27,8 @@ class Problem(ctypes.Structure):
 
 class Debug(ctypes.Structure):
     _fields_ = [("pooled_q", ctypes.c_void_p), ("pooled_k", ctypes.c_void_p),
-                ("logits", ctypes.c_void_p), ("o_s", ctypes.c_void_p), ("o_l", ctypes.c_void_p)]
+                ("logits", ctypes.c_void_p), ("o_s", ctypes.c_void_p), ("o_l", ctypes.c_void_p),
+                ("events", ctypes.c_void_p * 6)]
 
 
 class SLAError(RuntimeError):
@@ -175,3 +176,72 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if debug:
         return out, mask, dbg_t
     return out, mask
+
+
+class Plan:
+    """A prepared sla_forward call: the problem, the device buffers and the
+    ctypes argument list are built once, so repeated calls only enqueue work
+    (used by the benchmark and by callers that run the same shape often)."""
+
+    def __init__(self, q, k, v, proj_q, proj_k, alpha, kh, kl, mask_in=None, quant=False):
+        lib = load_library()
+        B, H, N, d = q.shape
+        Nb = (N + 63) // 64
+        dev = q.device
+        hs = d * d if (proj_q is not None and proj_q.dim() == 3) else 0
+        self.problem = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32",
+                                    kh, kl, quant, hs)
+        self.nbytes = workspace_bytes(self.problem)
+        self.workspace = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(q)
+        self.mask = None if mask_in is not None else torch.empty((B, H, Nb, Nb), dtype=torch.int8,
+                                                                 device=dev)
+        self._keep = (q, k, v, proj_q, proj_k, alpha, mask_in)
+        self.device = dev
+        self.lib = lib
+        self._args = [ctypes.byref(self.problem), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
+                      _ptr(proj_k), _ptr(alpha), _ptr(mask_in), _ptr(self.out), _ptr(self.mask),
+                      _ptr(self.workspace), ctypes.c_size_t(self.nbytes)]
+        self.dims = (B, H, N, d, Nb)
+
+    def run(self, events=None):
+        """Enqueues one forward pass on torch's current stream. `events`: optional
+        sequence of 6 raw hipEvent_t handles recorded around the five kernels."""
+        stream = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+        if events is None:
+            rc = self.lib.sla_forward(*self._args, stream)
+        else:
+            dbg = Debug(None, None, None, None, None, (ctypes.c_void_p * 6)(*events))
+            rc = self.lib.sla_forward_debug(*self._args, stream, ctypes.byref(dbg))
+        _check(rc)
+        return self.out
+
+
+class HipEvents:
+    """Raw HIP events through the HIP runtime (for per-kernel timing)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))

@@ -73,3 +73,45 @@ __device__ __forceinline__ float group4_sum(float v) {
 }
 
 }  // namespace sla
+
+namespace sla {
+
+typedef short s16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+
+// D += A * B with A: 16x16, B: 16x16 bf16, D: 16x16 f32. Lane l holds
+// A[l%16][4*(l/16) .. +3], B[4*(l/16) .. +3][l%16], D as in mfma_bf16.
+__device__ __forceinline__ f32x4 mfma_bf16_k16(const uint2& a, const uint2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (other counters left alone), gfx9 encoding.
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+// 16-byte asynchronous copy global -> LDS: lane l writes lds_wave_base + 16*l.
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (void __attribute__((address_space(3)))*)lds_wave_base,
+                                   16, 0, 0);
+}
+
+}  // namespace sla
+
+namespace sla {
+
+// s_waitcnt immediate that waits for this wave's LDS (and scalar memory)
+// operations only; vector-memory operations may stay in flight.
+constexpr int kWaitLgkm0 = 0xf | (0x3 << 14) | (0x7 << 4) | (0x0 << 8);
+
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes are
+// complete, then all waves meet. Unlike __syncthreads() it does not wait for
+// outstanding global loads (such as asynchronous global->LDS copies of the next
+// tile), which must be waited for explicitly before their data is read.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+}  // namespace sla

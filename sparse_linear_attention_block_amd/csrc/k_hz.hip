@@ -17,8 +17,10 @@
 //     output layout hx[bh][j/4][c*d + r][j%4] gives the linear-branch GEMM
 //     its k operand (4 consecutive key blocks) contiguous;
 //  3. z_j[r] (from the same bf16 phi values) goes to column d*d + r;
-//  4. the V^T tile of each block is copied to vt[bh][j][c][t] for the sparse
-//     kernel, whose P.V product needs the token index contiguous.
+//  4. the V^T tile of each block is copied to vt for the sparse kernel, whose
+//     P.V product needs the token index contiguous: for each half of the keys
+//     a [d][32] block, keys permuted into that kernel's MFMA k-slot order and
+//     16-byte chunks swizzled against LDS bank conflicts.
 // Tokens past N and blocks past Nb are zero in LDS, so they add nothing.
 //
 // f32 path: one workgroup per key block, plain FMA loops, hx[bh][j][c*d + r].
@@ -209,15 +211,21 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
     w.y = pack_bf2(z[2], z[3]);
     *reinterpret_cast<uint2*>(hxg + ((size_t)D * D + tid) * 4) = w;
   }
-  // ---- V^T tiles for the sparse kernel
+  // ---- V^T tiles for the sparse kernel, in the order its LDS copy wants:
+  // vt[bh][j][kh][c][32] holds the 32 keys 32kh .. 32kh+31 of feature c as four
+  // 16-byte chunks; chunk q carries keys {4q..4q+3, 16+4q..16+4q+3} (the k
+  // slots of one MFMA lane group) and sits at position q ^ ((c >> 1) & 3), so
+  // that 8 lanes reading 8 consecutive rows touch distinct LDS banks.
   for (int jj = 0; jj < 4; ++jj) {
     const int j = 4 * jq + jj;
     if (j >= Nb) break;
     uint16_t* dst = vt + ((size_t)bh * Nb + j) * D * kBlock;
     for (int x = tid; x < D * 8; x += 256) {
-      const int c = x >> 3, ch = x & 7;
-      *reinterpret_cast<uint4*>(dst + c * kBlock + ch * 8) =
-          *reinterpret_cast<const uint4*>(&vT[jj][c][ch * 8]);
+      const int khh = x / (D * 4), rem = x % (D * 4), c = rem >> 2, q = rem & 3;
+      const uint2 lo = *reinterpret_cast<const uint2*>(&vT[jj][c][32 * khh + 4 * q]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&vT[jj][c][32 * khh + 16 + 4 * q]);
+      *reinterpret_cast<uint4*>(dst + ((size_t)khh * D + c) * 32 + 8 * (q ^ ((c >> 1) & 3))) =
+          make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   }
 }

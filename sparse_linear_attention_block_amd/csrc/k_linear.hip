@@ -11,12 +11,10 @@
 //
 // The kernel computes the transpose Hx^T = hx^T M01^T: the hx operand has 4
 // consecutive key blocks per 8-byte word (written so by K3), which is the k
-// layout the MFMA A operand needs; the mask tile is turned into bf16 0/1 once
-// per workgroup in LDS and read as the B operand; each lane then holds 4
-// consecutive n of one query block and stores them as one 8-byte word.
-//
-// Workgroup tile: 256 n x 128 query blocks, 4 waves of 64 n x 128 i each,
-// k steps of 32 key blocks, LDS double-buffered mask tiles.
+// layout the MFMA A operand needs; the mask is first turned into a bf16 0/1
+// indicator (k_indicator) in a layout the GEMM copies straight into LDS and
+// reads as the B operand; each lane then holds 4 consecutive n of one query
+// block and stores them as one 8-byte word.
 #include "sla_internal.h"
 #include "dev_common.h"
 
@@ -25,51 +23,73 @@ namespace {
 
 constexpr int kTN = 256;  // n per workgroup
 constexpr int kTI = 128;  // query blocks per workgroup
-constexpr int kMS = 40;   // LDS row stride of the mask tile (bf16 elements)
 
-__global__ __launch_bounds__(256) void k_linear_bf16(const int8_t* __restrict__ mask,
-                                                     const uint16_t* __restrict__ hx,
-                                                     uint16_t* __restrict__ Hx, int Nb, int Nbp,
-                                                     int NN) {
-  __shared__ __attribute__((aligned(16))) uint16_t ms[2][kTI][kMS];
+__device__ __forceinline__ int xcd_remap(int L, int T) {
+  const int q = T >> 3, rm = T & 7;
+  const int x = L & 7, pos = L >> 3;
+  return x * q + min(x, rm) + pos;
+}
+
+// The marginal indicator M01[i][j] = (Mc[i][j] == 0) as bf16 0/1, one
+// [Nb128][32] slab per 32-key step; chunk q (keys 8q..8q+7 of the step) of row
+// i sits at chunk position q ^ ((i >> 1) & 3), so that 8 lanes reading 8
+// consecutive rows of the slab hit distinct LDS banks. Rows >= Nb and keys >=
+// Nb are 0.
+__global__ __launch_bounds__(256) void k_indicator(const int8_t* __restrict__ mask,
+                                                   uint16_t* __restrict__ ind, int Nb, int Nbp,
+                                                   int Nb128) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int s = blockIdx.y, bh = blockIdx.z;
+  const int q = t & 3, i = t >> 2;
+  if (i >= Nb128) return;
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int j = 32 * s + 8 * q + 2 * e + hh;
+      if (i < Nb && j < Nb && mask[((size_t)bh * Nb + i) * Nb + j] == 0) v |= 0x3f80u << (16 * hh);
+    }
+    w[e] = v;
+  }
+  uint16_t* dst = ind + (((size_t)bh * (Nbp / 32) + s) * Nb128 + i) * 32 + 8 * (q ^ ((i >> 1) & 3));
+  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Hx^T = hx^T M01^T for one (batch, head): workgroup tile 256 n x 128 query
+// blocks, wave w owns n0 + 64w .. +63 against all 128 rows, k steps of 32 key
+// blocks. The hx operand (4 key blocks per 8-byte word, as written by the h/z
+// kernel) goes straight from global memory to registers one step ahead; the
+// indicator slab of a step arrives in LDS by direct asynchronous copies,
+// double-buffered, one LDS barrier per step. Workgroups are remapped so that
+// the row tiles of one n range run back to back on one XCD and share hx in L2.
+__global__ __launch_bounds__(256, 2) void k_linear_bf16(const uint16_t* __restrict__ ind,
+                                                        const uint16_t* __restrict__ hx,
+                                                        uint16_t* __restrict__ Hx, int Nb, int Nbp,
+                                                        int Nb128, int NN, int ntn, int nti) {
+  __shared__ __attribute__((aligned(16))) uint16_t bA[kTI * 32];
+  __shared__ __attribute__((aligned(16))) uint16_t bB[kTI * 32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.z;
-  const int i0 = blockIdx.y * kTI;
-  const int n0 = blockIdx.x * kTN + wave * 64;
-  const int Nb4 = Nbp / 4;
-  const int8_t* mrow = mask + (size_t)bh * Nb * Nb;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int it = id % nti;
+  const int rest = id / nti;
+  const int nt = rest % ntn, bh = rest / ntn;
+  const int i0 = it * kTI;
+  const int n0 = nt * kTN + wave * 64;
+  const int S = Nbp / 32, Nb4 = Nbp / 4;
+  const uint16_t* indb = ind + ((size_t)bh * S * Nb128 + i0) * 32;
   const uint16_t* hb = hx + (size_t)bh * Nb4 * NN * 4;
 
-  // staging assignment: row si, 16 key blocks starting at 16*sh
-  const int si = tid >> 1, sh = tid & 1;
-  auto stage = [&](int s, int buf) {
-    const int i = i0 + si;
-    uint32_t w[8];
+  auto issue = [&](int s, uint16_t* dst) {  // 8 KB slab: two 16-byte copies per lane
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j0 = 32 * s + 16 * sh + 2 * e;
-      uint32_t lo = 0, hi = 0;
-      if (i < Nb && j0 < Nb && mrow[(size_t)i * Nb + j0] == 0) lo = 0x3f80u;
-      if (i < Nb && j0 + 1 < Nb && mrow[(size_t)i * Nb + j0 + 1] == 0) hi = 0x3f80u;
-      w[e] = lo | (hi << 16);
+    for (int u = 0; u < 2; ++u) {
+      const int G = 64 * (4 * u + wave) + lane;
+      load_lds16(indb + (size_t)s * Nb128 * 32 + (size_t)G * 8, dst + 512 * (4 * u + wave));
     }
-    uint4* dst = reinterpret_cast<uint4*>(&ms[buf][si][16 * sh]);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   };
-
-  f32x4 acc[4][8];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int S = Nbp / 32;
-  for (int s = 0; s < S; ++s) {
-    stage(s, s & 1);
-    __syncthreads();
-    uint4 a[4];
+  auto loadA = [&](int s, uint4* a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int n = n0 + 16 * mt + l16;
@@ -82,16 +102,39 @@ __global__ __launch_bounds__(256) void k_linear_bf16(const int8_t* __restrict__ 
         a[mt] = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+
+  f32x4 acc[4][8];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const uint4 b = *reinterpret_cast<const uint4*>(&ms[s & 1][16 * nt + l16][8 * g]);
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_bf16(a[mt], b, acc[mt][nt]);
+    for (int n2 = 0; n2 < 8; ++n2) acc[mt][n2] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int s, const uint16_t* cur, uint16_t* nxt, const uint4* a, uint4* an) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // slab s and operand s have landed
+    lds_barrier();
+    if (s + 1 < S) {
+      issue(s + 1, nxt);
+      loadA(s + 1, an);
     }
+#pragma unroll
+    for (int n2 = 0; n2 < 8; ++n2) {
+      const int row = 16 * n2 + l16;
+      const uint4 b = *reinterpret_cast<const uint4*>(cur + row * 32 + 8 * (g ^ ((row >> 1) & 3)));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][n2] = mfma_bf16(a[mt], b, acc[mt][n2]);
+    }
+  };
+  uint4 aA[4], aB[4];
+  issue(0, bA);
+  loadA(0, aA);
+  for (int s = 0; s < S; s += 2) {
+    step(s, bA, bB, aA, aB);
+    if (s + 1 < S) step(s + 1, bB, bA, aB, aA);
   }
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    const int i = i0 + 16 * nt + l16;
+  for (int n2 = 0; n2 < 8; ++n2) {
+    const int i = i0 + 16 * n2 + l16;
     if (i >= Nb) continue;
     uint16_t* orow = Hx + ((size_t)bh * Nb + i) * NN;
 #pragma unroll
@@ -99,8 +142,8 @@ __global__ __launch_bounds__(256) void k_linear_bf16(const int8_t* __restrict__ 
       const int n = n0 + 16 * mt + 4 * g;
       if (n < NN) {
         uint2 w;
-        w.x = pack_bf2(acc[mt][nt][0], acc[mt][nt][1]);
-        w.y = pack_bf2(acc[mt][nt][2], acc[mt][nt][3]);
+        w.x = pack_bf2(acc[mt][n2][0], acc[mt][n2][1]);
+        w.y = pack_bf2(acc[mt][n2][2], acc[mt][n2][3]);
         *reinterpret_cast<uint2*>(orow + n) = w;
       }
     }
@@ -124,11 +167,18 @@ __global__ __launch_bounds__(256) void k_linear_f32(const int8_t* __restrict__ m
 
 }  // namespace
 
+hipError_t launch_indicator(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s) {
+  dim3 grid(D.Nb128 * 4 / 256, D.Nbp / 32, D.BH);
+  hipLaunchKernelGGL(k_indicator, grid, dim3(256), 0, s, mask, w.ind, D.Nb, D.Nbp, D.Nb128);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s) {
   if (D.bf16) {
-    dim3 grid((D.NN + kTN - 1) / kTN, (D.Nb + kTI - 1) / kTI, D.BH);
-    hipLaunchKernelGGL(k_linear_bf16, grid, dim3(256), 0, s, mask, (const uint16_t*)w.hx,
-                       (uint16_t*)w.Hx, D.Nb, D.Nbp, D.NN);
+    const int ntn = (D.NN + kTN - 1) / kTN, nti = D.Nb128 / kTI;
+    hipLaunchKernelGGL(k_linear_bf16, dim3(D.BH * ntn * nti), dim3(256), 0, s,
+                       (const uint16_t*)w.ind, (const uint16_t*)w.hx, (uint16_t*)w.Hx, D.Nb,
+                       D.Nbp, D.Nb128, D.NN, ntn, nti);
   } else {
     dim3 grid((D.NN + 255) / 256, D.Nb, D.BH);
     hipLaunchKernelGGL(k_linear_f32, grid, dim3(256), 0, s, mask, (const float*)w.hx,

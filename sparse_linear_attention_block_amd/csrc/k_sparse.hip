@@ -12,19 +12,25 @@
 //
 // bf16 path. The critical list of the row is compacted from the mask into LDS
 // with wave ballots (the lookup table of the SLA explainer, section 2.3, built
-// on chip per query block). Each of the 4 waves owns 16 queries. Per critical
-// key tile (64 keys) the workgroup stages K (row-major) and V^T (from K3) in
-// LDS, double-buffered with register prefetch of the next tile, then:
-//   S^T = K Q^T    MFMA 16x16x32: K rows as A, the wave's Q (registers) as B;
-//                  each lane gets 4 consecutive keys of one query;
-//   online softmax in the exp2 domain, row max over the 4 lane groups;
-//   O^T += V^T P^T MFMA 16x16x32: P^T never leaves registers - the 8 k slots
-//                  of a lane are its keys {4g..4g+3, 16+4g..16+4g+3} and the
-//                  V^T operand is read from LDS in the same key order.
-// Epilogue: O_s = acc / l; phi(Q) from the Q registers (softmax over the d
-// features in f32, rounded to bf16); num^T = H_i^T phi(Q)^T on MFMA with H_i^T
-// read straight from K4's output; den = phi(Q) . Z_i; O_l = num / den;
-// O = alpha O_s + (1 - alpha) O_l, rows past N not written.
+// on chip per query block). One workgroup of 4 waves owns a query block; the
+// waves split the 64 keys of a tile into two halves and the 64 queries into
+// two halves. Tiles arrive by direct global->LDS copies (no register
+// staging), double-buffered one tile ahead, one barrier per tile. Per tile:
+//   S^T = K Q^T    MFMA 16x16x32, the wave's 32 keys as A (row-swizzled LDS),
+//                  its 32 queries (registers) as B; a lane gets 4 keys of one
+//                  query per 16-key tile;
+//   online softmax per wave against a reference max that is only raised
+//                  when some score exceeds it by more than 2^8: the common
+//                  path needs no cross-lane reduction and no rescale (exact:
+//                  softmax does not depend on the reference);
+//   O^T += V^T P^T MFMA 16x16x32 with P^T straight from registers: a lane's 8
+//                  k slots are its keys {4g..4g+3, 16+4g..16+4g+3}, and the h/z
+//                  kernel stored V^T in that key order.
+// The two key halves are combined through LDS (max-rescaled partial sums);
+// each wave then finishes half the features of its 32 queries: O_s = acc / l,
+// phi(Q) (softmax over the features in f32, rounded to bf16), num^T =
+// H_i^T phi(Q)^T on MFMA with H_i^T read from K4's output, den = phi(Q).Z_i,
+// O = alpha O_s + (1 - alpha) O_l, staged in LDS and written as full rows.
 // Workgroups are remapped so that each XCD walks a contiguous range of
 // (batch, head, query block): neighbouring query blocks share most critical
 // key tiles, which then come from the XCD's L2.
@@ -67,224 +73,297 @@ __device__ int compact_row(const int8_t* __restrict__ mrow, int Nb, int8_t value
 
 template <int D>
 struct FaCfg {
-  static constexpr int KS = D + 8;   // K tile row stride (elements), 16-byte aligned rows
-  static constexpr int VS = 64 + 4;  // V^T tile row stride (elements), 8-byte aligned rows
+  static constexpr int C = D / 8;                  // 16-byte chunks per K row
+  static constexpr int TILE = kBlock * D;          // elements of one K (or V^T) tile
+  static constexpr int INSTR = TILE / 8 / 256;     // 16-byte async copies per lane per operand
   static constexpr int NN = D * D + D;
-  static constexpr int KCH = kBlock * D / 8 / 256;  // 16-byte K chunks per thread
-  static constexpr int VCH = D * kBlock / 8 / 256;  // 16-byte V^T chunks per thread
+  static constexpr int KSTEPS = D / 32;
+  static constexpr int FT = D / 16;                // feature tiles of O
+  static constexpr int FTH = FT / 2;               // feature tiles each wave finishes
+  static constexpr int OS = D + 8;                 // LDS row stride of the staged output
 };
 
+// Workgroup: 4 waves, one query block (64 queries). Wave w takes key half
+// kh = w & 1 (keys 32kh .. 32kh+31 of every critical tile) and query half
+// qh = w >> 1 (queries 32qh .. 32qh+31), so every product is a full-rate
+// 16x16x32 MFMA (the P.V product contracts over the wave's 32 keys). Each wave
+// keeps its own reference maximum per query; the two key halves are combined
+// once at the end like the partial results of a split softmax.
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const int8_t* __restrict__ mask,
     const uint16_t* __restrict__ Hx, const float* __restrict__ alpha, uint16_t* __restrict__ O,
     float* __restrict__ dbg_os, float* __restrict__ dbg_ol, int H, int N, int Nb) {
-  using C = FaCfg<D>;
-  constexpr int KS = C::KS, VS = C::VS, NN = C::NN, KCH = C::KCH, VCH = C::VCH;
-  constexpr int KSTEPS = D / 32;
-  constexpr int FT = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBlock][KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D][VS];
+  using Cf = FaCfg<D>;
+  constexpr int C = Cf::C, TILE = Cf::TILE, INSTR = Cf::INSTR, NN = Cf::NN;
+  constexpr int KSTEPS = Cf::KSTEPS, FT = Cf::FT, FTH = Cf::FTH, OS = Cf::OS;
+  constexpr float TAU = 8.0f;  // a stale reference max may lag the tile max by 2^8 at most
+  // Two tile buffers (K then V^T each) as distinct LDS objects, so that reads of
+  // one provably do not alias the asynchronous copies into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t bufA[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t bufB[2 * TILE];
   __shared__ uint16_t list[kMaxNb];
+  __shared__ float xm[4][2][16];
+  __shared__ float xl[4][2][16];
   __shared__ int wsum[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int T = gridDim.x;
-  const int id = xcd_remap(blockIdx.x, T);
+  const int kh = wave & 1, qh = wave >> 1;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / Nb, i = id - bh * Nb;
   const int h = bh % H;
 
   const int8_t* mrow = mask + ((size_t)bh * Nb + i) * Nb;
   const int ncrit = compact_row(mrow, Nb, (int8_t)1, list, wsum);
 
-  // the wave's 16 queries as MFMA B operands: Q[t][32ks + 8g .. +7]
-  const int tq = i * kBlock + wave * 16 + l16;
-  const bool qvalid = tq < N;
-  const uint16_t* qrow = Q + ((size_t)bh * N + (qvalid ? tq : 0)) * D;
-  uint4 qr[KSTEPS];
+  // the wave's 32 queries as MFMA B operands: Q[t][32ks + 8g .. +7]
+  uint4 qr[2][KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks)
-    qr[ks] = qvalid ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g)
-                    : make_uint4(0, 0, 0, 0);
+  for (int qt = 0; qt < 2; ++qt) {
+    const int t = min(i * kBlock + 32 * qh + 16 * qt + l16, N - 1);  // rows past N are never stored
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qr[qt][ks] = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + t) * D + 32 * ks + 8 * g);
+  }
 
   const uint16_t* Kb = K + (size_t)bh * N * D;
-  const uint16_t* Vb = vt + (size_t)bh * Nb * D * kBlock;
-  uint4 kreg[KCH], vreg[VCH];
-  auto load_tile = [&](int j) {
+  const uint16_t* Vb = vt + (size_t)bh * Nb * TILE;
+  // K rows land in LDS with their 16-byte chunks XOR-swizzled by the row
+  // index (16 lanes reading 16 rows at one column hit distinct banks); the
+  // V^T tile is copied as laid out by the h/z kernel.
+  auto issue = [&](int j, uint16_t* dst) {
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int x = tid + 256 * u;
-      const int key = x / (D / 8), ch = x % (D / 8);
-      const int t = j * kBlock + key;
-      kreg[u] = t < N ? *reinterpret_cast<const uint4*>(Kb + (size_t)t * D + ch * 8)
-                      : make_uint4(0, 0, 0, 0);
-    }
-    const uint16_t* vsrc = Vb + (size_t)j * D * kBlock;
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int x = tid + 256 * u;
-      vreg[u] = *reinterpret_cast<const uint4*>(vsrc + (size_t)x * 8);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int x = tid + 256 * u;
-      const int key = x / (D / 8), ch = x % (D / 8);
-      *reinterpret_cast<uint4*>(&Ks[buf][key][ch * 8]) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int x = tid + 256 * u;
-      const int c = x / 8, ch = x % 8;
-      uint2* dst = reinterpret_cast<uint2*>(&Vs[buf][c][ch * 8]);
-      dst[0] = make_uint2(vreg[u].x, vreg[u].y);
-      dst[1] = make_uint2(vreg[u].z, vreg[u].w);
+    for (int u = 0; u < INSTR; ++u) {
+      const int G = 64 * (4 * u + wave) + lane;
+      const int r = G / C, sch = G % C;
+      const int ch = sch ^ (r & (C - 1));
+      const int t = min(j * kBlock + r, N - 1);  // rows past N are masked to -inf below
+      load_lds16(Kb + (size_t)t * D + ch * 8, dst + 512 * (4 * u + wave));
+      load_lds16(Vb + (size_t)j * TILE + (size_t)G * 8, dst + TILE + 512 * (4 * u + wave));
     }
   };
 
   const float sc = kLog2e / sqrtf((float)D);
-  f32x4 acc[FT];
+  f32x4 acc[FT][2];
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
+  for (int ft = 0; ft < FT; ++ft) acc[ft][0] = acc[ft][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mref[2] = {-INFINITY, -INFINITY};
+  float lp[2] = {0.f, 0.f};
 
-  if (ncrit > 0) {
-    load_tile(list[0]);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int c = 0; c < ncrit; ++c) {
-    const int buf = c & 1;
+  // one tile: wait for it, start the copy of the next one into the other
+  // buffer, S^T, online softmax against the wave's reference max, O^T += V^T P^T
+  auto step = [&](int c, const uint16_t* cur, uint16_t* nxt) {
     const int j = list[c];
-    if (c + 1 < ncrit) load_tile(list[c + 1]);
-    // S^T tile: 64 keys x 16 queries
-    f32x4 s[4];
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of tile c have landed
+    lds_barrier();  // all copies of tile c are in LDS; every wave is done with tile c-1
+    if (c + 1 < ncrit) issue(list[c + 1], nxt);
+    f32x4 s[2][2];  // [key tile][query tile]
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 2; ++kt) s[kt][0] = s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&Ks[buf][16 * kt + l16][32 * ks + 8 * g]);
-        s[kt] = mfma_bf16(a, qr[ks], s[kt]);
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int row = 32 * kh + 16 * kt + l16;
+        const uint4 a = *reinterpret_cast<const uint4*>(cur + (row * C + ((4 * ks + g) ^ (row & (C - 1)))) * 8);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma_bf16(a, qr[qt][ks], s[kt][qt]);
+      }
+    const int kbase = j * kBlock + 32 * kh + 4 * g;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool out = kbase + 16 * kt + r >= N;  // ragged last block
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt][r] = out ? -INFINITY : s[kt][qt][r];
+      }
+    // Reference max: raised only when some score exceeds it by more than 2^8
+    // (rare after the first tile); the 4 lane groups of a query then agree on
+    // the new value through a cross-group max, and acc / l are rescaled.
+    float lmax[2];
+    bool raise = false;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      lmax[qt] = fmaxf(fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3])),
+                       fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3]))) * sc;
+      raise |= lmax[qt] > mref[qt] + TAU;
+    }
+    if (__ballot(raise)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float tm = group4_max(lmax[qt]);
+        const float nref = tm > mref[qt] + TAU ? tm : mref[qt];
+        const float fac = nref == mref[qt] ? 1.0f : __builtin_amdgcn_exp2f(mref[qt] - nref);
+        mref[qt] = nref;
+        lp[qt] *= fac;
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) acc[ft][qt] *= fac;
       }
     }
-    const bool ragged = (j + 1) * kBlock > N;
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = s[kt][r] * sc;
-        if (ragged && j * kBlock + 16 * kt + 4 * g + r >= N) x = -INFINITY;
-        s[kt][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = group4_max(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float corr = exp2f(m_run - m_new);
-    m_run = m_new;
-    float lsum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[kt][r] - m_new);
-        s[kt][r] = p;
-        lsum += p;
-      }
-    l_part = l_part * corr + lsum;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) acc[ft] *= corr;
     uint4 pb[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      pb[u] = make_uint4(pack_bf2(s[2 * u][0], s[2 * u][1]), pack_bf2(s[2 * u][2], s[2 * u][3]),
-                         pack_bf2(s[2 * u + 1][0], s[2 * u + 1][1]),
-                         pack_bf2(s[2 * u + 1][2], s[2 * u + 1][3]));
+    for (int qt = 0; qt < 2; ++qt) {
+      const float meff = mref[qt] == -INFINITY ? 0.0f : mref[qt];  // no valid key yet: every p is 0
+      float p[2][4], ls = 0.f;
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(&Vs[buf][16 * ft + l16][32 * u + 4 * g]);
-        const uint2 hi =
-            *reinterpret_cast<const uint2*>(&Vs[buf][16 * ft + l16][32 * u + 16 + 4 * g]);
-        acc[ft] = mfma_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[u], acc[ft]);
-      }
-    if (c + 1 < ncrit) store_tile(buf ^ 1);
-    __syncthreads();
+        for (int r = 0; r < 4; ++r) {
+          p[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][r], sc, -meff));
+          ls += p[kt][r];
+        }
+      lp[qt] += ls;
+      pb[qt] = make_uint4(pack_bf2(p[0][0], p[0][1]), pack_bf2(p[0][2], p[0][3]),
+                          pack_bf2(p[1][0], p[1][1]), pack_bf2(p[1][2], p[1][3]));
+    }
+    const uint16_t* vtile = cur + TILE + kh * D * 32;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      const int c = 16 * ft + l16;
+      const uint4 a = *reinterpret_cast<const uint4*>(vtile + c * 32 + 8 * (g ^ ((c >> 1) & 3)));
+      acc[ft][0] = mfma_bf16(a, pb[0], acc[ft][0]);
+      acc[ft][1] = mfma_bf16(a, pb[1], acc[ft][1]);
+    }
+  };
+  if (ncrit > 0) issue(list[0], bufA);
+  for (int c = 0; c < ncrit; c += 2) {
+    step(c, bufA, bufB);
+    if (c + 1 < ncrit) step(c + 1, bufB, bufA);
   }
 
-  // ---- epilogue: sparse output, linear branch, mix
-  const float l = group4_sum(l_part);
-  const float inv_l = (ncrit > 0 && l > 0.f) ? 1.0f / l : 0.f;
-
-  // phi(Q): softmax over the D features of the lane's query, lane holds 8*KSTEPS of them
-  float qf[KSTEPS * 8];
+  // ---- combine the two key halves: wave kh finishes feature tiles [FTH*kh, FTH*kh + FTH)
+  float lw[2];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    const uint32_t w[4] = {qr[ks].x, qr[ks].y, qr[ks].z, qr[ks].w};
+  for (int qt = 0; qt < 2; ++qt) lw[qt] = group4_sum(lp[qt]);
+  __syncthreads();  // every wave is done with the tile buffers
+  float* ex = reinterpret_cast<float*>(bufA);  // [wave][FTH][2][64 lanes][4]
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qf[ks * 8 + 2 * e] = bf_lo(w[e]);
-      qf[ks * 8 + 2 * e + 1] = bf_hi(w[e]);
+  for (int f = 0; f < FTH; ++f)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+      *reinterpret_cast<f32x4*>(ex + (((wave * FTH + f) * 2 + qt) * 64 + lane) * 4) =
+          kh == 0 ? acc[FTH + f][qt] : acc[f][qt];  // the partner's half (static indices)
+  if (g == 0) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      xm[wave][qt][l16] = mref[qt];
+      xl[wave][qt][l16] = lw[qt];
     }
   }
-  float qm = -INFINITY;
+  __syncthreads();
+  const int partner = wave ^ 1;
+  f32x4 ofin[FTH][2];
+  float inv_l[2];
 #pragma unroll
-  for (int e = 0; e < KSTEPS * 8; ++e) qm = fmaxf(qm, qf[e]);
-  qm = group4_max(qm);
-  float qsum = 0.f;
+  for (int qt = 0; qt < 2; ++qt) {
+    const float m0 = mref[qt], m1 = xm[partner][qt][l16];
+    const float M = fmaxf(m0, m1);
+    const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+    const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    const float l = w0 * lw[qt] + w1 * xl[partner][qt][l16];
+    inv_l[qt] = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-  for (int e = 0; e < KSTEPS * 8; ++e) {
-    qf[e] = __expf(qf[e] - qm);
-    qsum += qf[e];
+    for (int f = 0; f < FTH; ++f) {
+      const f32x4 other = *reinterpret_cast<const f32x4*>(ex + (((partner * FTH + f) * 2 + qt) * 64 + lane) * 4);
+      ofin[f][qt] = (kh == 0 ? acc[f][qt] : acc[FTH + f][qt]) * w0 + other * w1;
+    }
   }
-  const float qinv = 1.0f / group4_sum(qsum);
+
+  // ---- linear branch: phi(Q) for the wave's 32 queries, den = phi(Q).Z_i, num^T = H_i^T phi(Q)^T
   const uint16_t* Hrow = Hx + ((size_t)bh * Nb + i) * NN;
-  uint4 fq[KSTEPS];
-  float den_part = 0.f;
+  float zf[KSTEPS * 8];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = pack_bf2(qf[ks * 8 + 2 * e] * qinv, qf[ks * 8 + 2 * e + 1] * qinv);
-    fq[ks] = make_uint4(w[0], w[1], w[2], w[3]);
     const uint4 z = *reinterpret_cast<const uint4*>(Hrow + D * D + 32 * ks + 8 * g);
     const uint32_t zw[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      den_part += bf_lo(w[e]) * bf_lo(zw[e]) + bf_hi(w[e]) * bf_hi(zw[e]);
+    for (int e = 0; e < 4; ++e) {
+      zf[ks * 8 + 2 * e] = bf_lo(zw[e]);
+      zf[ks * 8 + 2 * e + 1] = bf_hi(zw[e]);
+    }
   }
-  const float den = group4_sum(den_part);
-  const float inv_den = den > 0.f ? 1.0f / den : 0.f;
-  const float al = alpha[h];
-  const size_t orow = ((size_t)bh * N + tq) * D;
+  uint4 fq[2][KSTEPS];
+  float inv_den[2];
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    f32x4 nm = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qt = 0; qt < 2; ++qt) {
+    float qf[KSTEPS * 8];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const uint4 a =
-          *reinterpret_cast<const uint4*>(Hrow + (size_t)(16 * ft + l16) * D + 32 * ks + 8 * g);
-      nm = mfma_bf16(a, fq[ks], nm);
-    }
-    float os[4], ol[4], o[4];
+      const uint32_t w4[4] = {qr[qt][ks].x, qr[qt][ks].y, qr[qt][ks].z, qr[qt][ks].w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      os[r] = acc[ft][r] * inv_l;
-      ol[r] = nm[r] * inv_den;
-      o[r] = al * os[r] + (1.0f - al) * ol[r];
+      for (int e = 0; e < 4; ++e) {
+        qf[ks * 8 + 2 * e] = bf_lo(w4[e]);
+        qf[ks * 8 + 2 * e + 1] = bf_hi(w4[e]);
+      }
     }
-    if (qvalid) {
-      const int c0 = 16 * ft + 4 * g;
-      *reinterpret_cast<uint2*>(O + orow + c0) =
+    float qm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < KSTEPS * 8; ++e) qm = fmaxf(qm, qf[e]);
+    qm = group4_max(qm);
+    float qs = 0.f;
+#pragma unroll
+    for (int e = 0; e < KSTEPS * 8; ++e) {
+      qf[e] = __expf(qf[e] - qm);
+      qs += qf[e];
+    }
+    const float qinv = 1.0f / group4_sum(qs);
+    float dp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w4[e] = pack_bf2(qf[ks * 8 + 2 * e] * qinv, qf[ks * 8 + 2 * e + 1] * qinv);
+        dp += bf_lo(w4[e]) * zf[ks * 8 + 2 * e] + bf_hi(w4[e]) * zf[ks * 8 + 2 * e + 1];
+      }
+      fq[qt][ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+    const float den = group4_sum(dp);
+    inv_den[qt] = den > 0.f ? 1.0f / den : 0.f;
+  }
+  const float al = alpha[h];
+  uint16_t* ost = bufB;  // staged output tile [64][OS]
+#pragma unroll
+  for (int f = 0; f < FTH; ++f) {
+    const int ft = FTH * kh + f;
+    f32x4 nm[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(Hrow + (size_t)(16 * ft + l16) * D + 32 * ks + 8 * g);
+      nm[0] = mfma_bf16(a, fq[0][ks], nm[0]);
+      nm[1] = mfma_bf16(a, fq[1][ks], nm[1]);
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int q = 32 * qh + 16 * qt + l16;
+      float os[4], ol[4], o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        os[r] = ofin[f][qt][r] * inv_l[qt];
+        ol[r] = nm[qt][r] * inv_den[qt];
+        o[r] = al * os[r] + (1.0f - al) * ol[r];
+      }
+      *reinterpret_cast<uint2*>(ost + q * OS + 16 * ft + 4 * g) =
           make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
-      if (dbg_os) *reinterpret_cast<float4*>(dbg_os + orow + c0) = make_float4(os[0], os[1], os[2], os[3]);
-      if (dbg_ol) *reinterpret_cast<float4*>(dbg_ol + orow + c0) = make_float4(ol[0], ol[1], ol[2], ol[3]);
+      const int t = i * kBlock + q;
+      if (t < N && (dbg_os || dbg_ol)) {
+        const size_t off = ((size_t)bh * N + t) * D + 16 * ft + 4 * g;
+        if (dbg_os) *reinterpret_cast<float4*>(dbg_os + off) = make_float4(os[0], os[1], os[2], os[3]);
+        if (dbg_ol) *reinterpret_cast<float4*>(dbg_ol + off) = make_float4(ol[0], ol[1], ol[2], ol[3]);
+      }
     }
+  }
+  __syncthreads();
+  // full-row 16-byte stores of the staged tile
+  const int nrow = min(kBlock, N - i * kBlock);
+  uint16_t* Ob = O + ((size_t)bh * N + (size_t)i * kBlock) * D;
+  for (int x = tid; x < nrow * C; x += 256) {
+    const int row = x / C, ch = x % C;
+    *reinterpret_cast<uint4*>(Ob + (size_t)row * D + ch * 8) =
+        *reinterpret_cast<const uint4*>(ost + row * OS + ch * 8);
   }
 }
 

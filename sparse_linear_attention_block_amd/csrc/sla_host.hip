@@ -63,6 +63,7 @@ int make_dims(const sla_problem* p, sla::Dims* D) {
   D->n_h = n_h;
   D->n_l = n_l;
   D->Nbp = (Nb + 31) / 32 * 32;
+  D->Nb128 = (Nb + 127) / 128 * 128;
   D->NN = p->d * p->d + p->d;
   D->bf16 = p->dtype == SLA_BF16;
   D->quant = p->quant == SLA_QUANT_I8QK_F8PV;
@@ -89,6 +90,7 @@ size_t carve(const Dims& D, void* base, Work* w) {
     x.hx = take(BH * (D.Nbp / 4) * D.NN * 4 * sizeof(uint16_t));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(uint16_t));
     x.vt = (uint16_t*)take(BH * D.Nb * D.d * kBlock * sizeof(uint16_t));
+    x.ind = (uint16_t*)take(BH * D.Nbp * D.Nb128 * sizeof(uint16_t));
   } else {
     x.hx = take(BH * D.Nb * D.NN * sizeof(float));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(float));
@@ -187,12 +189,19 @@ int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const 
     if (e_ != hipSuccess) return fail(SLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e_)); \
   } while (0)
 
+  auto mark = [&](int k) -> hipError_t {
+    if (dbg && dbg->events[k]) return hipEventRecord((hipEvent_t)dbg->events[k], s);
+    return hipSuccess;
+  };
   const int8_t* mask = mask_in;
+  SLA_LAUNCH(mark(0), "event record");
   if (!mask_in) {
     SLA_LAUNCH(sla::launch_pool_proj(D, Q, K, proj_q, proj_k, proj_hs, w.pooled_q, w.pooled_k, s),
                "pool/proj kernel");
+    SLA_LAUNCH(mark(1), "event record");
     SLA_LAUNCH(sla::launch_select(D, w.pooled_q, w.pooled_k, mask_out, dbg ? dbg->logits : nullptr, s),
                "score/select kernel");
+    SLA_LAUNCH(mark(2), "event record");
     if (dbg && dbg->pooled_q)
       SLA_LAUNCH(hipMemcpyAsync(dbg->pooled_q, w.pooled_q, (size_t)D.BH * D.Nb * D.d * sizeof(double),
                                 hipMemcpyDeviceToDevice, s), "debug copy");
@@ -200,15 +209,22 @@ int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const 
       SLA_LAUNCH(hipMemcpyAsync(dbg->pooled_k, w.pooled_k, (size_t)D.BH * D.Nb * D.d * sizeof(double),
                                 hipMemcpyDeviceToDevice, s), "debug copy");
     mask = mask_out;
+  } else {
+    SLA_LAUNCH(mark(1), "event record");
+    SLA_LAUNCH(mark(2), "event record");
   }
   SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
+  SLA_LAUNCH(mark(3), "event record");
+  if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
   SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
+  SLA_LAUNCH(mark(4), "event record");
   float* dos = dbg ? dbg->o_s : nullptr;
   float* dol = dbg ? dbg->o_l : nullptr;
   if (D.bf16)
     SLA_LAUNCH(sla::launch_sparse(D, Q, K, mask, alpha, w, O, dos, dol, s), "sparse kernel");
   else
     SLA_LAUNCH(sla::launch_sparse_f32(D, Q, K, V, mask, alpha, w, O, dos, dol, s), "sparse kernel");
+  SLA_LAUNCH(mark(5), "event record");
 #undef SLA_LAUNCH
   g_err[0] = 0;
   return SLA_OK;

@@ -17,6 +17,7 @@ struct Dims {
   int B, H, N, d, BH, Nb;
   int n_h, n_l;
   int Nbp;          // Nb rounded up to a multiple of 32 (K extent of the linear GEMM)
+  int Nb128;        // Nb rounded up to a multiple of 128 (row tiles of the linear GEMM)
   int NN;           // d*d + d: one h_j (stored transposed, c-major) followed by z_j
   bool bf16;
   bool quant;
@@ -29,6 +30,8 @@ struct Work {
   void* hx;           // bf16: [BH, Nbp/4, NN, 4] (four key blocks interleaved per column)
                       // f32:  [BH, Nb, NN]
   void* Hx;           // [BH, Nb, NN] per query block: H_i^T (c-major) then Z_i; bf16 or f32
+  uint16_t* ind;      // bf16 only: [BH, Nbp/32, Nb128, 32] marginal indicator (Mc == 0) as 0/1,
+                      // one 32-key slab per k step, 16-byte chunks swizzled by row
   uint16_t* vt;       // bf16 only: [BH, Nb, d, 64] V^T of every key block (zero past N)
   int8_t* q8;         // quant only: [BH, N, d] int8 Q
   int8_t* k8;         // quant only: [BH, N, d] int8 K
@@ -47,6 +50,7 @@ hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const f
 hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8_t* mask,
                          double* dbg_logits, hipStream_t s);
 hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w, hipStream_t s);
+hipError_t launch_indicator(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
 hipError_t launch_linear(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
 hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const int8_t* mask,
                          const float* alpha, const Work& w, void* O, float* dbg_os,
