@@ -59,33 +59,40 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
   const uint16_t* Kb = K + (size_t)bh * N * D;
   const uint16_t* Vb = V + (size_t)bh * N * D;
 
-  for (int jj = 0; jj < 4; ++jj) {
+  // K and V rows of block jj+1 are loaded while block jj is processed
+  uint4 kr[2][2][CPT], vr[2][2][CPT];  // [register set][token of the pair][chunk]
+  bool valid[2][2];
+  auto load_block = [&](int jj, int set) {
     const int j = 4 * jq + jj;
-    uint4 kr[2][CPT], vr[2][CPT];
-    bool valid[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int t = j * kBlock + 2 * tp + u;
-      valid[u] = (j < Nb) && (t < N);
+      valid[set][u] = (j < Nb) && (t < N);
 #pragma unroll
       for (int q = 0; q < CPT; ++q) {
         const int ch = cg * CPT + q;
-        if (valid[u]) {
-          kr[u][q] = *reinterpret_cast<const uint4*>(Kb + (size_t)t * D + ch * 8);
-          vr[u][q] = *reinterpret_cast<const uint4*>(Vb + (size_t)t * D + ch * 8);
+        if (valid[set][u]) {
+          kr[set][u][q] = *reinterpret_cast<const uint4*>(Kb + (size_t)t * D + ch * 8);
+          vr[set][u][q] = *reinterpret_cast<const uint4*>(Vb + (size_t)t * D + ch * 8);
         } else {
-          kr[u][q] = make_uint4(0, 0, 0, 0);
-          vr[u][q] = make_uint4(0, 0, 0, 0);
+          kr[set][u][q] = make_uint4(0, 0, 0, 0);
+          vr[set][u][q] = make_uint4(0, 0, 0, 0);
         }
       }
     }
+  };
+  load_block(0, 0);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int cs = jj & 1;
+    if (jj + 1 < 4) load_block(jj + 1, cs ^ 1);
     // phi(K) row statistics: max then sum of exp over the D features
     float x[2][CPT * 8];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int q = 0; q < CPT; ++q) {
-        const uint32_t w[4] = {kr[u][q].x, kr[u][q].y, kr[u][q].z, kr[u][q].w};
+        const uint32_t w[4] = {kr[cs][u][q].x, kr[cs][u][q].y, kr[cs][u][q].z, kr[cs][u][q].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[u][q * 8 + 2 * e] = bf_lo(w[e]);
@@ -126,14 +133,14 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
       tstat[tid] = 1.0f / s;
     }
     __syncthreads();
-    const float inv0 = valid[0] ? tstat[2 * tp] : 0.f;
-    const float inv1 = valid[1] ? tstat[2 * tp + 1] : 0.f;
+    const float inv0 = valid[cs][0] ? tstat[2 * tp] : 0.f;
+    const float inv1 = valid[cs][1] ? tstat[2 * tp + 1] : 0.f;
     // transposed stores: word (token 2tp, token 2tp+1) of each feature
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int f0 = (cg * CPT + q) * 8;
-      const uint32_t v0[4] = {vr[0][q].x, vr[0][q].y, vr[0][q].z, vr[0][q].w};
-      const uint32_t v1[4] = {vr[1][q].x, vr[1][q].y, vr[1][q].z, vr[1][q].w};
+      const uint32_t v0[4] = {vr[cs][0][q].x, vr[cs][0][q].y, vr[cs][0][q].z, vr[cs][0][q].w};
+      const uint32_t v1[4] = {vr[cs][1][q].x, vr[cs][1][q].y, vr[cs][1][q].z, vr[cs][1][q].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t kw = pack_bf2(x[0][q * 8 + e] * inv0, x[1][q * 8 + e] * inv1);

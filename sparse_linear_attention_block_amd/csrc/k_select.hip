@@ -139,29 +139,34 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ pq,
                                                 double* __restrict__ dbg_logits, int Nb, int d,
                                                 int n_h, int n_l, int R) {
   extern __shared__ double lds[];
-  double* qs = lds;            // [R][d]
-  double* lg = lds + R * d;    // [R][Nb]
+  double* qs = lds;            // [8][d], rows past the workgroup's R are zero
+  double* lg = lds + 8 * d;    // [R][Nb]
   const int tid = threadIdx.x;
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * R;
   const int nr = min(R, Nb - i0);
   const double* Pq = pq + ((size_t)bh * Nb + i0) * d;
   const double* Pk = pk + (size_t)bh * Nb * d;
-  for (int x = tid; x < nr * d; x += 256) qs[x] = Pq[x];
+  for (int x = tid; x < 8 * d; x += 256) qs[x] = x < nr * d ? Pq[x] : 0.0;  // rows past nr: 0
   __syncthreads();
   const double sd = sqrt((double)d);
+  // one key row per thread; its d values arrive in batches of 16 double2
+  // loads issued back to back, so each batch costs one memory latency
   for (int j = tid; j < Nb; j += 256) {
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const double2* kr = reinterpret_cast<const double2*>(Pk + (size_t)j * d);
-    for (int c2 = 0; c2 < d / 2; ++c2) {
-      const double2 kv = kr[c2];
+    for (int cb = 0; cb < d / 2; cb += 16) {
+      double2 kv[16];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        if (r < nr) {
-          acc[r] = fma(qs[r * d + 2 * c2], kv.x, acc[r]);
-          acc[r] = fma(qs[r * d + 2 * c2 + 1], kv.y, acc[r]);
+      for (int u = 0; u < 16; ++u) kv[u] = kr[cb + u];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const double2 qv = *reinterpret_cast<const double2*>(&qs[r * d + 2 * (cb + u)]);
+          acc[r] = fma(qv.x, kv[u].x, acc[r]);
+          acc[r] = fma(qv.y, kv[u].y, acc[r]);
         }
-      }
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r)
@@ -182,9 +187,9 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ pq,
 hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8_t* mask,
                          double* dbg_logits, hipStream_t s) {
   // R rows per workgroup, bounded by LDS (logits + pooled queries in float64)
-  int R = 8;
-  while (R > 1 && (size_t)R * (D.Nb + D.d) * sizeof(double) > 64 * 1024) R >>= 1;
-  const size_t lds = (size_t)R * (D.Nb + D.d) * sizeof(double);
+  int R = 8;  // the logits loop always computes 8 rows; fewer are kept when LDS is short
+  while (R > 1 && (size_t)8 * D.d * sizeof(double) + (size_t)R * D.Nb * sizeof(double) > 64 * 1024) R >>= 1;
+  const size_t lds = ((size_t)8 * D.d + (size_t)R * D.Nb) * sizeof(double);
   dim3 grid((D.Nb + R - 1) / R, D.BH);
   const int E = (D.Nb + 63) / 64;
   auto kern = E <= 8 ? k_select<8> : E <= 16 ? k_select<16> : E <= 32 ? k_select<32> : k_select<64>;

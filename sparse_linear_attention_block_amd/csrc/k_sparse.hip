@@ -36,6 +36,8 @@
 // key tiles, which then come from the XCD's L2.
 //
 // f32 path: 4 threads per query, plain FMA, one key at a time.
+#include <type_traits>
+
 #include "sla_internal.h"
 #include "dev_common.h"
 
@@ -108,17 +110,16 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   __shared__ float xl[4][2][16];
   __shared__ int wsum[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS addresses
   const int l16 = lane & 15, g = lane >> 4;
   const int kh = wave & 1, qh = wave >> 1;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / Nb, i = id - bh * Nb;
   const int h = bh % H;
 
-  const int8_t* mrow = mask + ((size_t)bh * Nb + i) * Nb;
-  const int ncrit = compact_row(mrow, Nb, (int8_t)1, list, wsum);
-
-  // the wave's 32 queries as MFMA B operands: Q[t][32ks + 8g .. +7]
+  // the wave's 32 queries as MFMA B operands: Q[t][32ks + 8g .. +7] (issued first:
+  // they land while the critical list is compacted)
   uint4 qr[2][KSTEPS];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -128,20 +129,35 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
       qr[qt][ks] = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + t) * D + 32 * ks + 8 * g);
   }
 
+  const int8_t* mrow = mask + ((size_t)bh * Nb + i) * Nb;
+  const int ncrit = compact_row(mrow, Nb, (int8_t)1, list, wsum);
+
   const uint16_t* Kb = K + (size_t)bh * N * D;
   const uint16_t* Vb = vt + (size_t)bh * Nb * TILE;
   // K rows land in LDS with their 16-byte chunks XOR-swizzled by the row
   // index (16 lanes reading 16 rows at one column hit distinct banks); the
-  // V^T tile is copied as laid out by the h/z kernel.
+  // V^T tile is copied as laid out by the h/z kernel. The per-lane source
+  // offsets within a tile are the same for every tile.
+  int koff[INSTR];
+#pragma unroll
+  for (int u = 0; u < INSTR; ++u) {
+    const int G = 64 * (4 * u + wave) + lane;
+    const int r = G / C, sch = G % C;
+    koff[u] = r * D + (sch ^ (r & (C - 1))) * 8;
+  }
   auto issue = [&](int j, uint16_t* dst) {
+    const uint16_t* ksrc = Kb + (size_t)j * TILE;
+    const uint16_t* vsrc = Vb + (size_t)j * TILE;
+    const bool ragged = (j + 1) * kBlock > N;
 #pragma unroll
     for (int u = 0; u < INSTR; ++u) {
-      const int G = 64 * (4 * u + wave) + lane;
-      const int r = G / C, sch = G % C;
-      const int ch = sch ^ (r & (C - 1));
-      const int t = min(j * kBlock + r, N - 1);  // rows past N are masked to -inf below
-      load_lds16(Kb + (size_t)t * D + ch * 8, dst + 512 * (4 * u + wave));
-      load_lds16(Vb + (size_t)j * TILE + (size_t)G * 8, dst + TILE + 512 * (4 * u + wave));
+      int off = koff[u];
+      if (ragged) {  // rows past N: re-read row N-1 (masked to -inf below)
+        const int r = off / D;
+        off -= max(0, j * kBlock + r - (N - 1)) * D;
+      }
+      load_lds16(ksrc + off, dst + 512 * (4 * u + wave));
+      load_lds16(vsrc + (64 * (4 * u + wave) + lane) * 8, dst + TILE + 512 * (4 * u + wave));
     }
   };
 
@@ -171,15 +187,17 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma_bf16(a, qr[qt][ks], s[kt][qt]);
       }
-    const int kbase = j * kBlock + 32 * kh + 4 * g;
+    if ((j + 1) * kBlock > N) {  // ragged last block: keys past N take no part
+      const int kbase = j * kBlock + 32 * kh + 4 * g;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool out = kbase + 16 * kt + r >= N;  // ragged last block
+        for (int r = 0; r < 4; ++r) {
+          const bool out = kbase + 16 * kt + r >= N;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[kt][qt][r] = out ? -INFINITY : s[kt][qt][r];
-      }
+          for (int qt = 0; qt < 2; ++qt) s[kt][qt][r] = out ? -INFINITY : s[kt][qt][r];
+        }
+    }
     // Reference max: raised only when some score exceeds it by more than 2^8
     // (rare after the first tile); the 4 lane groups of a query then agree on
     // the new value through a cross-group max, and acc / l are rescaled.
@@ -240,12 +258,17 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   for (int qt = 0; qt < 2; ++qt) lw[qt] = group4_sum(lp[qt]);
   __syncthreads();  // every wave is done with the tile buffers
   float* ex = reinterpret_cast<float*>(bufA);  // [wave][FTH][2][64 lanes][4]
+  // the accumulator halves are selected with compile-time indices (a runtime
+  // index would send the accumulator array through scratch memory)
+  auto send = [&](auto KH) {
+    constexpr int base = FTH * (1 - decltype(KH)::value);
 #pragma unroll
-  for (int f = 0; f < FTH; ++f)
+    for (int f = 0; f < FTH; ++f)
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-      *reinterpret_cast<f32x4*>(ex + (((wave * FTH + f) * 2 + qt) * 64 + lane) * 4) =
-          kh == 0 ? acc[FTH + f][qt] : acc[f][qt];  // the partner's half (static indices)
+      for (int qt = 0; qt < 2; ++qt)
+        *reinterpret_cast<f32x4*>(ex + (((wave * FTH + f) * 2 + qt) * 64 + lane) * 4) = acc[base + f][qt];
+  };
+  if (kh == 0) send(std::integral_constant<int, 0>{}); else send(std::integral_constant<int, 1>{});
   if (g == 0) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -257,20 +280,25 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   const int partner = wave ^ 1;
   f32x4 ofin[FTH][2];
   float inv_l[2];
+  auto keep = [&](auto KH) {
+    constexpr int base = FTH * decltype(KH)::value;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float m0 = mref[qt], m1 = xm[partner][qt][l16];
-    const float M = fmaxf(m0, m1);
-    const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
-    const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-    const float l = w0 * lw[qt] + w1 * xl[partner][qt][l16];
-    inv_l[qt] = l > 0.f ? 1.0f / l : 0.f;
+    for (int qt = 0; qt < 2; ++qt) {
+      const float m0 = mref[qt], m1 = xm[partner][qt][l16];
+      const float M = fmaxf(m0, m1);
+      const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+      const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+      const float l = w0 * lw[qt] + w1 * xl[partner][qt][l16];
+      inv_l[qt] = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-    for (int f = 0; f < FTH; ++f) {
-      const f32x4 other = *reinterpret_cast<const f32x4*>(ex + (((partner * FTH + f) * 2 + qt) * 64 + lane) * 4);
-      ofin[f][qt] = (kh == 0 ? acc[f][qt] : acc[FTH + f][qt]) * w0 + other * w1;
+      for (int f = 0; f < FTH; ++f) {
+        const f32x4 other =
+            *reinterpret_cast<const f32x4*>(ex + (((partner * FTH + f) * 2 + qt) * 64 + lane) * 4);
+        ofin[f][qt] = acc[base + f][qt] * w0 + other * w1;
+      }
     }
-  }
+  };
+  if (kh == 0) keep(std::integral_constant<int, 0>{}); else keep(std::integral_constant<int, 1>{});
 
   // ---- linear branch: phi(Q) for the wave's 32 queries, den = phi(Q).Z_i, num^T = H_i^T phi(Q)^T
   const uint16_t* Hrow = Hx + ((size_t)bh * Nb + i) * NN;

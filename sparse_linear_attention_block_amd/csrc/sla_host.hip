@@ -86,6 +86,7 @@ size_t carve(const Dims& D, void* base, Work* w) {
   Work x = {};
   x.pooled_q = (double*)take(BH * D.Nb * D.d * sizeof(double));
   x.pooled_k = (double*)take(BH * D.Nb * D.d * sizeof(double));
+  x.pooled_raw = (double*)take(2 * BH * D.Nb * D.d * sizeof(double));
   if (D.bf16) {
     x.hx = take(BH * (D.Nbp / 4) * D.NN * 4 * sizeof(uint16_t));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(uint16_t));
@@ -196,7 +197,7 @@ int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const 
   const int8_t* mask = mask_in;
   SLA_LAUNCH(mark(0), "event record");
   if (!mask_in) {
-    SLA_LAUNCH(sla::launch_pool_proj(D, Q, K, proj_q, proj_k, proj_hs, w.pooled_q, w.pooled_k, s),
+    SLA_LAUNCH(sla::launch_pool_proj(D, Q, K, proj_q, proj_k, proj_hs, w.pooled_raw, w.pooled_q, w.pooled_k, s),
                "pool/proj kernel");
     SLA_LAUNCH(mark(1), "event record");
     SLA_LAUNCH(sla::launch_select(D, w.pooled_q, w.pooled_k, mask_out, dbg ? dbg->logits : nullptr, s),

@@ -27,6 +27,7 @@ struct Dims {
 struct Work {
   double* pooled_q;   // [BH, Nb, d]
   double* pooled_k;   // [BH, Nb, d]
+  double* pooled_raw; // [2, BH, Nb, d] block means before the router projection
   void* hx;           // bf16: [BH, Nbp/4, NN, 4] (four key blocks interleaved per column)
                       // f32:  [BH, Nb, NN]
   void* Hx;           // [BH, Nb, NN] per query block: H_i^T (c-major) then Z_i; bf16 or f32
@@ -45,7 +46,7 @@ size_t carve(const Dims& D, void* base, Work* w);  // returns bytes needed (base
 
 // ---- launchers (each enqueues one or more kernels on `s`, returns hipError_t)
 hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const float* proj_q,
-                            const float* proj_k, int proj_hs, double* pq, double* pk,
+                            const float* proj_k, int proj_hs, double* raw, double* pq, double* pk,
                             hipStream_t s);
 hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8_t* mask,
                          double* dbg_logits, hipStream_t s);
