@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void k_pool_proj(const double* __restrict__ ra
     if (ct >= nct) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = r0 + 4 * g + e;                // D[4g + e][l16]
+      const int r = r0 + g + 4 * e;                // f64 16x16 layout: D[g + 4e][l16]
       if (r < Nb) out[(size_t)r * d + 16 * ct + l16] = acc[ct][e];
     }
   }
