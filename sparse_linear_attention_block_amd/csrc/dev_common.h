@@ -115,3 +115,64 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 }  // namespace sla
+
+namespace sla {
+
+// float -> OCP fp8 e4m3 (finite, max 448) with round-to-nearest-even and
+// saturation: the hardware conversion rounds to nearest even but turns
+// magnitudes above 464 into NaN, so the input is clamped to +-448 first.
+// Returns the byte in the low 8 bits.
+__device__ __forceinline__ uint32_t f2e4m3(float x) {
+  x = fminf(fmaxf(x, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xffu;
+}
+// four floats -> four e4m3 bytes in one word (element 0 in the low byte)
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  c = fminf(fmaxf(c, -448.0f), 448.0f);
+  d = fminf(fmaxf(d, -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+// symmetric int8 code: round-to-nearest-even of x * inv, clamped to +-127
+__device__ __forceinline__ int q_i8(float x, float inv) {
+  return (int)fminf(fmaxf(__builtin_rintf(x * inv), -127.0f), 127.0f);
+}
+
+}  // namespace sla
+
+namespace sla {
+
+// Workgroup L of T (dispatched round-robin over the 8 XCDs) -> logical index:
+// each XCD gets a contiguous range of logical indices, so neighbouring tiles
+// share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int L, int T) {
+  const int q = T >> 3, rm = T & 7;
+  const int x = L & 7, pos = L >> 3;
+  return x * q + min(x, rm) + pos;
+}
+
+// Compacts the indices j with mrow[j] == value, ascending, into list; returns the count.
+__device__ inline int compact_row(const int8_t* __restrict__ mrow, int Nb, int8_t value,
+                           uint16_t* list, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int total = 0;
+  for (int base = 0; base < Nb; base += 256) {
+    const int j = base + tid;
+    const bool f = (j < Nb) && (mrow[j] == value);
+    const uint64_t bal = __ballot(f);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int off = total;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (f) list[off + before] = (uint16_t)j;
+    total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  return total;
+}
+
+}  // namespace sla

@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
                                                  const uint16_t* __restrict__ V,
                                                  uint16_t* __restrict__ hx,
                                                  uint16_t* __restrict__ vt, int N, int Nb,
-                                                 int Nb4) {
+                                                 int Nb4, uint8_t* __restrict__ v8t,
+                                                 float* __restrict__ vsc) {
   using C = HzCfg<D>;
   constexpr int TS = C::TS, CPT = C::CPT, NN = C::NN;
   __shared__ __attribute__((aligned(16))) uint16_t kT[4][D][TS];
@@ -223,7 +224,8 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
   // 16-byte chunks; chunk q carries keys {4q..4q+3, 16+4q..16+4q+3} (the k
   // slots of one MFMA lane group) and sits at position q ^ ((c >> 1) & 3), so
   // that 8 lanes reading 8 consecutive rows touch distinct LDS banks.
-  for (int jj = 0; jj < 4; ++jj) {
+  // (the 8-bit sparse branch reads V8^T below instead: then vt is NULL)
+  for (int jj = 0; jj < 4 && vt != nullptr; ++jj) {
     const int j = 4 * jq + jj;
     if (j >= Nb) break;
     uint16_t* dst = vt + ((size_t)bh * Nb + j) * D * kBlock;
@@ -233,6 +235,52 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
       const uint2 hi = *reinterpret_cast<const uint2*>(&vT[jj][c][32 * khh + 16 + 4 * q]);
       *reinterpret_cast<uint4*>(dst + ((size_t)khh * D + c) * 32 + 8 * (q ^ ((c >> 1) & 3))) =
           make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
+  if (v8t == nullptr) return;  // uniform: no 8-bit copy of V wanted
+  // ---- 8-bit sparse branch: V^T of each block in OCP e4m3 with one absmax
+  // scale per block (absmax / 448; an all-zero block gets scale 1). Row c of a
+  // block holds four 16-byte chunks; chunk g carries keys 16kt + 4g + r in the
+  // order (kt, r), the k slots one lane group of the 8-bit sparse kernel's
+  // 16x16x128 product takes from one tile, and sits at position
+  // g ^ ((c >> 1) & 3) against LDS bank conflicts.
+  __shared__ float vmax[4][4];
+  const int cq = tid >> 2, gq = tid & 3;  // rows cq and cq + 64 (D = 128) of chunk gq
+  float am[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float m = 0.f;
+    for (int c = cq; c < D; c += 64)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint2 w = *reinterpret_cast<const uint2*>(&vT[jj][c][16 * kt + 4 * gq]);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf_lo(w.x)), fabsf(bf_hi(w.x))),
+                           fmaxf(fabsf(bf_lo(w.y)), fabsf(bf_hi(w.y)))));
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0) vmax[jj][tid >> 6] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    am[jj] = fmaxf(fmaxf(vmax[jj][0], vmax[jj][1]), fmaxf(vmax[jj][2], vmax[jj][3]));
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = 4 * jq + jj;
+    if (j >= Nb) break;
+    const float inv = am[jj] > 0.f ? 448.0f / am[jj] : 1.0f;
+    if (tid == 0) vsc[(size_t)bh * Nb + j] = am[jj] > 0.f ? am[jj] / 448.0f : 1.0f;
+    uint8_t* dst = v8t + ((size_t)bh * Nb + j) * D * kBlock;
+    for (int c = cq; c < D; c += 64) {
+      uint32_t o[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint2 w = *reinterpret_cast<const uint2*>(&vT[jj][c][16 * kt + 4 * gq]);
+        o[kt] = pack_e4m3x4(bf_lo(w.x) * inv, bf_hi(w.x) * inv, bf_lo(w.y) * inv, bf_hi(w.y) * inv);
+      }
+      *reinterpret_cast<uint4*>(dst + (size_t)c * 64 + 16 * (gq ^ ((c >> 1) & 3))) =
+          make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
@@ -292,10 +340,12 @@ hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w,
     dim3 grid(D.Nbp / 4, D.BH);
     if (D.d == 128)
       hipLaunchKernelGGL(k_hz_bf16<128>, grid, dim3(256), 0, s, (const uint16_t*)K,
-                         (const uint16_t*)V, (uint16_t*)w.hx, w.vt, D.N, D.Nb, D.Nbp / 4);
+                         (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4, w.v8t,
+                         w.vs);
     else
       hipLaunchKernelGGL(k_hz_bf16<64>, grid, dim3(256), 0, s, (const uint16_t*)K,
-                         (const uint16_t*)V, (uint16_t*)w.hx, w.vt, D.N, D.Nb, D.Nbp / 4);
+                         (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4, w.v8t,
+                         w.vs);
   } else {
     dim3 grid(D.Nb, D.BH);
     const size_t lds = 2 * kBlock * D.d * sizeof(float);

@@ -24,12 +24,6 @@ namespace {
 constexpr int kTN = 256;  // n per workgroup
 constexpr int kTI = 128;  // query blocks per workgroup
 
-__device__ __forceinline__ int xcd_remap(int L, int T) {
-  const int q = T >> 3, rm = T & 7;
-  const int x = L & 7, pos = L >> 3;
-  return x * q + min(x, rm) + pos;
-}
-
 // The marginal indicator M01[i][j] = (Mc[i][j] == 0) as bf16 0/1, one
 // [Nb128][32] slab per 32-key step; chunk q (keys 8q..8q+7 of the step) of row
 // i sits at chunk position q ^ ((i >> 1) & 3), so that 8 lanes reading 8

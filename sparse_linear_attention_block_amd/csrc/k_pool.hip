@@ -11,7 +11,8 @@
 //
 // k_pool_sum: grid (ceil(Nb/2), B*H, 2), z = 0 for Q and 1 for K; each
 //   workgroup sums 2 blocks with every 16-byte load of a thread issued before
-//   the first add; the means go to raw[z][bh][block][d].
+//   the first add; the means go to raw[z][bh][block][d] (the 8-bit sparse
+//   branch also takes its per-head channel means of Q and K from them).
 // k_pool_proj: grid (ceil(Nb/64), B*H, 2); float64 MFMA 16x16x4 against the
 //   head's router matrix (f32 [in][out], staged in LDS), 16 block means per wave.
 #include "sla_internal.h"
@@ -81,10 +82,10 @@ __global__ __launch_bounds__(256) void k_pool_sum(const T* __restrict__ Q, const
   for (int o = tid; o < kG * d; o += 256) {
     const int b = o / d, col = o % d, blk = blk0 + b;
     if (blk >= Nb) continue;
-    double s = 0.0;
-    for (int u = 0; u < RG; ++u) s += part[b][u * d + col];
+    double sum = 0.0;
+    for (int u = 0; u < RG; ++u) sum += part[b][u * d + col];
     const int cnt = min(kBlock, N - blk * kBlock);
-    raw[(((size_t)z * BH + bh) * Nb + blk) * d + col] = s / (double)cnt;
+    raw[(((size_t)z * BH + bh) * Nb + blk) * d + col] = sum / (double)cnt;
   }
 }
 
@@ -136,9 +137,8 @@ __global__ __launch_bounds__(256) void k_pool_proj(const double* __restrict__ ra
 
 }  // namespace
 
-hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const float* proj_q,
-                            const float* proj_k, int proj_hs, double* raw, double* pq, double* pk,
-                            hipStream_t s) {
+hipError_t launch_pool_sum(const Dims& D, const void* Q, const void* K, double* raw,
+                           hipStream_t s) {
   dim3 g1((D.Nb + kG - 1) / kG, D.BH, 2);
   if (D.bf16)
     hipLaunchKernelGGL(k_pool_sum<uint16_t>, g1, dim3(256), 0, s, (const uint16_t*)Q,
@@ -146,7 +146,13 @@ hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const f
   else
     hipLaunchKernelGGL(k_pool_sum<float>, g1, dim3(256), 0, s, (const float*)Q, (const float*)K,
                        raw, D.N, D.d, D.Nb, D.BH);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const float* proj_q,
+                            const float* proj_k, int proj_hs, double* raw, double* pq, double* pk,
+                            hipStream_t s) {
+  hipError_t e = launch_pool_sum(D, Q, K, raw, s);
   if (e != hipSuccess) return e;
   dim3 g2((D.Nb + kPR - 1) / kPR, D.BH, 2);
   hipLaunchKernelGGL(k_pool_proj, g2, dim3(256), 0, s, raw, proj_q, proj_k, proj_hs, pq, pk, D.H,

@@ -46,33 +46,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ int xcd_remap(int L, int T) {
-  const int q = T >> 3, rm = T & 7;
-  const int x = L & 7, pos = L >> 3;
-  return x * q + min(x, rm) + pos;
-}
-
-// Compacts the indices j with mrow[j] == value, ascending, into list; returns the count.
-__device__ int compact_row(const int8_t* __restrict__ mrow, int Nb, int8_t value,
-                           uint16_t* list, int* wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int total = 0;
-  for (int base = 0; base < Nb; base += 256) {
-    const int j = base + tid;
-    const bool f = (j < Nb) && (mrow[j] == value);
-    const uint64_t bal = __ballot(f);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(bal);
-    __syncthreads();
-    int off = total;
-    for (int w = 0; w < wave; ++w) off += wsum[w];
-    if (f) list[off + before] = (uint16_t)j;
-    total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-  }
-  return total;
-}
-
 template <int D>
 struct FaCfg {
   static constexpr int C = D / 8;                  // 16-byte chunks per K row

@@ -52,8 +52,6 @@ int make_dims(const sla_problem* p, sla::Dims* D) {
     return fail(SLA_ERR_ARG, "kh and kl select %d + %d > %d blocks per row", n_h, n_l, Nb);
   if (p->quant == SLA_QUANT_I8QK_F8PV && p->dtype != SLA_BF16)
     return fail(SLA_ERR_UNSUPPORTED, "the 8-bit sparse branch needs bf16 inputs");
-  if (p->quant == SLA_QUANT_I8QK_F8PV)
-    return fail(SLA_ERR_UNSUPPORTED, "the 8-bit sparse branch is not built");
   D->B = p->B;
   D->H = p->H;
   D->N = p->N;
@@ -90,17 +88,17 @@ size_t carve(const Dims& D, void* base, Work* w) {
   if (D.bf16) {
     x.hx = take(BH * (D.Nbp / 4) * D.NN * 4 * sizeof(uint16_t));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(uint16_t));
-    x.vt = (uint16_t*)take(BH * D.Nb * D.d * kBlock * sizeof(uint16_t));
+    if (!D.quant) x.vt = (uint16_t*)take(BH * D.Nb * D.d * kBlock * sizeof(uint16_t));
     x.ind = (uint16_t*)take(BH * D.Nbp * D.Nb128 * sizeof(uint16_t));
   } else {
     x.hx = take(BH * D.Nb * D.NN * sizeof(float));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(float));
   }
   if (D.quant) {
-    x.q8 = (int8_t*)take(BH * D.N * D.d);
-    x.k8 = (int8_t*)take(BH * D.N * D.d);
-    x.qs = (float*)take(BH * D.Nb * sizeof(float));
+    x.qkmean = (float*)take(2 * BH * D.d * sizeof(float));
+    x.k8 = (int8_t*)take(BH * D.Nb * kBlock * D.d);
     x.ks = (float*)take(BH * D.Nb * sizeof(float));
+    x.kb = (float*)take(BH * D.Nb * kBlock * sizeof(float));
     x.v8t = (uint8_t*)take(BH * D.Nb * D.d * kBlock);
     x.vs = (float*)take(BH * D.Nb * sizeof(float));
   }
@@ -211,17 +209,22 @@ int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const 
                                 hipMemcpyDeviceToDevice, s), "debug copy");
     mask = mask_out;
   } else {
+    // the 8-bit branch smooths Q and K with their channel means, taken from the block means
+    if (D.quant) SLA_LAUNCH(sla::launch_pool_sum(D, Q, K, w.pooled_raw, s), "pool kernel");
     SLA_LAUNCH(mark(1), "event record");
     SLA_LAUNCH(mark(2), "event record");
   }
   SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
+  if (D.quant) SLA_LAUNCH(sla::launch_quant_k(D, K, w, s), "K quantisation kernel");
   SLA_LAUNCH(mark(3), "event record");
   if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
   SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
   SLA_LAUNCH(mark(4), "event record");
   float* dos = dbg ? dbg->o_s : nullptr;
   float* dol = dbg ? dbg->o_l : nullptr;
-  if (D.bf16)
+  if (D.quant)
+    SLA_LAUNCH(sla::launch_sparse_q8(D, Q, mask, alpha, w, O, dos, dol, s), "8-bit sparse kernel");
+  else if (D.bf16)
     SLA_LAUNCH(sla::launch_sparse(D, Q, K, mask, alpha, w, O, dos, dol, s), "sparse kernel");
   else
     SLA_LAUNCH(sla::launch_sparse_f32(D, Q, K, V, mask, alpha, w, O, dos, dol, s), "sparse kernel");

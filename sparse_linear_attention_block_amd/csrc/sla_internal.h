@@ -33,21 +33,27 @@ struct Work {
   void* Hx;           // [BH, Nb, NN] per query block: H_i^T (c-major) then Z_i; bf16 or f32
   uint16_t* ind;      // bf16 only: [BH, Nbp/32, Nb128, 32] marginal indicator (Mc == 0) as 0/1,
                       // one 32-key slab per k step, 16-byte chunks swizzled by row
-  uint16_t* vt;       // bf16 only: [BH, Nb, d, 64] V^T of every key block (zero past N)
-  int8_t* q8;         // quant only: [BH, N, d] int8 Q
-  int8_t* k8;         // quant only: [BH, N, d] int8 K
-  float* qs;          // quant only: [BH, Nb] per-block scales of Q
-  float* ks;          // quant only: [BH, Nb] per-block scales of K
-  uint8_t* v8t;       // quant only: [BH, Nb, d, 64] fp8 e4m3 V^T
+  uint16_t* vt;       // bf16 without quant: [BH, Nb, d, 64] V^T of every key block (zero past N)
+  float* qkmean;      // quant only: [2, BH, d] channel means of Q and K over the N tokens
+  int8_t* k8;         // quant only: [BH, Nb*64, d] int8 of K - mean(K), zero rows past N;
+                      // bytes of each row in the score product's k-slot order (k_quant.hip)
+  float* ks;          // quant only: [BH, Nb] per-block scales of k8
+  float* kb;          // quant only: [BH, Nb*64] per-key bias mean(Q).(K - mean(K)), 0 past N
+  uint8_t* v8t;       // quant only: [BH, Nb, d, 4, 16] fp8 e4m3 V^T (see the h/z kernel)
   float* vs;          // quant only: [BH, Nb] per-block scales of V
 };
 
 size_t carve(const Dims& D, void* base, Work* w);  // returns bytes needed (base may be NULL)
 
 // ---- launchers (each enqueues one or more kernels on `s`, returns hipError_t)
+hipError_t launch_pool_sum(const Dims& D, const void* Q, const void* K, double* raw,
+                           hipStream_t s);
 hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const float* proj_q,
                             const float* proj_k, int proj_hs, double* raw, double* pq, double* pk,
                             hipStream_t s);
+hipError_t launch_quant_k(const Dims& D, const void* K, const Work& w, hipStream_t s);
+hipError_t launch_sparse_q8(const Dims& D, const void* Q, const int8_t* mask, const float* alpha,
+                            const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
 hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8_t* mask,
                          double* dbg_logits, hipStream_t s);
 hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w, hipStream_t s);
@@ -59,7 +65,5 @@ hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const int8
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,
                              const int8_t* mask, const float* alpha, const Work& w, void* O,
                              float* dbg_os, float* dbg_ol, hipStream_t s);
-hipError_t launch_quant_qk(const Dims& D, const void* Q, const void* K, const Work& w,
-                           hipStream_t s);
 
 }  // namespace sla
