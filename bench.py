@@ -27,6 +27,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 BASELINE_TFLOPS = 2996.0  # SLA forward kernel at 95% sparsity, Wan2.1-1.3B (SLA paper summary, Fig. 6)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_8BIT_TFLOPS = 5000.0  # MI355X dense fp8 MFMA (int8: 5.0 POP/s)
 PEAK_HBM_GBS = 8000.0
 KERNELS = ["pool_proj", "score_select", "hz", "linear_sum", "sparse_attn_mix"]
 KERNEL_SOURCES = {"sparse_attn_mix": "k_sparse.hip", "hz": "k_hz.hip", "linear_sum": "k_linear.hip",
@@ -60,8 +61,11 @@ def pages_flop_fraction(kh, N, d):
     return kh + (2.0 * N * d * d) / (4.0 * N * N * d)
 
 
-def kernel_bytes(B, H, N, d, Nb, n_h):
-    """Compulsory HBM bytes of each bf16 kernel per launch (each tensor once)."""
+def kernel_bytes(B, H, N, d, Nb, n_h, quant=False):
+    """Compulsory HBM bytes of each bf16 kernel per launch (each tensor once).
+    With the 8-bit sparse branch the h/z stage also reads K once more and
+    writes int8 K, its key bias and fp8 V^T in place of bf16 V^T, and the
+    sparse kernel reads those 8-bit tiles."""
     X = 2.0 * B * H * N * d
     BH = B * H
     NN = d * d + d
@@ -69,6 +73,16 @@ def kernel_bytes(B, H, N, d, Nb, n_h):
     hx = 2.0 * BH * Nbp * NN
     Hx = 2.0 * BH * Nb * NN
     vt = 2.0 * BH * Nb * d * 64
+    X8 = BH * Nb * 64 * d * 1.0     # one 8-bit copy, whole blocks
+    kbias = 4.0 * BH * Nb * 64
+    if quant:
+        return {
+            "pool_proj": 2 * X + 2 * 8.0 * BH * Nb * d,
+            "score_select": 2 * 8.0 * BH * Nb * d + BH * Nb * Nb,
+            "hz": 2 * X + hx + X8 + X + X8 + kbias,
+            "linear_sum": hx + Hx + BH * Nb * Nb,
+            "sparse_attn_mix": X + X8 + kbias + X8 + Hx + X,
+        }
     return {
         "pool_proj": 2 * X + 2 * 8.0 * BH * Nb * d,
         "score_select": 2 * 8.0 * BH * Nb * d + BH * Nb * Nb,
@@ -86,7 +100,7 @@ def _source_sha(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic_from_profile(kernel, workload):
+def _traffic_from_profile(kernel, workload, source):
     """HBM bytes per launch from a committed counter summary of the same kernel
     source and workload, or None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.json")
@@ -95,7 +109,7 @@ def _traffic_from_profile(kernel, workload):
     try:
         with open(path) as f:
             rec = json.load(f)
-        if rec.get("source_sha") != _source_sha(KERNEL_SOURCES[kernel]):
+        if rec.get("source_sha") != _source_sha(source):
             return None
         return float(rec["bytes_per_launch"])
     except (OSError, ValueError, KeyError):
@@ -145,6 +159,9 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--hbm-calib-mib", type=int, default=0,
+                    help="before the warm-up, copy a buffer of this many MiB three times "
+                         "(a plain copy kernel of known size, to scale HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the SLA2 forward pass is built and timed on a "
@@ -168,6 +185,15 @@ def main():
     plan = sla.Plan(q, k, v, pq, pk, al, x.kh, x.kl, quant=cfg.quant)
     B, H, N, d, Nb = plan.dims
     _, n_h, n_l = sla.block_counts(N, x.kh, x.kl, B=B, H=H, d=d, dtype=cfg.dtype)
+    if args.hbm_calib_mib > 0:
+        src = torch.ones(args.hbm_calib_mib * 2 ** 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: 3 x {args.hbm_calib_mib} MiB read + written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     for _ in range(args.warmup):
         plan.run()
@@ -193,8 +219,10 @@ def main():
     k5_flops = sparse_kernel_flops(B, H, Nb, n_h, d)
     k5_ms = per_kernel["sparse_attn_mix"]
     achieved = k5_flops / (k5_ms * 1e-3) / 1e12
-    traffic = _traffic_from_profile("sparse_attn_mix", cfg.name)
-    kb = kernel_bytes(B, H, N, d, Nb, n_h)
+    peak = PEAK_8BIT_TFLOPS if cfg.quant else PEAK_BF16_TFLOPS
+    k5_src = "k_sparse_q8.hip" if cfg.quant else KERNEL_SOURCES["sparse_attn_mix"]
+    traffic = _traffic_from_profile("sparse_attn_mix", cfg.name, k5_src)
+    kb = kernel_bytes(B, H, N, d, Nb, n_h, cfg.quant)
     gbs = {name: kb[name] / (per_kernel[name] * 1e-3) / 1e9 for name in KERNELS}
     print(f"[bench] {cfg.name}: {ms:.3f} ms/step, per kernel (ms) " +
           ", ".join(f"{n}={t:.4f}" for n, t in per_kernel.items()), file=sys.stderr, flush=True)
@@ -210,14 +238,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / BASELINE_TFLOPS, 3) if args.config == 3 else None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": ("i8+fp8 (sparse branch), bf16 (linear branch)" if cfg.quant
+                  else "bf16" if cfg.dtype == "bf16" else "f32"),
         "data": "synthetic: seeded video-DiT-shaped Q/K/V (3-axis sin/cos position field + noise), "
                 "calibrated to the pages' attention-weight shares",
         "config": {"workload": cfg.name, "B": B, "H": H, "N": N, "d": d, "kh": x.kh, "kl": x.kl,
                    "Nb": Nb, "n_h": n_h, "n_l": n_l, "quant": cfg.quant,
                    "sparsity": round(1 - n_h / Nb, 4)},
         "roofline": {"kernel": "sparse_attn_mix", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "flops_per_launch": k5_flops, "ms_per_launch": round(k5_ms, 5)},
         "kernels_ms": {n: round(t, 5) for n, t in per_kernel.items()},
         "kernels_hbm_gbs": {n: round(t, 1) for n, t in gbs.items()},

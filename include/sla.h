@@ -58,9 +58,12 @@ typedef enum { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype;
 typedef enum {
   SLA_QUANT_NONE = 0,
   /* 8-bit sparse branch (SLA2 article, quantisation-aware paragraph): Q and
-   * K as int8 and V as fp8 e4m3, each with one absmax scale per 64-token
-   * block; P as fp8 e4m3 with one scale per row of every key tile.
-   * Requires dtype == SLA_BF16. The linear branch stays bf16. */
+   * K minus their channel means over the N tokens as int8 (the Q mean enters
+   * as an exact per-key float32 bias, the K mean cancels in the softmax) and
+   * V as fp8 e4m3, each with one absmax scale per 64-token block; P as fp8
+   * e4m3 with one scale per query row and pair of 64-key tiles.
+   * Requires dtype == SLA_BF16. The linear branch stays bf16; the mask is
+   * decided from the unquantised inputs. */
   SLA_QUANT_I8QK_F8PV = 1
 } sla_quant;
 
