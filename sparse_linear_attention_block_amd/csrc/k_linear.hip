@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kTN = 256;  // n per workgroup
 constexpr int kTI = 128;  // query blocks per workgroup
+constexpr int kOS = kTN + 8;  // row stride of the staged output (bf16)
 
 // The marginal indicator M01[i][j] = (Mc[i][j] == 0) as bf16 0/1, one
 // [Nb128][32] slab per 32-key step; chunk q (keys 8q..8q+7 of the step) of row
@@ -56,15 +57,19 @@ __global__ __launch_bounds__(256) void k_indicator(const int8_t* __restrict__ ma
 // blocks. The hx operand (4 key blocks per 8-byte word, as written by the h/z
 // kernel) goes straight from global memory to registers one step ahead; the
 // indicator slab of a step arrives in LDS by direct asynchronous copies,
-// double-buffered, one LDS barrier per step. Workgroups are remapped so that
-// the row tiles of one n range run back to back on one XCD and share hx in L2.
+// double-buffered, one LDS barrier per step. The finished tile is staged in LDS
+// in two halves and written as contiguous 16-byte stores along each row.
+// Workgroups are remapped so that the row tiles of one n range run back to back
+// on one XCD and share hx in L2.
 __global__ __launch_bounds__(256, 2) void k_linear_bf16(const uint16_t* __restrict__ ind,
                                                         const uint16_t* __restrict__ hx,
                                                         uint16_t* __restrict__ Hx, int Nb, int Nbp,
                                                         int Nb128, int NN, int ntn, int nti) {
   __shared__ __attribute__((aligned(16))) uint16_t bA[kTI * 32];
   __shared__ __attribute__((aligned(16))) uint16_t bB[kTI * 32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t ost[64 * kOS];  // half the output tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int it = id % nti;
@@ -126,20 +131,33 @@ __global__ __launch_bounds__(256, 2) void k_linear_bf16(const uint16_t* __restri
     step(s, bA, bB, aA, aB);
     if (s + 1 < S) step(s + 1, bB, bA, aB, aA);
   }
+  // the output tile goes out in two halves of 64 query blocks, staged in LDS so
+  // that every row segment of 256 columns is written as contiguous 16-byte stores
 #pragma unroll
-  for (int n2 = 0; n2 < 8; ++n2) {
-    const int i = i0 + 16 * n2 + l16;
-    if (i >= Nb) continue;
-    uint16_t* orow = Hx + ((size_t)bh * Nb + i) * NN;
+  for (int half = 0; half < 2; ++half) {
+    if (half) __syncthreads();  // the first half has been copied out
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int n = n0 + 16 * mt + 4 * g;
-      if (n < NN) {
+    for (int n4 = 0; n4 < 4; ++n4) {
+      const int n2 = 4 * half + n4;
+      const int il = 16 * n4 + l16;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
         uint2 w;
         w.x = pack_bf2(acc[mt][n2][0], acc[mt][n2][1]);
         w.y = pack_bf2(acc[mt][n2][2], acc[mt][n2][3]);
-        *reinterpret_cast<uint2*>(orow + n) = w;
+        *reinterpret_cast<uint2*>(ost + il * kOS + 64 * wave + 16 * mt + 4 * g) = w;
       }
+    }
+    __syncthreads();
+    const int nbase = nt * kTN;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int x = 256 * u + tid;          // 64 rows x 32 chunks of 16 bytes
+      const int row = x >> 5, ch = x & 31;
+      const int i = i0 + 64 * half + row, n = nbase + 8 * ch;
+      if (i < Nb && n < NN)
+        *reinterpret_cast<uint4*>(Hx + ((size_t)bh * Nb + i) * NN + n) =
+            *reinterpret_cast<const uint4*>(ost + row * kOS + 8 * ch);
     }
   }
 }

@@ -5,14 +5,16 @@
 // -1 for the bottom kl%, 0 otherwise). Softmax is monotone in each row, so the
 // ranking is taken on the logits themselves and Pc is never materialised.
 //
-// One workgroup owns R query-block rows of one (batch, head). Phase 1 forms
-// the R x Nb float64 logits in LDS (k-bar rows stream from L2). Phase 2 gives
-// each row to one wave, which finds the two class boundaries without sorting:
+// k_logits: the float64 logits of one (batch, head) as a GEMM on float64 MFMA
+//   16x16x4, one 64 x 64 tile per workgroup: the 64 pooled keys of the tile are
+//   staged once in LDS (padded rows), each wave keeps its 16 pooled queries in
+//   registers. The logits go to HBM ([B*H, Nb, Nb] float64).
+// k_classify: one wave per row finds the two class boundaries without sorting:
 //  * every logit is rounded to float32 and mapped to an order-preserving
 //    uint32 key (round-to-nearest is monotone, so key order never contradicts
 //    float64 order);
-//  * a 32-step bitwise search over the key finds the n_h-th largest key T and
-//    the n_l-th smallest key L, counting with wave ballots;
+//  * a radix select (four 8-bit passes over a per-wave LDS histogram) finds
+//    the n_h-th largest key T and the n_l-th smallest key L;
 //  * keys strictly above T are critical, strictly below L negligible; the few
 //    elements whose key equals T (or L) are ordered exactly by their float64
 //    logit and then by block index (lower index first), which reproduces the
@@ -34,10 +36,71 @@ __device__ __forceinline__ int wave_count(bool p) {
   return __popcll(__ballot(p));
 }
 
-// One wave classifies one row of Nb logits held in LDS (Nb <= 64 * kMaxE).
+// The k-th largest (from_top) or k-th smallest valid key of a wave's row,
+// 1 <= k <= number of valid keys: four 8-bit radix passes, each a 256-bin
+// histogram in the wave's own LDS slice of the keys that match the digits found
+// so far, scanned across lanes to find the bin where the running count
+// reaches k. Equal keys are counted with their multiplicity, so the result is
+// the value v with #(keys beyond v) < k <= #(keys at or beyond v).
+template <int kMaxE>
+__device__ uint32_t radix_select(const uint32_t* key, int E, int Nb, int k, bool from_top,
+                                 uint32_t* __restrict__ hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[64 * q + lane] = 0u;
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+    for (int e = 0; e < kMaxE; ++e) {
+      if (e >= E) break;
+      const int j = lane + 64 * e;
+      if (j < Nb && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    // lane l owns the order positions 4l .. 4l+3 (bins from the top or from the bottom)
+    int c[4], tot = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int o = 4 * lane + q;
+      c[q] = (int)hist[from_top ? 255 - o : o];
+      tot += c[q];
+    }
+    int incl = tot;  // inclusive scan over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    const int excl = incl - tot;
+    const uint64_t hit = __ballot(excl < need && incl >= need);
+    const int hl = __ffsll((unsigned long long)hit) - 1;
+    int before = excl, digit = 0;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!found && before + c[q] >= need) {
+        digit = from_top ? 255 - (4 * lane + q) : 4 * lane + q;
+        found = true;
+      } else if (!found) {
+        before += c[q];
+      }
+    }
+    digit = __shfl(digit, hl);
+    before = __shfl(before, hl);
+    need -= before;
+    prefix |= (uint32_t)digit << shift;
+    pmask |= 0xffu << shift;
+  }
+  return prefix;
+}
+
+// One wave classifies one row of Nb float64 logits (Nb <= 64 * kMaxE).
 template <int kMaxE>
 __device__ void classify_row(const double* __restrict__ lg, int Nb, int n_h, int n_l,
-                             int8_t* __restrict__ mrow) {
+                             int8_t* __restrict__ mrow, uint32_t* __restrict__ hist) {
   const int lane = threadIdx.x & 63;
   const int E = (Nb + 63) >> 6;
   uint32_t key[kMaxE];
@@ -68,20 +131,9 @@ __device__ void classify_row(const double* __restrict__ lg, int Nb, int n_h, int
     return c;
   };
 
-  // T: largest key with at least n_h keys >= T; L: smallest key with at least n_l keys <= L
-  uint32_t T = 0, L = 0xffffffffu;
-  if (n_h > 0) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      if (cnt_ge(cand) >= n_h) T = cand;
-    }
-  }
-  if (n_l > 0) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = L & ~(1u << bit);
-      if (cnt_le(cand) >= n_l) L = cand;
-    }
-  }
+  // T: the n_h-th largest key; L: the n_l-th smallest key
+  const uint32_t T = n_h > 0 ? radix_select<kMaxE>(key, E, Nb, n_h, true, hist) : 0u;
+  const uint32_t L = n_l > 0 ? radix_select<kMaxE>(key, E, Nb, n_l, false, hist) : 0xffffffffu;
   // sizes of the strict parts and of the tie groups at the two boundaries
   const int gt_h = (n_h > 0 && T != 0xffffffffu) ? cnt_ge(T + 1) : 0;
   const int need_h = n_h > 0 ? n_h - gt_h : 0;
@@ -132,69 +184,79 @@ __device__ void classify_row(const double* __restrict__ lg, int Nb, int n_h, int
   }
 }
 
-template <int kMaxE>
-__global__ __launch_bounds__(256) void k_select(const double* __restrict__ pq,
+template <int D>
+__global__ __launch_bounds__(256) void k_logits(const double* __restrict__ pq,
                                                 const double* __restrict__ pk,
-                                                int8_t* __restrict__ mask,
-                                                double* __restrict__ dbg_logits, int Nb, int d,
-                                                int n_h, int n_l, int R) {
-  extern __shared__ double lds[];
-  double* qs = lds;            // [8][d], rows past the workgroup's R are zero
-  double* lg = lds + 8 * d;    // [R][Nb]
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * R;
-  const int nr = min(R, Nb - i0);
-  const double* Pq = pq + ((size_t)bh * Nb + i0) * d;
-  const double* Pk = pk + (size_t)bh * Nb * d;
-  for (int x = tid; x < 8 * d; x += 256) qs[x] = x < nr * d ? Pq[x] : 0.0;  // rows past nr: 0
+                                                double* __restrict__ lg, int Nb) {
+  constexpr int KS = D / 4;   // k steps of the 16x16x4 product
+  constexpr int PS = D + 4;   // padded LDS row stride (doubles)
+  __shared__ __attribute__((aligned(16))) double kt[64 * PS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
+  const double* Pk = pk + ((size_t)bh * Nb + j0) * D;
+  for (int x = tid; x < 64 * D / 2; x += 256) {  // key rows past Nb are zero
+    const int row = x / (D / 2), c2 = x % (D / 2);
+    const double2 v = j0 + row < Nb ? reinterpret_cast<const double2*>(Pk + (size_t)row * D)[c2]
+                                    : make_double2(0.0, 0.0);
+    *reinterpret_cast<double2*>(&kt[row * PS + 2 * c2]) = v;
+  }
+  const int ir = min(i0 + 16 * wave + l16, Nb - 1);  // rows past Nb are never stored
+  const double* qrow = pq + ((size_t)bh * Nb + ir) * D;
+  double a[KS];                                       // A[row l16][k = 4ks + g]
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) a[ks] = qrow[4 * ks + g];
   __syncthreads();
-  const double sd = sqrt((double)d);
-  // one key row per thread; its d values arrive in batches of 16 double2
-  // loads issued back to back, so each batch costs one memory latency
-  for (int j = tid; j < Nb; j += 256) {
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const double2* kr = reinterpret_cast<const double2*>(Pk + (size_t)j * d);
-    for (int cb = 0; cb < d / 2; cb += 16) {
-      double2 kv[16];
+  typedef double f64x4 __attribute__((__vector_size__(4 * sizeof(double))));
+  f64x4 acc[4];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) kv[u] = kr[cb + u];
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const double2 qv = *reinterpret_cast<const double2*>(&qs[r * d + 2 * (cb + u)]);
-          acc[r] = fma(qv.x, kv[u].x, acc[r]);
-          acc[r] = fma(qv.y, kv[u].y, acc[r]);
-        }
+    for (int ct = 0; ct < 4; ++ct)
+      acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[ks], kt[(16 * ct + l16) * PS + 4 * ks + g],
+                                                     acc[ct], 0, 0, 0);
+  const double sd = sqrt((double)D);
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int j = j0 + 16 * ct + l16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + 16 * wave + g + 4 * e;       // f64 16x16 layout: D[g + 4e][l16]
+      if (i < Nb && j < Nb) lg[((size_t)bh * Nb + i) * Nb + j] = acc[ct][e] / sd;
     }
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      if (r < nr) lg[r * Nb + j] = acc[r] / sd;
   }
-  __syncthreads();
-  if (dbg_logits) {
-    double* out = dbg_logits + ((size_t)bh * Nb + i0) * Nb;
-    for (int x = tid; x < nr * Nb; x += 256) out[x] = lg[x];
-  }
-  const int wave = tid >> 6;
-  for (int r = wave; r < nr; r += 4)
-    classify_row<kMaxE>(lg + (size_t)r * Nb, Nb, n_h, n_l, mask + ((size_t)bh * Nb + i0 + r) * Nb);
+}
+
+// one wave per row of the [rows, Nb] logits
+template <int kMaxE>
+__global__ __launch_bounds__(256) void k_classify(const double* __restrict__ lg,
+                                                  int8_t* __restrict__ mask, int Nb, int n_h,
+                                                  int n_l, int rows) {
+  __shared__ uint32_t hist[4][256];  // one histogram per wave
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;  // whole wave; the kernel has no barrier
+  classify_row<kMaxE>(lg + (size_t)row * Nb, Nb, n_h, n_l, mask + (size_t)row * Nb, hist[wave]);
 }
 
 }  // namespace
 
 hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8_t* mask,
-                         double* dbg_logits, hipStream_t s) {
-  // R rows per workgroup, bounded by LDS (logits + pooled queries in float64)
-  int R = 8;  // the logits loop always computes 8 rows; fewer are kept when LDS is short
-  while (R > 1 && (size_t)8 * D.d * sizeof(double) + (size_t)R * D.Nb * sizeof(double) > 64 * 1024) R >>= 1;
-  const size_t lds = ((size_t)8 * D.d + (size_t)R * D.Nb) * sizeof(double);
-  dim3 grid((D.Nb + R - 1) / R, D.BH);
+                         double* lg, hipStream_t s) {
+  const int nt = (D.Nb + 63) / 64;
+  dim3 g1(nt, nt, D.BH);
+  if (D.d == 128)
+    hipLaunchKernelGGL(k_logits<128>, g1, dim3(256), 0, s, pq, pk, lg, D.Nb);
+  else
+    hipLaunchKernelGGL(k_logits<64>, g1, dim3(256), 0, s, pq, pk, lg, D.Nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows = D.BH * D.Nb;
   const int E = (D.Nb + 63) / 64;
-  auto kern = E <= 8 ? k_select<8> : E <= 16 ? k_select<16> : E <= 32 ? k_select<32> : k_select<64>;
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, pq, pk, mask, dbg_logits, D.Nb, D.d,
-                     D.n_h, D.n_l, R);
+  auto kern = E <= 8 ? k_classify<8> : E <= 16 ? k_classify<16> : E <= 32 ? k_classify<32> : k_classify<64>;
+  hipLaunchKernelGGL(kern, dim3((rows + 3) / 4), dim3(256), 0, s, lg, mask, D.Nb, D.n_h, D.n_l, rows);
   return hipGetLastError();
 }
 

@@ -85,6 +85,7 @@ size_t carve(const Dims& D, void* base, Work* w) {
   x.pooled_q = (double*)take(BH * D.Nb * D.d * sizeof(double));
   x.pooled_k = (double*)take(BH * D.Nb * D.d * sizeof(double));
   x.pooled_raw = (double*)take(2 * BH * D.Nb * D.d * sizeof(double));
+  x.logits = (double*)take(BH * D.Nb * D.Nb * sizeof(double));
   if (D.bf16) {
     x.hx = take(BH * (D.Nbp / 4) * D.NN * 4 * sizeof(uint16_t));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(uint16_t));
@@ -198,7 +199,8 @@ int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const 
     SLA_LAUNCH(sla::launch_pool_proj(D, Q, K, proj_q, proj_k, proj_hs, w.pooled_raw, w.pooled_q, w.pooled_k, s),
                "pool/proj kernel");
     SLA_LAUNCH(mark(1), "event record");
-    SLA_LAUNCH(sla::launch_select(D, w.pooled_q, w.pooled_k, mask_out, dbg ? dbg->logits : nullptr, s),
+    SLA_LAUNCH(sla::launch_select(D, w.pooled_q, w.pooled_k, mask_out,
+                                  (dbg && dbg->logits) ? dbg->logits : w.logits, s),
                "score/select kernel");
     SLA_LAUNCH(mark(2), "event record");
     if (dbg && dbg->pooled_q)

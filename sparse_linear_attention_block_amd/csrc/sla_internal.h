@@ -28,6 +28,7 @@ struct Work {
   double* pooled_q;   // [BH, Nb, d]
   double* pooled_k;   // [BH, Nb, d]
   double* pooled_raw; // [2, BH, Nb, d] block means before the router projection
+  double* logits;     // [BH, Nb, Nb] pooled logits pool(Q) pool(K)^T / sqrt(d)
   void* hx;           // bf16: [BH, Nbp/4, NN, 4] (four key blocks interleaved per column)
                       // f32:  [BH, Nb, NN]
   void* Hx;           // [BH, Nb, NN] per query block: H_i^T (c-major) then Z_i; bf16 or f32
@@ -55,7 +56,7 @@ hipError_t launch_quant_k(const Dims& D, const void* K, const Work& w, hipStream
 hipError_t launch_sparse_q8(const Dims& D, const void* Q, const int8_t* mask, const float* alpha,
                             const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
 hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8_t* mask,
-                         double* dbg_logits, hipStream_t s);
+                         double* lg, hipStream_t s);  // lg: [BH, Nb, Nb] float64 logits (written)
 hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w, hipStream_t s);
 hipError_t launch_indicator(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
 hipError_t launch_linear(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
