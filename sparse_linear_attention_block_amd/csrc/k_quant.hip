@@ -29,16 +29,26 @@
 namespace sla {
 namespace {
 
-__global__ __launch_bounds__(256) void k_qk_mean(const double* __restrict__ raw,
-                                                 float* __restrict__ qkmean, int N, int d,
-                                                 int Nb, int BH) {
-  __shared__ double part[256];
+__global__ __launch_bounds__(1024) void k_qk_mean(const double* __restrict__ raw,
+                                                  float* __restrict__ qkmean, int N, int d,
+                                                  int Nb, int BH) {
+  __shared__ double part[1024];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x, z = blockIdx.y;
-  const int RG = 256 / d, c = tid % d, rg = tid / d;
+  const int RG = 1024 / d, c = tid % d, rg = tid / d;
   const double* src = raw + ((size_t)z * BH + bh) * Nb * d;
+  // 8 block means in flight per thread (rows past Nb re-read a valid row, weight 0)
   double s = 0.0;
-  for (int j = rg; j < Nb; j += RG) s += (double)min(kBlock, N - j * kBlock) * src[(size_t)j * d + c];
+  for (int j0 = rg; j0 < Nb; j0 += 8 * RG) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(size_t)min(j0 + u * RG, Nb - 1) * d + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * RG;
+      if (j < Nb) s += (double)min(kBlock, N - j * kBlock) * v[u];
+    }
+  }
   part[tid] = s;
   __syncthreads();
   if (tid < d) {
@@ -67,8 +77,7 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t* __restrict__ K,
 #pragma unroll
   for (int m = 0; m < CPT; ++m) {
     const int f0 = 8 * (qt + 4 * m);
-    const uint4 w = valid ? *reinterpret_cast<const uint4*>(K + ((size_t)bh * N + t) * D + f0)
-                          : make_uint4(0, 0, 0, 0);
+    const uint4 w = *reinterpret_cast<const uint4*>(K + ((size_t)bh * N + min(t, N - 1)) * D + f0);
     const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
     const float4 k0 = *reinterpret_cast<const float4*>(km + f0);
     const float4 k1 = *reinterpret_cast<const float4*>(km + f0 + 4);
@@ -114,7 +123,7 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t* __restrict__ K,
 
 hipError_t launch_quant_k(const Dims& D, const void* K, const Work& w, hipStream_t s) {
   if (!D.quant || !D.bf16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_qk_mean, dim3(D.BH, 2), dim3(256), 0, s, w.pooled_raw, w.qkmean, D.N, D.d,
+  hipLaunchKernelGGL(k_qk_mean, dim3(D.BH, 2), dim3(1024), 0, s, w.pooled_raw, w.qkmean, D.N, D.d,
                      D.Nb, D.BH);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

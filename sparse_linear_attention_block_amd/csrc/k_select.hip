@@ -104,10 +104,14 @@ __device__ void classify_row(const double* __restrict__ lg, int Nb, int n_h, int
   const int lane = threadIdx.x & 63;
   const int E = (Nb + 63) >> 6;
   uint32_t key[kMaxE];
+  double v[kMaxE];
+  // all loads first (slots past Nb re-read the last logit), then the keys
+#pragma unroll
+  for (int e = 0; e < kMaxE; ++e) v[e] = lg[min(lane + 64 * e, Nb - 1)];
 #pragma unroll
   for (int e = 0; e < kMaxE; ++e) {
     const int j = lane + 64 * e;
-    key[e] = (e < E && j < Nb) ? order_key(lg[j]) : 0u;
+    key[e] = (e < E && j < Nb) ? order_key(v[e]) : 0u;
   }
   // counts over valid elements only: invalid slots carry key 0 and are masked
   auto cnt_ge = [&](uint32_t t) {
@@ -195,11 +199,19 @@ __global__ __launch_bounds__(256) void k_logits(const double* __restrict__ pq,
   const int l16 = lane & 15, g = lane >> 4;
   const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
   const double* Pk = pk + ((size_t)bh * Nb + j0) * D;
-  for (int x = tid; x < 64 * D / 2; x += 256) {  // key rows past Nb are zero
-    const int row = x / (D / 2), c2 = x % (D / 2);
-    const double2 v = j0 + row < Nb ? reinterpret_cast<const double2*>(Pk + (size_t)row * D)[c2]
-                                    : make_double2(0.0, 0.0);
-    *reinterpret_cast<double2*>(&kt[row * PS + 2 * c2]) = v;
+  // key rows past Nb re-read row Nb - 1 (their columns are never stored); all
+  // loads are issued before the first LDS write
+  constexpr int NL = 64 * D / 2 / 256;
+  double2 kv[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int x = 256 * u + tid, row = x / (D / 2), c2 = x % (D / 2);
+    kv[u] = reinterpret_cast<const double2*>(Pk + (size_t)min(row, Nb - 1 - j0) * D)[c2];
+  }
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int x = 256 * u + tid, row = x / (D / 2), c2 = x % (D / 2);
+    *reinterpret_cast<double2*>(&kt[row * PS + 2 * c2]) = kv[u];
   }
   const int ir = min(i0 + 16 * wave + l16, Nb - 1);  // rows past Nb are never stored
   const double* qrow = pq + ((size_t)bh * Nb + ir) * D;

@@ -26,11 +26,15 @@
 //   O^T += V^T P^T MFMA 16x16x32 with P^T straight from registers: a lane's 8
 //                  k slots are its keys {4g..4g+3, 16+4g..16+4g+3}, and the h/z
 //                  kernel stored V^T in that key order.
+// All K fragments of a tile are read before its first product and the V^T
+// fragments right after the last one, so their LDS latency overlaps. While the
+// last tile is processed, H_i^T (from K4's output, rows swizzled like K) is
+// copied into the idle tile buffer and Z_i into the spent critical list.
 // The two key halves are combined through LDS (max-rescaled partial sums);
 // each wave then finishes half the features of its 32 queries: O_s = acc / l,
 // phi(Q) (softmax over the features in f32, rounded to bf16), num^T =
-// H_i^T phi(Q)^T on MFMA with H_i^T read from K4's output, den = phi(Q).Z_i,
-// O = alpha O_s + (1 - alpha) O_l, staged in LDS and written as full rows.
+// H_i^T phi(Q)^T on MFMA, den = phi(Q).Z_i, O = alpha O_s + (1 - alpha) O_l,
+// staged in LDS and written as full rows.
 // Workgroups are remapped so that each XCD walks a contiguous range of
 // (batch, head, query block): neighbouring query blocks share most critical
 // key tiles, which then come from the XCD's L2.
@@ -56,6 +60,7 @@ struct FaCfg {
   static constexpr int FT = D / 16;                // feature tiles of O
   static constexpr int FTH = FT / 2;               // feature tiles each wave finishes
   static constexpr int OS = D + 8;                 // LDS row stride of the staged output
+  static constexpr int HINSTR = D * D / 8 / 256;   // 16-byte copies per lane of H_i^T
 };
 
 // Workgroup: 4 waves, one query block (64 queries). Wave w takes key half
@@ -72,13 +77,13 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     float* __restrict__ dbg_os, float* __restrict__ dbg_ol, int H, int N, int Nb) {
   using Cf = FaCfg<D>;
   constexpr int C = Cf::C, TILE = Cf::TILE, INSTR = Cf::INSTR, NN = Cf::NN;
-  constexpr int KSTEPS = Cf::KSTEPS, FT = Cf::FT, FTH = Cf::FTH, OS = Cf::OS;
+  constexpr int KSTEPS = Cf::KSTEPS, FT = Cf::FT, FTH = Cf::FTH, OS = Cf::OS, HINSTR = Cf::HINSTR;
   constexpr float TAU = 8.0f;  // a stale reference max may lag the tile max by 2^8 at most
   // Two tile buffers (K then V^T each) as distinct LDS objects, so that reads of
   // one provably do not alias the asynchronous copies into the other.
   __shared__ __attribute__((aligned(16))) uint16_t bufA[2 * TILE];
   __shared__ __attribute__((aligned(16))) uint16_t bufB[2 * TILE];
-  __shared__ uint16_t list[kMaxNb];
+  __shared__ __attribute__((aligned(16))) uint16_t list[kMaxNb];  // critical list, then Z_i
   __shared__ float xm[4][2][16];
   __shared__ float xl[4][2][16];
   __shared__ int wsum[4];
@@ -133,6 +138,19 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
       load_lds16(vsrc + (64 * (4 * u + wave) + lane) * 8, dst + TILE + 512 * (4 * u + wave));
     }
   };
+  // H_i^T (d x d, rows swizzled like the K tiles) into a free tile buffer, and
+  // Z_i into the critical-list area, for the epilogue
+  const uint16_t* Hrow = Hx + ((size_t)bh * Nb + i) * NN;
+  uint16_t* zbuf = list;
+  auto issueH = [&](uint16_t* dst) {
+#pragma unroll
+    for (int u = 0; u < HINSTR; ++u) {
+      const int G = 64 * (4 * u + wave) + lane;
+      const int r = G / C, sch = G % C;
+      load_lds16(Hrow + r * D + (sch ^ (r & (C - 1))) * 8, dst + 512 * (4 * u + wave));
+    }
+    if (wave == 0 && lane < C) load_lds16(Hrow + D * D + 8 * lane, zbuf);
+  };
 
   const float sc = kLog2e / sqrtf((float)D);
   f32x4 acc[FT][2];
@@ -147,19 +165,38 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     const int j = list[c];
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of tile c have landed
     lds_barrier();  // all copies of tile c are in LDS; every wave is done with tile c-1
-    if (c + 1 < ncrit) issue(list[c + 1], nxt);
+    if (c + 1 < ncrit)
+      issue(list[c + 1], nxt);
+    else
+      issueH(nxt);  // every wave has read list[c]: the list area is free
+    // all K fragments of the tile first (their LDS latency overlaps), then the products
+    uint4 ka[KSTEPS][2];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int row = 32 * kh + 16 * kt + l16;
+        ka[ks][kt] = *reinterpret_cast<const uint4*>(cur + (row * C + ((4 * ks + g) ^ (row & (C - 1)))) * 8);
+      }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 s[2][2];  // [key tile][query tile]
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s[kt][0] = s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int row = 32 * kh + 16 * kt + l16;
-        const uint4 a = *reinterpret_cast<const uint4*>(cur + (row * C + ((4 * ks + g) ^ (row & (C - 1)))) * 8);
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma_bf16(a, qr[qt][ks], s[kt][qt]);
-      }
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma_bf16(ka[ks][kt], qr[qt][ks], s[kt][qt]);
+    // the V^T fragments of the tile load while the softmax runs
+    const uint16_t* vtile = cur + TILE + kh * D * 32;
+    uint4 va[FT];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      const int c = 16 * ft + l16;
+      va[ft] = *reinterpret_cast<const uint4*>(vtile + c * 32 + 8 * (g ^ ((c >> 1) & 3)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if ((j + 1) * kBlock > N) {  // ragged last block: keys past N take no part
       const int kbase = j * kBlock + 32 * kh + 4 * g;
 #pragma unroll
@@ -210,16 +247,16 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
       pb[qt] = make_uint4(pack_bf2(p[0][0], p[0][1]), pack_bf2(p[0][2], p[0][3]),
                           pack_bf2(p[1][0], p[1][1]), pack_bf2(p[1][2], p[1][3]));
     }
-    const uint16_t* vtile = cur + TILE + kh * D * 32;
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      const int c = 16 * ft + l16;
-      const uint4 a = *reinterpret_cast<const uint4*>(vtile + c * 32 + 8 * (g ^ ((c >> 1) & 3)));
-      acc[ft][0] = mfma_bf16(a, pb[0], acc[ft][0]);
-      acc[ft][1] = mfma_bf16(a, pb[1], acc[ft][1]);
+      acc[ft][0] = mfma_bf16(va[ft], pb[0], acc[ft][0]);
+      acc[ft][1] = mfma_bf16(va[ft], pb[1], acc[ft][1]);
     }
   };
-  if (ncrit > 0) issue(list[0], bufA);
+  if (ncrit > 0)
+    issue(list[0], bufA);
+  else
+    issueH(bufA);
   for (int c = 0; c < ncrit; c += 2) {
     step(c, bufA, bufB);
     if (c + 1 < ncrit) step(c + 1, bufB, bufA);
@@ -229,8 +266,13 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   float lw[2];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) lw[qt] = group4_sum(lp[qt]);
-  __syncthreads();  // every wave is done with the tile buffers
-  float* ex = reinterpret_cast<float*>(bufA);  // [wave][FTH][2][64 lanes][4]
+  // the last tile's buffer takes the exchange and then the staged output; H_i^T
+  // arrived in the other one (bufA when there was no tile)
+  uint16_t* xbuf = (ncrit & 1) ? bufA : bufB;
+  const uint16_t* hbuf = (ncrit & 1) ? bufB : bufA;
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of H_i^T and Z_i
+  __syncthreads();  // every wave is done with the tile buffers; H_i^T and Z_i have landed
+  float* ex = reinterpret_cast<float*>(xbuf);  // [wave][FTH][2][64 lanes][4]
   // the accumulator halves are selected with compile-time indices (a runtime
   // index would send the accumulator array through scratch memory)
   auto send = [&](auto KH) {
@@ -272,13 +314,13 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     }
   };
   if (kh == 0) keep(std::integral_constant<int, 0>{}); else keep(std::integral_constant<int, 1>{});
+  __syncthreads();  // the exchange area becomes the output stage
 
   // ---- linear branch: phi(Q) for the wave's 32 queries, den = phi(Q).Z_i, num^T = H_i^T phi(Q)^T
-  const uint16_t* Hrow = Hx + ((size_t)bh * Nb + i) * NN;
   float zf[KSTEPS * 8];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    const uint4 z = *reinterpret_cast<const uint4*>(Hrow + D * D + 32 * ks + 8 * g);
+    const uint4 z = *reinterpret_cast<const uint4*>(zbuf + 32 * ks + 8 * g);
     const uint32_t zw[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -326,14 +368,15 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     inv_den[qt] = den > 0.f ? 1.0f / den : 0.f;
   }
   const float al = alpha[h];
-  uint16_t* ost = bufB;  // staged output tile [64][OS]
+  uint16_t* ost = xbuf;  // staged output tile [64][OS]
 #pragma unroll
   for (int f = 0; f < FTH; ++f) {
     const int ft = FTH * kh + f;
     f32x4 nm[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(Hrow + (size_t)(16 * ft + l16) * D + 32 * ks + 8 * g);
+      const int hr = 16 * ft + l16;
+      const uint4 a = *reinterpret_cast<const uint4*>(hbuf + (hr * C + ((4 * ks + g) ^ (hr & (C - 1)))) * 8);
       nm[0] = mfma_bf16(a, fq[0][ks], nm[0]);
       nm[1] = mfma_bf16(a, fq[1][ks], nm[1]);
     }
