@@ -136,6 +136,13 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
+// four floats known to lie in [-448, 448] (up to rounding, below the 464 at
+// which the conversion would give NaN) -> four e4m3 bytes, no clamp
+__device__ __forceinline__ uint32_t pack_e4m3x4_nosat(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
 // symmetric int8 code: round-to-nearest-even of x * inv, clamped to +-127
 __device__ __forceinline__ int q_i8(float x, float inv) {
   return (int)fminf(fmaxf(__builtin_rintf(x * inv), -127.0f), 127.0f);

@@ -17,7 +17,9 @@
 //   tokens of each block.
 // k_quant_k: grid (Nb, B*H), one 64-token key block per workgroup: K - k̄ in
 //   float32, absmax over the block (scale absmax / 127, 1 for an all-zero
-//   block), codes round-half-even and clamped to +-127, the bias b per key.
+//   block), codes round-half-even and clamped to +-127, the bias b per key
+//   (stored multiplied by log2(e) / sqrt(d), the unit of the sparse kernel's
+//   scores).
 //   Rows past N are zero with bias 0. The bytes of a row are stored in the
 //   k-slot order of the sparse kernel's int8 16x16x64 product: k step s
 //   (64 bytes), lane group g, byte e holds feature 32 (2s + e / 8) + 8g + e % 8,
@@ -59,6 +61,11 @@ __global__ __launch_bounds__(1024) void k_qk_mean(const double* __restrict__ raw
 }
 
 template <int D>
+__device__ __forceinline__ float kBiasScale() {
+  return 1.4426950408889634f / (D == 128 ? 11.313708498984761f : 8.0f);
+}
+
+template <int D>
 __global__ __launch_bounds__(256) void k_quant_k(const uint16_t* __restrict__ K,
                                                  const float* __restrict__ qkmean,
                                                  int8_t* __restrict__ k8, float* __restrict__ ksc,
@@ -95,7 +102,8 @@ __global__ __launch_bounds__(256) void k_quant_k(const uint16_t* __restrict__ K,
   }
   bias += __shfl_xor(bias, 1);
   bias += __shfl_xor(bias, 2);
-  if (qt == 0) kb[((size_t)bh * Nb + j) * kBlock + r] = valid ? bias : 0.f;
+  // stored in the sparse kernel's log2 score units: b * log2(e) / sqrt(d)
+  if (qt == 0) kb[((size_t)bh * Nb + j) * kBlock + r] = valid ? bias * kBiasScale<D>() : 0.f;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
   if (lane == 0) wmax[wave] = am;

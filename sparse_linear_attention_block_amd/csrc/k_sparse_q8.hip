@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
     const int j0 = __builtin_amdgcn_readfirstlane((int)list[c0]);
     const int j1 = has1 ? __builtin_amdgcn_readfirstlane((int)list[c0 + 1]) : j0;
     const float su0 = sq * ks_b[j0], su1 = sq * ks_b[j1];
-    const float sv0 = vs_b[j0], sv1 = has1 ? vs_b[j1] : 0.f;
+    const float sv0 = vs_b[j0], sv1 = has1 ? vs_b[j1] : 1.f;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of pair p have landed
     lds_barrier();  // all copies of pair p are in LDS; every wave is done with pair p-1
     if (p + 1 < npair) issue(p + 1, nxt);
@@ -206,9 +206,10 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
           s[t][kt] = mfma_i8(a, qr8[ks], s[t][kt]);
         }
     }
-    // dequantised scores plus key bias in the log2 domain; keys past N and a
-    // missing tile take no part
+    // dequantised scores plus key bias (stored already in the log2 domain); keys
+    // past N and a missing tile take no part
     float sf[2][4][4];
+    float tmax[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int j = t ? j1 : j0;
@@ -223,16 +224,12 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool out = !live || (rag && j * kBlock + 16 * kt + 4 * g + r >= N);
-          sf[t][kt][r] = out ? -INFINITY : fmaf((float)s[t][kt][r], su, bv[r] * sc);
+          sf[t][kt][r] = out ? -INFINITY : fmaf((float)s[t][kt][r], su, bv[r]);
         }
+        tmax[t] = fmaxf(tmax[t], fmaxf(fmaxf(sf[t][kt][0], sf[t][kt][1]), fmaxf(sf[t][kt][2], sf[t][kt][3])));
       }
     }
-    float lmax = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        lmax = fmaxf(lmax, fmaxf(fmaxf(sf[t][kt][0], sf[t][kt][1]), fmaxf(sf[t][kt][2], sf[t][kt][3])));
+    const float lmax = fmaxf(tmax[0], tmax[1]);
     if (__ballot(lmax > mref + TAU)) {
       const float tm = group4_max(lmax);
       const float nref = tm > mref + TAU ? tm : mref;
@@ -243,31 +240,33 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
       for (int ft = 0; ft < FT; ++ft) acc[ft] *= fac;
     }
     const float meff = mref == -INFINITY ? 0.0f : mref;  // no valid key yet: every p is 0
-    float ls = 0.f, pmax = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const float sv = t ? sv1 : sv0;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pt = __builtin_amdgcn_exp2f(sf[t][kt][r] - meff);
-          ls += pt;
-          sf[t][kt][r] = pt * sv;  // P' = P~ s_V
-          pmax = fmaxf(pmax, sf[t][kt][r]);
-        }
-    }
-    lp += ls;
-    pmax = group4_max(pmax);
-    const float pinv = pmax > 0.f ? 448.0f / pmax : 0.f;
-    const float sp = pmax * (1.0f / 448.0f);
+    // P' = P~ s_V and its row scale folded into the exponent: with
+    // M = max over the pair's tiles of (tile max + log2 s_V), the fp8 input of a
+    // key of tile t is 2^(s - off_t), off_t = M - log2 s_V(t) - log2 448, at most
+    // 448; s_P = 2^(M - meff) / 448; the tile's share of l (the unquantised
+    // P~ = 2^(s - meff)) is 2^(off_t - meff) times the sum of those inputs.
+    const float lsv0 = __log2f(sv0), lsv1 = has1 ? __log2f(sv1) : 0.f;
+    const float Mq = group4_max(fmaxf(tmax[0] + lsv0, tmax[1] + lsv1));
+    constexpr float kLog2_448 = 8.807354922057604f;
+    const float off0 = Mq - lsv0 - kLog2_448, off1 = Mq - lsv1 - kLog2_448;
+    float ssum[2] = {0.f, 0.f};
     i32x8 pb;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      const float off = t ? off1 : off0;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        pb[4 * t + kt] = (int)pack_e4m3x4(sf[t][kt][0] * pinv, sf[t][kt][1] * pinv,
-                                          sf[t][kt][2] * pinv, sf[t][kt][3] * pinv);
+      for (int kt = 0; kt < 4; ++kt) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = __builtin_amdgcn_exp2f(sf[t][kt][r] - off);
+          ssum[t] += e[r];
+        }
+        pb[4 * t + kt] = (int)pack_e4m3x4_nosat(e[0], e[1], e[2], e[3]);
+      }
+    }
+    lp += ssum[0] * __builtin_amdgcn_exp2f(off0 - meff) + ssum[1] * __builtin_amdgcn_exp2f(off1 - meff);
+    const float sp = __builtin_amdgcn_exp2f(Mq - meff) * (1.0f / 448.0f);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       const int c = 16 * ft + l16;

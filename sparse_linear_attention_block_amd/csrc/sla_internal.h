@@ -39,7 +39,7 @@ struct Work {
   int8_t* k8;         // quant only: [BH, Nb*64, d] int8 of K - mean(K), zero rows past N;
                       // bytes of each row in the score product's k-slot order (k_quant.hip)
   float* ks;          // quant only: [BH, Nb] per-block scales of k8
-  float* kb;          // quant only: [BH, Nb*64] per-key bias mean(Q).(K - mean(K)), 0 past N
+  float* kb;          // quant only: [BH, Nb*64] per-key bias mean(Q).(K - mean(K)) * log2(e)/sqrt(d), 0 past N
   uint8_t* v8t;       // quant only: [BH, Nb, d, 4, 16] fp8 e4m3 V^T (see the h/z kernel)
   float* vs;          // quant only: [BH, Nb] per-block scales of V
 };
