@@ -6,7 +6,8 @@
 // summary, Eq. 3). phi is the softmax over the d features of each key token
 // (SLA explainer, section 3.2; SLA paper summary, Table 2).
 //
-// bf16 path, one workgroup per 4 consecutive key blocks of one (batch, head):
+// bf16 path, one workgroup (8 waves for d = 128, 4 for d = 64) per 4
+// consecutive key blocks of one (batch, head):
 //  1. each block's K and V rows stream in with 16-byte loads (two tokens per
 //     lane), phi(K) is formed in float32 (row max / sum through LDS) and
 //     rounded to bf16, and phi(K)^T and V^T are written to LDS with the
@@ -32,31 +33,34 @@ namespace {
 
 template <int D>
 struct HzCfg {
+  static constexpr int NT = D == 128 ? 512 : 256;  // threads per workgroup
+  static constexpr int NW = NT / 64;               // waves
+  static constexpr int NCG = NT / 32;              // chunk groups (32 token pairs each)
   static constexpr int TS = 72;            // LDS row stride in tokens (144 B, 16-B aligned)
   static constexpr int CHUNKS = D / 8;     // 16-byte chunks per token row
-  static constexpr int CPT = CHUNKS / 8;   // chunks per thread (8 chunk groups)
+  static constexpr int CPT = CHUNKS / NCG; // chunks per thread
   static constexpr int NN = D * D + D;
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __restrict__ K,
                                                  const uint16_t* __restrict__ V,
                                                  uint16_t* __restrict__ hx,
                                                  uint16_t* __restrict__ vt, int N, int Nb,
                                                  int Nb4, uint8_t* __restrict__ v8t,
                                                  float* __restrict__ vsc) {
   using C = HzCfg<D>;
-  constexpr int TS = C::TS, CPT = C::CPT, NN = C::NN;
+  constexpr int TS = C::TS, CPT = C::CPT, NN = C::NN, NT = C::NT, NW = C::NW, NCG = C::NCG;
   __shared__ __attribute__((aligned(16))) uint16_t kT[4][D][TS];
   __shared__ __attribute__((aligned(16))) uint16_t vT[4][D][TS];
-  __shared__ float red[8][64];
+  __shared__ float red[NCG][64];
   __shared__ float tstat[64];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.y;
   const int jq = blockIdx.x;        // group of 4 key blocks
   const int tp = tid & 31;          // token pair
-  const int cg = tid >> 5;          // chunk group 0..7
+  const int cg = tid >> 5;          // chunk group
   const uint16_t* Kb = K + (size_t)bh * N * D;
   const uint16_t* Vb = V + (size_t)bh * N * D;
 
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
     if (tid < 64) {
       float m = red[0][tid];
 #pragma unroll
-      for (int g = 1; g < 8; ++g) m = fmaxf(m, red[g][tid]);
+      for (int g = 1; g < NCG; ++g) m = fmaxf(m, red[g][tid]);
       tstat[tid] = m;
     }
     __syncthreads();
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
     if (tid < 64) {
       float s = 0.f;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) s += red[g][tid];
+      for (int g = 0; g < NCG; ++g) s += red[g][tid];
       tstat[tid] = 1.0f / s;
     }
     __syncthreads();
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   constexpr int CT = D / 16;            // c tiles
-  constexpr int CT_PER_WAVE = CT / 4;   // 2 for D=128, 1 for D=64
+  constexpr int CT_PER_WAVE = CT / NW;  // 1 (D=128, 8 waves; D=64, 4 waves)
   uint16_t* hxg = hx + ((size_t)bh * Nb4 + jq) * NN * 4;
   for (int cti = 0; cti < CT_PER_WAVE; ++cti) {
     const int ct = wave * CT_PER_WAVE + cti;
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
     const int j = 4 * jq + jj;
     if (j >= Nb) break;
     uint16_t* dst = vt + ((size_t)bh * Nb + j) * D * kBlock;
-    for (int x = tid; x < D * 8; x += 256) {
+    for (int x = tid; x < D * 8; x += NT) {
       const int khh = x / (D * 4), rem = x % (D * 4), c = rem >> 2, q = rem & 3;
       const uint2 lo = *reinterpret_cast<const uint2*>(&vT[jj][c][32 * khh + 4 * q]);
       const uint2 hi = *reinterpret_cast<const uint2*>(&vT[jj][c][32 * khh + 16 + 4 * q]);
@@ -244,13 +248,13 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
   // order (kt, r), the k slots one lane group of the 8-bit sparse kernel's
   // 16x16x128 product takes from one tile, and sits at position
   // g ^ ((c >> 1) & 3) against LDS bank conflicts.
-  __shared__ float vmax[4][4];
-  const int cq = tid >> 2, gq = tid & 3;  // rows cq and cq + 64 (D = 128) of chunk gq
+  __shared__ float vmax[4][NW];
+  const int cq = tid >> 2, gq = tid & 3;  // rows cq, cq + NT/4, ... of chunk gq
   float am[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     float m = 0.f;
-    for (int c = cq; c < D; c += 64)
+    for (int c = cq; c < D; c += NT / 4)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const uint2 w = *reinterpret_cast<const uint2*>(&vT[jj][c][16 * kt + 4 * gq]);
@@ -263,8 +267,11 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
   }
   __syncthreads();
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
-    am[jj] = fmaxf(fmaxf(vmax[jj][0], vmax[jj][1]), fmaxf(vmax[jj][2], vmax[jj][3]));
+  for (int jj = 0; jj < 4; ++jj) {
+    am[jj] = vmax[jj][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) am[jj] = fmaxf(am[jj], vmax[jj][w]);
+  }
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int j = 4 * jq + jj;
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(256) void k_hz_bf16(const uint16_t* __restrict__ K,
     const float inv = am[jj] > 0.f ? 448.0f / am[jj] : 1.0f;
     if (tid == 0) vsc[(size_t)bh * Nb + j] = am[jj] > 0.f ? am[jj] / 448.0f : 1.0f;
     uint8_t* dst = v8t + ((size_t)bh * Nb + j) * D * kBlock;
-    for (int c = cq; c < D; c += 64) {
+    for (int c = cq; c < D; c += NT / 4) {
       uint32_t o[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
@@ -339,11 +346,11 @@ hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w,
   if (D.bf16) {
     dim3 grid(D.Nbp / 4, D.BH);
     if (D.d == 128)
-      hipLaunchKernelGGL(k_hz_bf16<128>, grid, dim3(256), 0, s, (const uint16_t*)K,
+      hipLaunchKernelGGL(k_hz_bf16<128>, grid, dim3(HzCfg<128>::NT), 0, s, (const uint16_t*)K,
                          (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4, w.v8t,
                          w.vs);
     else
-      hipLaunchKernelGGL(k_hz_bf16<64>, grid, dim3(256), 0, s, (const uint16_t*)K,
+      hipLaunchKernelGGL(k_hz_bf16<64>, grid, dim3(HzCfg<64>::NT), 0, s, (const uint16_t*)K,
                          (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4, w.v8t,
                          w.vs);
   } else {
