@@ -22,7 +22,9 @@
 //   online softmax per wave against a reference max that is only raised
 //                  when some score exceeds it by more than 2^8: the common
 //                  path needs no cross-lane reduction and no rescale (exact:
-//                  softmax does not depend on the reference);
+//                  softmax does not depend on the reference); the row sums
+//                  of P come from one more MFMA per query tile with an A
+//                  operand whose row 0 is all ones;
 //   O^T += V^T P^T MFMA 16x16x32 with P^T straight from registers: a lane's 8
 //                  k slots are its keys {4g..4g+3, 16+4g..16+4g+3}, and the h/z
 //                  kernel stored V^T in that key order.
@@ -123,19 +125,26 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     const int r = G / C, sch = G % C;
     koff[u] = r * D + (sch ^ (r & (C - 1))) * 8;
   }
-  auto issue = [&](int j, uint16_t* dst) {
+  // j is wave-uniform: the tile bases are scalar and every copy takes a scalar
+  // base plus a per-lane offset
+  auto issue = [&](int jv, uint16_t* dst) {
+    const int j = __builtin_amdgcn_readfirstlane(jv);
     const uint16_t* ksrc = Kb + (size_t)j * TILE;
     const uint16_t* vsrc = Vb + (size_t)j * TILE;
-    const bool ragged = (j + 1) * kBlock > N;
+    if ((j + 1) * kBlock > N) {  // ragged block: rows past N re-read row N-1 (masked below)
+      const int over = j * kBlock - (N - 1);
 #pragma unroll
-    for (int u = 0; u < INSTR; ++u) {
-      int off = koff[u];
-      if (ragged) {  // rows past N: re-read row N-1 (masked to -inf below)
-        const int r = off / D;
-        off -= max(0, j * kBlock + r - (N - 1)) * D;
+      for (int u = 0; u < INSTR; ++u) {
+        const int off = koff[u] - max(0, koff[u] / D + over) * D;
+        load_lds16(ksrc + off, dst + 512 * (4 * u + wave));
+        load_lds16(vsrc + (64 * (4 * u + wave) + lane) * 8, dst + TILE + 512 * (4 * u + wave));
       }
-      load_lds16(ksrc + off, dst + 512 * (4 * u + wave));
-      load_lds16(vsrc + (64 * (4 * u + wave) + lane) * 8, dst + TILE + 512 * (4 * u + wave));
+    } else {
+#pragma unroll
+      for (int u = 0; u < INSTR; ++u) {
+        load_lds16(ksrc + koff[u], dst + 512 * (4 * u + wave));
+        load_lds16(vsrc + (64 * (4 * u + wave) + lane) * 8, dst + TILE + 512 * (4 * u + wave));
+      }
     }
   };
   // H_i^T (d x d, rows swizzled like the K tiles) into a free tile buffer, and
@@ -157,12 +166,17 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) acc[ft][0] = acc[ft][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mref[2] = {-INFINITY, -INFINITY};
-  float lp[2] = {0.f, 0.f};
+  // Row sums of P come out of the MFMA unit: an A operand whose row 0 is all
+  // ones gives sum_k P[k][q] in row 0 of the product (lane group 0, register 0)
+  // and is rescaled together with acc.
+  f32x4 accl[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const uint32_t one2 = l16 == 0 ? 0x3f803f80u : 0u;  // two bf16 ones in row 0
+  const uint4 ones = make_uint4(one2, one2, one2, one2);
 
   // one tile: wait for it, start the copy of the next one into the other
   // buffer, S^T, online softmax against the wave's reference max, O^T += V^T P^T
   auto step = [&](int c, const uint16_t* cur, uint16_t* nxt) {
-    const int j = list[c];
+    const int j = __builtin_amdgcn_readfirstlane((int)list[c]);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of tile c have landed
     lds_barrier();  // all copies of tile c are in LDS; every wave is done with tile c-1
     if (c + 1 < ncrit)
@@ -226,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
         const float nref = tm > mref[qt] + TAU ? tm : mref[qt];
         const float fac = nref == mref[qt] ? 1.0f : __builtin_amdgcn_exp2f(mref[qt] - nref);
         mref[qt] = nref;
-        lp[qt] *= fac;
+        accl[qt] *= fac;
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) acc[ft][qt] *= fac;
       }
@@ -235,15 +249,11 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const float meff = mref[qt] == -INFINITY ? 0.0f : mref[qt];  // no valid key yet: every p is 0
-      float p[2][4], ls = 0.f;
+      float p[2][4];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][r], sc, -meff));
-          ls += p[kt][r];
-        }
-      lp[qt] += ls;
+        for (int r = 0; r < 4; ++r) p[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][r], sc, -meff));
       pb[qt] = make_uint4(pack_bf2(p[0][0], p[0][1]), pack_bf2(p[0][2], p[0][3]),
                           pack_bf2(p[1][0], p[1][1]), pack_bf2(p[1][2], p[1][3]));
     }
@@ -252,6 +262,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
       acc[ft][0] = mfma_bf16(va[ft], pb[0], acc[ft][0]);
       acc[ft][1] = mfma_bf16(va[ft], pb[1], acc[ft][1]);
     }
+    accl[0] = mfma_bf16(ones, pb[0], accl[0]);
+    accl[1] = mfma_bf16(ones, pb[1], accl[1]);
   };
   if (ncrit > 0)
     issue(list[0], bufA);
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   // ---- combine the two key halves: wave kh finishes feature tiles [FTH*kh, FTH*kh + FTH)
   float lw[2];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) lw[qt] = group4_sum(lp[qt]);
+  for (int qt = 0; qt < 2; ++qt) lw[qt] = __shfl(accl[qt][0], l16);  // from lane group 0
   // the last tile's buffer takes the exchange and then the staged output; H_i^T
   // arrived in the other one (bufA when there was no tile)
   uint16_t* xbuf = (ncrit & 1) ? bufA : bufB;
