@@ -13,8 +13,9 @@
 //  * every logit is rounded to float32 and mapped to an order-preserving
 //    uint32 key (round-to-nearest is monotone, so key order never contradicts
 //    float64 order);
-//  * a radix select (four 8-bit passes over a per-wave LDS histogram) finds
-//    the n_h-th largest key T and the n_l-th smallest key L;
+//  * a radix select (top byte by a ballot search, then three 8-bit passes over
+//    a per-wave LDS histogram) finds the n_h-th largest key T and the n_l-th
+//    smallest key L;
 //  * keys strictly above T are critical, strictly below L negligible; the few
 //    elements whose key equals T (or L) are ordered exactly by their float64
 //    logit and then by block index (lower index first), which reproduces the
@@ -37,18 +38,47 @@ __device__ __forceinline__ int wave_count(bool p) {
 }
 
 // The k-th largest (from_top) or k-th smallest valid key of a wave's row,
-// 1 <= k <= number of valid keys: four 8-bit radix passes, each a 256-bin
-// histogram in the wave's own LDS slice of the keys that match the digits found
-// so far, scanned across lanes to find the bin where the running count
-// reaches k. Equal keys are counted with their multiplicity, so the result is
+// 1 <= k <= number of valid keys: the top byte by a bitwise search with wave
+// ballots, then three 8-bit radix passes, each a 256-bin histogram in the
+// wave's own LDS slice of the keys that match the digits found so far, scanned
+// across lanes to find the bin where the running count reaches k. Equal keys are counted with their multiplicity, so the result is
 // the value v with #(keys beyond v) < k <= #(keys at or beyond v).
 template <int kMaxE>
 __device__ uint32_t radix_select(const uint32_t* key, int E, int Nb, int k, bool from_top,
                                  uint32_t* __restrict__ hist) {
   const int lane = threadIdx.x & 63;
-  uint32_t prefix = 0, pmask = 0;
+  // top byte by an 8-step search with wave ballots: logits of one row share
+  // few top bytes (sign and high exponent bits), which would serialise the
+  // histogram atomics of a first radix pass
+  auto count = [&](uint32_t lo, uint32_t hi) {  // keys in [lo, hi]
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < kMaxE; ++e) {
+      if (e >= E) break;
+      const int j = lane + 64 * e;
+      c += __popcll(__ballot(j < Nb && key[e] >= lo && key[e] <= hi));
+    }
+    return c;
+  };
+  uint32_t tb;
   int need = k;
-  for (int pass = 0; pass < 4; ++pass) {
+  if (from_top) {
+    tb = 0;
+    for (int bit = 7; bit >= 0; --bit) {
+      const uint32_t cand = tb | (1u << bit);
+      if (count(cand << 24, 0xffffffffu) >= need) tb = cand;
+    }
+    if (tb < 255) need -= count((tb + 1) << 24, 0xffffffffu);
+  } else {
+    tb = 255;
+    for (int bit = 7; bit >= 0; --bit) {
+      const uint32_t cand = tb & ~(1u << bit);
+      if (count(0u, (cand << 24) | 0xffffffu) >= need) tb = cand;
+    }
+    if (tb > 0) need -= count(0u, (tb << 24) - 1u);
+  }
+  uint32_t prefix = tb << 24, pmask = 0xff000000u;
+  for (int pass = 1; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
 #pragma unroll
     for (int q = 0; q < 4; ++q) hist[64 * q + lane] = 0u;
