@@ -32,6 +32,8 @@
 // Both tiles of a pair (K8, V8^T and the key bias) arrive by direct global->LDS copies,
 // double-buffered one pair ahead, one barrier per pair. A pair with one tile
 // (odd critical count) takes zeros for the missing operands.
+#include <type_traits>
+
 #include "sla_internal.h"
 #include "dev_common.h"
 
@@ -178,11 +180,12 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
   for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mref = -INFINITY, lp = 0.f;
 
-  auto step = [&](int p, const uint8_t* cur, uint8_t* nxt) {
-    const int c0 = 2 * p;
-    const bool has1 = c0 + 1 < ncrit;
-    const int j0 = __builtin_amdgcn_readfirstlane((int)list[c0]);
-    const int j1 = has1 ? __builtin_amdgcn_readfirstlane((int)list[c0 + 1]) : j0;
+  // FAST: both tiles present and no key past N (every pair but possibly the
+  // last and the one holding the ragged block), so no score needs masking
+  auto step = [&](auto fast_c, int p, int j0, int j1, const uint8_t* cur, uint8_t* nxt)
+                  __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_c)::value;
+    const bool has1 = FAST || 2 * p + 1 < ncrit;
     const float su0 = sq * ks_b[j0], su1 = sq * ks_b[j1];
     const float sv0 = vs_b[j0], sv1 = has1 ? vs_b[j1] : 1.f;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of pair p have landed
@@ -223,8 +226,13 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
         const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool out = !live || (rag && j * kBlock + 16 * kt + 4 * g + r >= N);
-          sf[t][kt][r] = out ? -INFINITY : fmaf((float)s[t][kt][r], su, bv[r]);
+          const float v = fmaf((float)s[t][kt][r], su, bv[r]);
+          if constexpr (FAST) {
+            sf[t][kt][r] = v;
+          } else {
+            const bool out = !live || (rag && j * kBlock + 16 * kt + 4 * g + r >= N);
+            sf[t][kt][r] = out ? -INFINITY : v;
+          }
         }
         tmax[t] = fmaxf(tmax[t], fmaxf(fmaxf(sf[t][kt][0], sf[t][kt][1]), fmaxf(sf[t][kt][2], sf[t][kt][3])));
       }
@@ -280,9 +288,22 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
       for (int r = 0; r < 4; ++r) acc[ft][r] = fmaf(t[r], sp, acc[ft][r]);
     }
   };
+  auto run = [&](int p, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+    const int j0 = __builtin_amdgcn_readfirstlane((int)list[2 * p]);
+    if (2 * p + 1 < ncrit) {
+      const int j1 = __builtin_amdgcn_readfirstlane((int)list[2 * p + 1]);
+      if ((max(j0, j1) + 1) * kBlock <= N) {
+        step(std::true_type{}, p, j0, j1, cur, nxt);
+        return;
+      }
+      step(std::false_type{}, p, j0, j1, cur, nxt);
+    } else {
+      step(std::false_type{}, p, j0, j0, cur, nxt);
+    }
+  };
   for (int p = 0; p < npair; p += 2) {
-    step(p, bufA, bufB);
-    if (p + 1 < npair) step(p + 1, bufB, bufA);
+    run(p, bufA, bufB);
+    if (p + 1 < npair) run(p + 1, bufB, bufA);
   }
 
   const float lw = group4_sum(lp);
