@@ -28,6 +28,16 @@ CFLAGS = [
 ]
 
 
+# Kernel files only (k_*.hip): no kernel takes or makes a NaN, and without this
+# every fmaxf of an MFMA result is preceded by a quieting v_max. Infinities are
+# still honoured. The host file keeps full NaN semantics for argument checks.
+KERNEL_FLAGS = ["-fno-honor-nans"]
+
+
+def _flags(src):
+    return CFLAGS + (KERNEL_FLAGS if os.path.basename(src).startswith("k_") else [])
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -46,7 +56,7 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16)
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        futs = [ex.submit(_run, [HIPCC, *CFLAGS, "-c", s, "-o", o], verbose)
+        futs = [ex.submit(_run, [HIPCC, *_flags(s), "-c", s, "-o", o], verbose)
                 for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()

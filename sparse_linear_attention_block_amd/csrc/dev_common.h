@@ -20,8 +20,11 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 __device__ __forceinline__ uint32_t f2bf(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return f2bf(lo) | (f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // D += A * B with A: 16x32, B: 32x16 bf16, D: 16x16 f32.
@@ -176,6 +179,58 @@ __device__ inline int compact_row(const int8_t* __restrict__ mrow, int Nb, int8_
     int off = total;
     for (int w = 0; w < wave; ++w) off += wsum[w];
     if (f) list[off + before] = (uint16_t)j;
+    total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  return total;
+}
+
+// The same compaction in two parts, so that a kernel can load the mask row
+// first, issue its other prologue loads, and wait only for the mask: mask_load
+// reads bytes j = tid + 256 k of the row for k < kMaskPre (every load is issued;
+// indices past the row re-read its last byte and are ignored), compact_loaded
+// builds the list from them with one barrier for all chunks; rows longer than
+// 256 kMaskPre blocks finish chunk by chunk as in compact_row. wsum holds
+// 4 kMaskPre ints.
+constexpr int kMaskPre = 8;
+__device__ __forceinline__ void mask_load(const int8_t* __restrict__ mrow, int Nb,
+                                          int8_t (&mv)[kMaskPre]) {
+#pragma unroll
+  for (int k = 0; k < kMaskPre; ++k) mv[k] = mrow[min((int)threadIdx.x + 256 * k, Nb - 1)];
+}
+__device__ inline int compact_loaded(const int8_t (&mv)[kMaskPre], const int8_t* __restrict__ mrow,
+                                     int Nb, int8_t value, uint16_t* list, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int before[kMaskPre];
+  uint32_t fbits = 0;
+#pragma unroll
+  for (int k = 0; k < kMaskPre; ++k) {
+    const bool f = tid + 256 * k < Nb && mv[k] == value;
+    const uint64_t bal = __ballot(f);
+    before[k] = __popcll(bal & ((1ull << lane) - 1ull));
+    fbits |= (uint32_t)f << k;
+    if (lane == 0) wsum[4 * k + wave] = __popcll(bal);
+  }
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int k = 0; k < kMaskPre; ++k) {
+    int off = total;
+    for (int w = 0; w < wave; ++w) off += wsum[4 * k + w];
+    if ((fbits >> k) & 1) list[off + before[k]] = (uint16_t)(tid + 256 * k);
+    total += wsum[4 * k] + wsum[4 * k + 1] + wsum[4 * k + 2] + wsum[4 * k + 3];
+  }
+  __syncthreads();
+  for (int base = 256 * kMaskPre; base < Nb; base += 256) {
+    const int j = base + tid;
+    const bool f = (j < Nb) && (mrow[j] == value);
+    const uint64_t bal = __ballot(f);
+    const int bef = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int off = total;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (f) list[off + bef] = (uint16_t)j;
     total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }

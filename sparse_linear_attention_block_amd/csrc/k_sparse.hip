@@ -34,9 +34,10 @@
 // copied into the idle tile buffer and Z_i into the spent critical list.
 // The two key halves are combined through LDS (max-rescaled partial sums);
 // each wave then finishes half the features of its 32 queries: O_s = acc / l,
-// phi(Q) (softmax over the features in f32, rounded to bf16), num^T =
-// H_i^T phi(Q)^T on MFMA, den = phi(Q).Z_i, O = alpha O_s + (1 - alpha) O_l,
-// staged in LDS and written as full rows.
+// phi(Q) (softmax over the features in f32, left unnormalised because the
+// normalisation cancels in O_l, rounded to bf16), num^T = H_i^T phi(Q)^T on
+// MFMA, den = phi(Q).Z_i, O = alpha O_s + (1 - alpha) O_l, staged in LDS and
+// written as full rows.
 // Workgroups are remapped so that each XCD walks a contiguous range of
 // (batch, head, query block): neighbouring query blocks share most critical
 // key tiles, which then come from the XCD's L2.
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   __shared__ __attribute__((aligned(16))) uint16_t list[kMaxNb];  // critical list, then Z_i
   __shared__ float xm[4][2][16];
   __shared__ float xl[4][2][16];
-  __shared__ int wsum[4];
+  __shared__ int wsum[4 * kMaskPre];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS addresses
@@ -98,8 +99,11 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   const int bh = id / Nb, i = id - bh * Nb;
   const int h = bh % H;
 
-  // the wave's 32 queries as MFMA B operands: Q[t][32ks + 8g .. +7] (issued first:
-  // they land while the critical list is compacted)
+  // the mask row first, then the wave's 32 queries as MFMA B operands:
+  // Q[t][32ks + 8g .. +7] (they land while the critical list is compacted)
+  const int8_t* mrow = mask + ((size_t)bh * Nb + i) * Nb;
+  int8_t mv[kMaskPre];
+  mask_load(mrow, Nb, mv);
   uint4 qr[2][KSTEPS];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -109,8 +113,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
       qr[qt][ks] = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + t) * D + 32 * ks + 8 * g);
   }
 
-  const int8_t* mrow = mask + ((size_t)bh * Nb + i) * Nb;
-  const int ncrit = compact_row(mrow, Nb, (int8_t)1, list, wsum);
+  const int ncrit = compact_loaded(mv, mrow, Nb, (int8_t)1, list, wsum);
 
   const uint16_t* Kb = K + (size_t)bh * N * D;
   const uint16_t* Vb = vt + (size_t)bh * Nb * TILE;
@@ -357,21 +360,18 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     float qm = -INFINITY;
 #pragma unroll
     for (int e = 0; e < KSTEPS * 8; ++e) qm = fmaxf(qm, qf[e]);
-    qm = group4_max(qm);
-    float qs = 0.f;
+    qm = group4_max(qm) * kLog2e;
+    // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
+    // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
 #pragma unroll
-    for (int e = 0; e < KSTEPS * 8; ++e) {
-      qf[e] = __expf(qf[e] - qm);
-      qs += qf[e];
-    }
-    const float qinv = 1.0f / group4_sum(qs);
+    for (int e = 0; e < KSTEPS * 8; ++e) qf[e] = __builtin_amdgcn_exp2f(fmaf(qf[e], kLog2e, -qm));
     float dp = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       uint32_t w4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w4[e] = pack_bf2(qf[ks * 8 + 2 * e] * qinv, qf[ks * 8 + 2 * e + 1] * qinv);
+        w4[e] = pack_bf2(qf[ks * 8 + 2 * e], qf[ks * 8 + 2 * e + 1]);
         dp += bf_lo(w4[e]) * zf[ks * 8 + 2 * e] + bf_hi(w4[e]) * zf[ks * 8 + 2 * e + 1];
       }
       fq[qt][ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
   __shared__ __attribute__((aligned(16))) uint8_t bufA[PAIR];
   __shared__ __attribute__((aligned(16))) uint8_t bufB[PAIR];
   __shared__ uint16_t list[kMaxNb];
-  __shared__ int wsum[4];
+  __shared__ int wsum[4 * kMaskPre];
   __shared__ float qmax[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -89,8 +89,11 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
   const int qrow = 16 * wave + l16;                // the lane's query within the block
   const int tq = min(i * kBlock + qrow, N - 1);    // rows past N are never stored
 
-  // the lane's query, features 32ks + 8g .. +7 (the bf16 B operand layout), and
-  // the channel means of Q for the same features
+  // the mask row first; then the lane's query, features 32ks + 8g .. +7 (the
+  // bf16 B operand layout), and the channel means of Q for the same features
+  const int8_t* mrow = mask + ((size_t)bh * Nb + i) * Nb;
+  int8_t mv[kMaskPre];
+  mask_load(mrow, Nb, mv);
   uint4 qr[KS];
   float4 qmv[KS][2];
 #pragma unroll
@@ -100,8 +103,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
     qmv[ks][1] = *reinterpret_cast<const float4*>(qkmean + (size_t)bh * D + 32 * ks + 8 * g + 4);
   }
 
-  const int8_t* mrow = mask + ((size_t)bh * Nb + i) * Nb;
-  const int ncrit = compact_row(mrow, Nb, (int8_t)1, list, wsum);
+  const int ncrit = compact_loaded(mv, mrow, Nb, (int8_t)1, list, wsum);
   const int npair = (ncrit + 1) >> 1;
 
   const int8_t* Kb = k8 + (size_t)bh * Nb * KT;
@@ -339,21 +341,18 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
     float qm = -INFINITY;
 #pragma unroll
     for (int e = 0; e < KS * 8; ++e) qm = fmaxf(qm, qf[e]);
-    qm = group4_max(qm);
-    float qs = 0.f;
+    qm = group4_max(qm) * kLog2e;
+    // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
+    // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
 #pragma unroll
-    for (int e = 0; e < KS * 8; ++e) {
-      qf[e] = __expf(qf[e] - qm);
-      qs += qf[e];
-    }
-    const float qinv = 1.0f / group4_sum(qs);
+    for (int e = 0; e < KS * 8; ++e) qf[e] = __builtin_amdgcn_exp2f(fmaf(qf[e], kLog2e, -qm));
     float dp = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint32_t w4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w4[e] = pack_bf2(qf[ks * 8 + 2 * e] * qinv, qf[ks * 8 + 2 * e + 1] * qinv);
+        w4[e] = pack_bf2(qf[ks * 8 + 2 * e], qf[ks * 8 + 2 * e + 1]);
         dp += bf_lo(w4[e]) * zf[ks * 8 + 2 * e] + bf_hi(w4[e]) * zf[ks * 8 + 2 * e + 1];
       }
       fq[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
