@@ -98,6 +98,20 @@ __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_wave_base
                                    16, 0, 0);
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (stride 0, 32-bit data
+// format word of the gfx9 descriptor). Copies through it take a per-lane 32-bit
+// offset and a wave-uniform scalar offset, so moving to the next tile costs no
+// vector instruction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16-byte asynchronous copy of base + soff + voff into LDS: lane l writes lds_wave_base + 16*l.
+__device__ __forceinline__ void load_lds16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff,
+                                               void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (void __attribute__((address_space(3)))*)lds_wave_base, 16, (int)voff, soff, 0, 0);
+}
+
 }  // namespace sla
 
 namespace sla {

@@ -128,25 +128,28 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     const int r = G / C, sch = G % C;
     koff[u] = r * D + (sch ^ (r & (C - 1))) * 8;
   }
-  // j is wave-uniform: the tile bases are scalar and every copy takes a scalar
-  // base plus a per-lane offset
+  // Copies go through buffer resources over this head's K rows and V^T tiles:
+  // the per-lane byte offsets stay in registers and the tile offset j * TILE
+  // (wave-uniform) is the scalar offset, so issuing a tile costs no vector
+  // instruction.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, N * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, Nb * TILE * 2);
   auto issue = [&](int jv, uint16_t* dst) {
     const int j = __builtin_amdgcn_readfirstlane(jv);
-    const uint16_t* ksrc = Kb + (size_t)j * TILE;
-    const uint16_t* vsrc = Vb + (size_t)j * TILE;
+    const int soff = j * TILE * 2;
     if ((j + 1) * kBlock > N) {  // ragged block: rows past N re-read row N-1 (masked below)
       const int over = j * kBlock - (N - 1);
 #pragma unroll
       for (int u = 0; u < INSTR; ++u) {
         const int off = koff[u] - max(0, koff[u] / D + over) * D;
-        load_lds16(ksrc + off, dst + 512 * (4 * u + wave));
-        load_lds16(vsrc + (64 * (4 * u + wave) + lane) * 8, dst + TILE + 512 * (4 * u + wave));
+        load_lds16_buf(krs, 2 * off, soff, dst + 512 * (4 * u + wave));
+        load_lds16_buf(vrs, (64 * (4 * u + wave) + lane) * 16, soff, dst + TILE + 512 * (4 * u + wave));
       }
     } else {
 #pragma unroll
       for (int u = 0; u < INSTR; ++u) {
-        load_lds16(ksrc + koff[u], dst + 512 * (4 * u + wave));
-        load_lds16(vsrc + (64 * (4 * u + wave) + lane) * 8, dst + TILE + 512 * (4 * u + wave));
+        load_lds16_buf(krs, 2 * koff[u], soff, dst + 512 * (4 * u + wave));
+        load_lds16_buf(vrs, (64 * (4 * u + wave) + lane) * 16, soff, dst + TILE + 512 * (4 * u + wave));
       }
     }
   };

@@ -118,22 +118,26 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
     const int r = G / C8, pos = G % C8;
     koff[u] = r * D + 16 * (pos ^ ksw<D>(r));
   }
-  // K8 rows past N are zero in memory (their scores are masked below)
+  // K8 rows past N are zero in memory (their scores are masked below). Copies go
+  // through buffer resources over this head's K8, V8^T and key biases; the tile
+  // offset (wave-uniform) is the scalar offset.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, Nb * KT);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, Nb * KT);
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bb, Nb * kBlock * 4);
   auto issue = [&](int p, uint8_t* dst) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int c = 2 * p + t;
       if (c >= ncrit) break;
       const int j = __builtin_amdgcn_readfirstlane((int)list[c]);
-      const int8_t* ksrc = Kb + (size_t)j * KT;
-      const uint8_t* vsrc = Vb + (size_t)j * KT;
 #pragma unroll
       for (int u = 0; u < CPL; ++u) {
-        load_lds16(ksrc + koff[u], dst + t * KT + 1024 * (4 * u + wave));
-        load_lds16(vsrc + 16 * (64 * (4 * u + wave) + lane), dst + (2 + t) * KT + 1024 * (4 * u + wave));
+        load_lds16_buf(krs, koff[u], j * KT, dst + t * KT + 1024 * (4 * u + wave));
+        load_lds16_buf(vrs, 16 * (64 * (4 * u + wave) + lane), j * KT,
+                       dst + (2 + t) * KT + 1024 * (4 * u + wave));
       }
       if (wave == 0 && lane < 16)  // the 64 key biases: 256 bytes
-        load_lds16(Bb + (size_t)j * kBlock + 4 * lane, dst + 4 * KT + 256 * t);
+        load_lds16_buf(brs, 16 * lane, j * kBlock * 4, dst + 4 * KT + 256 * t);
     }
   };
   if (npair > 0) issue(0, bufA);
