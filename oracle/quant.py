@@ -23,11 +23,17 @@ pages give no formats, scale granularity or rounding, so the readings are:
 * P: quantised per query row over the 128 keys of two consecutive critical
   key blocks (the critical list in ascending block order, taken in pairs; an
   odd last block forms a pair alone), after the V scale of each key's block is
-  folded in: P' = P~ * s_V, s_P = rowmax(P') / 448, P8 = e4m3(P' / s_P).
+  folded in: P' = P~ * s_V, s_P = 2^ceil(log2(rowmax(P') / 448)) (a power
+  of two: the E8M0 block scale that an MX-style fp8 product applies; the
+  largest code of the row lies in (224, 448]; the exponent is kept in the
+  E8M0 range [-127, 127]), P8 = e4m3(P' / s_P). P~ is taken against a
+  reference that is an integer in log2 units, so the codes P' / s_P depend on
+  the scores alone, not on the reference.
   The pair contributes s_P * sum_k P8[k] V8[k] to the numerator.
 * The softmax denominator sums the unquantised P~ (exp of the dequantised
   scores); P8 does not depend on the softmax reference, which cancels in
-  P' / rowmax(P').
+  P' / s_P (up to the range limit of the exponent, reached only by pairs
+  2^-118 below the row maximum).
 
 Codes are decided in float32 (the precision of the kernel that produces
 them); everything after the codes is float64.
@@ -133,7 +139,8 @@ def sparse_branch_q8(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mask: np.ndarr
             keys = slice(j * BLOCK, min((j + 1) * BLOCK, N))
             s = ((q8[rows] @ k8[keys].T) * (qs[i] * ks[j]) + bias[keys][None, :]) / np.sqrt(d)
             segs.append((j, keys, s))
-        m = max(s.max() for _, _, s in segs)
+        # reference: the row maximum rounded up to an integer power of two
+        m = np.ceil(max(s.max() for _, _, s in segs) / np.log(2.0)) * np.log(2.0)
         l = np.zeros((rows.stop - rows.start, 1))
         num = np.zeros((rows.stop - rows.start, d))
         for p in range(0, len(segs), 2):
@@ -142,10 +149,14 @@ def sparse_branch_q8(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mask: np.ndarr
             l += sum(x.sum(axis=1, keepdims=True) for x in pt)
             pp = [x * vs[j] for x, (j, _, _) in zip(pt, pair)]  # P' = P~ s_V
             pm = np.max(np.concatenate(pp, axis=1), axis=1, keepdims=True)
-            inv = np.where(pm > 0, E4M3_MAX / np.where(pm > 0, pm, 1.0), 0.0)
+            if quantize:                                       # s_P = 2^E, E8M0 range
+                E = np.ceil(np.log2(np.where(pm > 0, pm, 1.0) / E4M3_MAX))
+                sp = np.ldexp(1.0, np.clip(E, -127, 127).astype(np.int64))
+            else:
+                sp = np.ones_like(pm)
             acc = np.zeros_like(num)
             for x, (_, keys, _) in zip(pp, pair):
-                acc += fp8(x * inv) @ v8[keys]
-            num += acc * (pm / E4M3_MAX)
+                acc += fp8(x / sp) @ v8[keys]
+            num += acc * sp
         out[rows] = num / l
     return out

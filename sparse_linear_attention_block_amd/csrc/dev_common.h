@@ -48,6 +48,11 @@ __device__ __forceinline__ i32x4 mfma_i8(const uint4& a, const uint4& b, i32x4 c
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// The same with a per-lane E8M0 block scale on B: the 32 k values lane l holds
+// of column l%16 are multiplied by 2^(sb - 127) (A keeps unit scales).
+__device__ __forceinline__ f32x4 mfma_fp8_sb(const i32x8& a, const i32x8& b, f32x4 c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
 
 __device__ __forceinline__ float wave_max16(float v) {  // over the 16 lanes of a row group
   v = fmaxf(v, __shfl_xor(v, 1));

@@ -16,7 +16,9 @@
 // P is quantised per query row over the 128 keys that one fp8 product
 // contracts: P' = P~ * s_V(key block) (the V scale is folded into P, since
 // the two tiles of one product may come from blocks with different V scales),
-// s_P = rowmax(P') / 448, P8 = e4m3(P' / s_P), and acc += s_P * (V8^T P8).
+// s_P = 2^ceil(log2(rowmax(P') / 448)) (a power of two, so the largest code
+// lies in (224, 448]), P8 = e4m3(P' / s_P), and acc += s_P * (V8^T P8) with
+// s_P applied by the fp8 product as its E8M0 block scale.
 // The softmax denominator l sums the unquantised P~.
 //
 // One workgroup of 4 waves per query block; wave w owns queries 16w .. 16w+15
@@ -246,7 +248,9 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
     const float lmax = fmaxf(tmax[0], tmax[1]);
     if (__ballot(lmax > mref + TAU)) {
       const float tm = group4_max(lmax);
-      const float nref = tm > mref + TAU ? tm : mref;
+      // an integer reference: the fp8 codes below then depend on the scores
+      // alone, not on when the reference was raised
+      const float nref = tm > mref + TAU ? ceilf(tm) : mref;
       const float fac = nref == mref ? 1.0f : __builtin_amdgcn_exp2f(mref - nref);
       mref = nref;
       lp *= fac;
@@ -254,15 +258,19 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
       for (int ft = 0; ft < FT; ++ft) acc[ft] *= fac;
     }
     const float meff = mref == -INFINITY ? 0.0f : mref;  // no valid key yet: every p is 0
-    // P' = P~ s_V and its row scale folded into the exponent: with
-    // M = max over the pair's tiles of (tile max + log2 s_V), the fp8 input of a
-    // key of tile t is 2^(s - off_t), off_t = M - log2 s_V(t) - log2 448, at most
-    // 448; s_P = 2^(M - meff) / 448; the tile's share of l (the unquantised
-    // P~ = 2^(s - meff)) is 2^(off_t - meff) times the sum of those inputs.
+    // P' = P~ s_V with P~ = 2^(s - meff). Its row scale over the pair is the
+    // power of two s_P = 2^E, E = ceil(log2 rowmax(P') - log2 448), so that the
+    // largest fp8 input lies in (224, 448]; the fp8 product applies it as the
+    // E8M0 block scale of its B operand. With meff an integer, meff + E =
+    // ceil(Mq - log2 448) and the codes 2^(s + log2 s_V - meff - E) are those
+    // of the scores alone. The fp8 input of a key of tile t is 2^(s - off_t),
+    // off_t = meff - log2 s_V(t) + E, and the tile's share of l (the
+    // unquantised P~) is 2^(off_t - meff) times the sum of those inputs.
     const float lsv0 = __log2f(sv0), lsv1 = has1 ? __log2f(sv1) : 0.f;
     const float Mq = group4_max(fmaxf(tmax[0] + lsv0, tmax[1] + lsv1));
     constexpr float kLog2_448 = 8.807354922057604f;
-    const float off0 = Mq - lsv0 - kLog2_448, off1 = Mq - lsv1 - kLog2_448;
+    const float E = fminf(fmaxf(ceilf(Mq - meff - kLog2_448), -127.f), 127.f);
+    const float off0 = meff - lsv0 + E, off1 = meff - lsv1 + E;
     float ssum[2] = {0.f, 0.f};
     i32x8 pb;
 #pragma unroll
@@ -279,8 +287,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
         pb[4 * t + kt] = (int)pack_e4m3x4_nosat(e[0], e[1], e[2], e[3]);
       }
     }
-    lp += ssum[0] * __builtin_amdgcn_exp2f(off0 - meff) + ssum[1] * __builtin_amdgcn_exp2f(off1 - meff);
-    const float sp = __builtin_amdgcn_exp2f(Mq - meff) * (1.0f / 448.0f);
+    lp += ssum[0] * __builtin_amdgcn_exp2f(E - lsv0) + ssum[1] * __builtin_amdgcn_exp2f(E - lsv1);
+    const int sb = (int)E + 127;
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       const int c = 16 * ft + l16;
@@ -289,9 +297,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
       const uint4 v1 = has1 ? *reinterpret_cast<const uint4*>(cur + 3 * KT + off) : make_uint4(0, 0, 0, 0);
       const i32x8 a = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
                        (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      const f32x4 t = mfma_fp8(a, pb, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[ft][r] = fmaf(t[r], sp, acc[ft][r]);
+      acc[ft] = mfma_fp8_sb(a, pb, acc[ft], sb);
     }
   };
   auto run = [&](int p, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
