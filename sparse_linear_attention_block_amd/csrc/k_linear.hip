@@ -9,98 +9,111 @@
 // f32 accumulate) and costs 2*Nb*Nb*(d*d + d) flops per head instead of a
 // gather of (n_h + n_l) d x d blocks per query block from cache.
 //
-// The kernel computes the transpose Hx^T = hx^T M01^T: the hx operand has 4
-// consecutive key blocks per 8-byte word (written so by K3), which is the k
-// layout the MFMA A operand needs; the mask is first turned into a bf16 0/1
-// indicator (k_indicator) in a layout the GEMM copies straight into LDS and
-// reads as the B operand; each lane then holds 4 consecutive n of one query
-// block and stores them as one 8-byte word.
+// The product runs per workgroup over a 64-column slice of hx and up to 512
+// query blocks, so hx is read from memory once. The 0/1 matrix travels as
+// bits, one 32-bit word per (32-key step, query block), and each lane expands
+// its word into the bf16 B operand of the MFMA with two integer operations per
+// register; the hx operand (4 consecutive key blocks per 8-byte word, written
+// so by K3) is the A operand.
+#include <type_traits>
+
 #include "sla_internal.h"
 #include "dev_common.h"
 
 namespace sla {
 namespace {
 
-constexpr int kTN = 256;  // n per workgroup
-constexpr int kTI = 128;  // query blocks per workgroup
-constexpr int kOS = kTN + 8;  // row stride of the staged output (bf16)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// The marginal indicator M01[i][j] = (Mc[i][j] == 0) as bf16 0/1, one
-// [Nb128][32] slab per 32-key step; chunk q (keys 8q..8q+7 of the step) of row
-// i sits at chunk position q ^ ((i >> 1) & 3), so that 8 lanes reading 8
-// consecutive rows of the slab hit distinct LDS banks. Rows >= Nb and keys >=
-// Nb are 0.
+constexpr int kTN = 64;    // hx columns per workgroup
+constexpr int kRows = 128; // query blocks per wave (4 waves per workgroup)
+
+// The marginal indicator M01[i][j] = (Mc[i][j] == 0) as bits. Word W(s, i)
+// covers keys 32s .. 32s+31 of query block i: for lane group g and e < 4,
+// bit 4g + e is key 32s + 8g + 2e and bit 16 + 4g + e is key 32s + 8g + 2e + 1
+// (the two bf16 halves of register e of that lane group's B operand). The word
+// sits at [bh][s][i / 128][i % 16][(i / 16) % 8], so that a lane reads the
+// words of its 8 query tiles as 32 contiguous bytes. Rows >= Nb and keys >= Nb
+// are 0.
 __global__ __launch_bounds__(256) void k_indicator(const int8_t* __restrict__ mask,
-                                                   uint16_t* __restrict__ ind, int Nb, int Nbp,
+                                                   uint32_t* __restrict__ ind, int Nb, int Nbp,
                                                    int Nb128) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const int s = blockIdx.y, bh = blockIdx.z;
-  const int q = t & 3, i = t >> 2;
+  const int S = Nbp / 32;
+  const int t = blockIdx.x * 256 + threadIdx.x;  // (i, s), s fastest
+  const int bh = blockIdx.y;
+  const int s = t % S, i = t / S;
   if (i >= Nb128) return;
-  uint32_t w[4];
+  uint32_t w = 0;
+  if (i < Nb) {
+    const int8_t* row = mask + ((size_t)bh * Nb + i) * Nb + 32 * s;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int j = 32 * s + 8 * q + 2 * e + hh;
-      if (i < Nb && j < Nb && mask[((size_t)bh * Nb + i) * Nb + j] == 0) v |= 0x3f80u << (16 * hh);
+    for (int k = 0; k < 32; ++k) {
+      const bool marg = 32 * s + k < Nb && row[min(k, Nb - 1 - 32 * s)] == 0;
+      const int g = k >> 3, e = (k & 7) >> 1, hi = k & 1;
+      w |= (uint32_t)marg << (16 * hi + 4 * g + e);
     }
-    w[e] = v;
   }
-  uint16_t* dst = ind + (((size_t)bh * (Nbp / 32) + s) * Nb128 + i) * 32 + 8 * (q ^ ((i >> 1) & 3));
-  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  ind[(((size_t)bh * S + s) * (Nb128 / 128) + i / 128) * 128 + (i % 16) * 8 + (i / 16) % 8] = w;
 }
 
-// Hx^T = hx^T M01^T for one (batch, head): workgroup tile 256 n x 128 query
-// blocks, wave w owns n0 + 64w .. +63 against all 128 rows, k steps of 32 key
-// blocks. The hx operand (4 key blocks per 8-byte word, as written by the h/z
-// kernel) goes straight from global memory to registers one step ahead; the
-// indicator slab of a step arrives in LDS by direct asynchronous copies,
-// double-buffered, one LDS barrier per step. The finished tile is staged in LDS
-// in two halves and written as contiguous 16-byte stores along each row.
-// Workgroups are remapped so that the row tiles of one n range run back to back
-// on one XCD and share hx in L2.
-__global__ __launch_bounds__(256, 2) void k_linear_bf16(const uint16_t* __restrict__ ind,
+// Hx^T = hx^T M01^T for one (batch, head): workgroup tile 64 columns n x 512
+// query blocks, wave w owns query blocks 128 w .. +127 of the tile against all
+// 64 columns (4 x 8 MFMA tiles), k steps of 32 key blocks. hx comes from memory
+// exactly once, so its latency is that of HBM: the 4 KB hx slab of a k step
+// arrives in LDS by direct copies kRing - 1 steps ahead (a ring of kRing
+// slots, one barrier per step); each wave reads its A operands from there. The
+// slots are distinct LDS objects picked at compile time (the loop is unrolled
+// by kRing), so the compiler sees that reads of one slot do not alias the
+// copies into another and does not wait for those copies. The indicator words
+// of each wave travel in the same slot. With no operand held in registers
+// across steps, three workgroups fit on a CU.
+// Each lane
+// holds 4 consecutive n of one query block per MFMA tile and stores them as
+// one 8-byte word; the wave fills whole 128-byte row segments. Workgroups are
+// remapped so that the column slices of one head run back to back on one XCD.
+constexpr int kRing = 6;              // hx slabs in flight or in use (a multiple of 3)
+constexpr int kSeg = 1024 + 128;      // bytes per wave segment of a slab (padded)
+constexpr int kSlab = 4 * kSeg + 4 * 512;  // one k step: 8 groups of 4 key blocks x 64 n x
+                                           // 8 bytes, then 128 indicator words per wave
+
+__global__ __launch_bounds__(256, 3) void k_linear_bf16(const uint32_t* __restrict__ ind,
                                                         const uint16_t* __restrict__ hx,
                                                         uint16_t* __restrict__ Hx, int Nb, int Nbp,
-                                                        int Nb128, int NN, int ntn, int nti) {
-  __shared__ __attribute__((aligned(16))) uint16_t bA[kTI * 32];
-  __shared__ __attribute__((aligned(16))) uint16_t bB[kTI * 32];
-  __shared__ __attribute__((aligned(16))) uint16_t ost[64 * kOS];  // half the output tile
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+                                                        int Nb128, int NN, int ntn, int nit) {
+  __shared__ __attribute__((aligned(16))) uint8_t slab0[kSlab];
+  __shared__ __attribute__((aligned(16))) uint8_t slab1[kSlab];
+  __shared__ __attribute__((aligned(16))) uint8_t slab2[kSlab];
+  __shared__ __attribute__((aligned(16))) uint8_t slab3[kSlab];
+  __shared__ __attribute__((aligned(16))) uint8_t slab4[kSlab];
+  __shared__ __attribute__((aligned(16))) uint8_t slab5[kSlab];
+  uint8_t* const slabs[kRing] = {slab0, slab1, slab2, slab3, slab4, slab5};
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int it = id % nti;
-  const int rest = id / nti;
+  const int it = id % nit;
+  const int rest = id / nit;
   const int nt = rest % ntn, bh = rest / ntn;
-  const int i0 = it * kTI;
-  const int n0 = nt * kTN + wave * 64;
+  const int ig = 4 * it + wave;          // the wave's group of 128 query blocks
+  const bool live = ig * kRows < Nb;     // wave-uniform; idle waves still take the barriers
+  const int NI = Nb128 / kRows;
   const int S = Nbp / 32, Nb4 = Nbp / 4;
-  const uint16_t* indb = ind + ((size_t)bh * S * Nb128 + i0) * 32;
-  const uint16_t* hb = hx + (size_t)bh * Nb4 * NN * 4;
-
-  auto issue = [&](int s, uint16_t* dst) {  // 8 KB slab: two 16-byte copies per lane
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int G = 64 * (4 * u + wave) + lane;
-      load_lds16(indb + (size_t)s * Nb128 * 32 + (size_t)G * 8, dst + 512 * (4 * u + wave));
-    }
-  };
-  auto loadA = [&](int s, uint4* a) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int n = n0 + 16 * mt + l16;
-      if (n < NN) {
-        const int q = 8 * s + 2 * g;
-        const uint2 lo = *reinterpret_cast<const uint2*>(hb + ((size_t)q * NN + n) * 4);
-        const uint2 hi = *reinterpret_cast<const uint2*>(hb + ((size_t)(q + 1) * NN + n) * 4);
-        a[mt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      } else {
-        a[mt] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  const int n0 = nt * kTN;
+  // buffer resources over this head's hx and indicator words: the per-lane
+  // byte offsets are fixed, the k step moves the scalar offset only
+  const __amdgpu_buffer_rsrc_t hrs = make_rsrc(hx + (size_t)bh * Nb4 * NN * 4, Nb4 * NN * 8);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(ind + (size_t)bh * S * NI * kRows, S * NI * kRows * 4);
+  // slab copy: wave w brings groups 2w (lanes 0-31) and 2w + 1 (lanes 32-63) of
+  // 4 key blocks, 16 bytes (two columns) per lane, into its segment
+  const uint32_t coff = ((uint32_t)(2 * wave + (lane >> 5)) * NN + n0 + 2 * (lane & 31)) * 8u;
+  // indicator copy: lanes 0-31 of a wave bring its 128 words (lanes 32-63 idle)
+  const uint32_t woff = (uint32_t)(min(ig, NI - 1) * kRows + 4 * (lane & 31)) * 4u;
+  // The slab of k step t (clamped) into a ring slot: two copies per wave.
+  auto copy = [&](int t, uint8_t* slot) {
+    const int tc = min(t, S - 1);
+    load_lds16_buf(hrs, coff, tc * 64 * NN, slot + wave * kSeg);
+    if (lane < 32) load_lds16_buf(wrs, woff, tc * NI * kRows * 4, slot + 4 * kSeg + wave * 512);
   };
 
   f32x4 acc[4][8];
@@ -109,55 +122,79 @@ __global__ __launch_bounds__(256, 2) void k_linear_bf16(const uint16_t* __restri
 #pragma unroll
     for (int n2 = 0; n2 < 8; ++n2) acc[mt][n2] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](int s, const uint16_t* cur, uint16_t* nxt, const uint4* a, uint4* an) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // slab s and operand s have landed
-    lds_barrier();
-    if (s + 1 < S) {
-      issue(s + 1, nxt);
-      loadA(s + 1, an);
-    }
-#pragma unroll
-    for (int n2 = 0; n2 < 8; ++n2) {
-      const int row = 16 * n2 + l16;
-      const uint4 b = *reinterpret_cast<const uint4*>(cur + row * 32 + 8 * (g ^ ((row >> 1) & 3)));
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt][n2] = mfma_bf16(a[mt], b, acc[mt][n2]);
-    }
-  };
-  uint4 aA[4], aB[4];
-  issue(0, bA);
-  loadA(0, aA);
-  for (int s = 0; s < S; s += 2) {
-    step(s, bA, bB, aA, aB);
-    if (s + 1 < S) step(s + 1, bB, bA, aB, aA);
-  }
-  // the output tile goes out in two halves of 64 query blocks, staged in LDS so
-  // that every row segment of 256 columns is written as contiguous 16-byte stores
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (half) __syncthreads();  // the first half has been copied out
-#pragma unroll
-    for (int n4 = 0; n4 < 4; ++n4) {
-      const int n2 = 4 * half + n4;
-      const int il = 16 * n4 + l16;
+  const int sh = 4 * g;
+  // A operand of lane (l16, g), tile mt: group 2g (low 8 bytes) and 2g + 1 (high)
+  // at column 16 mt + l16, both in the segment of wave g
+  const int aoff = g * kSeg + l16 * 8;
+  // One k step s at ring position P = s % kRing: copy(s + kRing - 1), two
+  // vector-memory operations per wave, so when step s starts only the two of
+  // step s - 1 may still be in flight and everything step s reads has landed.
+  auto step = [&](int s, auto Pc) {
+    constexpr int P = decltype(Pc)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+    lds_barrier();  // every wave's copies of slab s have landed; the slot of step s - 1 is free
+    copy(s + kRing - 1, slabs[(P + kRing - 1) % kRing]);
+    if (live) {
+      const uint8_t* slab = slabs[P] + aoff;
+      const uint4* w = reinterpret_cast<const uint4*>(slabs[P] + 4 * kSeg + wave * 512 + l16 * 32);
+      uint4 a[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        uint2 w;
-        w.x = pack_bf2(acc[mt][n2][0], acc[mt][n2][1]);
-        w.y = pack_bf2(acc[mt][n2][2], acc[mt][n2][3]);
-        *reinterpret_cast<uint2*>(ost + il * kOS + 64 * wave + 16 * mt + 4 * g) = w;
+        const uint2 lo = *reinterpret_cast<const uint2*>(slab + 128 * mt);
+        const uint2 hi = *reinterpret_cast<const uint2*>(slab + 512 + 128 * mt);
+        a[mt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+      const uint4 w0 = w[0], w1 = w[1];
+      const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int n2 = 0; n2 < 8; ++n2) {
+        // register e of the B operand: bf16 1.0 (0x3f80) in the halves whose bits are set
+        const uint32_t W = wv[n2] >> sh;
+        const uint4 b = make_uint4((W & 0x00010001u) * 0x3f80u, (W & 0x00020002u) * 0x1fc0u,
+                                   (W & 0x00040004u) * 0x0fe0u, (W & 0x00080008u) * 0x07f0u);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][n2] = mfma_bf16(a[mt], b, acc[mt][n2]);
       }
     }
-    __syncthreads();
-    const int nbase = nt * kTN;
+  };
+  // prologue: slabs 0 .. kRing - 2
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int x = 256 * u + tid;          // 64 rows x 32 chunks of 16 bytes
-      const int row = x >> 5, ch = x & 31;
-      const int i = i0 + 64 * half + row, n = nbase + 8 * ch;
-      if (i < Nb && n < NN)
-        *reinterpret_cast<uint4*>(Hx + ((size_t)bh * Nb + i) * NN + n) =
-            *reinterpret_cast<const uint4*>(ost + row * kOS + 8 * ch);
+  for (int t = 0; t + 1 < kRing; ++t) copy(t, slabs[t]);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  // unrolled by kRing: full rounds carry no condition (so the wait counts stay
+  // exact), the last steps follow
+  int s = 0;
+  for (; s + kRing <= S; s += kRing) {
+    step(s, I0{});
+    step(s + 1, I1{});
+    step(s + 2, I2{});
+    step(s + 3, I3{});
+    step(s + 4, I4{});
+    step(s + 5, I5{});
+  }
+  if (s < S) step(s, I0{});
+  if (s + 1 < S) step(s + 1, I1{});
+  if (s + 2 < S) step(s + 2, I2{});
+  if (s + 3 < S) step(s + 3, I3{});
+  if (s + 4 < S) step(s + 4, I4{});
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the clamped copies past the end land before exit
+
+  if (live) {
+#pragma unroll
+    for (int n2 = 0; n2 < 8; ++n2) {
+      const int i = ig * kRows + 16 * n2 + l16;
+      if (i < Nb) {
+        uint16_t* dst = Hx + ((size_t)bh * Nb + i) * NN + n0 + 4 * g;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          *reinterpret_cast<uint2*>(dst + 16 * mt) =
+              make_uint2(pack_bf2(acc[mt][n2][0], acc[mt][n2][1]), pack_bf2(acc[mt][n2][2], acc[mt][n2][3]));
+      }
     }
   }
 }
@@ -180,17 +217,20 @@ __global__ __launch_bounds__(256) void k_linear_f32(const int8_t* __restrict__ m
 }  // namespace
 
 hipError_t launch_indicator(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s) {
-  dim3 grid(D.Nb128 * 4 / 256, D.Nbp / 32, D.BH);
+  const int threads = D.Nb128 * (D.Nbp / 32);
+  dim3 grid((threads + 255) / 256, D.BH);
   hipLaunchKernelGGL(k_indicator, grid, dim3(256), 0, s, mask, w.ind, D.Nb, D.Nbp, D.Nb128);
   return hipGetLastError();
 }
 
 hipError_t launch_linear(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s) {
   if (D.bf16) {
-    const int ntn = (D.NN + kTN - 1) / kTN, nti = D.Nb128 / kTI;
-    hipLaunchKernelGGL(k_linear_bf16, dim3(D.BH * ntn * nti), dim3(256), 0, s,
-                       (const uint16_t*)w.ind, (const uint16_t*)w.hx, (uint16_t*)w.Hx, D.Nb,
-                       D.Nbp, D.Nb128, D.NN, ntn, nti);
+    // d (d + 1) is a multiple of 64 for the supported d, so column slices are whole
+    if (D.NN % kTN != 0) return hipErrorInvalidValue;
+    const int ntn = D.NN / kTN, nit = (D.Nb128 / kRows + 3) / 4;
+    hipLaunchKernelGGL(k_linear_bf16, dim3(D.BH * ntn * nit), dim3(256), 0, s,
+                       (const uint32_t*)w.ind, (const uint16_t*)w.hx, (uint16_t*)w.Hx, D.Nb,
+                       D.Nbp, D.Nb128, D.NN, ntn, nit);
   } else {
     dim3 grid((D.NN + 255) / 256, D.Nb, D.BH);
     hipLaunchKernelGGL(k_linear_f32, grid, dim3(256), 0, s, mask, (const float*)w.hx,

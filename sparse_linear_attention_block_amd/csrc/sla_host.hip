@@ -90,7 +90,7 @@ size_t carve(const Dims& D, void* base, Work* w) {
     x.hx = take(BH * (D.Nbp / 4) * D.NN * 4 * sizeof(uint16_t));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(uint16_t));
     if (!D.quant) x.vt = (uint16_t*)take(BH * D.Nb * D.d * kBlock * sizeof(uint16_t));
-    x.ind = (uint16_t*)take(BH * D.Nbp * D.Nb128 * sizeof(uint16_t));
+    x.ind = (uint32_t*)take(BH * (D.Nbp / 32) * D.Nb128 * sizeof(uint32_t));
   } else {
     x.hx = take(BH * D.Nb * D.NN * sizeof(float));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(float));

@@ -32,8 +32,8 @@ struct Work {
   void* hx;           // bf16: [BH, Nbp/4, NN, 4] (four key blocks interleaved per column)
                       // f32:  [BH, Nb, NN]
   void* Hx;           // [BH, Nb, NN] per query block: H_i^T (c-major) then Z_i; bf16 or f32
-  uint16_t* ind;      // bf16 only: [BH, Nbp/32, Nb128, 32] marginal indicator (Mc == 0) as 0/1,
-                      // one 32-key slab per k step, 16-byte chunks swizzled by row
+  uint32_t* ind;      // bf16 only: [BH, Nbp/32, Nb128/128, 16, 8] marginal indicator (Mc == 0)
+                      // as bits, one 32-bit word per (32-key step, query block) (k_linear.hip)
   uint16_t* vt;       // bf16 without quant: [BH, Nb, d, 64] V^T of every key block (zero past N)
   float* qkmean;      // quant only: [2, BH, d] channel means of Q and K over the N tokens
   int8_t* k8;         // quant only: [BH, Nb*64, d] int8 of K - mean(K), zero rows past N;
