@@ -74,6 +74,8 @@ __global__ __launch_bounds__(256) void k_indicator(const int8_t* __restrict__ ma
 // remapped so that the column slices of one head run back to back on one XCD.
 constexpr int kRing = 6;              // hx slabs in flight or in use (a multiple of 3)
 constexpr int kSeg = 1024 + 128;      // bytes per wave segment of a slab (padded)
+constexpr int kOSt = 128 + 16;       // bytes per staged output row (64 bf16, padded)
+static_assert(32 * kOSt <= 4 * kSeg + 4 * 512, "a 32-row output stage fits in one ring slot");
 constexpr int kSlab = 4 * kSeg + 4 * 512;  // one k step: 8 groups of 4 key blocks x 64 n x
                                            // 8 bytes, then 128 indicator words per wave
 
@@ -184,17 +186,32 @@ __global__ __launch_bounds__(256, 3) void k_linear_bf16(const uint32_t* __restri
   if (s + 4 < S) step(s + 4, I4{});
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the clamped copies past the end land before exit
 
+  // The tile goes out through LDS in four quarters of 32 query blocks per wave,
+  // so that every store is 16 bytes of a whole 128-byte row segment. Wave w
+  // stages in ring slot w, which is free once every wave is past its last step
+  // and the last copies have landed.
+  __syncthreads();
+  uint8_t* stage = wave == 0 ? slab0 : wave == 1 ? slab1 : wave == 2 ? slab2 : slab3;
   if (live) {
 #pragma unroll
-    for (int n2 = 0; n2 < 8; ++n2) {
-      const int i = ig * kRows + 16 * n2 + l16;
-      if (i < Nb) {
-        uint16_t* dst = Hx + ((size_t)bh * Nb + i) * NN + n0 + 4 * g;
+    for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+      for (int n4 = 0; n4 < 2; ++n4) {
+        const int n2 = 2 * qq + n4;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          *reinterpret_cast<uint2*>(dst + 16 * mt) =
+          *reinterpret_cast<uint2*>(stage + (16 * n4 + l16) * kOSt + (16 * mt + 4 * g) * 2) =
               make_uint2(pack_bf2(acc[mt][n2][0], acc[mt][n2][1]), pack_bf2(acc[mt][n2][2], acc[mt][n2][3]));
       }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // a wave reads back only its own rows
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = 8 * u + (lane >> 3), ch = lane & 7;
+        const int i = ig * kRows + 32 * qq + row;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kOSt + 16 * ch);
+        if (i < Nb) *reinterpret_cast<uint4*>(Hx + ((size_t)bh * Nb + i) * NN + n0 + 8 * ch) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // reads done before the next quarter overwrites
     }
   }
 }
