@@ -6,17 +6,19 @@
 // summary, Eq. 3). phi is the softmax over the d features of each key token
 // (SLA explainer, section 3.2; SLA paper summary, Table 2).
 //
-// bf16 path, one workgroup (8 waves for d = 128, 4 for d = 64) per 4
-// consecutive key blocks of one (batch, head):
+// bf16 path, one workgroup (8 waves for d = 128, 4 for d = 64) per 2
+// consecutive key blocks of one (batch, head), two workgroups per CU:
 //  1. each block's K and V rows stream in with 16-byte loads (two tokens per
 //     lane), phi(K) is formed in float32 (row max / sum through LDS) and
 //     rounded to bf16, and phi(K)^T and V^T are written to LDS with the
 //     token index contiguous, two tokens per 32-bit word;
 //  2. MFMA 16x16x32 (bf16 in, f32 accumulate) forms h_j^T[c][r] =
-//     sum_t V[t][c] phi(K)[t][r] for the 4 blocks at once, so every lane holds
-//     the same (c, r) of the 4 blocks and writes them as one 8-byte word: the
-//     output layout hx[bh][j/4][c*d + r][j%4] gives the linear-branch GEMM
-//     its k operand (4 consecutive key blocks) contiguous;
+//     sum_t V[t][c] phi(K)[t][r] for the 2 blocks at once, so every lane holds
+//     the same (c, r) of both and writes them as one 4-byte word, one half of
+//     the 8-byte word of the output layout hx[bh][j/4][c*d + r][j%4] (the
+//     linear-branch GEMM's k operand, 4 consecutive key blocks, contiguous);
+//     the workgroups of the two halves run on one XCD, so the halves meet in
+//     its L2;
 //  3. z_j[r] (from the same bf16 phi values) goes to column d*d + r;
 //  4. the V^T tile of each block is copied to vt for the sparse kernel, whose
 //     P.V product needs the token index contiguous: for each half of the keys
@@ -41,9 +43,10 @@ struct HzCfg {
   static constexpr int CPT = CHUNKS / NCG; // chunks per thread
   static constexpr int NN = D * D + D;
 };
+constexpr int JB = 2;  // key blocks per workgroup: half of a group of 4
 
 template <int D>
-__global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(HzCfg<D>::NT, 2) void k_hz_bf16(const uint16_t* __restrict__ K,
                                                  const uint16_t* __restrict__ V,
                                                  uint16_t* __restrict__ hx,
                                                  uint16_t* __restrict__ vt, int N, int Nb,
@@ -51,14 +54,18 @@ __global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __rest
                                                  float* __restrict__ vsc) {
   using C = HzCfg<D>;
   constexpr int TS = C::TS, CPT = C::CPT, NN = C::NN, NT = C::NT, NW = C::NW, NCG = C::NCG;
-  __shared__ __attribute__((aligned(16))) uint16_t kT[4][D][TS];
-  __shared__ __attribute__((aligned(16))) uint16_t vT[4][D][TS];
+  __shared__ __attribute__((aligned(16))) uint16_t kT[JB][D][TS];
+  __shared__ __attribute__((aligned(16))) uint16_t vT[JB][D][TS];
   __shared__ float red[NCG][64];
   __shared__ float tstat[64];
 
   const int tid = threadIdx.x;
-  const int bh = blockIdx.y;
-  const int jq = blockIdx.x;        // group of 4 key blocks
+  // workgroups remapped so that the two halves of a group of 4 key blocks run
+  // on one XCD: their 4-byte halves of each 8-byte hx word meet in its L2
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = id / (2 * Nb4);
+  const int jq = (id >> 1) % Nb4;   // group of 4 key blocks
+  const int half = id & 1;          // this workgroup's blocks: 4 jq + 2 half + jj, jj < JB
   const int tp = tid & 31;          // token pair
   const int cg = tid >> 5;          // chunk group
   const uint16_t* Kb = K + (size_t)bh * N * D;
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __rest
   uint4 kr[2][2][CPT], vr[2][2][CPT];  // [register set][token of the pair][chunk]
   bool valid[2][2];
   auto load_block = [&](int jj, int set) {
-    const int j = 4 * jq + jj;
+    const int j = 4 * jq + JB * half + jj;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int t = j * kBlock + 2 * tp + u;
@@ -88,9 +95,9 @@ __global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __rest
   };
   load_block(0, 0);
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
+  for (int jj = 0; jj < JB; ++jj) {
     const int cs = jj & 1;
-    if (jj + 1 < 4) load_block(jj + 1, cs ^ 1);
+    if (jj + 1 < JB) load_block(jj + 1, cs ^ 1);
     // phi(K) row statistics: max then sum of exp over the D features
     float x[2][CPT * 8];
 #pragma unroll
@@ -167,23 +174,23 @@ __global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __rest
   uint16_t* hxg = hx + ((size_t)bh * Nb4 + jq) * NN * 4;
   for (int cti = 0; cti < CT_PER_WAVE; ++cti) {
     const int ct = wave * CT_PER_WAVE + cti;
-    uint4 a[4][2];
+    uint4 a[JB][2];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         a[jj][u] = *reinterpret_cast<const uint4*>(&vT[jj][16 * ct + l16][32 * u + 8 * g]);
     for (int rh = 0; rh < D / 64; ++rh) {
-      f32x4 acc[4][4];
+      f32x4 acc[4][JB];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[rt][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < JB; ++jj) acc[rt][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * (4 * rh + rt) + l16;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
+        for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const uint4 b = *reinterpret_cast<const uint4*>(&kT[jj][r][32 * u + 8 * g]);
@@ -196,19 +203,17 @@ __global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __rest
 #pragma unroll
         for (int reg = 0; reg < 4; ++reg) {
           const int c = 16 * ct + 4 * g + reg;
-          uint2 w;
-          w.x = pack_bf2(acc[rt][0][reg], acc[rt][1][reg]);
-          w.y = pack_bf2(acc[rt][2][reg], acc[rt][3][reg]);
-          *reinterpret_cast<uint2*>(hxg + ((size_t)c * D + r) * 4) = w;
+          *reinterpret_cast<uint32_t*>(hxg + ((size_t)c * D + r) * 4 + JB * half) =
+              pack_bf2(acc[rt][0][reg], acc[rt][1][reg]);
         }
       }
     }
   }
   // ---- z_j[r] = sum_t phi(K)[t][r] over the same bf16 values
   if (tid < D) {
-    float z[4];
+    float z[JB];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < JB; ++jj) {
       float s = 0.f;
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
@@ -218,10 +223,7 @@ __global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __rest
       }
       z[jj] = s;
     }
-    uint2 w;
-    w.x = pack_bf2(z[0], z[1]);
-    w.y = pack_bf2(z[2], z[3]);
-    *reinterpret_cast<uint2*>(hxg + ((size_t)D * D + tid) * 4) = w;
+    *reinterpret_cast<uint32_t*>(hxg + ((size_t)D * D + tid) * 4 + JB * half) = pack_bf2(z[0], z[1]);
   }
   // ---- V^T tiles for the sparse kernel, in the order its LDS copy wants:
   // vt[bh][j][kh][c][32] holds the 32 keys 32kh .. 32kh+31 of feature c as four
@@ -229,8 +231,8 @@ __global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __rest
   // slots of one MFMA lane group) and sits at position q ^ ((c >> 1) & 3), so
   // that 8 lanes reading 8 consecutive rows touch distinct LDS banks.
   // (the 8-bit sparse branch reads V8^T below instead: then vt is NULL)
-  for (int jj = 0; jj < 4 && vt != nullptr; ++jj) {
-    const int j = 4 * jq + jj;
+  for (int jj = 0; jj < JB && vt != nullptr; ++jj) {
+    const int j = 4 * jq + JB * half + jj;
     if (j >= Nb) break;
     uint16_t* dst = vt + ((size_t)bh * Nb + j) * D * kBlock;
     for (int x = tid; x < D * 8; x += NT) {
@@ -248,11 +250,11 @@ __global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __rest
   // order (kt, r), the k slots one lane group of the 8-bit sparse kernel's
   // 16x16x128 product takes from one tile, and sits at position
   // g ^ ((c >> 1) & 3) against LDS bank conflicts.
-  __shared__ float vmax[4][NW];
+  __shared__ float vmax[JB][NW];
   const int cq = tid >> 2, gq = tid & 3;  // rows cq, cq + NT/4, ... of chunk gq
-  float am[4];
+  float am[JB];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
+  for (int jj = 0; jj < JB; ++jj) {
     float m = 0.f;
     for (int c = cq; c < D; c += NT / 4)
 #pragma unroll
@@ -267,14 +269,14 @@ __global__ __launch_bounds__(HzCfg<D>::NT) void k_hz_bf16(const uint16_t* __rest
   }
   __syncthreads();
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
+  for (int jj = 0; jj < JB; ++jj) {
     am[jj] = vmax[jj][0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) am[jj] = fmaxf(am[jj], vmax[jj][w]);
   }
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int j = 4 * jq + jj;
+  for (int jj = 0; jj < JB; ++jj) {
+    const int j = 4 * jq + JB * half + jj;
     if (j >= Nb) break;
     const float inv = am[jj] > 0.f ? 448.0f / am[jj] : 1.0f;
     if (tid == 0) vsc[(size_t)bh * Nb + j] = am[jj] > 0.f ? am[jj] / 448.0f : 1.0f;
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(256) void k_hz_f32(const float* __restrict__ K,
 
 hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w, hipStream_t s) {
   if (D.bf16) {
-    dim3 grid(D.Nbp / 4, D.BH);
+    dim3 grid(D.Nbp / 4 * 2 * D.BH);
     if (D.d == 128)
       hipLaunchKernelGGL(k_hz_bf16<128>, grid, dim3(HzCfg<128>::NT), 0, s, (const uint16_t*)K,
                          (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4, w.v8t,
