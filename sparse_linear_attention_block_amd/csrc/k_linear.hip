@@ -39,22 +39,32 @@ constexpr int kRows = 128; // query blocks per wave (4 waves per workgroup)
 __global__ __launch_bounds__(256) void k_indicator(const int8_t* __restrict__ mask,
                                                    uint32_t* __restrict__ ind, int Nb, int Nbp,
                                                    int Nb128) {
-  const int S = Nbp / 32;
-  const int t = blockIdx.x * 256 + threadIdx.x;  // (i, s), s fastest
+  // one wave per query block, two k steps per iteration: lane L takes key
+  // 32 (s + L / 32) + k(L % 32) with k(16 hi + 4 g + e) = 8 g + 2 e + hi, so the
+  // wave's ballot is the two words W(s), W(s + 1) in their bit layout
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int bh = blockIdx.y;
-  const int s = t % S, i = t / S;
-  if (i >= Nb128) return;
-  uint32_t w = 0;
-  if (i < Nb) {
-    const int8_t* row = mask + ((size_t)bh * Nb + i) * Nb + 32 * s;
+  const int S = Nbp / 32, NI = Nb128 / 128;
+  if (i >= Nb128) return;  // wave-uniform
+  const int L = lane & 31, k = 8 * ((L >> 2) & 3) + 2 * (L & 3) + (L >> 4);
+  const int8_t* row = mask + ((size_t)bh * Nb + min(i, Nb - 1)) * Nb;
+  uint32_t* dst = ind + ((size_t)bh * S * NI + i / 128) * 128 + (i % 16) * 8 + (i / 16) % 8;
+  // eight step pairs per round, every load of a round issued before the first ballot
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    int8_t m[8];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const bool marg = 32 * s + k < Nb && row[min(k, Nb - 1 - 32 * s)] == 0;
-      const int g = k >> 3, e = (k & 7) >> 1, hi = k & 1;
-      w |= (uint32_t)marg << (16 * hi + 4 * g + e);
+    for (int u = 0; u < 8; ++u) m[u] = row[min(32 * (s0 + 2 * u + (lane >> 5)) + k, Nb - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + 2 * u;
+      if (s >= S) break;  // uniform
+      const int j = 32 * (s + (lane >> 5)) + k;
+      const uint64_t w = __ballot(i < Nb && j < Nb && m[u] == 0);
+      if (lane == 0) dst[(size_t)s * NI * 128] = (uint32_t)w;
+      if (lane == 32 && s + 1 < S) dst[(size_t)(s + 1) * NI * 128] = (uint32_t)(w >> 32);
     }
   }
-  ind[(((size_t)bh * S + s) * (Nb128 / 128) + i / 128) * 128 + (i % 16) * 8 + (i / 16) % 8] = w;
 }
 
 // Hx^T = hx^T M01^T for one (batch, head): workgroup tile 64 columns n x 512
@@ -234,8 +244,7 @@ __global__ __launch_bounds__(256) void k_linear_f32(const int8_t* __restrict__ m
 }  // namespace
 
 hipError_t launch_indicator(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s) {
-  const int threads = D.Nb128 * (D.Nbp / 32);
-  dim3 grid((threads + 255) / 256, D.BH);
+  dim3 grid(D.Nb128 / 4, D.BH);  // one wave per query block (rows past Nb get zeros)
   hipLaunchKernelGGL(k_indicator, grid, dim3(256), 0, s, mask, w.ind, D.Nb, D.Nbp, D.Nb128);
   return hipGetLastError();
 }
