@@ -61,7 +61,8 @@ typedef enum {
    * K minus their channel means over the N tokens as int8 (the Q mean enters
    * as an exact per-key float32 bias, the K mean cancels in the softmax) and
    * V as fp8 e4m3, each with one absmax scale per 64-token block; P as fp8
-   * e4m3 with one scale per query row and pair of 64-key tiles.
+   * e4m3 with one power-of-two scale per query row and pair of 64-key tiles
+   * (the largest code of the row in (224, 448]).
    * Requires dtype == SLA_BF16. The linear branch stays bf16; the mask is
    * decided from the unquantised inputs. */
   SLA_QUANT_I8QK_F8PV = 1
