@@ -14,8 +14,8 @@
 //    uint32 key (round-to-nearest is monotone, so key order never contradicts
 //    float64 order);
 //  * a radix select (top byte by a ballot search, then three 8-bit passes over
-//    a per-wave LDS histogram) finds the n_h-th largest key T and the n_l-th
-//    smallest key L;
+//    per-wave LDS histograms) finds the n_h-th largest key T and the n_l-th
+//    smallest key L, both searches in the same sweeps;
 //  * keys strictly above T are critical, strictly below L negligible; the few
 //    elements whose key equals T (or L) are ordered exactly by their float64
 //    logit and then by block index (lower index first), which reproduces the
@@ -37,65 +37,57 @@ __device__ __forceinline__ int wave_count(bool p) {
   return __popcll(__ballot(p));
 }
 
-// The k-th largest (from_top) or k-th smallest valid key of a wave's row,
-// 1 <= k <= number of valid keys: the top byte by a bitwise search with wave
-// ballots, then three 8-bit radix passes, each a 256-bin histogram in the
-// wave's own LDS slice of the keys that match the digits found so far, scanned
-// across lanes to find the bin where the running count reaches k. Equal keys are counted with their multiplicity, so the result is
-// the value v with #(keys beyond v) < k <= #(keys at or beyond v).
+// The kt-th largest key T and the kb-th smallest key L of a wave's row
+// (1 <= kt, kb <= number of valid keys), found together so that the two
+// searches' latencies overlap: the top byte of each by a bitwise search with
+// wave ballots, then three 8-bit radix passes, each a pair of 256-bin
+// histograms in the wave's own LDS slice of the keys that match the digits
+// found so far, scanned across lanes to find the bin where the running count
+// reaches the rank. Equal keys are counted with their multiplicity, so T is the
+// value v with #(keys above v) < kt <= #(keys at or above v), and L likewise
+// from below.
 template <int kMaxE>
-__device__ uint32_t radix_select(const uint32_t* key, int E, int Nb, int k, bool from_top,
-                                 uint32_t* __restrict__ hist) {
+__device__ void radix_select2(const uint32_t* key, int E, int Nb, int kt, int kb,
+                              uint32_t* __restrict__ hist, uint32_t& T, uint32_t& L) {
   const int lane = threadIdx.x & 63;
-  // top byte by an 8-step search with wave ballots: logits of one row share
-  // few top bytes (sign and high exponent bits), which would serialise the
-  // histogram atomics of a first radix pass
-  auto count = [&](uint32_t lo, uint32_t hi) {  // keys in [lo, hi]
-    int c = 0;
+  // #keys >= lo and #keys <= hi in one sweep (the top byte comes first: logits of
+  // one row share few top bytes, which would serialise a first radix pass)
+  auto count2 = [&](uint32_t lo, uint32_t hi, int& ct, int& cb) {
+    ct = 0;
+    cb = 0;
 #pragma unroll
     for (int e = 0; e < kMaxE; ++e) {
       if (e >= E) break;
-      const int j = lane + 64 * e;
-      c += __popcll(__ballot(j < Nb && key[e] >= lo && key[e] <= hi));
+      const bool valid = lane + 64 * e < Nb;
+      ct += __popcll(__ballot(valid && key[e] >= lo));
+      cb += __popcll(__ballot(valid && key[e] <= hi));
     }
-    return c;
   };
-  uint32_t tb;
-  int need = k;
-  if (from_top) {
-    tb = 0;
-    for (int bit = 7; bit >= 0; --bit) {
-      const uint32_t cand = tb | (1u << bit);
-      if (count(cand << 24, 0xffffffffu) >= need) tb = cand;
-    }
-    if (tb < 255) need -= count((tb + 1) << 24, 0xffffffffu);
-  } else {
-    tb = 255;
-    for (int bit = 7; bit >= 0; --bit) {
-      const uint32_t cand = tb & ~(1u << bit);
-      if (count(0u, (cand << 24) | 0xffffffu) >= need) tb = cand;
-    }
-    if (tb > 0) need -= count(0u, (tb << 24) - 1u);
+  uint32_t tbt = 0, tbb = 255;
+  int nt = kt, nb = kb;
+  for (int bit = 7; bit >= 0; --bit) {
+    const uint32_t ct_cand = tbt | (1u << bit), cb_cand = tbb & ~(1u << bit);
+    int ct, cb;
+    count2(ct_cand << 24, (cb_cand << 24) | 0xffffffu, ct, cb);
+    if (ct >= nt) tbt = ct_cand;
+    if (cb >= nb) tbb = cb_cand;
   }
-  uint32_t prefix = tb << 24, pmask = 0xff000000u;
-  for (int pass = 1; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hist[64 * q + lane] = 0u;
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-#pragma unroll
-    for (int e = 0; e < kMaxE; ++e) {
-      if (e >= E) break;
-      const int j = lane + 64 * e;
-      if (j < Nb && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    // lane l owns the order positions 4l .. 4l+3 (bins from the top or from the bottom)
+  {
+    int ct, cb;
+    count2(tbt < 255 ? (tbt + 1) << 24 : 0xffffffffu, tbb > 0 ? (tbb << 24) - 1u : 0u, ct, cb);
+    if (tbt < 255) nt -= ct;
+    if (tbb > 0) nb -= cb;
+  }
+  uint32_t pt = tbt << 24, pb = tbb << 24, pmask = 0xff000000u;
+  uint32_t* ht = hist;
+  uint32_t* hb = hist + 256;
+  // the bin where the running count from the top (or the bottom) reaches need
+  auto find = [&](const uint32_t* h, bool from_top, int need, int& digit, int& before) {
     int c[4], tot = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int o = 4 * lane + q;
-      c[q] = (int)hist[from_top ? 255 - o : o];
+      const int o = 4 * lane + q;  // lane l owns the order positions 4l .. 4l+3
+      c[q] = (int)h[from_top ? 255 - o : o];
       tot += c[q];
     }
     int incl = tot;  // inclusive scan over lanes
@@ -107,24 +99,48 @@ __device__ uint32_t radix_select(const uint32_t* key, int E, int Nb, int k, bool
     const int excl = incl - tot;
     const uint64_t hit = __ballot(excl < need && incl >= need);
     const int hl = __ffsll((unsigned long long)hit) - 1;
-    int before = excl, digit = 0;
+    int bef = excl, dg = 0;
     bool found = false;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (!found && before + c[q] >= need) {
-        digit = from_top ? 255 - (4 * lane + q) : 4 * lane + q;
+      if (!found && bef + c[q] >= need) {
+        dg = from_top ? 255 - (4 * lane + q) : 4 * lane + q;
         found = true;
       } else if (!found) {
-        before += c[q];
+        bef += c[q];
       }
     }
-    digit = __shfl(digit, hl);
-    before = __shfl(before, hl);
-    need -= before;
-    prefix |= (uint32_t)digit << shift;
+    digit = __shfl(dg, hl);
+    before = __shfl(bef, hl);
+  };
+  for (int pass = 1; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ht[64 * q + lane] = 0u;
+      hb[64 * q + lane] = 0u;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+    for (int e = 0; e < kMaxE; ++e) {
+      if (e >= E) break;
+      if (lane + 64 * e >= Nb) continue;
+      const uint32_t bin = (key[e] >> shift) & 255u;
+      if ((key[e] & pmask) == pt) atomicAdd(&ht[bin], 1u);
+      if ((key[e] & pmask) == pb) atomicAdd(&hb[bin], 1u);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    int dt, bt, db, bb;
+    find(ht, true, nt, dt, bt);
+    find(hb, false, nb, db, bb);
+    nt -= bt;
+    nb -= bb;
+    pt |= (uint32_t)dt << shift;
+    pb |= (uint32_t)db << shift;
     pmask |= 0xffu << shift;
   }
-  return prefix;
+  T = pt;
+  L = pb;
 }
 
 // One wave classifies one row of Nb float64 logits (Nb <= 64 * kMaxE).
@@ -143,38 +159,29 @@ __device__ void classify_row(const double* __restrict__ lg, int Nb, int n_h, int
     const int j = lane + 64 * e;
     key[e] = (e < E && j < Nb) ? order_key(v[e]) : 0u;
   }
-  // counts over valid elements only: invalid slots carry key 0 and are masked
-  auto cnt_ge = [&](uint32_t t) {
-    int c = 0;
+  // T: the n_h-th largest key; L: the n_l-th smallest key (a side with no
+  // blocks is searched at rank 1 and then ignored)
+  uint32_t T, L;
+  radix_select2<kMaxE>(key, E, Nb, max(n_h, 1), max(n_l, 1), hist, T, L);
+  if (n_h == 0) T = 0u;
+  if (n_l == 0) L = 0xffffffffu;
+  // sizes of the strict parts and of the tie groups at the two boundaries, in one sweep
+  int ge1 = 0, ge0 = 0, le1 = 0, le0 = 0;
 #pragma unroll
-    for (int e = 0; e < kMaxE; ++e) {
-      if (e >= E) break;
-      const int j = lane + 64 * e;
-      c += wave_count(j < Nb && key[e] >= t);
-    }
-    return c;
-  };
-  auto cnt_le = [&](uint32_t t) {
-    int c = 0;
-#pragma unroll
-    for (int e = 0; e < kMaxE; ++e) {
-      if (e >= E) break;
-      const int j = lane + 64 * e;
-      c += wave_count(j < Nb && key[e] <= t);
-    }
-    return c;
-  };
-
-  // T: the n_h-th largest key; L: the n_l-th smallest key
-  const uint32_t T = n_h > 0 ? radix_select<kMaxE>(key, E, Nb, n_h, true, hist) : 0u;
-  const uint32_t L = n_l > 0 ? radix_select<kMaxE>(key, E, Nb, n_l, false, hist) : 0xffffffffu;
-  // sizes of the strict parts and of the tie groups at the two boundaries
-  const int gt_h = (n_h > 0 && T != 0xffffffffu) ? cnt_ge(T + 1) : 0;
+  for (int e = 0; e < kMaxE; ++e) {
+    if (e >= E) break;
+    const bool valid = lane + 64 * e < Nb;
+    ge1 += wave_count(valid && T != 0xffffffffu && key[e] >= T + 1);
+    ge0 += wave_count(valid && key[e] >= T);
+    le1 += wave_count(valid && L != 0u && key[e] <= L - 1);
+    le0 += wave_count(valid && key[e] <= L);
+  }
+  const int gt_h = n_h > 0 ? ge1 : 0;
   const int need_h = n_h > 0 ? n_h - gt_h : 0;
-  const int grp_h = n_h > 0 ? cnt_ge(T) - gt_h : 0;
-  const int lt_l = (n_l > 0 && L != 0u) ? cnt_le(L - 1) : 0;
+  const int grp_h = n_h > 0 ? ge0 - gt_h : 0;
+  const int lt_l = n_l > 0 ? le1 : 0;
   const int need_l = n_l > 0 ? n_l - lt_l : 0;
-  const int grp_l = n_l > 0 ? cnt_le(L) - lt_l : 0;
+  const int grp_l = n_l > 0 ? le0 - lt_l : 0;
 
 #pragma unroll
   for (int e = 0; e < kMaxE; ++e) {
@@ -276,7 +283,7 @@ template <int kMaxE>
 __global__ __launch_bounds__(256) void k_classify(const double* __restrict__ lg,
                                                   int8_t* __restrict__ mask, int Nb, int n_h,
                                                   int n_l, int rows) {
-  __shared__ uint32_t hist[4][256];  // one histogram per wave
+  __shared__ uint32_t hist[4][512];  // two histograms per wave
   const int wave = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;  // whole wave; the kernel has no barrier
