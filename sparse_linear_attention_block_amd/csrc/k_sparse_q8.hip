@@ -242,9 +242,60 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
             sf[t][kt][r] = out ? -INFINITY : v;
           }
         }
-        tmax[t] = fmaxf(tmax[t], fmaxf(fmaxf(sf[t][kt][0], sf[t][kt][1]), fmaxf(sf[t][kt][2], sf[t][kt][3])));
       }
+      // three-input max chain over the tile's 16 scores
+      float m = fmaxf(fmaxf(sf[t][0][0], sf[t][0][1]), sf[t][0][2]);
+#pragma unroll
+      for (int x = 3; x + 1 < 16; x += 2)
+        m = fmaxf(fmaxf(m, sf[t][x >> 2][x & 3]), sf[t][(x + 1) >> 2][(x + 1) & 3]);
+      tmax[t] = fmaxf(m, sf[t][3][3]);
     }
+    // the rest of the pair; called on both sides of the (rare) reference raise,
+    // so that the common path keeps the accumulators where the products left them
+    auto finish = [&]() __attribute__((always_inline)) {
+      const float meff = mref == -INFINITY ? 0.0f : mref;  // no valid key yet: every p is 0
+      // P' = P~ s_V with P~ = 2^(s - meff). Its row scale over the pair is the
+      // power of two s_P = 2^E, E = ceil(log2 rowmax(P') - log2 448), so that the
+      // largest fp8 input lies in (224, 448]; the fp8 product applies it as the
+      // E8M0 block scale of its B operand. With meff an integer, meff + E =
+      // ceil(Mq - log2 448) and the codes 2^(s + log2 s_V - meff - E) are those
+      // of the scores alone. The fp8 input of a key of tile t is 2^(s - off_t),
+      // off_t = meff - log2 s_V(t) + E, and the tile's share of l (the
+      // unquantised P~) is 2^(off_t - meff) times the sum of those inputs.
+      const float lsv0 = __log2f(sv0), lsv1 = has1 ? __log2f(sv1) : 0.f;
+      const float Mq = group4_max(fmaxf(tmax[0] + lsv0, tmax[1] + lsv1));
+      constexpr float kLog2_448 = 8.807354922057604f;
+      const float E = fminf(fmaxf(ceilf(Mq - meff - kLog2_448), -127.f), 127.f);
+      const float off0 = meff - lsv0 + E, off1 = meff - lsv1 + E;
+      float ssum[2] = {0.f, 0.f};
+      i32x8 pb;
+  #pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float off = t ? off1 : off0;
+  #pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          float e[4];
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            e[r] = __builtin_amdgcn_exp2f(sf[t][kt][r] - off);
+            ssum[t] += e[r];
+          }
+          pb[4 * t + kt] = (int)pack_e4m3x4_nosat(e[0], e[1], e[2], e[3]);
+        }
+      }
+      lp += ssum[0] * __builtin_amdgcn_exp2f(E - lsv0) + ssum[1] * __builtin_amdgcn_exp2f(E - lsv1);
+      const int sb = (int)E + 127;
+  #pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        const int c = 16 * ft + l16;
+        const int off = c * 64 + 16 * (g ^ ((c >> 1) & 3));
+        const uint4 v0 = *reinterpret_cast<const uint4*>(cur + 2 * KT + off);
+        const uint4 v1 = has1 ? *reinterpret_cast<const uint4*>(cur + 3 * KT + off) : make_uint4(0, 0, 0, 0);
+        const i32x8 a = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                         (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        acc[ft] = mfma_fp8_sb(a, pb, acc[ft], sb);
+      }
+    };
     const float lmax = fmaxf(tmax[0], tmax[1]);
     if (__ballot(lmax > mref + TAU)) {
       const float tm = group4_max(lmax);
@@ -256,48 +307,9 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
       lp *= fac;
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) acc[ft] *= fac;
-    }
-    const float meff = mref == -INFINITY ? 0.0f : mref;  // no valid key yet: every p is 0
-    // P' = P~ s_V with P~ = 2^(s - meff). Its row scale over the pair is the
-    // power of two s_P = 2^E, E = ceil(log2 rowmax(P') - log2 448), so that the
-    // largest fp8 input lies in (224, 448]; the fp8 product applies it as the
-    // E8M0 block scale of its B operand. With meff an integer, meff + E =
-    // ceil(Mq - log2 448) and the codes 2^(s + log2 s_V - meff - E) are those
-    // of the scores alone. The fp8 input of a key of tile t is 2^(s - off_t),
-    // off_t = meff - log2 s_V(t) + E, and the tile's share of l (the
-    // unquantised P~) is 2^(off_t - meff) times the sum of those inputs.
-    const float lsv0 = __log2f(sv0), lsv1 = has1 ? __log2f(sv1) : 0.f;
-    const float Mq = group4_max(fmaxf(tmax[0] + lsv0, tmax[1] + lsv1));
-    constexpr float kLog2_448 = 8.807354922057604f;
-    const float E = fminf(fmaxf(ceilf(Mq - meff - kLog2_448), -127.f), 127.f);
-    const float off0 = meff - lsv0 + E, off1 = meff - lsv1 + E;
-    float ssum[2] = {0.f, 0.f};
-    i32x8 pb;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const float off = t ? off1 : off0;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        float e[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = __builtin_amdgcn_exp2f(sf[t][kt][r] - off);
-          ssum[t] += e[r];
-        }
-        pb[4 * t + kt] = (int)pack_e4m3x4_nosat(e[0], e[1], e[2], e[3]);
-      }
-    }
-    lp += ssum[0] * __builtin_amdgcn_exp2f(E - lsv0) + ssum[1] * __builtin_amdgcn_exp2f(E - lsv1);
-    const int sb = (int)E + 127;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      const int c = 16 * ft + l16;
-      const int off = c * 64 + 16 * (g ^ ((c >> 1) & 3));
-      const uint4 v0 = *reinterpret_cast<const uint4*>(cur + 2 * KT + off);
-      const uint4 v1 = has1 ? *reinterpret_cast<const uint4*>(cur + 3 * KT + off) : make_uint4(0, 0, 0, 0);
-      const i32x8 a = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                       (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      acc[ft] = mfma_fp8_sb(a, pb, acc[ft], sb);
+      finish();
+    } else {
+      finish();
     }
   };
   auto run = [&](int p, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
