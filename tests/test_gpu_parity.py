@@ -165,3 +165,43 @@ def test_deterministic():
     a = run_gpu(x, debug=False)
     b = run_gpu(x, debug=False)
     assert np.array_equal(a["O"], b["O"]) and np.array_equal(a["mask"], b["mask"])
+
+
+def test_long_rows_past_the_prefetched_mask():
+    """Nb = 2188 > 2048: the sparse kernel's compaction finishes the mask row
+    chunk by chunk past the 2048 entries it prefetches, one row has every block
+    critical (2188 tiles), another only blocks on both sides of index 2048 and
+    the ragged last block; the linear GEMM runs with idle waves past the last
+    query block and an odd number of k steps; the mask itself (classify with 35
+    keys per lane) is checked on every row."""
+    from workloads.configs import WorkloadConfig
+    N = 140000
+    cfg = WorkloadConfig(11, "long", 1, 1, N, 64, None, "bf16", 0.01, 0.05, "learned",
+                         ("const", 0.4), False, 79, qk="normal")
+    x = make_inputs(cfg)
+    Nb = cfg.Nb
+    assert Nb == 2188
+    ref = orc.forward(x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha, x.kh, x.kl, compute_outputs=False)
+    g = run_gpu(x, debug=False)
+    exact, excused, bad = compare_masks(g["mask"], ref.mask, ref.logits, ref.n_h, ref.n_l)
+    _flush(f"long rows: mask rows exact={exact} near-tie={excused} bad={len(bad)}")
+    assert not bad, bad[:10]
+    rng = np.random.default_rng(11)
+    mask = rng.choice([1, 0, -1], size=(1, 1, Nb, Nb), p=[0.01, 0.9, 0.09]).astype(np.int8)
+    mask[0, 0, 1, :] = 1                                  # every block critical
+    mask[0, 0, 2, :] = 0
+    mask[0, 0, 2, [0, 5, 2046, 2047, 2048, 2049, 2100, Nb - 1]] = 1
+    mask[0, 0, Nb - 1, :] = -1
+    mask[0, 0, Nb - 1, [3, 2050, Nb - 1]] = 1             # ragged query and key block
+    qb = [0, 1, 2, 1500, Nb - 1]
+    sub = orc.forward(x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha, x.kh, x.kl,
+                      mask_in=mask, query_blocks={(0, 0): qb})
+    gi = run_gpu(x, mask_in=mask, debug=True)
+    rows = orc.token_rows(qb, N)
+    for name, key in (("O", "O"), ("O_s", "o_s"), ("O_l", "o_l")):
+        r = getattr(sub, name)[(0, 0)]
+        gg = gi[key][0, 0][rows]
+        e = rel_l1(gg, r)
+        m = float(np.abs(gg - r).max())
+        _flush(f"long rows {name}: rel-L1 {e:.2e} max-abs {m:.2e}")
+        assert e <= BF16_REL_L1 and m <= BF16_MAX_ABS, (name, e, m)

@@ -107,3 +107,24 @@ def test_q8_deterministic():
     a = run_gpu(x, debug=False, quant=True)
     b = run_gpu(x, debug=False, quant=True)
     assert np.array_equal(a["O"], b["O"]) and np.array_equal(a["mask"], b["mask"])
+
+
+def test_q8_long_rows_past_the_prefetched_mask():
+    """Nb = 2188 > 2048 in 8-bit mode: one row with every block critical (1094
+    tile pairs), one with critical blocks on both sides of index 2048 and an
+    odd count, the ragged last row; the compaction finishes the mask row past
+    the 2048 entries it prefetches."""
+    from workloads.configs import WorkloadConfig
+    N = 140000
+    cfg = WorkloadConfig(12, "long_q8", 1, 1, N, 64, None, "bf16", 0.01, 0.05, "learned",
+                         ("const", 0.4), True, 80, qk="normal")
+    x = make_inputs(cfg)
+    Nb = cfg.Nb
+    rng = np.random.default_rng(12)
+    mask = rng.choice([1, 0, -1], size=(1, 1, Nb, Nb), p=[0.01, 0.9, 0.09]).astype(np.int8)
+    mask[0, 0, 1, :] = 1
+    mask[0, 0, 2, :] = 0
+    mask[0, 0, 2, [0, 5, 2046, 2047, 2048, 2100, Nb - 1]] = 1
+    mask[0, 0, Nb - 1, :] = -1
+    mask[0, 0, Nb - 1, [3, 2050, Nb - 1]] = 1
+    _check(x, heads=[(0, 0)], qblocks={(0, 0): [0, 1, 2, 1500, Nb - 1]}, mask=mask)
