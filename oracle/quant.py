@@ -42,8 +42,9 @@ Parity status: e4m3 and int8 pinned against closed-form codes and the
 torch float8_e4m3fn cast; the branch pinned by an exactly representable case
 (O_s = mean of V), by exact 2^k scaling in V, by the unquantised sparse
 branch when the quantisers are switched off (the smoothing algebra, bias and
-pairing are then exact) and by the error bound against it. The 8-bit sparse branch itself is judged
-against the unquantised oracle; this emulation narrows a failure down.
+pairing are then exact) and by the error bound against it. The 8-bit
+sparse branch on the GPU is held to the unquantised oracle; this emulation
+narrows a failure down.
 """
 
 import numpy as np
