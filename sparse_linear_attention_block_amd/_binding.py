@@ -217,12 +217,22 @@ class Plan:
         return self.out
 
 
+# hipEventDisableSystemFence: the event's record skips the system-scope release
+# (an L2 writeback and invalidation), which would otherwise stall the stream for
+# several microseconds between the kernels it brackets and make the following
+# kernel start on a cold L2. Timestamps stay valid once the device has been
+# synchronised.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 class HipEvents:
-    """Raw HIP events through the HIP runtime (for per-kernel timing)."""
+    """Raw HIP events through the HIP runtime (for per-kernel timing), created
+    without a system-scope fence so that recording them does not perturb the
+    kernels they bracket."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -231,8 +241,8 @@ class HipEvents:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(e.value)
         return out
 

@@ -33,11 +33,12 @@
 // last tile is processed, H_i^T (from K4's output, rows swizzled like K) is
 // copied into the idle tile buffer and Z_i into the spent critical list.
 // The two key halves are combined through LDS (max-rescaled partial sums);
-// each wave then finishes half the features of its 32 queries: O_s = acc / l,
-// phi(Q) (softmax over the features in f32, left unnormalised because the
-// normalisation cancels in O_l, rounded to bf16), num^T = H_i^T phi(Q)^T on
-// MFMA, den = phi(Q).Z_i, O = alpha O_s + (1 - alpha) O_l, staged in LDS and
-// written as full rows.
+// each wave then finishes all features of one 16-query tile (so phi is formed
+// once per query): O_s = acc / l, phi(Q) (softmax over the features in f32,
+// left unnormalised because the normalisation cancels in O_l, rounded to
+// bf16), num^T = H_i^T phi(Q)^T and den = phi(Q).Z_i on MFMA (Z_i as row 0 of
+// an A operand), O = alpha O_s + (1 - alpha) O_l, staged in LDS and written
+// as full rows.
 // Workgroups are remapped so that each XCD walks a contiguous range of
 // (batch, head, query block): neighbouring query blocks share most critical
 // key tiles, which then come from the XCD's L2.
@@ -61,7 +62,6 @@ struct FaCfg {
   static constexpr int NN = D * D + D;
   static constexpr int KSTEPS = D / 32;
   static constexpr int FT = D / 16;                // feature tiles of O
-  static constexpr int FTH = FT / 2;               // feature tiles each wave finishes
   static constexpr int OS = D + 8;                 // LDS row stride of the staged output
   static constexpr int HINSTR = D * D / 8 / 256;   // 16-byte copies per lane of H_i^T
 };
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     float* __restrict__ dbg_os, float* __restrict__ dbg_ol, int H, int N, int Nb) {
   using Cf = FaCfg<D>;
   constexpr int C = Cf::C, TILE = Cf::TILE, INSTR = Cf::INSTR, NN = Cf::NN;
-  constexpr int KSTEPS = Cf::KSTEPS, FT = Cf::FT, FTH = Cf::FTH, OS = Cf::OS, HINSTR = Cf::HINSTR;
+  constexpr int KSTEPS = Cf::KSTEPS, FT = Cf::FT, OS = Cf::OS, HINSTR = Cf::HINSTR;
   constexpr float TAU = 8.0f;  // a stale reference max may lag the tile max by 2^8 at most
   // Two tile buffers (K then V^T each) as distinct LDS objects, so that reads of
   // one provably do not alias the asynchronous copies into the other.
@@ -280,7 +280,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     if (c + 1 < ncrit) step(c + 1, bufB, bufA);
   }
 
-  // ---- combine the two key halves: wave kh finishes feature tiles [FTH*kh, FTH*kh + FTH)
+  // ---- combine the two key halves: wave (kh, qh) finishes every feature of
+  // query tile kh of its query half, so each query's phi(Q) is formed once
   float lw[2];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) lw[qt] = __shfl(accl[qt][0], l16);  // from lane group 0
@@ -290,16 +291,15 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   const uint16_t* hbuf = (ncrit & 1) ? bufB : bufA;
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of H_i^T and Z_i
   __syncthreads();  // every wave is done with the tile buffers; H_i^T and Z_i have landed
-  float* ex = reinterpret_cast<float*>(xbuf);  // [wave][FTH][2][64 lanes][4]
-  // the accumulator halves are selected with compile-time indices (a runtime
-  // index would send the accumulator array through scratch memory)
+  float* ex = reinterpret_cast<float*>(xbuf);  // [wave][FT][64 lanes][4]
+  // The query tile is chosen with compile-time indices (a runtime index would
+  // send the accumulator array through scratch memory): wave kh sends its
+  // partial sums of query tile 1 - kh and keeps those of query tile kh.
   auto send = [&](auto KH) {
-    constexpr int base = FTH * (1 - decltype(KH)::value);
+    constexpr int qs = 1 - decltype(KH)::value;
 #pragma unroll
-    for (int f = 0; f < FTH; ++f)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-        *reinterpret_cast<f32x4*>(ex + (((wave * FTH + f) * 2 + qt) * 64 + lane) * 4) = acc[base + f][qt];
+    for (int ft = 0; ft < FT; ++ft)
+      *reinterpret_cast<f32x4*>(ex + ((wave * FT + ft) * 64 + lane) * 4) = acc[ft][qs];
   };
   if (kh == 0) send(std::integral_constant<int, 0>{}); else send(std::integral_constant<int, 1>{});
   if (g == 0) {
@@ -310,109 +310,98 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     }
   }
   __syncthreads();
+  // own (this wave's partial sums), oth (the partner's) and their max-rescale
+  // weights w0, w1; O_s = (w0 own + w1 oth) / l
   const int partner = wave ^ 1;
-  f32x4 ofin[FTH][2];
-  float inv_l[2];
+  f32x4 own[FT], oth[FT];
+  float w0, w1, inv_l;
+  uint4 qk[KSTEPS];  // the query tile's Q fragments
   auto keep = [&](auto KH) {
-    constexpr int base = FTH * decltype(KH)::value;
+    constexpr int qt = decltype(KH)::value;
+    const float m0 = mref[qt], m1 = xm[partner][qt][l16];
+    const float M = fmaxf(m0, m1);
+    w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+    w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    const float l = w0 * lw[qt] + w1 * xl[partner][qt][l16];
+    inv_l = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float m0 = mref[qt], m1 = xm[partner][qt][l16];
-      const float M = fmaxf(m0, m1);
-      const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
-      const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-      const float l = w0 * lw[qt] + w1 * xl[partner][qt][l16];
-      inv_l[qt] = l > 0.f ? 1.0f / l : 0.f;
-#pragma unroll
-      for (int f = 0; f < FTH; ++f) {
-        const f32x4 other =
-            *reinterpret_cast<const f32x4*>(ex + (((partner * FTH + f) * 2 + qt) * 64 + lane) * 4);
-        ofin[f][qt] = acc[base + f][qt] * w0 + other * w1;
-      }
+    for (int ft = 0; ft < FT; ++ft) {
+      own[ft] = acc[ft][qt];
+      oth[ft] = *reinterpret_cast<const f32x4*>(ex + ((partner * FT + ft) * 64 + lane) * 4);
     }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qk[ks] = qr[qt][ks];
   };
   if (kh == 0) keep(std::integral_constant<int, 0>{}); else keep(std::integral_constant<int, 1>{});
-  __syncthreads();  // the exchange area becomes the output stage
 
-  // ---- linear branch: phi(Q) for the wave's 32 queries, den = phi(Q).Z_i, num^T = H_i^T phi(Q)^T
-  float zf[KSTEPS * 8];
+  // ---- linear branch for the wave's 16 queries: phi(Q); den = phi(Q).Z_i and
+  // num^T = H_i^T phi(Q)^T on MFMA
+  float qf[KSTEPS * 8];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const uint32_t w4[4] = {qk[ks].x, qk[ks].y, qk[ks].z, qk[ks].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[ks * 8 + 2 * e] = bf_lo(w4[e]);
+      qf[ks * 8 + 2 * e + 1] = bf_hi(w4[e]);
+    }
+  }
+  float qm = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < KSTEPS * 8; ++e) qm = fmaxf(qm, qf[e]);
+  qm = group4_max(qm) * kLog2e;
+  // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
+  // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
+  uint4 fq[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    uint32_t w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w4[e] = pack_bf2(__builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e], kLog2e, -qm)),
+                       __builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e + 1], kLog2e, -qm)));
+    fq[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+  // den: an A operand whose row 0 is Z_i gives phi(Q).Z_i in row 0 of the product
+  f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     const uint4 z = *reinterpret_cast<const uint4*>(zbuf + 32 * ks + 8 * g);
-    const uint32_t zw[4] = {z.x, z.y, z.z, z.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      zf[ks * 8 + 2 * e] = bf_lo(zw[e]);
-      zf[ks * 8 + 2 * e + 1] = bf_hi(zw[e]);
-    }
+    dacc = mfma_bf16(l16 == 0 ? z : make_uint4(0u, 0u, 0u, 0u), fq[ks], dacc);
   }
-  uint4 fq[2][KSTEPS];
-  float inv_den[2];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float qf[KSTEPS * 8];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const uint32_t w4[4] = {qr[qt][ks].x, qr[qt][ks].y, qr[qt][ks].z, qr[qt][ks].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qf[ks * 8 + 2 * e] = bf_lo(w4[e]);
-        qf[ks * 8 + 2 * e + 1] = bf_hi(w4[e]);
-      }
-    }
-    float qm = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < KSTEPS * 8; ++e) qm = fmaxf(qm, qf[e]);
-    qm = group4_max(qm) * kLog2e;
-    // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
-    // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
-#pragma unroll
-    for (int e = 0; e < KSTEPS * 8; ++e) qf[e] = __builtin_amdgcn_exp2f(fmaf(qf[e], kLog2e, -qm));
-    float dp = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      uint32_t w4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w4[e] = pack_bf2(qf[ks * 8 + 2 * e], qf[ks * 8 + 2 * e + 1]);
-        dp += bf_lo(w4[e]) * zf[ks * 8 + 2 * e] + bf_hi(w4[e]) * zf[ks * 8 + 2 * e + 1];
-      }
-      fq[qt][ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-    }
-    const float den = group4_sum(dp);
-    inv_den[qt] = den > 0.f ? 1.0f / den : 0.f;
-  }
+  const float den = __shfl(dacc[0], l16);  // from lane group 0
+  const float inv_den = den > 0.f ? 1.0f / den : 0.f;
   const float al = alpha[h];
+  const float cs0 = al * inv_l * w0, cs1 = al * inv_l * w1, cl = (1.0f - al) * inv_den;
+  __syncthreads();  // every wave has read the exchange area: it becomes the output stage
   uint16_t* ost = xbuf;  // staged output tile [64][OS]
+  const int q = 32 * qh + 16 * kh + l16;
+  const int t = i * kBlock + q;
+  const bool dbg = (dbg_os || dbg_ol) && t < N;
 #pragma unroll
-  for (int f = 0; f < FTH; ++f) {
-    const int ft = FTH * kh + f;
-    f32x4 nm[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int ft = 0; ft < FT; ++ft) {
+    f32x4 nm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const int hr = 16 * ft + l16;
       const uint4 a = *reinterpret_cast<const uint4*>(hbuf + (hr * C + ((4 * ks + g) ^ (hr & (C - 1)))) * 8);
-      nm[0] = mfma_bf16(a, fq[0][ks], nm[0]);
-      nm[1] = mfma_bf16(a, fq[1][ks], nm[1]);
+      nm = mfma_bf16(a, fq[ks], nm);
     }
+    float o[4];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int q = 32 * qh + 16 * qt + l16;
-      float os[4], ol[4], o[4];
+    for (int r = 0; r < 4; ++r) o[r] = fmaf(own[ft][r], cs0, fmaf(oth[ft][r], cs1, nm[r] * cl));
+    *reinterpret_cast<uint2*>(ost + q * OS + 16 * ft + 4 * g) =
+        make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+    if (dbg) {
+      const size_t off = ((size_t)bh * N + t) * D + 16 * ft + 4 * g;
+      float os[4], ol[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        os[r] = ofin[f][qt][r] * inv_l[qt];
-        ol[r] = nm[qt][r] * inv_den[qt];
-        o[r] = al * os[r] + (1.0f - al) * ol[r];
+        os[r] = (own[ft][r] * w0 + oth[ft][r] * w1) * inv_l;
+        ol[r] = nm[r] * inv_den;
       }
-      *reinterpret_cast<uint2*>(ost + q * OS + 16 * ft + 4 * g) =
-          make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
-      const int t = i * kBlock + q;
-      if (t < N && (dbg_os || dbg_ol)) {
-        const size_t off = ((size_t)bh * N + t) * D + 16 * ft + 4 * g;
-        if (dbg_os) *reinterpret_cast<float4*>(dbg_os + off) = make_float4(os[0], os[1], os[2], os[3]);
-        if (dbg_ol) *reinterpret_cast<float4*>(dbg_ol + off) = make_float4(ol[0], ol[1], ol[2], ol[3]);
-      }
+      if (dbg_os) *reinterpret_cast<float4*>(dbg_os + off) = make_float4(os[0], os[1], os[2], os[3]);
+      if (dbg_ol) *reinterpret_cast<float4*>(dbg_ol + off) = make_float4(ol[0], ol[1], ol[2], ol[3]);
     }
   }
   __syncthreads();
