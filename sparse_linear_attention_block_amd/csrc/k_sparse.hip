@@ -183,13 +183,11 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   // buffer, S^T, online softmax against the wave's reference max, O^T += V^T P^T
   auto step = [&](int c, const uint16_t* cur, uint16_t* nxt) {
     const int j = __builtin_amdgcn_readfirstlane((int)list[c]);
+    const int jn = list[min(c + 1, ncrit - 1)];  // read before the K fragments queue behind it
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of tile c have landed
     lds_barrier();  // all copies of tile c are in LDS; every wave is done with tile c-1
-    if (c + 1 < ncrit)
-      issue(list[c + 1], nxt);
-    else
-      issueH(nxt);  // every wave has read list[c]: the list area is free
-    // all K fragments of the tile first (their LDS latency overlaps), then the products
+    // all K fragments of the tile first (their LDS latency overlaps the issue of
+    // the next tile's copies), then the products
     uint4 ka[KSTEPS][2];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
@@ -198,6 +196,11 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
         const int row = 32 * kh + 16 * kt + l16;
         ka[ks][kt] = *reinterpret_cast<const uint4*>(cur + (row * C + ((4 * ks + g) ^ (row & (C - 1)))) * 8);
       }
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < ncrit)
+      issue(jn, nxt);
+    else
+      issueH(nxt);  // every wave has read list[c]: the list area is free
     __builtin_amdgcn_sched_barrier(0);
     f32x4 s[2][2];  // [key tile][query tile]
 #pragma unroll
