@@ -11,8 +11,9 @@ FLOPS = O(full attention)/t, SLA paper summary, section 5 "Efficiency"),
 ms per step, a roofline entry for the dominant kernel (block-sparse attention,
 timed on every step of the timed region with HIP events recorded around it on
 the stream it runs on), a per-stage breakdown from a separate pass with every
-kernel bracketed, and the float64 CPU oracle timed on a bounded sample of the
-same workload.
+kernel bracketed, per-step median/p10/p90 with and without a cache flush
+between steps (a further pass, outside the timed region), and the float64 CPU
+oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 3] [--no-cpu]
 """
@@ -153,6 +154,36 @@ def cpu_baseline(cfg, x, seconds):
             "seconds": dt}
 
 
+def step_distribution(torch, plan, hev, steps, flush_mib):
+    """Per-step times after the timed region: each step bracketed by two
+    fence-free HIP events on its stream. The unflushed steps run back to back;
+    the flushed ones each follow a write of flush_mib MiB (outside the events),
+    which evicts the L2 and the MALL. Reported as median, p10 and p90 in ms."""
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run(flush):
+        evs = hev.create(2 * steps)
+        for s in range(steps):
+            if flush is not None:
+                flush.fill_(s & 0xFF)
+            hev.record(evs[2 * s], stream)
+            plan.run()
+            hev.record(evs[2 * s + 1], stream)
+        torch.cuda.synchronize()
+        t = np.array([hev.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for s in range(steps)])
+        hev.destroy(evs)
+        return [round(float(np.percentile(t, q)), 5) for q in (50, 10, 90)]
+
+    out = {"steps": steps}
+    out["median"], out["p10"], out["p90"] = run(None)
+    if flush_mib > 0:
+        buf = torch.empty(flush_mib * 2 ** 20, dtype=torch.uint8, device="cuda")
+        out["flush_mib"] = flush_mib
+        out["flushed_median"], out["flushed_p10"], out["flushed_p90"] = run(buf)
+        del buf
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +192,8 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="MiB written between the flushed per-step timings (0: no flushed pass)")
     ap.add_argument("--hbm-calib-mib", type=int, default=0,
                     help="before the warm-up, copy a buffer of this many MiB three times "
                          "(a plain copy kernel of known size, to scale HBM counters)")
@@ -227,6 +260,7 @@ def main():
                   for i, name in enumerate(KERNELS)}
     for e in bevs:
         hev.destroy(e)
+    dist = step_distribution(torch, plan, hev, min(args.steps, 50), args.flush_mib)
 
     F = dense_flops(B, H, N, d)
     value = F / (ms * 1e-3) / 1e12
@@ -261,6 +295,7 @@ def main():
         "roofline": {"kernel": "sparse_attn_mix", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "flops_per_launch": k5_flops, "ms_per_launch": round(k5_ms, 5)},
+        "step_distribution": dist,
         "kernels_ms": {n: round(t, 5) for n, t in per_kernel.items()},
         "kernels_hbm_gbs": {n: round(t, 1) for n, t in gbs.items()},
     }

@@ -236,6 +236,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -245,6 +246,11 @@ class HipEvents:
                 raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(e.value)
         return out
+
+    def record(self, ev, stream) -> None:
+        """Records raw event ev on the raw hipStream_t stream (an int or None)."""
+        if self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
