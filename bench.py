@@ -66,9 +66,9 @@ def pages_flop_fraction(kh, N, d):
 
 def kernel_bytes(B, H, N, d, Nb, n_h, quant=False):
     """Compulsory HBM bytes of each bf16 kernel per launch (each tensor once).
-    With the 8-bit sparse branch the h/z stage also reads K once more and
-    writes int8 K, its key bias and fp8 V^T in place of bf16 V^T, and the
-    sparse kernel reads those 8-bit tiles."""
+    With the 8-bit sparse branch the h/z stage also writes int8 K and its key
+    bias (from the K rows it reads anyway) and fp8 V^T in place of bf16 V^T,
+    and the sparse kernel reads those 8-bit tiles."""
     X = 2.0 * B * H * N * d
     BH = B * H
     NN = d * d + d
@@ -82,7 +82,7 @@ def kernel_bytes(B, H, N, d, Nb, n_h, quant=False):
         return {
             "pool_proj": 2 * X + 2 * 8.0 * BH * Nb * d,
             "score_select": 2 * 8.0 * BH * Nb * d + BH * Nb * Nb,
-            "hz": 2 * X + hx + X8 + X + X8 + kbias,
+            "hz": 2 * X + hx + X8 + X8 + kbias,
             "linear_sum": hx + Hx + BH * Nb * Nb,
             "sparse_attn_mix": X + X8 + kbias + X8 + Hx + X,
         }

@@ -25,6 +25,12 @@
 //     a [d][32] block, keys permuted into that kernel's MFMA k-slot order and
 //     16-byte chunks swizzled against LDS bank conflicts.
 // Tokens past N and blocks past Nb are zero in LDS, so they add nothing.
+// 8-bit sparse branch: from the K rows already in registers the same pass forms
+// K - mean(K), its int8 codes with one absmax scale per block and the per-key
+// bias mean(Q).(K - mean(K)) (see k_quant.hip for the smoothing), and V^T in
+// e4m3 with one absmax scale per block; the block maxima and the bias sums
+// share the first phase's barriers, so the 8-bit outputs cost no extra pass
+// over K.
 //
 // f32 path: one workgroup per key block, plain FMA loops, hx[bh][j][c*d + r].
 #include "sla_internal.h"
@@ -46,18 +52,30 @@ struct HzCfg {
 constexpr int JB = 2;  // key blocks per workgroup: half of a group of 4
 
 template <int D>
+__device__ __forceinline__ float kBiasScale() {
+  return 1.4426950408889634f / (D == 128 ? 11.313708498984761f : 8.0f);
+}
+
+template <int D>
 __global__ __launch_bounds__(HzCfg<D>::NT, 2) void k_hz_bf16(const uint16_t* __restrict__ K,
                                                  const uint16_t* __restrict__ V,
                                                  uint16_t* __restrict__ hx,
                                                  uint16_t* __restrict__ vt, int N, int Nb,
                                                  int Nb4, uint8_t* __restrict__ v8t,
-                                                 float* __restrict__ vsc) {
+                                                 float* __restrict__ vsc,
+                                                 const float* __restrict__ qkmean,
+                                                 int8_t* __restrict__ k8, float* __restrict__ ksc,
+                                                 float* __restrict__ kb, int BH) {
   using C = HzCfg<D>;
   constexpr int TS = C::TS, CPT = C::CPT, NN = C::NN, NT = C::NT, NW = C::NW, NCG = C::NCG;
   __shared__ __attribute__((aligned(16))) uint16_t kT[JB][D][TS];
   __shared__ __attribute__((aligned(16))) uint16_t vT[JB][D][TS];
   __shared__ float red[NCG][64];
   __shared__ float tstat[64];
+  // 8-bit sparse branch only: the wave maxima of |K - mean(K)| and of |V|
+  __shared__ float kam[NW];
+  __shared__ float vmax[JB][NW];
+  const bool quant = v8t != nullptr;  // uniform
 
   const int tid = threadIdx.x;
   // workgroups remapped so that the two halves of a group of 4 key blocks run
@@ -111,19 +129,106 @@ __global__ __launch_bounds__(HzCfg<D>::NT, 2) void k_hz_bf16(const uint16_t* __r
           x[u][q * 8 + 2 * e + 1] = bf_hi(w[e]);
         }
       }
+    // row maxima: lanes l and l + 32 of a wave hold the same two tokens (chunk
+    // groups 2w, 2w + 1), so one exchange leaves one partial per wave in red[w]
+    const int wv = tid >> 6;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float m = -INFINITY;
 #pragma unroll
       for (int e = 0; e < CPT * 8; ++e) m = fmaxf(m, x[u][e]);
-      red[cg][2 * tp + u] = m;
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if ((tid & 32) == 0) red[wv][2 * tp + u] = m;
+    }
+    const int j = 4 * jq + JB * half + jj;
+    // 8-bit sparse branch: K - mean(K) of the thread's two tokens, their bias
+    // partials mean(Q).(k - mean(K)) over its features, and |K - mean(K)|, |V|
+    // maxima (the block absmax scales), all at the barrier that follows
+    float ks[2][CPT * 8];
+    if (quant) {
+      const float* qm = qkmean + (size_t)bh * D;
+      const float* km = qkmean + ((size_t)BH + bh) * D;
+      float bsum[2] = {0.f, 0.f};
+      float am = 0.f, av = 0.f;
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int f0 = (cg * CPT + q) * 8;
+        const float4 k0 = *reinterpret_cast<const float4*>(km + f0);
+        const float4 k1 = *reinterpret_cast<const float4*>(km + f0 + 4);
+        const float4 q0 = *reinterpret_cast<const float4*>(qm + f0);
+        const float4 q1 = *reinterpret_cast<const float4*>(qm + f0 + 4);
+        const float kmv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        const float qmv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t vw[4] = {vr[cs][u][q].x, vr[cs][u][q].y, vr[cs][u][q].z, vr[cs][u][q].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float kx = valid[cs][u] ? x[u][q * 8 + e] - kmv[e] : 0.f;
+            ks[u][q * 8 + e] = kx;
+            bsum[u] = fmaf(qmv[e], kx, bsum[u]);
+            am = fmaxf(am, fabsf(kx));
+            av = fmaxf(av, fabsf((e & 1) ? bf_hi(vw[e >> 1]) : bf_lo(vw[e >> 1])));
+          }
+        }
+      }
+      // bias partials, one per wave after the same exchange, in red[NW + w]
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float b = bsum[u] + __shfl_xor(bsum[u], 32);
+        if ((tid & 32) == 0) red[NW + wv][2 * tp + u] = b;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        am = fmaxf(am, __shfl_xor(am, o));
+        av = fmaxf(av, __shfl_xor(av, o));
+      }
+      if ((tid & 63) == 0) {
+        kam[tid >> 6] = am;
+        vmax[jj][tid >> 6] = av;
+      }
     }
     __syncthreads();
     if (tid < 64) {
       float m = red[0][tid];
 #pragma unroll
-      for (int g = 1; g < NCG; ++g) m = fmaxf(m, red[g][tid]);
+      for (int g = 1; g < NW; ++g) m = fmaxf(m, red[g][tid]);
       tstat[tid] = m;
+      if (quant && j < Nb) {
+        // the key bias, stored in the sparse kernel's log2 score units; 0 past N
+        float b = 0.f;
+#pragma unroll
+        for (int g = 0; g < NW; ++g) b += red[NW + g][tid];
+        kb[((size_t)bh * Nb + j) * kBlock + tid] = j * kBlock + tid < N ? b * kBiasScale<D>() : 0.f;
+      }
+    }
+    if (quant && j < Nb) {
+      // int8 codes of K - mean(K) with the block's absmax scale (absmax / 127; 1
+      // for an all-zero block), round-half-even, clamped to +-127; rows past N
+      // are zero. The bytes of a row go in the k-slot order of the sparse
+      // kernel's int8 16x16x64 product: chunk ch = qt + 4m (features 8ch .. +7)
+      // at 64 (m / 2) + 16 qt + 8 (m % 2).
+      float amk = kam[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) amk = fmaxf(amk, kam[w]);
+      const float inv = amk > 0.f ? 127.0f / amk : 1.0f;
+      if (tid == 0) ksc[(size_t)bh * Nb + j] = amk > 0.f ? amk / 127.0f : 1.0f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        int8_t* dst = k8 + (((size_t)bh * Nb + j) * kBlock + 2 * tp + u) * D;
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+          const int ch = cg * CPT + q, qt = ch & 3, m = ch >> 2;
+          uint32_t o[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float* v4 = &ks[u][q * 8 + 4 * hh];
+            o[hh] = (uint32_t)(q_i8(v4[0], inv) & 0xff) | ((uint32_t)(q_i8(v4[1], inv) & 0xff) << 8) |
+                    ((uint32_t)(q_i8(v4[2], inv) & 0xff) << 16) | ((uint32_t)(q_i8(v4[3], inv) & 0xff) << 24);
+          }
+          *reinterpret_cast<uint2*>(dst + 64 * (m >> 1) + 16 * qt + 8 * (m & 1)) = make_uint2(o[0], o[1]);
+        }
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -250,24 +355,9 @@ __global__ __launch_bounds__(HzCfg<D>::NT, 2) void k_hz_bf16(const uint16_t* __r
   // order (kt, r), the k slots one lane group of the 8-bit sparse kernel's
   // 16x16x128 product takes from one tile, and sits at position
   // g ^ ((c >> 1) & 3) against LDS bank conflicts.
-  __shared__ float vmax[JB][NW];
+  // (the block absmax of |V| was reduced in the first phase)
   const int cq = tid >> 2, gq = tid & 3;  // rows cq, cq + NT/4, ... of chunk gq
   float am[JB];
-#pragma unroll
-  for (int jj = 0; jj < JB; ++jj) {
-    float m = 0.f;
-    for (int c = cq; c < D; c += NT / 4)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const uint2 w = *reinterpret_cast<const uint2*>(&vT[jj][c][16 * kt + 4 * gq]);
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf_lo(w.x)), fabsf(bf_hi(w.x))),
-                           fmaxf(fabsf(bf_lo(w.y)), fabsf(bf_hi(w.y)))));
-      }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if ((tid & 63) == 0) vmax[jj][tid >> 6] = m;
-  }
-  __syncthreads();
 #pragma unroll
   for (int jj = 0; jj < JB; ++jj) {
     am[jj] = vmax[jj][0];
@@ -349,12 +439,12 @@ hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w,
     dim3 grid(D.Nbp / 4 * 2 * D.BH);
     if (D.d == 128)
       hipLaunchKernelGGL(k_hz_bf16<128>, grid, dim3(HzCfg<128>::NT), 0, s, (const uint16_t*)K,
-                         (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4, w.v8t,
-                         w.vs);
+                         (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4,
+                         D.quant ? w.v8t : nullptr, w.vs, w.qkmean, w.k8, w.ks, w.kb, D.BH);
     else
       hipLaunchKernelGGL(k_hz_bf16<64>, grid, dim3(HzCfg<64>::NT), 0, s, (const uint16_t*)K,
-                         (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4, w.v8t,
-                         w.vs);
+                         (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4,
+                         D.quant ? w.v8t : nullptr, w.vs, w.qkmean, w.k8, w.ks, w.kb, D.BH);
   } else {
     dim3 grid(D.Nb, D.BH);
     const size_t lds = 2 * kBlock * D.d * sizeof(float);

@@ -216,8 +216,8 @@ int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const 
     SLA_LAUNCH(mark(1), "event record");
     SLA_LAUNCH(mark(2), "event record");
   }
+  if (D.quant) SLA_LAUNCH(sla::launch_qk_mean(D, w, s), "channel-mean kernel");
   SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
-  if (D.quant) SLA_LAUNCH(sla::launch_quant_k(D, K, w, s), "K quantisation kernel");
   SLA_LAUNCH(mark(3), "event record");
   if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
   SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");

@@ -52,7 +52,7 @@ hipError_t launch_pool_sum(const Dims& D, const void* Q, const void* K, double* 
 hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const float* proj_q,
                             const float* proj_k, int proj_hs, double* raw, double* pq, double* pk,
                             hipStream_t s);
-hipError_t launch_quant_k(const Dims& D, const void* K, const Work& w, hipStream_t s);
+hipError_t launch_qk_mean(const Dims& D, const Work& w, hipStream_t s);
 hipError_t launch_sparse_q8(const Dims& D, const void* Q, const int8_t* mask, const float* alpha,
                             const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
 hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8_t* mask,
