@@ -12,33 +12,33 @@
 //
 // bf16 path. The critical list of the row is compacted from the mask into LDS
 // with wave ballots (the lookup table of the SLA explainer, section 2.3, built
-// on chip per query block). One workgroup of 4 waves owns a query block; the
-// waves split the 64 keys of a tile into two halves and the 64 queries into
-// two halves. Tiles arrive by direct global->LDS copies (no register
-// staging), double-buffered one tile ahead, one barrier per tile. Per tile:
-//   S^T = K Q^T    MFMA 16x16x32, the wave's 32 keys as A (row-swizzled LDS),
-//                  its 32 queries (registers) as B; a lane gets 4 keys of one
-//                  query per 16-key tile;
-//   online softmax per wave against a reference max that is only raised
-//                  when some score exceeds it by more than 2^8: the common
-//                  path needs no cross-lane reduction and no rescale (exact:
-//                  softmax does not depend on the reference); the row sums
-//                  of P come from one more MFMA per query tile with an A
-//                  operand whose row 0 is all ones;
+// on chip per query block). One workgroup of 4 waves owns a query block; wave
+// w owns queries 16w .. 16w+15 against every key, so its online softmax needs
+// no partner. The keys of a critical tile are taken 32 at a time (a step):
+// the K rows and V^T columns of a step arrive by direct global->LDS copies (no
+// register staging) into one of two 16 KB buffers, one step ahead, one barrier
+// per step, and three workgroups fit on a CU. Per step:
+//   S^T = K Q^T    MFMA 16x16x32, the step's 32 keys as A (row-swizzled LDS),
+//                  the wave's 16 queries (registers) as B; a lane gets 4 keys
+//                  of one query per 16-key tile;
+//   online softmax against a reference max that is only raised when some
+//                  score exceeds it by more than 2^8: the common path needs no
+//                  cross-lane reduction and no rescale (exact: softmax does
+//                  not depend on the reference); the row sums of P come from
+//                  one more MFMA with an A operand whose row 0 is all ones;
 //   O^T += V^T P^T MFMA 16x16x32 with P^T straight from registers: a lane's 8
 //                  k slots are its keys {4g..4g+3, 16+4g..16+4g+3}, and the h/z
 //                  kernel stored V^T in that key order.
-// All K fragments of a tile are read before its first product and the V^T
-// fragments right after the last one, so their LDS latency overlaps. While the
-// last tile is processed, H_i^T (from K4's output, rows swizzled like K) is
-// copied into the idle tile buffer and Z_i into the spent critical list.
-// The two key halves are combined through LDS (max-rescaled partial sums);
-// each wave then finishes all features of one 16-query tile (so phi is formed
-// once per query): O_s = acc / l, phi(Q) (softmax over the features in f32,
-// left unnormalised because the normalisation cancels in O_l, rounded to
-// bf16), num^T = H_i^T phi(Q)^T and den = phi(Q).Z_i on MFMA (Z_i as row 0 of
-// an A operand), O = alpha O_s + (1 - alpha) O_l, staged in LDS and written
-// as full rows.
+// All K fragments of a step are read before the next step's copies are issued
+// and before its first product, and the V^T fragments right after the last
+// one, so their LDS latency overlaps. During the last step the first half of
+// H_i^T (from K4's output, rows swizzled like K) is copied into the idle buffer
+// and Z_i into the spent critical list; the second half follows into the other
+// buffer while phi(Q) is formed. Each wave then finishes its 16 queries:
+// O_s = acc / l, phi(Q) (softmax over the features in f32, left unnormalised
+// because the normalisation cancels in O_l, rounded to bf16), num^T =
+// H_i^T phi(Q)^T and den = phi(Q).Z_i on MFMA (Z_i as row 0 of an A operand),
+// O = alpha O_s + (1 - alpha) O_l, staged in LDS and written as full rows.
 // Workgroups are remapped so that each XCD walks a contiguous range of
 // (batch, head, query block): neighbouring query blocks share most critical
 // key tiles, which then come from the XCD's L2.
@@ -57,70 +57,70 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int D>
 struct FaCfg {
   static constexpr int C = D / 8;                  // 16-byte chunks per K row
-  static constexpr int TILE = kBlock * D;          // elements of one K (or V^T) tile
-  static constexpr int INSTR = TILE / 8 / 256;     // 16-byte async copies per lane per operand
+  static constexpr int HT = 32 * D;                // elements of one half tile (32 keys) of K or of V^T
+  static constexpr int INSTR = HT / 8 / 256;       // 16-byte async copies per lane per operand and step
   static constexpr int NN = D * D + D;
   static constexpr int KSTEPS = D / 32;
   static constexpr int FT = D / 16;                // feature tiles of O
   static constexpr int OS = D + 8;                 // LDS row stride of the staged output
-  static constexpr int HINSTR = D * D / 8 / 256;   // 16-byte copies per lane of H_i^T
+  static constexpr int HROWS = 2 * HT / D;         // rows of H_i^T one step buffer holds (64)
+  static constexpr int HPARTS = D / HROWS;         // buffers H_i^T takes (2 at d = 128, 1 at d = 64)
+  static constexpr int HINSTR = HROWS * D / 8 / 256;  // 16-byte copies per lane of one part
 };
 
-// Workgroup: 4 waves, one query block (64 queries). Wave w takes key half
-// kh = w & 1 (keys 32kh .. 32kh+31 of every critical tile) and query half
-// qh = w >> 1 (queries 32qh .. 32qh+31), so every product is a full-rate
-// 16x16x32 MFMA (the P.V product contracts over the wave's 32 keys). Each wave
-// keeps its own reference maximum per query; the two key halves are combined
-// once at the end like the partial results of a split softmax.
+// Workgroup: 4 waves, one query block (64 queries). Wave w owns queries
+// 16w .. 16w+15 against every key, so its softmax needs no partner; the keys
+// of a critical tile are taken 32 at a time (a step), so that each product is a
+// full-rate 16x16x32 MFMA (P.V contracts over the step's 32 keys), the step
+// buffers are 16 KB and three workgroups fit on a CU.
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_sparse_bf16(
+__global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const int8_t* __restrict__ mask,
     const uint16_t* __restrict__ Hx, const float* __restrict__ alpha, uint16_t* __restrict__ O,
     float* __restrict__ dbg_os, float* __restrict__ dbg_ol, int H, int N, int Nb) {
   using Cf = FaCfg<D>;
-  constexpr int C = Cf::C, TILE = Cf::TILE, INSTR = Cf::INSTR, NN = Cf::NN;
-  constexpr int KSTEPS = Cf::KSTEPS, FT = Cf::FT, OS = Cf::OS, HINSTR = Cf::HINSTR;
-  constexpr float TAU = 8.0f;  // a stale reference max may lag the tile max by 2^8 at most
-  // Two tile buffers (K then V^T each) as distinct LDS objects, so that reads of
-  // one provably do not alias the asynchronous copies into the other.
-  __shared__ __attribute__((aligned(16))) uint16_t bufA[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t bufB[2 * TILE];
+  constexpr int C = Cf::C, HT = Cf::HT, INSTR = Cf::INSTR, NN = Cf::NN;
+  constexpr int KSTEPS = Cf::KSTEPS, FT = Cf::FT, OS = Cf::OS;
+  constexpr int HROWS = Cf::HROWS, HPARTS = Cf::HPARTS, HINSTR = Cf::HINSTR;
+  constexpr float TAU = 8.0f;  // a stale reference max may lag the step max by 2^8 at most
+  // Two step buffers (32 K rows, then the matching 32 columns of V^T) as
+  // distinct LDS objects, so that reads of one provably do not alias the
+  // asynchronous copies into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t bufA[2 * HT];
+  __shared__ __attribute__((aligned(16))) uint16_t bufB[2 * HT];
   __shared__ __attribute__((aligned(16))) uint16_t list[kMaxNb];  // critical list, then Z_i
-  __shared__ float xm[4][2][16];
-  __shared__ float xl[4][2][16];
   __shared__ int wsum[4 * kMaskPre];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS addresses
   const int l16 = lane & 15, g = lane >> 4;
-  const int kh = wave & 1, qh = wave >> 1;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / Nb, i = id - bh * Nb;
   const int h = bh % H;
 
-  // the mask row first, then the wave's 32 queries as MFMA B operands:
+  // the mask row first, then the wave's 16 queries as MFMA B operands:
   // Q[t][32ks + 8g .. +7] (they land while the critical list is compacted)
   const int8_t* mrow = mask + ((size_t)bh * Nb + i) * Nb;
   int8_t mv[kMaskPre];
   mask_load(mrow, Nb, mv);
-  uint4 qr[2][KSTEPS];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int t = min(i * kBlock + 32 * qh + 16 * qt + l16, N - 1);  // rows past N are never stored
+  uint4 qr[KSTEPS];
+  {
+    const int t = min(i * kBlock + 16 * wave + l16, N - 1);  // rows past N are never stored
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
-      qr[qt][ks] = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + t) * D + 32 * ks + 8 * g);
+      qr[ks] = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + t) * D + 32 * ks + 8 * g);
   }
 
   const int ncrit = compact_loaded(mv, mrow, Nb, (int8_t)1, list, wsum);
+  const int nstep = 2 * ncrit;  // step s: keys 32 (s & 1) .. +31 of critical tile s >> 1
 
   const uint16_t* Kb = K + (size_t)bh * N * D;
-  const uint16_t* Vb = vt + (size_t)bh * Nb * TILE;
+  const uint16_t* Vb = vt + (size_t)bh * Nb * 2 * HT;
   // K rows land in LDS with their 16-byte chunks XOR-swizzled by the row
   // index (16 lanes reading 16 rows at one column hit distinct banks); the
-  // V^T tile is copied as laid out by the h/z kernel. The per-lane source
-  // offsets within a tile are the same for every tile.
+  // V^T half tile is copied as laid out by the h/z kernel. The per-lane source
+  // offsets within a half tile are the same for every step.
   int koff[INSTR];
 #pragma unroll
   for (int u = 0; u < INSTR; ++u) {
@@ -128,91 +128,91 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
     const int r = G / C, sch = G % C;
     koff[u] = r * D + (sch ^ (r & (C - 1))) * 8;
   }
-  // Copies go through buffer resources over this head's K rows and V^T tiles:
-  // the per-lane byte offsets stay in registers and the tile offset j * TILE
-  // (wave-uniform) is the scalar offset, so issuing a tile costs no vector
-  // instruction.
+  // Copies go through buffer resources over this head's K rows and V^T half
+  // tiles: the per-lane byte offsets stay in registers and the step's offset
+  // (wave-uniform) is the scalar offset.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, N * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, Nb * TILE * 2);
-  auto issue = [&](int jv, uint16_t* dst) {
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, Nb * 2 * HT * 2);
+  auto issue = [&](int jv, int hv, uint16_t* dst) {
     const int j = __builtin_amdgcn_readfirstlane(jv);
-    const int soff = j * TILE * 2;
-    if ((j + 1) * kBlock > N) {  // ragged block: rows past N re-read row N-1 (masked below)
-      const int over = j * kBlock - (N - 1);
+    const int hh = __builtin_amdgcn_readfirstlane(hv);
+    const int row0 = j * kBlock + 32 * hh;
+    const int sk = row0 * D * 2, sv = (2 * j + hh) * HT * 2;
+    if (row0 + 32 > N) {  // ragged: rows past N re-read row N-1 (masked below)
+      const int over = row0 - (N - 1);
 #pragma unroll
       for (int u = 0; u < INSTR; ++u) {
         const int off = koff[u] - max(0, koff[u] / D + over) * D;
-        load_lds16_buf(krs, 2 * off, soff, dst + 512 * (4 * u + wave));
-        load_lds16_buf(vrs, (64 * (4 * u + wave) + lane) * 16, soff, dst + TILE + 512 * (4 * u + wave));
+        load_lds16_buf(krs, 2 * off, sk, dst + 512 * (4 * u + wave));
+        load_lds16_buf(vrs, (64 * (4 * u + wave) + lane) * 16, sv, dst + HT + 512 * (4 * u + wave));
       }
     } else {
 #pragma unroll
       for (int u = 0; u < INSTR; ++u) {
-        load_lds16_buf(krs, 2 * koff[u], soff, dst + 512 * (4 * u + wave));
-        load_lds16_buf(vrs, (64 * (4 * u + wave) + lane) * 16, soff, dst + TILE + 512 * (4 * u + wave));
+        load_lds16_buf(krs, 2 * koff[u], sk, dst + 512 * (4 * u + wave));
+        load_lds16_buf(vrs, (64 * (4 * u + wave) + lane) * 16, sv, dst + HT + 512 * (4 * u + wave));
       }
     }
   };
-  // H_i^T (d x d, rows swizzled like the K tiles) into a free tile buffer, and
-  // Z_i into the critical-list area, for the epilogue
+  // H_i^T (d x d, rows swizzled like the K rows) in parts of HROWS rows, one
+  // step buffer each, and Z_i into the critical-list area, for the epilogue
   const uint16_t* Hrow = Hx + ((size_t)bh * Nb + i) * NN;
   uint16_t* zbuf = list;
-  auto issueH = [&](uint16_t* dst) {
+  auto issueH = [&](int part, uint16_t* dst) {
 #pragma unroll
     for (int u = 0; u < HINSTR; ++u) {
       const int G = 64 * (4 * u + wave) + lane;
       const int r = G / C, sch = G % C;
-      load_lds16(Hrow + r * D + (sch ^ (r & (C - 1))) * 8, dst + 512 * (4 * u + wave));
+      load_lds16(Hrow + (part * HROWS + r) * D + (sch ^ (r & (C - 1))) * 8, dst + 512 * (4 * u + wave));
     }
-    if (wave == 0 && lane < C) load_lds16(Hrow + D * D + 8 * lane, zbuf);
+    if (part == 0 && wave == 0 && lane < C) load_lds16(Hrow + D * D + 8 * lane, zbuf);
   };
 
   const float sc = kLog2e / sqrtf((float)D);
-  f32x4 acc[FT][2];
+  f32x4 acc[FT];
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) acc[ft][0] = acc[ft][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mref[2] = {-INFINITY, -INFINITY};
+  for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mref = -INFINITY;
   // Row sums of P come out of the MFMA unit: an A operand whose row 0 is all
   // ones gives sum_k P[k][q] in row 0 of the product (lane group 0, register 0)
   // and is rescaled together with acc.
-  f32x4 accl[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 accl = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint32_t one2 = l16 == 0 ? 0x3f803f80u : 0u;  // two bf16 ones in row 0
   const uint4 ones = make_uint4(one2, one2, one2, one2);
 
-  // one tile: wait for it, start the copy of the next one into the other
-  // buffer, S^T, online softmax against the wave's reference max, O^T += V^T P^T
-  auto step = [&](int c, const uint16_t* cur, uint16_t* nxt) {
-    const int j = __builtin_amdgcn_readfirstlane((int)list[c]);
-    const int jn = list[min(c + 1, ncrit - 1)];  // read before the K fragments queue behind it
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of tile c have landed
-    lds_barrier();  // all copies of tile c are in LDS; every wave is done with tile c-1
-    // all K fragments of the tile first (their LDS latency overlaps the issue of
-    // the next tile's copies), then the products
+  // one step: wait for its half tile, start the copy of the next one into the
+  // other buffer, S^T, online softmax against the wave's reference max,
+  // O^T += V^T P^T
+  auto step = [&](int s, const uint16_t* cur, uint16_t* nxt) {
+    const int j = __builtin_amdgcn_readfirstlane((int)list[s >> 1]);
+    const int hh = s & 1;
+    const int jn = list[min((s + 1) >> 1, ncrit - 1)];  // read before the K fragments queue behind it
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of step s have landed
+    lds_barrier();  // all copies of step s are in LDS; every wave is done with step s-1
+    // all K fragments of the step first (their LDS latency overlaps the issue of
+    // the next step's copies), then the products
     uint4 ka[KSTEPS][2];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int row = 32 * kh + 16 * kt + l16;
+        const int row = 16 * kt + l16;
         ka[ks][kt] = *reinterpret_cast<const uint4*>(cur + (row * C + ((4 * ks + g) ^ (row & (C - 1)))) * 8);
       }
     __builtin_amdgcn_sched_barrier(0);
-    if (c + 1 < ncrit)
-      issue(jn, nxt);
+    if (s + 1 < nstep)
+      issue(jn, (s + 1) & 1, nxt);
     else
-      issueH(nxt);  // every wave has read list[c]: the list area is free
+      issueH(0, nxt);  // every wave has read list[s >> 1]: the list area is free
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 s[2][2];  // [key tile][query tile]
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) s[kt][0] = s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 sv[2];  // [key tile]
+    sv[0] = sv[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma_bf16(ka[ks][kt], qr[qt][ks], s[kt][qt]);
-    // the V^T fragments of the tile load while the softmax runs
-    const uint16_t* vtile = cur + TILE + kh * D * 32;
+      for (int kt = 0; kt < 2; ++kt) sv[kt] = mfma_bf16(ka[ks][kt], qr[ks], sv[kt]);
+    // the V^T fragments of the step load while the softmax runs
+    const uint16_t* vtile = cur + HT;
     uint4 va[FT];
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
@@ -220,129 +220,62 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
       va[ft] = *reinterpret_cast<const uint4*>(vtile + c * 32 + 8 * (g ^ ((c >> 1) & 3)));
     }
     __builtin_amdgcn_sched_barrier(0);
-    if ((j + 1) * kBlock > N) {  // ragged last block: keys past N take no part
-      const int kbase = j * kBlock + 32 * kh + 4 * g;
+    if (j * kBlock + 32 * hh + 32 > N) {  // ragged last block: keys past N take no part
+      const int kbase = j * kBlock + 32 * hh + 4 * g;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool out = kbase + 16 * kt + r >= N;
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) s[kt][qt][r] = out ? -INFINITY : s[kt][qt][r];
-        }
+        for (int r = 0; r < 4; ++r) sv[kt][r] = kbase + 16 * kt + r >= N ? -INFINITY : sv[kt][r];
     }
     // Reference max: raised only when some score exceeds it by more than 2^8
-    // (rare after the first tile); the 4 lane groups of a query then agree on
+    // (rare after the first step); the 4 lane groups of a query then agree on
     // the new value through a cross-group max, and acc / l are rescaled.
-    float lmax[2];
-    bool raise = false;
+    const float lmax = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                             fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3]))) * sc;
+    if (__ballot(lmax > mref + TAU)) {
+      const float tm = group4_max(lmax);
+      const float nref = tm > mref + TAU ? tm : mref;
+      const float fac = nref == mref ? 1.0f : __builtin_amdgcn_exp2f(mref - nref);
+      mref = nref;
+      accl *= fac;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      lmax[qt] = fmaxf(fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3])),
-                       fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3]))) * sc;
-      raise |= lmax[qt] > mref[qt] + TAU;
+      for (int ft = 0; ft < FT; ++ft) acc[ft] *= fac;
     }
-    if (__ballot(raise)) {
+    const float meff = mref == -INFINITY ? 0.0f : mref;  // no valid key yet: every p is 0
+    float p[2][4];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float tm = group4_max(lmax[qt]);
-        const float nref = tm > mref[qt] + TAU ? tm : mref[qt];
-        const float fac = nref == mref[qt] ? 1.0f : __builtin_amdgcn_exp2f(mref[qt] - nref);
-        mref[qt] = nref;
-        accl[qt] *= fac;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) acc[ft][qt] *= fac;
-      }
-    }
-    uint4 pb[2];
+      for (int r = 0; r < 4; ++r) p[kt][r] = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], sc, -meff));
+    const uint4 pb = make_uint4(pack_bf2(p[0][0], p[0][1]), pack_bf2(p[0][2], p[0][3]),
+                                pack_bf2(p[1][0], p[1][1]), pack_bf2(p[1][2], p[1][3]));
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float meff = mref[qt] == -INFINITY ? 0.0f : mref[qt];  // no valid key yet: every p is 0
-      float p[2][4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[kt][r] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][r], sc, -meff));
-      pb[qt] = make_uint4(pack_bf2(p[0][0], p[0][1]), pack_bf2(p[0][2], p[0][3]),
-                          pack_bf2(p[1][0], p[1][1]), pack_bf2(p[1][2], p[1][3]));
-    }
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      acc[ft][0] = mfma_bf16(va[ft], pb[0], acc[ft][0]);
-      acc[ft][1] = mfma_bf16(va[ft], pb[1], acc[ft][1]);
-    }
-    accl[0] = mfma_bf16(ones, pb[0], accl[0]);
-    accl[1] = mfma_bf16(ones, pb[1], accl[1]);
+    for (int ft = 0; ft < FT; ++ft) acc[ft] = mfma_bf16(va[ft], pb, acc[ft]);
+    accl = mfma_bf16(ones, pb, accl);
   };
-  if (ncrit > 0)
-    issue(list[0], bufA);
+  if (nstep > 0)
+    issue(list[0], 0, bufA);
   else
-    issueH(bufA);
-  for (int c = 0; c < ncrit; c += 2) {
-    step(c, bufA, bufB);
-    if (c + 1 < ncrit) step(c + 1, bufB, bufA);
+    issueH(0, bufA);
+  for (int s = 0; s < nstep; s += 2) {  // nstep is even
+    step(s, bufA, bufB);
+    step(s + 1, bufB, bufA);
   }
 
-  // ---- combine the two key halves: wave (kh, qh) finishes every feature of
-  // query tile kh of its query half, so each query's phi(Q) is formed once
-  float lw[2];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) lw[qt] = __shfl(accl[qt][0], l16);  // from lane group 0
-  // the last tile's buffer takes the exchange and then the staged output; H_i^T
-  // arrived in the other one (bufA when there was no tile)
-  uint16_t* xbuf = (ncrit & 1) ? bufA : bufB;
-  const uint16_t* hbuf = (ncrit & 1) ? bufB : bufA;
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of H_i^T and Z_i
-  __syncthreads();  // every wave is done with the tile buffers; H_i^T and Z_i have landed
-  float* ex = reinterpret_cast<float*>(xbuf);  // [wave][FT][64 lanes][4]
-  // The query tile is chosen with compile-time indices (a runtime index would
-  // send the accumulator array through scratch memory): wave kh sends its
-  // partial sums of query tile 1 - kh and keeps those of query tile kh.
-  auto send = [&](auto KH) {
-    constexpr int qs = 1 - decltype(KH)::value;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-      *reinterpret_cast<f32x4*>(ex + ((wave * FT + ft) * 64 + lane) * 4) = acc[ft][qs];
-  };
-  if (kh == 0) send(std::integral_constant<int, 0>{}); else send(std::integral_constant<int, 1>{});
-  if (g == 0) {
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      xm[wave][qt][l16] = mref[qt];
-      xl[wave][qt][l16] = lw[qt];
-    }
+  // ---- epilogue: O_s = acc / l; phi(Q) of the wave's 16 queries; den =
+  // phi(Q).Z_i and num^T = H_i^T phi(Q)^T on MFMA; the mix; full-row stores.
+  // H_i^T part 0 went into bufA during the last step (in the prologue when
+  // there was no step); part 1 (d = 128) follows into bufB.
+  const float lw = __shfl(accl[0], l16);  // from lane group 0
+  const float inv_l = lw > 0.f ? 1.0f / lw : 0.f;
+  if constexpr (HPARTS == 2) {
+    lds_barrier();  // every wave is done with bufB
+    issueH(1, bufB);
   }
-  __syncthreads();
-  // own (this wave's partial sums), oth (the partner's) and their max-rescale
-  // weights w0, w1; O_s = (w0 own + w1 oth) / l
-  const int partner = wave ^ 1;
-  f32x4 own[FT], oth[FT];
-  float w0, w1, inv_l;
-  uint4 qk[KSTEPS];  // the query tile's Q fragments
-  auto keep = [&](auto KH) {
-    constexpr int qt = decltype(KH)::value;
-    const float m0 = mref[qt], m1 = xm[partner][qt][l16];
-    const float M = fmaxf(m0, m1);
-    w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
-    w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-    const float l = w0 * lw[qt] + w1 * xl[partner][qt][l16];
-    inv_l = l > 0.f ? 1.0f / l : 0.f;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      own[ft] = acc[ft][qt];
-      oth[ft] = *reinterpret_cast<const f32x4*>(ex + ((partner * FT + ft) * 64 + lane) * 4);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qk[ks] = qr[qt][ks];
-  };
-  if (kh == 0) keep(std::integral_constant<int, 0>{}); else keep(std::integral_constant<int, 1>{});
-
-  // ---- linear branch for the wave's 16 queries: phi(Q); den = phi(Q).Z_i and
-  // num^T = H_i^T phi(Q)^T on MFMA
   float qf[KSTEPS * 8];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    const uint32_t w4[4] = {qk[ks].x, qk[ks].y, qk[ks].z, qk[ks].w};
+    const uint32_t w4[4] = {qr[ks].x, qr[ks].y, qr[ks].z, qr[ks].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       qf[ks * 8 + 2 * e] = bf_lo(w4[e]);
@@ -365,6 +298,12 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
                        __builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e + 1], kLog2e, -qm)));
     fq[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
   }
+  // part 0 of H_i^T and Z_i have landed (part 1's copies, issued after them, may not)
+  if constexpr (HPARTS == 2)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(HINSTR));
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  lds_barrier();
   // den: an A operand whose row 0 is Z_i gives phi(Q).Z_i in row 0 of the product
   f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -374,47 +313,63 @@ __global__ __launch_bounds__(256, 2) void k_sparse_bf16(
   }
   const float den = __shfl(dacc[0], l16);  // from lane group 0
   const float inv_den = den > 0.f ? 1.0f / den : 0.f;
+  f32x4 nm[FT];
+  auto numpart = [&](auto PART, const uint16_t* hb) {
+    constexpr int part = decltype(PART)::value;
+#pragma unroll
+    for (int f = 0; f < FT / HPARTS; ++f) {
+      const int ft = part * (FT / HPARTS) + f;
+      nm[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int hr = 16 * f + l16;  // row within the part
+        const uint4 a = *reinterpret_cast<const uint4*>(hb + (hr * C + ((4 * ks + g) ^ (hr & (C - 1)))) * 8);
+        nm[ft] = mfma_bf16(a, fq[ks], nm[ft]);
+      }
+    }
+  };
+  numpart(std::integral_constant<int, 0>{}, bufA);
+  if constexpr (HPARTS == 2) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    numpart(std::integral_constant<int, 1>{}, bufB);
+  }
   const float al = alpha[h];
-  const float cs0 = al * inv_l * w0, cs1 = al * inv_l * w1, cl = (1.0f - al) * inv_den;
-  __syncthreads();  // every wave has read the exchange area: it becomes the output stage
-  uint16_t* ost = xbuf;  // staged output tile [64][OS]
-  const int q = 32 * qh + 16 * kh + l16;
+  const float cs = al * inv_l, cl = (1.0f - al) * inv_den;
+  lds_barrier();  // every wave has read H_i^T: the buffers become the output stage
+  // wave w stages its 16 rows in buffer w / 2 and writes them back itself
+  uint16_t* ost = ((wave >> 1) ? bufB : bufA) + (wave & 1) * 16 * OS;
+  const int q = 16 * wave + l16;
   const int t = i * kBlock + q;
   const bool dbg = (dbg_os || dbg_ol) && t < N;
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
-    f32x4 nm = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int hr = 16 * ft + l16;
-      const uint4 a = *reinterpret_cast<const uint4*>(hbuf + (hr * C + ((4 * ks + g) ^ (hr & (C - 1)))) * 8);
-      nm = mfma_bf16(a, fq[ks], nm);
-    }
     float o[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = fmaf(own[ft][r], cs0, fmaf(oth[ft][r], cs1, nm[r] * cl));
-    *reinterpret_cast<uint2*>(ost + q * OS + 16 * ft + 4 * g) =
+    for (int r = 0; r < 4; ++r) o[r] = fmaf(acc[ft][r], cs, nm[ft][r] * cl);
+    *reinterpret_cast<uint2*>(ost + l16 * OS + 16 * ft + 4 * g) =
         make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
     if (dbg) {
       const size_t off = ((size_t)bh * N + t) * D + 16 * ft + 4 * g;
-      float os[4], ol[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        os[r] = (own[ft][r] * w0 + oth[ft][r] * w1) * inv_l;
-        ol[r] = nm[r] * inv_den;
-      }
-      if (dbg_os) *reinterpret_cast<float4*>(dbg_os + off) = make_float4(os[0], os[1], os[2], os[3]);
-      if (dbg_ol) *reinterpret_cast<float4*>(dbg_ol + off) = make_float4(ol[0], ol[1], ol[2], ol[3]);
+      if (dbg_os)
+        *reinterpret_cast<float4*>(dbg_os + off) =
+            make_float4(acc[ft][0] * inv_l, acc[ft][1] * inv_l, acc[ft][2] * inv_l, acc[ft][3] * inv_l);
+      if (dbg_ol)
+        *reinterpret_cast<float4*>(dbg_ol + off) =
+            make_float4(nm[ft][0] * inv_den, nm[ft][1] * inv_den, nm[ft][2] * inv_den, nm[ft][3] * inv_den);
     }
   }
-  __syncthreads();
-  // full-row 16-byte stores of the staged tile
-  const int nrow = min(kBlock, N - i * kBlock);
-  uint16_t* Ob = O + ((size_t)bh * N + (size_t)i * kBlock) * D;
-  for (int x = tid; x < nrow * C; x += 256) {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // a wave reads back only its own rows
+  // full-row 16-byte stores of the wave's staged rows
+  const int nrow = min(16, N - (i * kBlock + 16 * wave));
+  uint16_t* Ob = O + ((size_t)bh * N + (size_t)i * kBlock + 16 * wave) * D;
+#pragma unroll
+  for (int x0 = 0; x0 < 16 * C; x0 += 64) {
+    const int x = x0 + lane;
     const int row = x / C, ch = x % C;
-    *reinterpret_cast<uint4*>(Ob + (size_t)row * D + ch * 8) =
-        *reinterpret_cast<const uint4*>(ost + row * OS + ch * 8);
+    if (row < nrow)
+      *reinterpret_cast<uint4*>(Ob + (size_t)row * D + ch * 8) =
+          *reinterpret_cast<const uint4*>(ost + row * OS + ch * 8);
   }
 }
 
