@@ -27,6 +27,17 @@ section / equation on it):
 8. SLA2 mix O = alpha * O_s + (1 - alpha) * O_l (SLA2 article, the
    "learnable mixing ratio" paragraph).
 
+The SLA (v1) formulation differs in two places, both selectable here:
+* output fusion O = O_s + Proj(O_l) with a learned d x d linear map Proj
+  (SLA paper summary, section 4, step 4 and the final-output formula; SLA
+  explainer, section 2.1 on Eq. 6's projection), read as O_l @ proj_o with
+  proj_o indexed [in, out] like the router matrices, no bias;
+* the feature map phi(x) = elu(x) + 1, elementwise (SLA paper summary, the
+  symbols of Eq. 3 and Table 2's "SLA (elu+1)" row; SLA2 blog, section 4.2),
+  besides the softmax (SLA explainer, section 3.2).
+SLA (v1) has no learned router: its compressed map pools Q and K directly,
+which is proj_q = proj_k = None here (the identity).
+
 Readings where the pages are silent (all listed in the design notes):
 counts n_h = max(1, floor(kh*Nb + 1e-9)) when kh > 0, n_l = floor(kl*Nb + 1e-9);
 one total order per row, logit descending then block index ascending, critical
@@ -74,6 +85,15 @@ def phi(x: np.ndarray) -> np.ndarray:
     z = x - x.max(axis=-1, keepdims=True)
     e = np.exp(z)
     return e / e.sum(axis=-1, keepdims=True)
+
+
+def phi_elu1(x: np.ndarray) -> np.ndarray:
+    """Feature map ELU+1, elementwise: x + 1 where x > 0, exp(x) elsewhere
+    (ELU with unit scale, shifted by one so that every feature is positive)."""
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+FEATURE_MAPS = {"softmax": phi, "elu1": phi_elu1}
 
 
 def router_pool(X: np.ndarray, proj: np.ndarray) -> np.ndarray:
@@ -129,13 +149,15 @@ def sparse_branch(q: np.ndarray, K: np.ndarray, V: np.ndarray, crit: np.ndarray)
     return (P @ V) / P.sum(axis=1, keepdims=True)
 
 
-def linear_branch(q: np.ndarray, K: np.ndarray, V: np.ndarray, marg: np.ndarray) -> np.ndarray:
+def linear_branch(q: np.ndarray, K: np.ndarray, V: np.ndarray, marg: np.ndarray,
+                  feature: str = "softmax") -> np.ndarray:
     """Linear attention of the query rows over the marginal key tokens:
     A = phi(q) phi(K)^T kept on marginal entries, O_l = A V / rowsum(A).
-    Zero if no key is marginal."""
+    Zero if no key is marginal. feature: "softmax" or "elu1"."""
+    f = FEATURE_MAPS[feature]
     if not marg.any():
         return np.zeros((q.shape[0], V.shape[1]))
-    A = phi(q) @ phi(K).T
+    A = f(q) @ f(K).T
     A = np.where(marg[None, :], A, 0.0)
     return (A @ V) / A.sum(axis=1, keepdims=True)
 
@@ -148,6 +170,7 @@ class OracleResult:
     O: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)     # (b,h) -> [N,d] or rows
     O_s: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)
     O_l: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)
+    O_lp: Dict[Tuple[int, int], np.ndarray] = field(default_factory=dict)  # Proj(O_l), SLA fusion
     pooled_q: Optional[np.ndarray] = None   # [B, H, Nb, d]
     pooled_k: Optional[np.ndarray] = None
     logits: Optional[np.ndarray] = None     # [B, H, Nb, Nb]
@@ -165,13 +188,18 @@ def _f64(x) -> np.ndarray:
 def forward(Q, K, V, proj_q, proj_k, alpha, kh: float, kl: float,
             mask_in=None, query_blocks: Optional[Dict[Tuple[int, int], Iterable[int]]] = None,
             heads: Optional[Iterable[Tuple[int, int]]] = None,
-            compute_outputs: bool = True) -> OracleResult:
-    """SLA2 forward pass in float64.
+            compute_outputs: bool = True, feature: str = "softmax",
+            proj_o=None) -> OracleResult:
+    """SLA2 (or, with proj_o, SLA) forward pass in float64.
 
     Q, K, V: [B, H, N, d] (numpy or torch, any float dtype; upcast exactly).
-    proj_q, proj_k: [d, d] shared by all heads, or [H, d, d].
-    alpha: [H].  mask_in: optional [B, H, Nb, Nb] block mask in {1, 0, -1}
-    that replaces steps 2-4.
+    proj_q, proj_k: [d, d] shared by all heads, or [H, d, d]; both None for
+    no router projection (the block means of Q and K themselves).
+    alpha: [H] (SLA2 mix; ignored with proj_o).  mask_in: optional
+    [B, H, Nb, Nb] block mask in {1, 0, -1} that replaces steps 2-4.
+    feature: the linear branch's feature map, "softmax" or "elu1".
+    proj_o: None for the SLA2 mix, else the SLA output map ([d, d] or
+    [H, d, d], indexed [in, out]): O = O_s + O_l @ proj_o.
     heads: the (b, h) pairs to process (default all).
     query_blocks: optional per-(b, h) subset of query blocks for which O is
     produced (the mask is always formed for every row of a processed head).
@@ -181,10 +209,15 @@ def forward(Q, K, V, proj_q, proj_k, alpha, kh: float, kl: float,
     Q = _f64(Q)
     K = _f64(K)
     V = _f64(V)
-    pq = _f64(proj_q)
-    pk = _f64(proj_k)
-    al = _f64(alpha).reshape(-1)
     B, H, N, d = Q.shape
+    if (proj_q is None) != (proj_k is None):
+        raise ValueError("proj_q and proj_k are both given or both None")
+    pq = np.eye(d) if proj_q is None else _f64(proj_q)
+    pk = np.eye(d) if proj_k is None else _f64(proj_k)
+    if feature not in FEATURE_MAPS:
+        raise ValueError("unknown feature map %r" % (feature,))
+    po = None if proj_o is None else _f64(proj_o)
+    al = None if po is not None else _f64(alpha).reshape(-1)
     Nb = num_blocks(N)
     n_h, n_l = block_counts(Nb, kh, kl)
     res = OracleResult(n_h, n_l, np.zeros((B, H, Nb, Nb), dtype=np.int8))
@@ -216,12 +249,17 @@ def forward(Q, K, V, proj_q, proj_k, alpha, kh: float, kl: float,
             t0, t1 = i * BLOCK, min((i + 1) * BLOCK, N)
             q = Q[b, h, t0:t1]
             Os.append(sparse_branch(q, K[b, h], V[b, h], token_mask(m[i], 1, N)))
-            Ol.append(linear_branch(q, K[b, h], V[b, h], token_mask(m[i], 0, N)))
+            Ol.append(linear_branch(q, K[b, h], V[b, h], token_mask(m[i], 0, N), feature))
         Os = np.concatenate(Os, axis=0) if Os else np.zeros((0, d))
         Ol = np.concatenate(Ol, axis=0) if Ol else np.zeros((0, d))
         res.O_s[(b, h)] = Os
         res.O_l[(b, h)] = Ol
-        res.O[(b, h)] = al[h] * Os + (1.0 - al[h]) * Ol
+        if po is None:
+            res.O[(b, h)] = al[h] * Os + (1.0 - al[h]) * Ol
+        else:
+            poh = po[h] if po.ndim == 3 else po
+            res.O_lp[(b, h)] = Ol @ poh
+            res.O[(b, h)] = Os + res.O_lp[(b, h)]
     return res
 
 
