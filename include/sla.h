@@ -14,6 +14,11 @@
  * phi(K_j)^T V_j and rowsum(phi(K_j)^T) over marginal j (phi = softmax over
  * the features), negligible blocks are skipped, and
  * O = alpha_h * O_s + (1 - alpha_h) * O_l.
+ * The SLA formulation (SLA paper summary, section 4, step 4 and the
+ * final-output formula) fuses the branches as O = O_s + Proj(O_l) with a
+ * learned d x d linear map instead (sla1_forward), and the linear branch may
+ * use phi = ELU + 1 instead of the softmax (Eq. 3's symbol list and Table 2;
+ * sla_problem.phi, for either formulation).
  *
  * Conventions shared by every entry point:
  *  - Q, K, V, O are [B, H, N, d] contiguous, row-major, 16-byte aligned
@@ -68,13 +73,20 @@ typedef enum {
   SLA_QUANT_I8QK_F8PV = 1
 } sla_quant;
 
+/* Feature map phi of the linear branch, applied to every query and key token
+ * of the un-projected Q and K. */
+typedef enum {
+  SLA_PHI_SOFTMAX = 0,  /* softmax over the d features of the token             */
+  SLA_PHI_ELU1 = 1      /* elementwise elu(x) + 1: x + 1 for x > 0, exp(x) else */
+} sla_phi;
+
 typedef struct {
   int32_t B, H, N, d;         /* d in {64, 128}                                  */
   int32_t dtype;              /* sla_dtype of Q, K, V, O                         */
   int32_t quant;              /* sla_quant                                       */
-  int32_t proj_head_stride;   /* 0: proj_q/proj_k are one [d, d] matrix for all  */
-                              /* heads; d*d: they are [H, d, d]                  */
-  int32_t reserved;           /* must be 0                                       */
+  int32_t proj_head_stride;   /* 0: proj_q/proj_k (and proj_o) are one [d, d]    */
+                              /* matrix for all heads; d*d: they are [H, d, d]   */
+  int32_t phi;                /* sla_phi                                         */
   double  kh, kl;             /* critical / negligible fractions in [0, 1]       */
 } sla_problem;
 
@@ -113,7 +125,9 @@ int sla_workspace_bytes(const sla_problem* p, size_t* bytes);
 /* The SLA2 forward pass.
  *  Q, K, V   device, dtype, [B, H, N, d].
  *  proj_q,   device float32 router matrices indexed [in, out], one [d, d] or
- *  proj_k    [H, d, d] (see proj_head_stride); may be NULL when mask_in is given.
+ *  proj_k    [H, d, d] (see proj_head_stride). Both NULL: no router projection,
+ *            the compressed map pools Q and K themselves (as SLA does); one
+ *            NULL and the other not is SLA_ERR_ARG.
  *  alpha     device float32 [H], the per-head mixing ratio.
  *  mask_in   NULL, or a device int8 [B, H, Nb, Nb] block mask with values in
  *            {1, 0, -1} that replaces the router, pooling and classification;
@@ -143,6 +157,32 @@ int sla_forward_debug(const sla_problem* p,
                       void* O, int8_t* mask_out,
                       void* workspace, size_t workspace_bytes,
                       void* stream, const sla_debug* dbg);
+
+/* The SLA forward pass: as sla_forward, but the branches are fused as
+ * O = O_s + Proj(O_l), Proj(x) = x proj_o (SLA paper summary, section 4,
+ * step 4; SLA explainer, section 2.1 on the projection of its Eq. 6).
+ *  proj_o    device float32, indexed [in, out], one [d, d] or [H, d, d] (see
+ *            proj_head_stride); required. No bias term.
+ * Every other argument is as for sla_forward; there is no alpha. Requires
+ * quant == SLA_QUANT_NONE (SLA_ERR_UNSUPPORTED otherwise). The workspace size
+ * is sla_workspace_bytes(p), as for sla_forward. */
+int sla1_forward(const sla_problem* p,
+                 const void* Q, const void* K, const void* V,
+                 const float* proj_q, const float* proj_k, const float* proj_o,
+                 const int8_t* mask_in,
+                 void* O, int8_t* mask_out,
+                 void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* sla1_forward plus the debug outputs of `dbg` (which may be NULL); o_l then
+ * receives Proj(O_l), the linear branch's term of the sum. */
+int sla1_forward_debug(const sla_problem* p,
+                       const void* Q, const void* K, const void* V,
+                       const float* proj_q, const float* proj_k, const float* proj_o,
+                       const int8_t* mask_in,
+                       void* O, int8_t* mask_out,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream, const sla_debug* dbg);
 
 /* Static text of a status code. */
 const char* sla_status_str(int status);

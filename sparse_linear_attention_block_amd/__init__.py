@@ -4,14 +4,15 @@ Five hand-written HIP kernels behind the C ABI of include/sla.h:
 router projection + block mean pooling, compressed scores + three-way block
 classification, per-key-block linear state h_j / z_j, the marginal-block
 sums (one MFMA product per head), and block-sparse online-softmax attention
-over the critical blocks with the linear-branch output and the SLA2 mix
-fused into its epilogue. This package is the argument-marshalling binding.
+over the critical blocks with the linear-branch output and the SLA2 mix (or
+the SLA output fusion O = O_s + Proj(O_l)) fused into its epilogue. This
+package is the argument-marshalling binding.
 """
 
 from ._binding import (  # noqa: F401
-    LIB_PATH, HipEvents, Plan, SLAError, block_counts, forward, load_library, make_problem,
-    workspace_bytes,
+    LIB_PATH, HipEvents, Plan, SLAError, block_counts, forward, forward_sla1, load_library,
+    make_problem, workspace_bytes,
 )
 
-__all__ = ["forward", "Plan", "HipEvents", "block_counts", "workspace_bytes", "load_library",
+__all__ = ["forward", "forward_sla1", "Plan", "HipEvents", "block_counts", "workspace_bytes", "load_library",
            "make_problem", "SLAError", "LIB_PATH"]

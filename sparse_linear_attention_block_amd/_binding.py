@@ -16,12 +16,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
 SLA_OK, SLA_ERR_ARG, SLA_ERR_UNSUPPORTED, SLA_ERR_WORKSPACE, SLA_ERR_HIP = 0, -1, -2, -3, -4
 SLA_F32, SLA_BF16 = 0, 1
 SLA_QUANT_NONE, SLA_QUANT_I8QK_F8PV = 0, 1
+SLA_PHI_SOFTMAX, SLA_PHI_ELU1 = 0, 1
+_PHI = {"softmax": SLA_PHI_SOFTMAX, "elu1": SLA_PHI_ELU1}
 
 
 class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("quant", ctypes.c_int32),
-                ("proj_head_stride", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("proj_head_stride", ctypes.c_int32), ("phi", ctypes.c_int32),
                 ("kh", ctypes.c_double), ("kl", ctypes.c_double)]
 
 
@@ -61,6 +63,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sla_forward.restype = ctypes.c_int
     lib.sla_forward_debug.argtypes = _FWD_ARGS + [ctypes.POINTER(Debug)]
     lib.sla_forward_debug.restype = ctypes.c_int
+    # the SLA formulation: proj_o in alpha's place
+    lib.sla1_forward.argtypes = _FWD_ARGS
+    lib.sla1_forward.restype = ctypes.c_int
+    lib.sla1_forward_debug.argtypes = _FWD_ARGS + [ctypes.POINTER(Debug)]
+    lib.sla1_forward_debug.restype = ctypes.c_int
     lib.sla_status_str.argtypes = [ctypes.c_int]
     lib.sla_status_str.restype = ctypes.c_char_p
     lib.sla_last_error.argtypes = []
@@ -78,9 +85,11 @@ def _check(rc: int) -> None:
 
 
 def make_problem(B: int, H: int, N: int, d: int, dtype: str, kh: float, kl: float,
-                 quant: bool = False, proj_head_stride: int = 0) -> Problem:
+                 quant: bool = False, proj_head_stride: int = 0, phi: str = "softmax") -> Problem:
+    if phi not in _PHI:
+        raise ValueError(f"phi must be one of {sorted(_PHI)}")
     return Problem(B, H, N, d, SLA_BF16 if dtype in ("bf16", torch.bfloat16) else SLA_F32,
-                   SLA_QUANT_I8QK_F8PV if quant else SLA_QUANT_NONE, proj_head_stride, 0,
+                   SLA_QUANT_I8QK_F8PV if quant else SLA_QUANT_NONE, proj_head_stride, _PHI[phi],
                    float(kh), float(kl))
 
 
@@ -105,18 +114,8 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-            proj_q: Optional[torch.Tensor], proj_k: Optional[torch.Tensor], alpha: torch.Tensor,
-            kh: float, kl: float, mask_in: Optional[torch.Tensor] = None, *,
-            quant: bool = False, out: Optional[torch.Tensor] = None,
-            mask_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            debug: bool = False):
-    """SLA2 forward on the GPU: returns (O, mask) or (O, mask, debug dict).
-
-    q, k, v: [B, H, N, d] contiguous bf16 or float32 device tensors.
-    proj_q, proj_k: float32 [d, d] or [H, d, d] (may be None with mask_in).
-    alpha: float32 [H]. mask_in: optional int8 [B, H, Nb, Nb] in {1, 0, -1}.
-    """
+def _run(q, k, v, proj_q, proj_k, alpha, proj_o, kh, kl, mask_in, quant, out, mask_out,
+         workspace, debug, phi):
     lib = load_library()
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
@@ -131,20 +130,33 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     Nb = (N + 63) // 64
     dev = q.device
     hs = 0
+    if (proj_q is None) != (proj_k is None):
+        raise ValueError("proj_q and proj_k are both given or both None")
     if proj_q is not None:
-        if proj_q.dtype != torch.float32 or proj_k is None or proj_k.shape != proj_q.shape:
+        if proj_q.dtype != torch.float32 or proj_k.shape != proj_q.shape:
             raise ValueError("proj_q and proj_k must be float32 tensors of one shape")
         proj_q, proj_k = proj_q.contiguous(), proj_k.contiguous()
         hs = d * d if proj_q.dim() == 3 else 0
-    if alpha.dtype != torch.float32 or alpha.numel() != H:
-        raise ValueError("alpha must be float32 with H entries")
-    alpha = alpha.contiguous()
+    if proj_o is not None:
+        if proj_o.dtype != torch.float32 or proj_o.shape[-2:] != (d, d) or proj_o.dim() not in (2, 3):
+            raise ValueError("proj_o must be float32 [d, d] or [H, d, d]")
+        if proj_o.dim() == 3 and proj_o.shape[0] != H:
+            raise ValueError("a per-head proj_o must have H matrices")
+        ohs = d * d if proj_o.dim() == 3 else 0
+        if proj_q is not None and ohs != hs:
+            raise ValueError("proj_q, proj_k and proj_o share one head stride: all [d, d] or all [H, d, d]")
+        hs = ohs
+        proj_o = proj_o.contiguous()
+    else:
+        if alpha.dtype != torch.float32 or alpha.numel() != H:
+            raise ValueError("alpha must be float32 with H entries")
+        alpha = alpha.contiguous()
     if mask_in is not None:
         if mask_in.dtype != torch.int8 or tuple(mask_in.shape) != (B, H, Nb, Nb):
             raise ValueError("mask_in must be int8 [B, H, Nb, Nb]")
         mask_in = mask_in.contiguous()
     p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", kh, kl,
-                     quant, hs)
+                     quant, hs, phi)
     need = workspace_bytes(p)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -165,12 +177,12 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     with torch.cuda.device(dev):
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         args = [ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q), _ptr(proj_k),
-                _ptr(alpha), _ptr(mask_in), _ptr(out), _ptr(mask_out), _ptr(workspace),
-                ctypes.c_size_t(workspace.numel() * workspace.element_size()), stream]
-        if debug:
-            rc = lib.sla_forward_debug(*args, ctypes.byref(dbg))
+                _ptr(alpha if proj_o is None else proj_o), _ptr(mask_in), _ptr(out), _ptr(mask_out),
+                _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()), stream]
+        if proj_o is None:
+            rc = lib.sla_forward_debug(*args, ctypes.byref(dbg)) if debug else lib.sla_forward(*args)
         else:
-            rc = lib.sla_forward(*args)
+            rc = lib.sla1_forward_debug(*args, ctypes.byref(dbg)) if debug else lib.sla1_forward(*args)
     _check(rc)
     mask = mask_out if mask_out is not None else mask_in
     if debug:
@@ -178,30 +190,72 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, mask
 
 
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            proj_q: Optional[torch.Tensor], proj_k: Optional[torch.Tensor], alpha: torch.Tensor,
+            kh: float, kl: float, mask_in: Optional[torch.Tensor] = None, *,
+            quant: bool = False, out: Optional[torch.Tensor] = None,
+            mask_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            debug: bool = False, phi: str = "softmax"):
+    """SLA2 forward on the GPU (sla_forward): returns (O, mask) or (O, mask, debug dict).
+
+    q, k, v: [B, H, N, d] contiguous bf16 or float32 device tensors.
+    proj_q, proj_k: float32 [d, d] or [H, d, d], or both None (no router projection).
+    alpha: float32 [H]. mask_in: optional int8 [B, H, Nb, Nb] in {1, 0, -1}.
+    phi: the linear branch's feature map, "softmax" or "elu1".
+    """
+    return _run(q, k, v, proj_q, proj_k, alpha, None, kh, kl, mask_in, quant, out, mask_out,
+                workspace, debug, phi)
+
+
+def forward_sla1(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj_o: torch.Tensor,
+                 kh: float, kl: float, mask_in: Optional[torch.Tensor] = None, *,
+                 proj_q: Optional[torch.Tensor] = None, proj_k: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, mask_out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, debug: bool = False,
+                 phi: str = "softmax"):
+    """SLA forward on the GPU (sla1_forward): O = O_s + O_l proj_o.
+
+    proj_o: float32 [d, d] or [H, d, d], indexed [in, out]. The router matrices
+    are optional (None: the block means of Q and K are compared directly).
+    Returns (O, mask) or, with debug, (O, mask, debug dict) whose "o_l" is
+    Proj(O_l).
+    """
+    if proj_o is None:
+        raise ValueError("proj_o is required")
+    return _run(q, k, v, proj_q, proj_k, None, proj_o, kh, kl, mask_in, False, out, mask_out,
+                workspace, debug, phi)
+
+
 class Plan:
-    """A prepared sla_forward call: the problem, the device buffers and the
+    """A prepared sla_forward (or, with proj_o, sla1_forward) call: the problem, the device buffers and the
     ctypes argument list are built once, so repeated calls only enqueue work
     (used by the benchmark and by callers that run the same shape often)."""
 
-    def __init__(self, q, k, v, proj_q, proj_k, alpha, kh, kl, mask_in=None, quant=False):
+    def __init__(self, q, k, v, proj_q, proj_k, alpha, kh, kl, mask_in=None, quant=False,
+                 phi="softmax", proj_o=None):
         lib = load_library()
         B, H, N, d = q.shape
         Nb = (N + 63) // 64
         dev = q.device
-        hs = d * d if (proj_q is not None and proj_q.dim() == 3) else 0
+        hs = d * d if ((proj_q is not None and proj_q.dim() == 3) or
+                       (proj_o is not None and proj_o.dim() == 3)) else 0
         self.problem = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32",
-                                    kh, kl, quant, hs)
+                                    kh, kl, quant, hs, phi)
+        self.sla1 = proj_o is not None
         self.nbytes = workspace_bytes(self.problem)
         self.workspace = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=dev)
         self.out = torch.empty_like(q)
         self.mask = None if mask_in is not None else torch.empty((B, H, Nb, Nb), dtype=torch.int8,
                                                                  device=dev)
-        self._keep = (q, k, v, proj_q, proj_k, alpha, mask_in)
+        self._keep = (q, k, v, proj_q, proj_k, alpha, mask_in, proj_o)
         self.device = dev
         self.lib = lib
         self._args = [ctypes.byref(self.problem), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
-                      _ptr(proj_k), _ptr(alpha), _ptr(mask_in), _ptr(self.out), _ptr(self.mask),
-                      _ptr(self.workspace), ctypes.c_size_t(self.nbytes)]
+                      _ptr(proj_k), _ptr(proj_o if self.sla1 else alpha), _ptr(mask_in),
+                      _ptr(self.out), _ptr(self.mask), _ptr(self.workspace),
+                      ctypes.c_size_t(self.nbytes)]
+        self._fwd = lib.sla1_forward if self.sla1 else lib.sla_forward
+        self._fwd_debug = lib.sla1_forward_debug if self.sla1 else lib.sla_forward_debug
         self.dims = (B, H, N, d, Nb)
 
     def run(self, events=None):
@@ -209,10 +263,10 @@ class Plan:
         sequence of 6 raw hipEvent_t handles recorded around the five kernels."""
         stream = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
         if events is None:
-            rc = self.lib.sla_forward(*self._args, stream)
+            rc = self._fwd(*self._args, stream)
         else:
             dbg = Debug(None, None, None, None, None, (ctypes.c_void_p * 6)(*events))
-            rc = self.lib.sla_forward_debug(*self._args, stream, ctypes.byref(dbg))
+            rc = self._fwd_debug(*self._args, stream, ctypes.byref(dbg))
         _check(rc)
         return self.out
 

@@ -80,6 +80,12 @@ __device__ __forceinline__ float group4_sum(float v) {
   return v;
 }
 
+// Feature map elu(x) + 1 (elementwise): x + 1 above zero, exp(x) at or below
+// (the hardware base-2 exponential of x log2(e)).
+__device__ __forceinline__ float elu1(float x) {
+  return x > 0.f ? x + 1.0f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
 }  // namespace sla
 
 namespace sla {

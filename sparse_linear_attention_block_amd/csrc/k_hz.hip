@@ -4,7 +4,8 @@
 // h_j = phi(K_j)^T V_j (d x d) and z_j = rowsum(phi(K_j)^T) (d) are formed once
 // per key block so that a query block only has to add them up (SLA paper
 // summary, Eq. 3). phi is the softmax over the d features of each key token
-// (SLA explainer, section 3.2; SLA paper summary, Table 2).
+// (SLA explainer, section 3.2; SLA paper summary, Table 2), or elu + 1 taken
+// elementwise (Eq. 3's symbol list; Table 2's "SLA (elu+1)" row).
 //
 // bf16 path, one workgroup (8 waves for d = 128, 4 for d = 64) per 2
 // consecutive key blocks of one (batch, head), two workgroups per CU:
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(HzCfg<D>::NT, 2) void k_hz_bf16(const uint16_t* __r
                                                  float* __restrict__ vsc,
                                                  const float* __restrict__ qkmean,
                                                  int8_t* __restrict__ k8, float* __restrict__ ksc,
-                                                 float* __restrict__ kb, int BH) {
+                                                 float* __restrict__ kb, int BH, int elu) {
   using C = HzCfg<D>;
   constexpr int TS = C::TS, CPT = C::CPT, NN = C::NN, NT = C::NT, NW = C::NW, NCG = C::NCG;
   __shared__ __attribute__((aligned(16))) uint16_t kT[JB][D][TS];
@@ -235,10 +236,15 @@ __global__ __launch_bounds__(HzCfg<D>::NT, 2) void k_hz_bf16(const uint16_t* __r
     for (int u = 0; u < 2; ++u) {
       const float m = tstat[2 * tp + u];
       float s = 0.f;
+      if (elu) {  // uniform
 #pragma unroll
-      for (int e = 0; e < CPT * 8; ++e) {
-        x[u][e] = __expf(x[u][e] - m);
-        s += x[u][e];
+        for (int e = 0; e < CPT * 8; ++e) x[u][e] = elu1(x[u][e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPT * 8; ++e) {
+          x[u][e] = __expf(x[u][e] - m);
+          s += x[u][e];
+        }
       }
       red[cg][2 * tp + u] = s;
     }
@@ -250,8 +256,9 @@ __global__ __launch_bounds__(HzCfg<D>::NT, 2) void k_hz_bf16(const uint16_t* __r
       tstat[tid] = 1.0f / s;
     }
     __syncthreads();
-    const float inv0 = valid[cs][0] ? tstat[2 * tp] : 0.f;
-    const float inv1 = valid[cs][1] ? tstat[2 * tp + 1] : 0.f;
+    // the softmax is normalised per token; elu + 1 is not
+    const float inv0 = valid[cs][0] ? (elu ? 1.0f : tstat[2 * tp]) : 0.f;
+    const float inv1 = valid[cs][1] ? (elu ? 1.0f : tstat[2 * tp + 1]) : 0.f;
     // transposed stores: word (token 2tp, token 2tp+1) of each feature
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
@@ -387,7 +394,8 @@ __global__ __launch_bounds__(HzCfg<D>::NT, 2) void k_hz_bf16(const uint16_t* __r
 // ---------------------------------------------------------------- f32 path
 __global__ __launch_bounds__(256) void k_hz_f32(const float* __restrict__ K,
                                                 const float* __restrict__ V,
-                                                float* __restrict__ hx, int N, int d, int Nb) {
+                                                float* __restrict__ hx, int N, int d, int Nb,
+                                                int elu) {
   extern __shared__ float sm[];
   float* phk = sm;               // [64][d]
   float* vs = sm + kBlock * d;   // [64][d]
@@ -405,7 +413,9 @@ __global__ __launch_bounds__(256) void k_hz_f32(const float* __restrict__ K,
   __syncthreads();
   if (tid < kBlock) {
     float* row = phk + tid * d;
-    if (tid < nt) {
+    if (tid < nt && elu) {
+      for (int c = 0; c < d; ++c) row[c] = row[c] > 0.f ? row[c] + 1.0f : expf(row[c]);
+    } else if (tid < nt) {
       float m = -INFINITY;
       for (int c = 0; c < d; ++c) m = fmaxf(m, row[c]);
       float s = 0.f;
@@ -440,16 +450,16 @@ hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w,
     if (D.d == 128)
       hipLaunchKernelGGL(k_hz_bf16<128>, grid, dim3(HzCfg<128>::NT), 0, s, (const uint16_t*)K,
                          (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4,
-                         D.quant ? w.v8t : nullptr, w.vs, w.qkmean, w.k8, w.ks, w.kb, D.BH);
+                         D.quant ? w.v8t : nullptr, w.vs, w.qkmean, w.k8, w.ks, w.kb, D.BH, D.elu ? 1 : 0);
     else
       hipLaunchKernelGGL(k_hz_bf16<64>, grid, dim3(HzCfg<64>::NT), 0, s, (const uint16_t*)K,
                          (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4,
-                         D.quant ? w.v8t : nullptr, w.vs, w.qkmean, w.k8, w.ks, w.kb, D.BH);
+                         D.quant ? w.v8t : nullptr, w.vs, w.qkmean, w.k8, w.ks, w.kb, D.BH, D.elu ? 1 : 0);
   } else {
     dim3 grid(D.Nb, D.BH);
     const size_t lds = 2 * kBlock * D.d * sizeof(float);
     hipLaunchKernelGGL(k_hz_f32, grid, dim3(256), lds, s, (const float*)K, (const float*)V,
-                       (float*)w.hx, D.N, D.d, D.Nb);
+                       (float*)w.hx, D.N, D.d, D.Nb, D.elu ? 1 : 0);
   }
   return hipGetLastError();
 }

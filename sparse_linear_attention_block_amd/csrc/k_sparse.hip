@@ -39,6 +39,14 @@
 // because the normalisation cancels in O_l, rounded to bf16), num^T =
 // H_i^T phi(Q)^T and den = phi(Q).Z_i on MFMA (Z_i as row 0 of an A operand),
 // O = alpha O_s + (1 - alpha) O_l, staged in LDS and written as full rows.
+// The SLA fusion O = O_s + Proj(O_l) (SLA paper summary, section 4, step 4)
+// is a second epilogue product: num^T, rounded to bf16, is already in the k-slot
+// order of a B operand (each lane holds features {4g..4g+3, 16+4g..16+4g+3} of
+// every 32-feature step), and Proj^T comes as A-operand fragments packed once
+// per call in that same feature order (k_pack_proj), read straight from L2;
+// (num Proj)^T has num^T's layout, so the mix and the stores are unchanged.
+// With phi = elu + 1 (SLA paper summary, Eq. 3's symbol list) phi(Q) is taken
+// elementwise instead of the softmax over the features.
 // Workgroups are remapped so that each XCD walks a contiguous range of
 // (batch, head, query block): neighbouring query blocks share most critical
 // key tiles, which then come from the XCD's L2.
@@ -73,11 +81,12 @@ struct FaCfg {
 // of a critical tile are taken 32 at a time (a step), so that each product is a
 // full-rate 16x16x32 MFMA (P.V contracts over the step's 32 keys), the step
 // buffers are 16 KB and three workgroups fit on a CU.
-template <int D>
+template <int D, bool PROJ>
 __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const int8_t* __restrict__ mask,
-    const uint16_t* __restrict__ Hx, const float* __restrict__ alpha, uint16_t* __restrict__ O,
+    const uint16_t* __restrict__ Hx, const float* __restrict__ alpha,
+    const uint16_t* __restrict__ wo, int wo_hs, int elu, uint16_t* __restrict__ O,
     float* __restrict__ dbg_os, float* __restrict__ dbg_ol, int H, int N, int Nb) {
   using Cf = FaCfg<D>;
   constexpr int C = Cf::C, HT = Cf::HT, INSTR = Cf::INSTR, NN = Cf::NN;
@@ -282,21 +291,31 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
       qf[ks * 8 + 2 * e + 1] = bf_hi(w4[e]);
     }
   }
-  float qm = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < KSTEPS * 8; ++e) qm = fmaxf(qm, qf[e]);
-  qm = group4_max(qm) * kLog2e;
-  // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
-  // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
   uint4 fq[KSTEPS];
+  if (elu) {  // uniform: phi = elu + 1, elementwise
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    uint32_t w4[4];
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint32_t w4[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w4[e] = pack_bf2(__builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e], kLog2e, -qm)),
-                       __builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e + 1], kLog2e, -qm)));
-    fq[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      for (int e = 0; e < 4; ++e) w4[e] = pack_bf2(elu1(qf[ks * 8 + 2 * e]), elu1(qf[ks * 8 + 2 * e + 1]));
+      fq[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  } else {
+    float qm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < KSTEPS * 8; ++e) qm = fmaxf(qm, qf[e]);
+    qm = group4_max(qm) * kLog2e;
+    // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
+    // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w4[e] = pack_bf2(__builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e], kLog2e, -qm)),
+                         __builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e + 1], kLog2e, -qm)));
+      fq[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
   }
   // part 0 of H_i^T and Z_i have landed (part 1's copies, issued after them, may not)
   if constexpr (HPARTS == 2)
@@ -334,8 +353,39 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     lds_barrier();
     numpart(std::integral_constant<int, 1>{}, bufB);
   }
-  const float al = alpha[h];
-  const float cs = al * inv_l, cl = (1.0f - al) * inv_den;
+  float cs, cl;
+  if constexpr (PROJ) {
+    // Proj(O_l) = O_l W. B operand: num^T rounded to bf16, its k slots the
+    // features {4g..4g+3, 16+4g..16+4g+3} of each 32-feature step; A operand:
+    // W^T in the same feature order (k_pack_proj), one fragment set per output
+    // tile, the next tile's fragments in flight while the current one multiplies.
+    uint4 nb[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      nb[ks] = make_uint4(pack_bf2(nm[2 * ks][0], nm[2 * ks][1]), pack_bf2(nm[2 * ks][2], nm[2 * ks][3]),
+                          pack_bf2(nm[2 * ks + 1][0], nm[2 * ks + 1][1]),
+                          pack_bf2(nm[2 * ks + 1][2], nm[2 * ks + 1][3]));
+    const uint4* wf = reinterpret_cast<const uint4*>(wo + (size_t)h * wo_hs) + lane;
+    uint4 wa[2][KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) wa[0][ks] = wf[ks * 64];
+#pragma unroll
+    for (int nt = 0; nt < FT; ++nt) {
+      if (nt + 1 < FT) {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) wa[(nt + 1) & 1][ks] = wf[((nt + 1) * KSTEPS + ks) * 64];
+      }
+      nm[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) nm[nt] = mfma_bf16(wa[nt & 1][ks], nb[ks], nm[nt]);
+    }
+    cs = inv_l;  // O = O_s + Proj(O_l)
+    cl = inv_den;
+  } else {
+    const float al = alpha[h];
+    cs = al * inv_l;
+    cl = (1.0f - al) * inv_den;
+  }
   lds_barrier();  // every wave has read H_i^T: the buffers become the output stage
   // wave w stages its 16 rows in buffer w / 2 and writes them back itself
   uint16_t* ost = ((wave >> 1) ? bufB : bufA) + (wave & 1) * 16 * OS;
@@ -381,6 +431,8 @@ __global__ __launch_bounds__(256) void k_sparse_f32(const float* __restrict__ Q,
                                                     const int8_t* __restrict__ mask,
                                                     const float* __restrict__ Hx,
                                                     const float* __restrict__ alpha,
+                                                    const float* __restrict__ proj_o,
+                                                    int proj_hs, int elu,
                                                     float* __restrict__ O,
                                                     float* __restrict__ dbg_os,
                                                     float* __restrict__ dbg_ol, int H, int N,
@@ -435,23 +487,29 @@ __global__ __launch_bounds__(256) void k_sparse_f32(const float* __restrict__ Q,
       m = mn;
     }
   }
-  // linear branch
-  float qm = -INFINITY;
+  // linear branch: phi(q) (softmax over the features, or elu + 1 elementwise)
+  float f[P];
+  if (elu) {
 #pragma unroll
-  for (int e = 0; e < P; ++e) qm = fmaxf(qm, q[e]);
-  qm = fmaxf(qm, __shfl_xor(qm, 1));
-  qm = fmaxf(qm, __shfl_xor(qm, 2));
-  float f[P], fs = 0.f;
+    for (int e = 0; e < P; ++e) f[e] = q[e] > 0.f ? q[e] + 1.0f : expf(q[e]);
+  } else {
+    float qm = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < P; ++e) {
-    f[e] = expf(q[e] - qm);
-    fs += f[e];
+    for (int e = 0; e < P; ++e) qm = fmaxf(qm, q[e]);
+    qm = fmaxf(qm, __shfl_xor(qm, 1));
+    qm = fmaxf(qm, __shfl_xor(qm, 2));
+    float fs = 0.f;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      f[e] = expf(q[e] - qm);
+      fs += f[e];
+    }
+    fs += __shfl_xor(fs, 1);
+    fs += __shfl_xor(fs, 2);
+    const float finv = 1.0f / fs;
+#pragma unroll
+    for (int e = 0; e < P; ++e) f[e] *= finv;
   }
-  fs += __shfl_xor(fs, 1);
-  fs += __shfl_xor(fs, 2);
-  const float finv = 1.0f / fs;
-#pragma unroll
-  for (int e = 0; e < P; ++e) f[e] *= finv;
   const float* Hrow = Hx + ((size_t)bh * Nb + i) * NN;
   float den = 0.f;
 #pragma unroll
@@ -472,54 +530,112 @@ __global__ __launch_bounds__(256) void k_sparse_f32(const float* __restrict__ Q,
 #pragma unroll
     for (int e = 0; e < P; ++e) num[e] = fmaf(fr, Hrow[(size_t)(part * P + e) * D + r], num[e]);
   }
+  if (proj_o) {  // uniform: SLA fusion, num <- num W (the division by den commutes with it)
+    const float* W = proj_o + (size_t)h * proj_hs;
+    float pr[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) pr[e] = 0.f;
+    for (int r = 0; r < D; ++r) {
+      const int src = (lane & ~3) | (r / P);
+      float nr = 0.f;
+#pragma unroll
+      for (int e = 0; e < P; ++e)
+        if (e == r % P) nr = num[e];
+      nr = __shfl(nr, src);
+#pragma unroll
+      for (int e = 0; e < P; ++e) pr[e] = fmaf(nr, W[(size_t)r * D + part * P + e], pr[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < P; ++e) num[e] = pr[e];
+  }
   if (!valid) return;
   const float inv_l = (ncrit > 0 && l > 0.f) ? 1.0f / l : 0.f;
   const float inv_den = den > 0.f ? 1.0f / den : 0.f;
-  const float al = alpha[h];
+  const float al = proj_o ? 1.0f : alpha[h];
+  const float bl = proj_o ? 1.0f : 1.0f - al;
   const size_t orow = ((size_t)bh * N + t) * D + part * P;
 #pragma unroll
   for (int e = 0; e < P; ++e) {
     const float os = acc[e] * inv_l, ol = num[e] * inv_den;
-    O[orow + e] = al * os + (1.0f - al) * ol;
+    O[orow + e] = al * os + bl * ol;
     if (dbg_os) dbg_os[orow + e] = os;
     if (dbg_ol) dbg_ol[orow + e] = ol;
   }
 }
 
-}  // namespace
-
-hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const int8_t* mask,
-                         const float* alpha, const Work& w, void* O, float* dbg_os,
-                         float* dbg_ol, hipStream_t s) {
-  if (D.bf16) {
-    const int T = D.BH * D.Nb;
-    if (D.d == 128)
-      hipLaunchKernelGGL(k_sparse_bf16<128>, dim3(T), dim3(256), 0, s, (const uint16_t*)Q,
-                         (const uint16_t*)K, w.vt, mask, (const uint16_t*)w.Hx, alpha,
-                         (uint16_t*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
-    else
-      hipLaunchKernelGGL(k_sparse_bf16<64>, dim3(T), dim3(256), 0, s, (const uint16_t*)Q,
-                         (const uint16_t*)K, w.vt, mask, (const uint16_t*)w.Hx, alpha,
-                         (uint16_t*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
-  } else {
-    // the f32 path reads V directly; vt is not formed
-    return hipErrorInvalidValue;
+// The SLA output map W ([in][out] float32, one [D][D] matrix per workgroup)
+// as bf16 A-operand fragments of the epilogue product (num W)^T = W^T num^T:
+// entry ((nt * D/32 + ks) * 64 + lane) holds, for output feature
+// n = 16 nt + lane % 16 and g = lane / 16, the 8 values W[c][n] with
+// c = 32 ks + 16 (j / 4) + 4 g + j % 4, j = 0..7 (the k-slot order of num^T).
+template <int D>
+__global__ __launch_bounds__(256) void k_pack_proj(const float* __restrict__ W,
+                                                   uint16_t* __restrict__ wo) {
+  constexpr int FT = D / 16, KS = D / 32;
+  const float* Wh = W + (size_t)blockIdx.x * D * D;
+  uint4* out = reinterpret_cast<uint4*>(wo + (size_t)blockIdx.x * D * D);
+  for (int x = threadIdx.x; x < FT * KS * 64; x += 256) {
+    const int lane = x & 63, ks = (x >> 6) % KS, nt = (x >> 6) / KS;
+    const int n = 16 * nt + (lane & 15), g = lane >> 4;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = Wh[(size_t)(32 * ks + 16 * (j >> 2) + 4 * g + (j & 3)) * D + n];
+    out[x] = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                        pack_bf2(v[6], v[7]));
   }
+}
+
+template <int D>
+hipError_t launch_bf16(const Dims& D_, const void* Q, const void* K, const int8_t* mask,
+                       const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
+                       float* dbg_ol, hipStream_t s) {
+  const int T = D_.BH * D_.Nb;
+  const int elu = D_.elu ? 1 : 0;
+  if (proj)
+    hipLaunchKernelGGL((k_sparse_bf16<D, true>), dim3(T), dim3(256), 0, s, (const uint16_t*)Q,
+                       (const uint16_t*)K, w.vt, mask, (const uint16_t*)w.Hx, alpha, w.wo,
+                       D_.proj_hs, elu, (uint16_t*)O, dbg_os, dbg_ol, D_.H, D_.N, D_.Nb);
+  else
+    hipLaunchKernelGGL((k_sparse_bf16<D, false>), dim3(T), dim3(256), 0, s, (const uint16_t*)Q,
+                       (const uint16_t*)K, w.vt, mask, (const uint16_t*)w.Hx, alpha, w.wo,
+                       D_.proj_hs, elu, (uint16_t*)O, dbg_os, dbg_ol, D_.H, D_.N, D_.Nb);
   return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_pack_proj(const Dims& D, const float* proj_o, const Work& w, hipStream_t s) {
+  if (!D.bf16 || !proj_o) return hipErrorInvalidValue;
+  const int hs = D.proj_hs ? D.H : 1;
+  if (D.d == 128)
+    hipLaunchKernelGGL(k_pack_proj<128>, dim3(hs), dim3(256), 0, s, proj_o, w.wo);
+  else
+    hipLaunchKernelGGL(k_pack_proj<64>, dim3(hs), dim3(256), 0, s, proj_o, w.wo);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const int8_t* mask,
+                         const float* alpha, const float* proj_o, const Work& w, void* O,
+                         float* dbg_os, float* dbg_ol, hipStream_t s) {
+  // the f32 path reads V directly; vt is not formed
+  if (!D.bf16) return hipErrorInvalidValue;
+  if (D.d == 128) return launch_bf16<128>(D, Q, K, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
+  return launch_bf16<64>(D, Q, K, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
+}
+
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,
-                             const int8_t* mask, const float* alpha, const Work& w, void* O,
-                             float* dbg_os, float* dbg_ol, hipStream_t s) {
+                             const int8_t* mask, const float* alpha, const float* proj_o,
+                             const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s) {
   dim3 grid(D.Nb, D.BH);
+  const int elu = D.elu ? 1 : 0;
   if (D.d == 128)
     hipLaunchKernelGGL(k_sparse_f32<128>, grid, dim3(256), 0, s, (const float*)Q,
-                       (const float*)K, (const float*)V, mask, (const float*)w.Hx, alpha,
-                       (float*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
+                       (const float*)K, (const float*)V, mask, (const float*)w.Hx, alpha, proj_o,
+                       D.proj_hs, elu, (float*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
   else
     hipLaunchKernelGGL(k_sparse_f32<64>, grid, dim3(256), 0, s, (const float*)Q,
-                       (const float*)K, (const float*)V, mask, (const float*)w.Hx, alpha,
-                       (float*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
+                       (const float*)K, (const float*)V, mask, (const float*)w.Hx, alpha, proj_o,
+                       D.proj_hs, elu, (float*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
     const int8_t* __restrict__ k8, const float* __restrict__ ksc, const float* __restrict__ kbias,
     const uint8_t* __restrict__ v8t, const float* __restrict__ vsc,
     const int8_t* __restrict__ mask, const uint16_t* __restrict__ Hx,
-    const float* __restrict__ alpha, uint16_t* __restrict__ O, float* __restrict__ dbg_os,
+    const float* __restrict__ alpha, int elu, uint16_t* __restrict__ O, float* __restrict__ dbg_os,
     float* __restrict__ dbg_ol, int H, int N, int Nb) {
   using Cf = Q8Cfg<D>;
   constexpr int C8 = Cf::C8, KT = Cf::KT, PAIR = Cf::PAIR, CPL = Cf::CPL, KS8 = Cf::KS8;
@@ -360,14 +360,19 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
         qf[ks * 8 + 2 * e + 1] = bf_hi(w4[e]);
       }
     }
-    float qm = -INFINITY;
+    if (elu) {  // uniform: phi = elu + 1, elementwise
 #pragma unroll
-    for (int e = 0; e < KS * 8; ++e) qm = fmaxf(qm, qf[e]);
-    qm = group4_max(qm) * kLog2e;
-    // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
-    // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
+      for (int e = 0; e < KS * 8; ++e) qf[e] = elu1(qf[e]);
+    } else {
+      float qm = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < KS * 8; ++e) qf[e] = __builtin_amdgcn_exp2f(fmaf(qf[e], kLog2e, -qm));
+      for (int e = 0; e < KS * 8; ++e) qm = fmaxf(qm, qf[e]);
+      qm = group4_max(qm) * kLog2e;
+      // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
+      // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
+#pragma unroll
+      for (int e = 0; e < KS * 8; ++e) qf[e] = __builtin_amdgcn_exp2f(fmaf(qf[e], kLog2e, -qm));
+    }
     float dp = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -428,11 +433,11 @@ hipError_t launch_sparse_q8(const Dims& D, const void* Q, const int8_t* mask, co
   if (D.d == 128)
     hipLaunchKernelGGL(k_sparse_q8<128>, dim3(T), dim3(256), 0, s, (const uint16_t*)Q, w.qkmean,
                        w.k8, w.ks, w.kb, w.v8t, w.vs, mask, (const uint16_t*)w.Hx, alpha,
-                       (uint16_t*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
+                       D.elu ? 1 : 0, (uint16_t*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
   else
     hipLaunchKernelGGL(k_sparse_q8<64>, dim3(T), dim3(256), 0, s, (const uint16_t*)Q, w.qkmean,
                        w.k8, w.ks, w.kb, w.v8t, w.vs, mask, (const uint16_t*)w.Hx, alpha,
-                       (uint16_t*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
+                       D.elu ? 1 : 0, (uint16_t*)O, dbg_os, dbg_ol, D.H, D.N, D.Nb);
   return hipGetLastError();
 }
 

@@ -34,7 +34,8 @@ int make_dims(const sla_problem* p, sla::Dims* D) {
     return fail(SLA_ERR_ARG, "unknown dtype %d", p->dtype);
   if (p->quant != SLA_QUANT_NONE && p->quant != SLA_QUANT_I8QK_F8PV)
     return fail(SLA_ERR_ARG, "unknown quant mode %d", p->quant);
-  if (p->reserved != 0) return fail(SLA_ERR_ARG, "reserved field must be 0");
+  if (p->phi != SLA_PHI_SOFTMAX && p->phi != SLA_PHI_ELU1)
+    return fail(SLA_ERR_ARG, "unknown feature map %d", p->phi);
   if (!(p->kh >= 0.0 && p->kh <= 1.0) || !(p->kl >= 0.0 && p->kl <= 1.0))
     return fail(SLA_ERR_ARG, "kh and kl must lie in [0, 1] (got %g, %g)", p->kh, p->kl);
   if (p->d != 64 && p->d != 128) return fail(SLA_ERR_UNSUPPORTED, "head dim %d not built", p->d);
@@ -65,6 +66,8 @@ int make_dims(const sla_problem* p, sla::Dims* D) {
   D->NN = p->d * p->d + p->d;
   D->bf16 = p->dtype == SLA_BF16;
   D->quant = p->quant == SLA_QUANT_I8QK_F8PV;
+  D->elu = p->phi == SLA_PHI_ELU1;
+  D->proj_hs = p->proj_head_stride;
   return SLA_OK;
 }
 
@@ -91,6 +94,7 @@ size_t carve(const Dims& D, void* base, Work* w) {
     x.Hx = take(BH * D.Nb * D.NN * sizeof(uint16_t));
     if (!D.quant) x.vt = (uint16_t*)take(BH * D.Nb * D.d * kBlock * sizeof(uint16_t));
     x.ind = (uint32_t*)take(BH * (D.Nbp / 32) * D.Nb128 * sizeof(uint32_t));
+    x.wo = (uint16_t*)take((size_t)(D.proj_hs ? D.H : 1) * D.d * D.d * sizeof(uint16_t));
   } else {
     x.hx = take(BH * D.Nb * D.NN * sizeof(float));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(float));
@@ -111,7 +115,7 @@ size_t carve(const Dims& D, void* base, Work* w) {
 
 extern "C" {
 
-int sla_version(void) { return (1 << 16) | 0; }
+int sla_version(void) { return (1 << 16) | 1; }
 
 const char* sla_status_str(int status) {
   switch (status) {
@@ -135,6 +139,7 @@ int sla_block_counts(const sla_problem* p, int32_t* nb, int32_t* n_h, int32_t* n
   q.quant = SLA_QUANT_NONE;
   if (q.d != 64 && q.d != 128) q.d = 64;
   q.proj_head_stride = 0;
+  q.phi = SLA_PHI_SOFTMAX;
   const int rc = make_dims(&q, &D);
   if (rc != SLA_OK) return rc;
   if (nb) *nb = D.Nb;
@@ -154,21 +159,32 @@ int sla_workspace_bytes(const sla_problem* p, size_t* bytes) {
   return SLA_OK;
 }
 
-int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const void* V,
-                      const float* proj_q, const float* proj_k, const float* alpha,
-                      const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
-                      size_t workspace_bytes, void* stream, const sla_debug* dbg) {
+}  // extern "C"
+
+namespace {
+
+// Both formulations: proj_o == NULL is SLA2 (O = alpha O_s + (1 - alpha) O_l),
+// otherwise SLA (O = O_s + O_l proj_o).
+int run_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                const float* proj_q, const float* proj_k, const float* alpha, const float* proj_o,
+                const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
+                size_t workspace_bytes, void* stream, const sla_debug* dbg) {
   sla::Dims D;
   int rc = make_dims(p, &D);
   if (rc != SLA_OK) return rc;
-  if (!Q || !K || !V || !alpha || !O) return fail(SLA_ERR_ARG, "Q, K, V, alpha and O must not be NULL");
-  if (!mask_in && (!proj_q || !proj_k))
-    return fail(SLA_ERR_ARG, "proj_q and proj_k are required when mask_in is NULL");
+  const bool sla1 = proj_o != nullptr;
+  if (!Q || !K || !V || !O) return fail(SLA_ERR_ARG, "Q, K, V and O must not be NULL");
+  if (!sla1 && !alpha) return fail(SLA_ERR_ARG, "alpha must not be NULL");
+  if (sla1 && D.quant)
+    return fail(SLA_ERR_UNSUPPORTED, "the SLA output projection is built without the 8-bit sparse branch");
+  if ((proj_q == nullptr) != (proj_k == nullptr))
+    return fail(SLA_ERR_ARG, "proj_q and proj_k must both be given or both be NULL");
   if (!mask_in && !mask_out) return fail(SLA_ERR_ARG, "mask_out may be NULL only when mask_in is given");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
     return fail(SLA_ERR_ARG, "Q, K, V and O must be 16-byte aligned");
-  if ((proj_q && !aligned(proj_q, 4)) || (proj_k && !aligned(proj_k, 4)) || !aligned(alpha, 4))
-    return fail(SLA_ERR_ARG, "proj_q, proj_k and alpha must be 4-byte aligned");
+  if ((proj_q && !aligned(proj_q, 4)) || (proj_k && !aligned(proj_k, 4)) || (alpha && !aligned(alpha, 4)) ||
+      (proj_o && !aligned(proj_o, 4)))
+    return fail(SLA_ERR_ARG, "proj_q, proj_k, proj_o and alpha must be 4-byte aligned");
   if (dbg && ((dbg->pooled_q && !aligned(dbg->pooled_q, 8)) || (dbg->pooled_k && !aligned(dbg->pooled_k, 8)) ||
               (dbg->logits && !aligned(dbg->logits, 8)) || (dbg->o_s && !aligned(dbg->o_s, 16)) ||
               (dbg->o_l && !aligned(dbg->o_l, 16))))
@@ -196,18 +212,27 @@ int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const 
   const int8_t* mask = mask_in;
   SLA_LAUNCH(mark(0), "event record");
   if (!mask_in) {
-    SLA_LAUNCH(sla::launch_pool_proj(D, Q, K, proj_q, proj_k, proj_hs, w.pooled_raw, w.pooled_q, w.pooled_k, s),
-               "pool/proj kernel");
+    // without a router the block means themselves are compared
+    const double* pq = w.pooled_raw;
+    const double* pk = w.pooled_raw + (size_t)D.BH * D.Nb * D.d;
+    if (proj_q) {
+      SLA_LAUNCH(sla::launch_pool_proj(D, Q, K, proj_q, proj_k, proj_hs, w.pooled_raw, w.pooled_q,
+                                       w.pooled_k, s),
+                 "pool/proj kernel");
+      pq = w.pooled_q;
+      pk = w.pooled_k;
+    } else {
+      SLA_LAUNCH(sla::launch_pool_sum(D, Q, K, w.pooled_raw, s), "pool kernel");
+    }
     SLA_LAUNCH(mark(1), "event record");
-    SLA_LAUNCH(sla::launch_select(D, w.pooled_q, w.pooled_k, mask_out,
-                                  (dbg && dbg->logits) ? dbg->logits : w.logits, s),
+    SLA_LAUNCH(sla::launch_select(D, pq, pk, mask_out, (dbg && dbg->logits) ? dbg->logits : w.logits, s),
                "score/select kernel");
     SLA_LAUNCH(mark(2), "event record");
     if (dbg && dbg->pooled_q)
-      SLA_LAUNCH(hipMemcpyAsync(dbg->pooled_q, w.pooled_q, (size_t)D.BH * D.Nb * D.d * sizeof(double),
+      SLA_LAUNCH(hipMemcpyAsync(dbg->pooled_q, pq, (size_t)D.BH * D.Nb * D.d * sizeof(double),
                                 hipMemcpyDeviceToDevice, s), "debug copy");
     if (dbg && dbg->pooled_k)
-      SLA_LAUNCH(hipMemcpyAsync(dbg->pooled_k, w.pooled_k, (size_t)D.BH * D.Nb * D.d * sizeof(double),
+      SLA_LAUNCH(hipMemcpyAsync(dbg->pooled_k, pk, (size_t)D.BH * D.Nb * D.d * sizeof(double),
                                 hipMemcpyDeviceToDevice, s), "debug copy");
     mask = mask_out;
   } else {
@@ -224,24 +249,54 @@ int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const 
   SLA_LAUNCH(mark(4), "event record");
   float* dos = dbg ? dbg->o_s : nullptr;
   float* dol = dbg ? dbg->o_l : nullptr;
+  if (sla1 && D.bf16) SLA_LAUNCH(sla::launch_pack_proj(D, proj_o, w, s), "projection packing kernel");
   if (D.quant)
     SLA_LAUNCH(sla::launch_sparse_q8(D, Q, mask, alpha, w, O, dos, dol, s), "8-bit sparse kernel");
   else if (D.bf16)
-    SLA_LAUNCH(sla::launch_sparse(D, Q, K, mask, alpha, w, O, dos, dol, s), "sparse kernel");
+    SLA_LAUNCH(sla::launch_sparse(D, Q, K, mask, alpha, proj_o, w, O, dos, dol, s), "sparse kernel");
   else
-    SLA_LAUNCH(sla::launch_sparse_f32(D, Q, K, V, mask, alpha, w, O, dos, dol, s), "sparse kernel");
+    SLA_LAUNCH(sla::launch_sparse_f32(D, Q, K, V, mask, alpha, proj_o, w, O, dos, dol, s), "sparse kernel");
   SLA_LAUNCH(mark(5), "event record");
 #undef SLA_LAUNCH
   g_err[0] = 0;
   return SLA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int sla_forward_debug(const sla_problem* p, const void* Q, const void* K, const void* V,
+                      const float* proj_q, const float* proj_k, const float* alpha,
+                      const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
+                      size_t workspace_bytes, void* stream, const sla_debug* dbg) {
+  return run_forward(p, Q, K, V, proj_q, proj_k, alpha, nullptr, mask_in, O, mask_out, workspace,
+                     workspace_bytes, stream, dbg);
+}
+
 int sla_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
                 const float* proj_q, const float* proj_k, const float* alpha,
                 const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  return sla_forward_debug(p, Q, K, V, proj_q, proj_k, alpha, mask_in, O, mask_out, workspace,
-                           workspace_bytes, stream, nullptr);
+  return run_forward(p, Q, K, V, proj_q, proj_k, alpha, nullptr, mask_in, O, mask_out, workspace,
+                     workspace_bytes, stream, nullptr);
+}
+
+int sla1_forward_debug(const sla_problem* p, const void* Q, const void* K, const void* V,
+                       const float* proj_q, const float* proj_k, const float* proj_o,
+                       const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
+                       size_t workspace_bytes, void* stream, const sla_debug* dbg) {
+  if (!proj_o) return fail(SLA_ERR_ARG, "proj_o must not be NULL");
+  return run_forward(p, Q, K, V, proj_q, proj_k, nullptr, proj_o, mask_in, O, mask_out, workspace,
+                     workspace_bytes, stream, dbg);
+}
+
+int sla1_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
+                 const float* proj_q, const float* proj_k, const float* proj_o,
+                 const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return sla1_forward_debug(p, Q, K, V, proj_q, proj_k, proj_o, mask_in, O, mask_out, workspace,
+                            workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"

@@ -21,6 +21,8 @@ struct Dims {
   int NN;           // d*d + d: one h_j (stored transposed, c-major) followed by z_j
   bool bf16;
   bool quant;
+  bool elu;         // feature map elu(x) + 1 instead of the softmax over the features
+  int proj_hs;      // head stride of proj_q / proj_k / proj_o in elements: 0 or d*d
 };
 
 // Device workspace regions, carved from the caller's buffer.
@@ -42,6 +44,8 @@ struct Work {
   float* kb;          // quant only: [BH, Nb*64] per-key bias mean(Q).(K - mean(K)) * log2(e)/sqrt(d), 0 past N
   uint8_t* v8t;       // quant only: [BH, Nb, d, 4, 16] fp8 e4m3 V^T (see the h/z kernel)
   float* vs;          // quant only: [BH, Nb] per-block scales of V
+  uint16_t* wo;       // bf16 only: [Hs, d/16, d/32, 64, 8] the SLA output map Proj in bf16 MFMA
+                      // A-operand fragments (Hs = H if it is per head, else 1; k_sparse.hip)
 };
 
 size_t carve(const Dims& D, void* base, Work* w);  // returns bytes needed (base may be NULL)
@@ -60,11 +64,14 @@ hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8
 hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w, hipStream_t s);
 hipError_t launch_indicator(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
 hipError_t launch_linear(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
+// proj_o == NULL: the SLA2 mix with alpha; else O = O_s + O_l proj_o (alpha unused; the
+// bf16 kernel reads the fragments that launch_pack_proj wrote to w.wo)
+hipError_t launch_pack_proj(const Dims& D, const float* proj_o, const Work& w, hipStream_t s);
 hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const int8_t* mask,
-                         const float* alpha, const Work& w, void* O, float* dbg_os,
-                         float* dbg_ol, hipStream_t s);
+                         const float* alpha, const float* proj_o, const Work& w, void* O,
+                         float* dbg_os, float* dbg_ol, hipStream_t s);
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,
-                             const int8_t* mask, const float* alpha, const Work& w, void* O,
-                             float* dbg_os, float* dbg_ol, hipStream_t s);
+                             const int8_t* mask, const float* alpha, const float* proj_o,
+                             const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
 
 }  // namespace sla

@@ -23,12 +23,19 @@ def to_dev(x, inputs=None):
     return x.to("cuda").contiguous()
 
 
-def run_gpu(x, mask_in=None, debug=True, quant=False):
-    """Runs the HIP path on the seeded inputs `x` (workloads.Inputs). Returns numpy arrays."""
+def run_gpu(x, mask_in=None, debug=True, quant=False, phi="softmax", proj_o=None, router=True):
+    """Runs the HIP path on the seeded inputs `x` (workloads.Inputs). Returns numpy arrays.
+    proj_o: None for the SLA2 mix (sla_forward), else the SLA output map
+    (sla1_forward); router=False passes no router matrices."""
     q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
-    pq, pk, al = x.proj_q.cuda(), x.proj_k.cuda(), x.alpha.cuda()
+    pq, pk = (x.proj_q.cuda(), x.proj_k.cuda()) if router else (None, None)
     mi = None if mask_in is None else torch.from_numpy(np.ascontiguousarray(mask_in)).cuda()
-    res = sla.forward(q, k, v, pq, pk, al, x.kh, x.kl, mask_in=mi, debug=debug, quant=quant)
+    if proj_o is None:
+        res = sla.forward(q, k, v, pq, pk, x.alpha.cuda(), x.kh, x.kl, mask_in=mi, debug=debug,
+                          quant=quant, phi=phi)
+    else:
+        res = sla.forward_sla1(q, k, v, proj_o.cuda(), x.kh, x.kl, mask_in=mi, proj_q=pq,
+                               proj_k=pk, debug=debug, phi=phi)
     torch.cuda.synchronize()
     out = {"O": res[0].float().cpu().numpy(), "mask": res[1].cpu().numpy()}
     if debug:

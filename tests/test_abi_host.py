@@ -19,14 +19,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "sla.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sla_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sla1?_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = sla.load_library()
     names = _declared_functions()
     assert {"sla_forward", "sla_forward_debug", "sla_workspace_bytes", "sla_block_counts",
-            "sla_status_str", "sla_last_error", "sla_version"} <= set(names)
+            "sla_status_str", "sla_last_error", "sla_version", "sla1_forward",
+            "sla1_forward_debug"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.sla_version() >> 16 == 1
@@ -73,7 +74,7 @@ def good():
     (lambda p: setattr(p, "kh", float("nan")), B.SLA_ERR_ARG),
     (lambda p: setattr(p, "kl", 1.5), B.SLA_ERR_ARG),
     (lambda p: (setattr(p, "kh", 0.6), setattr(p, "kl", 0.5)), B.SLA_ERR_ARG),
-    (lambda p: setattr(p, "reserved", 1), B.SLA_ERR_ARG),
+    (lambda p: setattr(p, "phi", 7), B.SLA_ERR_ARG),
     (lambda p: setattr(p, "proj_head_stride", 5), B.SLA_ERR_ARG),
     (lambda p: setattr(p, "d", 96), B.SLA_ERR_UNSUPPORTED),
     (lambda p: (setattr(p, "dtype", B.SLA_F32), setattr(p, "quant", 1)), B.SLA_ERR_UNSUPPORTED),
@@ -96,7 +97,9 @@ def test_null_problem():
     (dict(Q=None), B.SLA_ERR_ARG),
     (dict(alpha_none=True), B.SLA_ERR_ARG),
     (dict(O=None), B.SLA_ERR_ARG),
-    (dict(pq=None), B.SLA_ERR_ARG),          # router needed without mask_in
+    (dict(pq=None), B.SLA_ERR_ARG),          # one router matrix without the other
+    (dict(pk=None), B.SLA_ERR_ARG),
+    (dict(pq=None, pk=None), B.SLA_ERR_WORKSPACE),  # no router is valid: the workspace check follows
     (dict(mo=None), B.SLA_ERR_ARG),          # mask_out needed without mask_in
     (dict(Q=0x10008), B.SLA_ERR_ARG),        # misaligned
     (dict(al=0x10002), B.SLA_ERR_ARG),
@@ -116,3 +119,35 @@ def test_status_strings():
     for c in (0, -1, -2, -3, -4):
         assert lib.sla_status_str(c)
     assert b"unknown" in lib.sla_status_str(42)
+
+
+def _fwd1(p, Q=0x10000, K=0x10000, V=0x10000, pq=None, pk=None, po=0x10000, mi=None,
+          O=0x10000, mo=0x10000, ws=0x10000, wsb=0):
+    lib = sla.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.sla1_forward(ctypes.byref(p), vp(Q), vp(K), vp(V), vp(pq), vp(pk), vp(po), vp(mi),
+                            vp(O), vp(mo), vp(ws), ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(po=None), B.SLA_ERR_ARG),          # the output map is required
+    (dict(po=0x10002), B.SLA_ERR_ARG),       # misaligned
+    (dict(pq=0x10000), B.SLA_ERR_ARG),       # one router matrix without the other
+    (dict(quant=True), B.SLA_ERR_UNSUPPORTED),
+    (dict(), B.SLA_ERR_WORKSPACE),           # valid up to the workspace; no alpha needed
+    (dict(pq=0x10000, pk=0x10000), B.SLA_ERR_WORKSPACE),
+])
+def test_sla1_errors(kw, code):
+    p = good()
+    if kw.pop("quant", False):
+        p.quant = B.SLA_QUANT_I8QK_F8PV
+    assert _fwd1(p, **kw) == code
+    assert sla.load_library().sla_last_error()
+
+
+def test_feature_map_does_not_change_sizes():
+    a = sla.make_problem(1, 12, 32760, 128, "bf16", 0.05, 0.10)
+    b = sla.make_problem(1, 12, 32760, 128, "bf16", 0.05, 0.10, phi="elu1")
+    assert sla.workspace_bytes(a) == sla.workspace_bytes(b)
+    with pytest.raises(ValueError):
+        sla.make_problem(1, 1, 64, 64, "bf16", 0.5, 0.0, phi="relu")

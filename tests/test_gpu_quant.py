@@ -32,20 +32,20 @@ def _head_f64(t, b, h):
     return t[b, h].double().numpy()
 
 
-def _check(x, heads=None, qblocks=None, mask=None):
+def _check(x, heads=None, qblocks=None, mask=None, phi="softmax"):
     """Mask parity (unless a mask is given), then O, O_l, O_s with the oracle mask injected."""
     if mask is None:
         ref = orc.forward(x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha, x.kh, x.kl,
                           compute_outputs=False)
-        g = run_gpu(x, debug=False, quant=True)
+        g = run_gpu(x, debug=False, quant=True, phi=phi)
         exact, excused, bad = compare_masks(g["mask"], ref.mask, ref.logits, ref.n_h, ref.n_l)
         _flush(f"mask rows exact={exact} near-tie={excused} bad={len(bad)}")
         assert not bad, bad[:10]
         mask = ref.mask
     heads = heads or [(b, h) for b in range(x.B) for h in range(x.H)]
     sub = orc.forward(x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha, x.kh, x.kl, mask_in=mask,
-                      heads=heads, query_blocks=qblocks)
-    gi = run_gpu(x, mask_in=mask, debug=True, quant=True)
+                      heads=heads, query_blocks=qblocks, feature=phi)
+    gi = run_gpu(x, mask_in=mask, debug=True, quant=True, phi=phi)
     for (b, h) in heads:
         qb = None if qblocks is None else qblocks[(b, h)]
         rows = np.arange(x.N) if qb is None else orc.token_rows(qb, x.N)
@@ -70,6 +70,13 @@ def _check(x, heads=None, qblocks=None, mask=None):
 def test_config5_recipe_small(N, kh):
     x = make_inputs(CONFIGS[5], H=2, N=N, **({} if kh is None else {"kh": kh}))
     _check(x)
+
+
+@pytest.mark.parametrize("N", [1000, 4096])
+def test_config5_recipe_elu1(N):
+    # the feature map only touches the (bf16) linear branch of the 8-bit path
+    x = make_inputs(CONFIGS[5], H=2, N=N)
+    _check(x, phi="elu1")
 
 
 def test_config5_full_sampled():

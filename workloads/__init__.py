@@ -7,4 +7,4 @@ from it without sharing any computation.
 """
 
 from .configs import CONFIGS, WorkloadConfig, get_config  # noqa: F401
-from .synth import Inputs, make_inputs, sincos_posemb  # noqa: F401
+from .synth import Inputs, make_inputs, make_proj_o, sincos_posemb  # noqa: F401

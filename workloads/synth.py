@@ -34,7 +34,7 @@ from .configs import WorkloadConfig
 POSEMB_SCALE = 3.4
 
 # stream ids of the counter-keyed generators
-_S_AQ, _S_AK, _S_NQ, _S_NK, _S_V, _S_PQ, _S_PK, _S_ALPHA, _S_Q, _S_K = range(10)
+_S_AQ, _S_AK, _S_NQ, _S_NK, _S_V, _S_PQ, _S_PK, _S_ALPHA, _S_Q, _S_K, _S_PO = range(11)
 
 
 def _rng(seed: int, stream: int, b: int = 0, h: int = 0) -> np.random.Generator:
@@ -134,3 +134,19 @@ def make_inputs(cfg: WorkloadConfig, *, B: Optional[int] = None, H: Optional[int
                   torch.from_numpy(pk.astype(np.float32)),
                   torch.from_numpy(al[:H].astype(np.float32)),
                   cfg.kh if kh is None else kh, cfg.kl if kl is None else kl)
+
+
+def make_proj_o(cfg: WorkloadConfig, *, H: Optional[int] = None, per_head: bool = False) -> torch.Tensor:
+    """SLA's learned output map Proj (O = O_s + Proj(O_l)) as float32, indexed
+    [in, out]: one [d, d] matrix, or [H, d, d] with per_head. Entries are
+    i.i.d. N(0, 1/d), a map of unit gain (the pages give no initialisation);
+    head h of the per-head form has its own stream, so the leading heads match
+    at any H."""
+    d = cfg.d
+    if not per_head:
+        w = _rng(cfg.seed, _S_PO).standard_normal((d, d)) / np.sqrt(d)
+    else:
+        H = cfg.H if H is None else H
+        w = np.stack([_rng(cfg.seed, _S_PO, 0, h + 1).standard_normal((d, d)) / np.sqrt(d)
+                      for h in range(H)])
+    return torch.from_numpy(w.astype(np.float32))
