@@ -16,6 +16,11 @@ between steps (a further pass, outside the timed region), and the float64 CPU
 oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 3] [--no-cpu]
+                    [--variant sla2|sla1] [--phi softmax|elu1]
+
+--variant sla1 times the SLA formulation instead (sla1_forward: no router, the
+branches fused as O = O_s + Proj(O_l) with a seeded d x d Proj), --phi elu1
+the ELU+1 feature map of the linear branch.
 """
 
 import argparse
@@ -50,10 +55,12 @@ def sparse_tile_flops(B, H, Nb, n_h, d):
     return 4.0 * B * H * Nb * n_h * 64 * 64 * d
 
 
-def sparse_kernel_flops(B, H, Nb, n_h, d):
+def sparse_kernel_flops(B, H, Nb, n_h, d, proj=False):
     """Algorithmic flops of the sparse-attention kernel per launch: the critical
-    tiles plus the linear-branch output phi(Q_i) [H_i | Z_i] of every query block."""
-    return sparse_tile_flops(B, H, Nb, n_h, d) + 2.0 * B * H * Nb * 64 * d * (d + 1)
+    tiles plus the linear-branch output phi(Q_i) [H_i | Z_i] of every query block,
+    and with proj (the SLA fusion) the d x d output map applied to O_l."""
+    f = sparse_tile_flops(B, H, Nb, n_h, d) + 2.0 * B * H * Nb * 64 * d * (d + 1)
+    return f + (2.0 * B * H * Nb * 64 * d * d if proj else 0.0)
 
 
 def pages_flop_fraction(kh, N, d):
@@ -119,10 +126,11 @@ def _traffic_from_profile(kernel, workload, source):
         return None
 
 
-def cpu_baseline(cfg, x, seconds):
+def cpu_baseline(cfg, x, seconds, phi="softmax", proj_o=None):
     """The float64 oracle as it stands, on one head: its mask (router, pooling,
     scores, ranking) and the outputs of evenly spaced query blocks until about
-    `seconds` of wall time; reported as dense-equivalent TFLOP/s of the sample."""
+    `seconds` of wall time; reported as dense-equivalent TFLOP/s of the sample.
+    With proj_o, the SLA formulation (no router, O = O_s + O_l proj_o)."""
     import threadpoolctl
     import oracle as orc
 
@@ -131,14 +139,16 @@ def cpu_baseline(cfg, x, seconds):
     info = threadpoolctl.threadpool_info()
     cores = max([p.get("num_threads", 1) for p in info] or [1])
     order = list(range(0, Nb, 7)) + [i for i in range(Nb) if i % 7]
+    pq, pk = (None, None) if proj_o is not None else (x.proj_q, x.proj_k)
+    po = None if proj_o is None else proj_o[0] if proj_o.dim() == 3 else proj_o
     t0 = time.perf_counter()
-    ref = orc.forward(x.q[:1, :1], x.k[:1, :1], x.v[:1, :1], x.proj_q, x.proj_k, x.alpha[:1],
-                      x.kh, x.kl, compute_outputs=False)
+    ref = orc.forward(x.q[:1, :1], x.k[:1, :1], x.v[:1, :1], pq, pk, x.alpha[:1],
+                      x.kh, x.kl, compute_outputs=False, feature=phi, proj_o=po)
     mask = ref.mask
     done = []
     for i in order:
-        orc.forward(x.q[:1, :1], x.k[:1, :1], x.v[:1, :1], x.proj_q, x.proj_k, x.alpha[:1],
-                    x.kh, x.kl, mask_in=mask, query_blocks={(0, 0): [i]})
+        orc.forward(x.q[:1, :1], x.k[:1, :1], x.v[:1, :1], pq, pk, x.alpha[:1],
+                    x.kh, x.kl, mask_in=mask, query_blocks={(0, 0): [i]}, feature=phi, proj_o=po)
         done.append(i)
         if time.perf_counter() - t0 > seconds and len(done) >= 4:
             break
@@ -191,6 +201,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--variant", choices=["sla2", "sla1"], default="sla2",
+                    help="sla2: router + alpha mix (sla_forward); sla1: no router, "
+                         "O = O_s + Proj(O_l) (sla1_forward)")
+    ap.add_argument("--phi", choices=["softmax", "elu1"], default="softmax",
+                    help="feature map of the linear branch")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="MiB written between the flushed per-step timings (0: no flushed pass)")
@@ -206,18 +221,28 @@ def main():
 
     import torch
     import sparse_linear_attention_block_amd as sla
-    from workloads import CONFIGS, make_inputs
+    from workloads import CONFIGS, make_inputs, make_proj_o
 
     cfg = CONFIGS[args.config]
+    sla1 = args.variant == "sla1"
+    if cfg.quant and sla1:
+        print("the SLA formulation is built without the 8-bit sparse branch", file=sys.stderr)
+        sys.exit(2)
     if cfg.quant:
         print("note: the 8-bit sparse branch is timed with quant=True", file=sys.stderr)
+    # the name the profiles of this workload are filed under
+    wl_name = cfg.name + ("_sla1" if sla1 else "") + ("_elu1" if args.phi == "elu1" else "")
     t0 = time.time()
     x = make_inputs(cfg)
     print(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     pq, pk, al = x.proj_q.to(dev), x.proj_k.to(dev), x.alpha.to(dev)
-    plan = sla.Plan(q, k, v, pq, pk, al, x.kh, x.kl, quant=cfg.quant)
+    proj_o = make_proj_o(cfg) if sla1 else None
+    if sla1:
+        plan = sla.Plan(q, k, v, None, None, None, x.kh, x.kl, phi=args.phi, proj_o=proj_o.to(dev))
+    else:
+        plan = sla.Plan(q, k, v, pq, pk, al, x.kh, x.kl, quant=cfg.quant, phi=args.phi)
     B, H, N, d, Nb = plan.dims
     _, n_h, n_l = sla.block_counts(N, x.kh, x.kl, B=B, H=H, d=d, dtype=cfg.dtype)
     if args.hbm_calib_mib > 0:
@@ -264,14 +289,14 @@ def main():
 
     F = dense_flops(B, H, N, d)
     value = F / (ms * 1e-3) / 1e12
-    k5_flops = sparse_kernel_flops(B, H, Nb, n_h, d)
+    k5_flops = sparse_kernel_flops(B, H, Nb, n_h, d, proj=sla1)
     achieved = k5_flops / (k5_ms * 1e-3) / 1e12
     peak = PEAK_8BIT_TFLOPS if cfg.quant else PEAK_BF16_TFLOPS
     k5_src = "k_sparse_q8.hip" if cfg.quant else KERNEL_SOURCES["sparse_attn_mix"]
-    traffic = _traffic_from_profile("sparse_attn_mix", cfg.name, k5_src)
+    traffic = _traffic_from_profile("sparse_attn_mix", wl_name, k5_src)
     kb = kernel_bytes(B, H, N, d, Nb, n_h, cfg.quant)
     gbs = {name: kb[name] / (per_kernel[name] * 1e-3) / 1e9 for name in KERNELS}
-    print(f"[bench] {cfg.name}: {ms:.3f} ms/step, per kernel (ms) " +
+    print(f"[bench] {wl_name}: {ms:.3f} ms/step, per kernel (ms) " +
           ", ".join(f"{n}={t:.4f}" for n, t in per_kernel.items()), file=sys.stderr, flush=True)
 
     line = {
@@ -289,9 +314,12 @@ def main():
                   else "bf16" if cfg.dtype == "bf16" else "f32"),
         "data": "synthetic: seeded video-DiT-shaped Q/K/V (3-axis sin/cos position field + noise), "
                 "calibrated to the pages' attention-weight shares",
-        "config": {"workload": cfg.name, "B": B, "H": H, "N": N, "d": d, "kh": x.kh, "kl": x.kl,
+        "config": {"workload": wl_name, "B": B, "H": H, "N": N, "d": d, "kh": x.kh, "kl": x.kl,
                    "Nb": Nb, "n_h": n_h, "n_l": n_l, "quant": cfg.quant,
-                   "sparsity": round(1 - n_h / Nb, 4)},
+                   "sparsity": round(1 - n_h / Nb, 4),
+                   "formulation": ("SLA: no router, O = O_s + Proj(O_l)" if sla1
+                                   else "SLA2: learned router, O = alpha O_s + (1 - alpha) O_l"),
+                   "phi": args.phi},
         "roofline": {"kernel": "sparse_attn_mix", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "flops_per_launch": k5_flops, "ms_per_launch": round(k5_ms, 5)},
@@ -300,7 +328,7 @@ def main():
         "kernels_hbm_gbs": {n: round(t, 1) for n, t in gbs.items()},
     }
     if not args.no_cpu:
-        cb = cpu_baseline(cfg, x, args.cpu_seconds)
+        cb = cpu_baseline(cfg, x, args.cpu_seconds, args.phi, proj_o)
         cb["value"] = round(cb["value"], 5)
         cb["seconds"] = round(cb["seconds"], 2)
         line["cpu_baseline"] = cb

@@ -81,12 +81,12 @@ struct FaCfg {
 // of a critical tile are taken 32 at a time (a step), so that each product is a
 // full-rate 16x16x32 MFMA (P.V contracts over the step's 32 keys), the step
 // buffers are 16 KB and three workgroups fit on a CU.
-template <int D, bool PROJ>
+template <int D, bool PROJ, bool ELU>
 __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const int8_t* __restrict__ mask,
     const uint16_t* __restrict__ Hx, const float* __restrict__ alpha,
-    const uint16_t* __restrict__ wo, int wo_hs, int elu, uint16_t* __restrict__ O,
+    const uint16_t* __restrict__ wo, int wo_hs, uint16_t* __restrict__ O,
     float* __restrict__ dbg_os, float* __restrict__ dbg_ol, int H, int N, int Nb) {
   using Cf = FaCfg<D>;
   constexpr int C = Cf::C, HT = Cf::HT, INSTR = Cf::INSTR, NN = Cf::NN;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     }
   }
   uint4 fq[KSTEPS];
-  if (elu) {  // uniform: phi = elu + 1, elementwise
+  if constexpr (ELU) {  // phi = elu + 1, elementwise
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       uint32_t w4[4];
@@ -585,21 +585,25 @@ __global__ __launch_bounds__(256) void k_pack_proj(const float* __restrict__ W,
   }
 }
 
-template <int D>
+template <int D, bool PROJ, bool ELU>
 hipError_t launch_bf16(const Dims& D_, const void* Q, const void* K, const int8_t* mask,
-                       const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
-                       float* dbg_ol, hipStream_t s) {
-  const int T = D_.BH * D_.Nb;
-  const int elu = D_.elu ? 1 : 0;
-  if (proj)
-    hipLaunchKernelGGL((k_sparse_bf16<D, true>), dim3(T), dim3(256), 0, s, (const uint16_t*)Q,
-                       (const uint16_t*)K, w.vt, mask, (const uint16_t*)w.Hx, alpha, w.wo,
-                       D_.proj_hs, elu, (uint16_t*)O, dbg_os, dbg_ol, D_.H, D_.N, D_.Nb);
-  else
-    hipLaunchKernelGGL((k_sparse_bf16<D, false>), dim3(T), dim3(256), 0, s, (const uint16_t*)Q,
-                       (const uint16_t*)K, w.vt, mask, (const uint16_t*)w.Hx, alpha, w.wo,
-                       D_.proj_hs, elu, (uint16_t*)O, dbg_os, dbg_ol, D_.H, D_.N, D_.Nb);
+                       const float* alpha, const Work& w, void* O, float* dbg_os, float* dbg_ol,
+                       hipStream_t s) {
+  hipLaunchKernelGGL((k_sparse_bf16<D, PROJ, ELU>), dim3(D_.BH * D_.Nb), dim3(256), 0, s,
+                     (const uint16_t*)Q, (const uint16_t*)K, w.vt, mask, (const uint16_t*)w.Hx, alpha,
+                     w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, D_.H, D_.N, D_.Nb);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_d(const Dims& D_, const void* Q, const void* K, const int8_t* mask,
+                         const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
+                         float* dbg_ol, hipStream_t s) {
+  if (proj)
+    return D_.elu ? launch_bf16<D, true, true>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s)
+                  : launch_bf16<D, true, false>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s);
+  return D_.elu ? launch_bf16<D, false, true>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s)
+                : launch_bf16<D, false, false>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s);
 }
 
 }  // namespace
@@ -619,8 +623,8 @@ hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const int8
                          float* dbg_os, float* dbg_ol, hipStream_t s) {
   // the f32 path reads V directly; vt is not formed
   if (!D.bf16) return hipErrorInvalidValue;
-  if (D.d == 128) return launch_bf16<128>(D, Q, K, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
-  return launch_bf16<64>(D, Q, K, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
+  if (D.d == 128) return launch_bf16_d<128>(D, Q, K, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
+  return launch_bf16_d<64>(D, Q, K, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
 }
 
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,

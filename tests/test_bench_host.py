@@ -39,3 +39,15 @@ def test_multi_gpu_request_exits_with_message():
     r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"),
                         "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_sla1_roofline_counts_the_output_map():
+    B, H, Nb, d = 1, 12, 512, 128
+    extra = bench.sparse_kernel_flops(B, H, Nb, 25, d, proj=True) - bench.sparse_kernel_flops(B, H, Nb, 25, d)
+    assert extra == 2.0 * B * H * Nb * 64 * d * d  # one d x d map per (tile-rounded) query token
+
+
+def test_sla1_with_the_8bit_branch_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"),
+                        "--config", "5", "--variant", "sla1"], capture_output=True, text=True)
+    assert r.returncode == 2 and "8-bit" in r.stderr
