@@ -267,3 +267,71 @@ def token_rows(rows: Iterable[int], N: int) -> np.ndarray:
     """Token indices covered by the given query blocks, in block order."""
     out = [np.arange(i * BLOCK, min((i + 1) * BLOCK, N)) for i in rows]
     return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)
+
+
+def compressed_map(logits: np.ndarray) -> np.ndarray:
+    """Pc = row softmax of the compressed logits (Eq. 1), float64."""
+    s = np.asarray(logits, dtype=np.float64)
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    # 1 / (1 + e^-x) written so that neither branch overflows
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def soft_topk(logits, k: float, tau: float):
+    """SoftTop-k of the compressed attention map, the differentiable stand-in
+    for Eq. 2's top-k in SLA2's first training stage (SLA2 article, the
+    two-stage training paragraphs, stage 1; SLA2 cross-paper synthesis, §3,
+    the item on the cost of the binary search for lambda_i).
+
+    For every row i of Pc = softmax(logits): M[i, j] = sigmoid((Pc[i, j] -
+    lambda_i) / tau), with lambda_i the value at which the row sums to k,
+    found by binary search (the row sum falls strictly from the row length to
+    0 as lambda rises). Readings: the sigmoid acts on Pc, the quantity the
+    hard top-k ranks; k is a count in [0, row length] (the hard top-k's n_h
+    makes tau -> 0 recover that mask); k = 0 gives zeros with lambda = +inf,
+    k = row length ones with lambda = -inf.
+
+    logits: [..., C] float64. Returns (M [..., C] float64, lambda [...] float64).
+    The search halves a bracket on which the row sum crosses k until its
+    midpoint no longer moves in float64.
+    """
+    if not tau > 0:
+        raise ValueError("tau must be positive")
+    P = compressed_map(logits)
+    C = P.shape[-1]
+    if not 0.0 <= k <= C:
+        raise ValueError("k must lie in [0, row length]")
+    rows = P.reshape(-1, C)
+    M = np.empty_like(rows)
+    lam = np.empty(rows.shape[0])
+    for r in range(rows.shape[0]):
+        p = rows[r]
+        if k == 0:
+            M[r], lam[r] = 0.0, np.inf
+            continue
+        if k == C:
+            M[r], lam[r] = 1.0, -np.inf
+            continue
+        # at lo every term is above k / C, at hi every term is below k / C
+        lo = p.min() - 60.0 * tau
+        hi = p.max() + 60.0 * tau
+        while True:
+            mid = 0.5 * (lo + hi)
+            if mid <= lo or mid >= hi:
+                break
+            if _sigmoid((p - mid) / tau).sum() > k:
+                lo = mid
+            else:
+                hi = mid
+        lam[r] = 0.5 * (lo + hi)
+        M[r] = _sigmoid((p - lam[r]) / tau)
+    return M.reshape(P.shape), lam.reshape(P.shape[:-1])
