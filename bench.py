@@ -20,7 +20,9 @@ oracle timed on a bounded sample of the same workload.
 
 --variant sla1 times the SLA formulation instead (sla1_forward: no router, the
 branches fused as O = O_s + Proj(O_l) with a seeded d x d Proj), --phi elu1
-the ELU+1 feature map of the linear branch.
+the ELU+1 feature map of the linear branch. --op soft_topk times SoftTop-k
+(sla_soft_topk) on the compressed logits of the workload instead of the
+forward pass, and prints that op's own line.
 """
 
 import argparse
@@ -164,6 +166,104 @@ def cpu_baseline(cfg, x, seconds, phi="softmax", proj_o=None):
             "seconds": dt}
 
 
+# SoftTop-k's search loop costs, per element and halving, 4 full-rate VALU ops
+# (subtract, scale, add, accumulate; 64 lanes per CU per clock) and 2
+# transcendental ones (exp2, reciprocal; 32 lanes per CU per clock on gfx950,
+# twice CDNA3's rate): 4/64 + 2/64 * 2 = 0.125 CU-clocks, so the chip's 256
+# CUs at 2.4 GHz evaluate at most 256 * 2.4e9 / 0.125 = 4.92e12 sigmoids per
+# second.
+PEAK_SIGMOID_PER_S = 256 * 2.4e9 / (4 / 64 + 2 / 32)
+
+
+def soft_topk_halvings(P, lam, tau):
+    """Halvings the float32 search makes per row: the bracket [min Pc - 60 tau,
+    max Pc + 60 tau] halved towards the returned threshold until its float32
+    midpoint stops moving."""
+    lo = (P.min(axis=-1) - 60.0 * tau).astype(np.float32)
+    hi = (P.max(axis=-1) + 60.0 * tau).astype(np.float32)
+    lam = lam.astype(np.float32)
+    n = np.zeros(lo.shape, dtype=np.int64)
+    for _ in range(256):
+        mid = np.float32(0.5) * (lo + hi)
+        act = (mid > lo) & (mid < hi)
+        if not act.any():
+            break
+        n += act
+        up = act & (mid < lam)
+        lo = np.where(up, mid, lo)
+        hi = np.where(act & ~up, mid, hi)
+    return n
+
+
+def bench_soft_topk(args, cfg, x, torch, sla):
+    """SoftTop-k over the workload's compressed logits (B*H*Nb rows of Nb),
+    budget n_h, temperature --tau (Pc units); one JSON line."""
+    import oracle as orc
+    dev = torch.device("cuda:0")
+    _, _, dbg = sla.forward(x.q.to(dev), x.k.to(dev), x.v.to(dev), x.proj_q.to(dev), x.proj_k.to(dev),
+                            x.alpha.to(dev), x.kh, x.kl, debug=True)
+    lg = dbg["logits"]
+    B, H, Nb = lg.shape[0], lg.shape[1], lg.shape[2]
+    rows = B * H * Nb
+    n_h = sla.block_counts(x.N, x.kh, x.kl, B=B, H=H, d=x.d, dtype=cfg.dtype)[1]
+    out = torch.empty(lg.shape, dtype=torch.float32, device=dev)
+    lam = torch.empty(lg.shape[:-1], dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        sla.soft_topk(lg, n_h, args.tau, out=out, lam=lam)
+    torch.cuda.synchronize()
+    hev = sla.HipEvents()
+    evs = hev.create(2 * args.steps)
+    stream = torch.cuda.current_stream().cuda_stream
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(args.steps):
+        hev.record(evs[2 * s], stream)
+        sla.soft_topk(lg, n_h, args.tau, out=out, lam=lam)
+        hev.record(evs[2 * s + 1], stream)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    k_ms = float(np.mean([hev.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for s in range(args.steps)]))
+    hev.destroy(evs)
+    lg_h = lg.cpu().numpy()
+    P = orc.compressed_map(lg_h)
+    halv = soft_topk_halvings(P, lam.cpu().numpy(), args.tau)
+    evals = float(((halv + 1) * Nb).sum())  # every halving plus the output pass
+    achieved = evals / (k_ms * 1e-3)
+    line = {
+        "metric": "SoftTop-k of the compressed attention map, rows per second",
+        "value": round(rows / (ms * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 (float64 logits in)",
+        "data": "the float64 compressed logits sla_forward computes for the seeded workload",
+        "config": {"workload": cfg.name + "_soft_topk", "rows": rows, "cols": Nb, "k": n_h,
+                   "tau": args.tau, "mean_halvings": round(float(halv.mean()), 2)},
+        "roofline": {"kernel": "k_soft_topk", "bound": "alu", "achieved": round(achieved / 1e12, 4),
+                     "peak": round(PEAK_SIGMOID_PER_S / 1e12, 4), "unit": "T sigmoid evaluations/s",
+                     "frac": round(achieved / PEAK_SIGMOID_PER_S, 4), "traffic": None,
+                     "ms_per_launch": round(k_ms, 5),
+                     "hbm_bytes_per_launch": rows * Nb * 12 + rows * 4},
+    }
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < args.cpu_seconds and done < rows:
+            orc.soft_topk(lg_h.reshape(rows, Nb)[done:done + 64], n_h, args.tau)
+            done += 64
+        dt = time.perf_counter() - t0
+        import threadpoolctl
+        cores = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+        line["cpu_baseline"] = {"value": round(done / dt, 1), "unit": "rows/s", "cores": int(cores),
+                                "kind": "oracle",
+                                "sample": f"the float64 oracle on the first {done} of {rows} rows "
+                                          f"in {dt:.1f} s"}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def step_distribution(torch, plan, hev, steps, flush_mib):
     """Per-step times after the timed region: each step bracketed by two
     fence-free HIP events on its stream. The unflushed steps run back to back;
@@ -206,6 +306,9 @@ def main():
                          "O = O_s + Proj(O_l) (sla1_forward)")
     ap.add_argument("--phi", choices=["softmax", "elu1"], default="softmax",
                     help="feature map of the linear branch")
+    ap.add_argument("--op", choices=["forward", "soft_topk"], default="forward",
+                    help="forward: the whole forward pass; soft_topk: SoftTop-k on its logits")
+    ap.add_argument("--tau", type=float, default=1e-3, help="SoftTop-k temperature (Pc units)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="MiB written between the flushed per-step timings (0: no flushed pass)")
@@ -235,6 +338,9 @@ def main():
     t0 = time.time()
     x = make_inputs(cfg)
     print(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    if args.op == "soft_topk":
+        bench_soft_topk(args, cfg, x, torch, sla)
+        return
     dev = torch.device("cuda:0")
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     pq, pk, al = x.proj_q.to(dev), x.proj_k.to(dev), x.alpha.to(dev)

@@ -184,6 +184,28 @@ int sla1_forward_debug(const sla_problem* p,
                        void* workspace, size_t workspace_bytes,
                        void* stream, const sla_debug* dbg);
 
+/* SoftTop-k of the compressed attention map, the differentiable stand-in for
+ * Eq. 2's top-k in SLA2's first training stage (SLA2 article, the two-stage
+ * training paragraphs, stage 1: a sigmoid with a temperature; SLA2
+ * cross-paper synthesis, section 3: a per-row threshold found by binary
+ * search so that each row meets its budget). For each row of logits s:
+ *   Pc = softmax(s),  out[j] = sigmoid((Pc[j] - lambda) / tau),
+ *   lambda such that sum_j out[j] = k.
+ *  logits  device float64 [rows, cols], row-major (for instance the logits
+ *          of sla_forward_debug: rows = B*H*Nb, cols = Nb).
+ *  k       the row budget in [0, cols]; n_h makes tau -> 0 the critical set.
+ *  tau     temperature in Pc units, in [1e-20, 1e20].
+ *  out     device float32 [rows, cols].
+ *  lambda  device float32 [rows] or NULL: the thresholds (+inf where k = 0,
+ *          -inf where k = cols, whose rows are all 0 or all 1).
+ * Pc and the search are float32 (max and differences of the logits in
+ * float64); the search halves a bracket on which the row sum crosses k until
+ * its midpoint stops moving. Returns SLA_OK once enqueued; SLA_ERR_ARG (NULL
+ * or misaligned pointers, rows < 1, cols outside [1, 4096], k or tau out of
+ * range) before any work; SLA_ERR_HIP if the launch fails. */
+int sla_soft_topk(const double* logits, int32_t rows, int32_t cols, double k, double tau,
+                  float* out, float* lambda, void* stream);
+
 /* Static text of a status code. */
 const char* sla_status_str(int status);
 

@@ -5,14 +5,15 @@ router projection + block mean pooling, compressed scores + three-way block
 classification, per-key-block linear state h_j / z_j, the marginal-block
 sums (one MFMA product per head), and block-sparse online-softmax attention
 over the critical blocks with the linear-branch output and the SLA2 mix (or
-the SLA output fusion O = O_s + Proj(O_l)) fused into its epilogue. This
-package is the argument-marshalling binding.
+the SLA output fusion O = O_s + Proj(O_l)) fused into its epilogue; and the
+SoftTop-k relaxation of the block selection. This package is the
+argument-marshalling binding.
 """
 
 from ._binding import (  # noqa: F401
     LIB_PATH, HipEvents, Plan, SLAError, block_counts, forward, forward_sla1, load_library,
-    make_problem, workspace_bytes,
+    make_problem, soft_topk, workspace_bytes,
 )
 
-__all__ = ["forward", "forward_sla1", "Plan", "HipEvents", "block_counts", "workspace_bytes", "load_library",
+__all__ = ["forward", "forward_sla1", "soft_topk", "Plan", "HipEvents", "block_counts", "workspace_bytes", "load_library",
            "make_problem", "SLAError", "LIB_PATH"]

@@ -68,6 +68,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sla1_forward.restype = ctypes.c_int
     lib.sla1_forward_debug.argtypes = _FWD_ARGS + [ctypes.POINTER(Debug)]
     lib.sla1_forward_debug.restype = ctypes.c_int
+    lib.sla_soft_topk.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                  ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sla_soft_topk.restype = ctypes.c_int
     lib.sla_status_str.argtypes = [ctypes.c_int]
     lib.sla_status_str.restype = ctypes.c_char_p
     lib.sla_last_error.argtypes = []
@@ -224,6 +227,29 @@ def forward_sla1(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj_o: torc
         raise ValueError("proj_o is required")
     return _run(q, k, v, proj_q, proj_k, None, proj_o, kh, kl, mask_in, False, out, mask_out,
                 workspace, debug, phi)
+
+
+def soft_topk(logits: torch.Tensor, k: float, tau: float, *, out: Optional[torch.Tensor] = None,
+              lam: Optional[torch.Tensor] = None):
+    """SoftTop-k on the GPU (sla_soft_topk): for every row of the float64 device
+    tensor `logits` [..., C], Pc = softmax(row) and M = sigmoid((Pc - lambda) / tau)
+    with lambda such that the row sums to k. Returns (M float32 [..., C],
+    lambda float32 [...])."""
+    lib = load_library()
+    if logits.dtype != torch.float64 or not logits.is_cuda or logits.dim() < 1:
+        raise ValueError("logits must be a float64 device tensor")
+    logits = logits.contiguous()
+    C = logits.shape[-1]
+    rows = logits.numel() // C if C else 0
+    if out is None:
+        out = torch.empty(logits.shape, dtype=torch.float32, device=logits.device)
+    if lam is None:
+        lam = torch.empty(logits.shape[:-1], dtype=torch.float32, device=logits.device)
+    with torch.cuda.device(logits.device):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(logits.device).cuda_stream)
+        rc = lib.sla_soft_topk(_ptr(logits), rows, C, float(k), float(tau), _ptr(out), _ptr(lam), stream)
+    _check(rc)
+    return out, lam
 
 
 class Plan:

@@ -299,4 +299,21 @@ int sla1_forward(const sla_problem* p, const void* Q, const void* K, const void*
                             workspace_bytes, stream, nullptr);
 }
 
+int sla_soft_topk(const double* logits, int32_t rows, int32_t cols, double k, double tau, float* out,
+                  float* lambda, void* stream) {
+  if (!logits || !out) return fail(SLA_ERR_ARG, "logits and out must not be NULL");
+  if (!aligned(logits, 8) || !aligned(out, 4) || (lambda && !aligned(lambda, 4)))
+    return fail(SLA_ERR_ARG, "logits must be 8-byte aligned, out and lambda 4-byte aligned");
+  if (rows < 1 || cols < 1 || cols > sla::kMaxNb)
+    return fail(SLA_ERR_ARG, "rows must be >= 1 and cols in [1, %d] (got %d, %d)", sla::kMaxNb, rows, cols);
+  if (!(k >= 0.0 && k <= (double)cols)) return fail(SLA_ERR_ARG, "k must lie in [0, cols] (got %g)", k);
+  if (!(tau >= 1e-20 && tau <= 1e20)) return fail(SLA_ERR_ARG, "tau must lie in [1e-20, 1e20] (got %g)", tau);
+  (void)hipGetLastError();  // a stale error from earlier work is not ours to report
+  const hipError_t e = sla::launch_soft_topk(logits, rows, cols, (float)k, (float)tau, out, lambda,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SLA_ERR_HIP, "soft top-k kernel: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return SLA_OK;
+}
+
 }  // extern "C"

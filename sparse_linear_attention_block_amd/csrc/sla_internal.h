@@ -74,4 +74,8 @@ hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const 
                              const int8_t* mask, const float* alpha, const float* proj_o,
                              const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
 
+// SoftTop-k rows of a float64 logit matrix (k_soft_topk.hip); cols <= 4096
+hipError_t launch_soft_topk(const double* logits, int rows, int cols, float k, float tau, float* out,
+                            float* lambda, hipStream_t s);
+
 }  // namespace sla

@@ -151,3 +151,19 @@ def test_feature_map_does_not_change_sizes():
     assert sla.workspace_bytes(a) == sla.workspace_bytes(b)
     with pytest.raises(ValueError):
         sla.make_problem(1, 1, 64, 64, "bf16", 0.5, 0.0, phi="relu")
+
+
+def _stk(lg=0x10000, rows=4, cols=64, k=3.0, tau=1e-3, out=0x10000, lam=None):
+    lib = sla.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.sla_soft_topk(vp(lg), rows, cols, k, tau, vp(out), vp(lam), None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(lg=None), dict(out=None), dict(lg=0x10004), dict(out=0x10002), dict(lam=0x10001),
+    dict(rows=0), dict(cols=0), dict(cols=4097), dict(k=-1.0), dict(k=64.5),
+    dict(k=float("nan")), dict(tau=0.0), dict(tau=-1.0), dict(tau=float("inf")),
+])
+def test_soft_topk_argument_errors(kw):
+    assert _stk(**kw) == B.SLA_ERR_ARG
+    assert sla.load_library().sla_last_error()

@@ -51,3 +51,14 @@ def test_sla1_with_the_8bit_branch_exits_with_message():
     r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"),
                         "--config", "5", "--variant", "sla1"], capture_output=True, text=True)
     assert r.returncode == 2 and "8-bit" in r.stderr
+
+
+def test_soft_topk_halvings_and_peak():
+    import numpy as np
+    import oracle as orc
+    lg = np.random.default_rng(3).standard_normal((20, 512)) * 3
+    M, lam = orc.soft_topk(lg, 25, 1e-3)
+    h = bench.soft_topk_halvings(orc.compressed_map(lg), lam, 1e-3)
+    # a float32 bracket ~0.12 wide halved to the spacing of floats near lambda
+    assert ((h >= 20) & (h <= 40)).all()
+    assert abs(bench.PEAK_SIGMOID_PER_S - 4.9152e12) < 1e9
