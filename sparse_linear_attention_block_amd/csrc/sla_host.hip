@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/sla.h: argument validation,
-// block counts, workspace carving and the launch order of the five kernels on
-// the caller's stream. No device memory is allocated here and no call
+// block counts, workspace carving, the launch order of the forward pass's
+// kernels on the caller's stream (SLA2 and SLA formulations), and the
+// SoftTop-k entry point. No device memory is allocated here and no call
 // synchronises.
 #include <math.h>
 #include <stdarg.h>
