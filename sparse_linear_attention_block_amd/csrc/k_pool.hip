@@ -161,11 +161,8 @@ hipError_t launch_pool_sum(const Dims& D, const void* Q, const void* K, double* 
   return hipGetLastError();
 }
 
-hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const float* proj_q,
-                            const float* proj_k, int proj_hs, double* raw, double* pq, double* pk,
-                            hipStream_t s) {
-  hipError_t e = launch_pool_sum(D, Q, K, raw, s);
-  if (e != hipSuccess) return e;
+hipError_t launch_pool_proj(const Dims& D, const float* proj_q, const float* proj_k, int proj_hs,
+                            const double* raw, double* pq, double* pk, hipStream_t s) {
   dim3 g2((D.Nb + kPR - 1) / kPR, D.BH, 2);
   if (D.d == 128)
     hipLaunchKernelGGL(k_pool_proj<128>, g2, dim3(256), 0, s, raw, proj_q, proj_k, proj_hs, pq, pk,

@@ -216,14 +216,12 @@ int run_forward(const sla_problem* p, const void* Q, const void* K, const void* 
     // without a router the block means themselves are compared
     const double* pq = w.pooled_raw;
     const double* pk = w.pooled_raw + (size_t)D.BH * D.Nb * D.d;
+    SLA_LAUNCH(sla::launch_pool_sum(D, Q, K, w.pooled_raw, s), "pool kernel");
     if (proj_q) {
-      SLA_LAUNCH(sla::launch_pool_proj(D, Q, K, proj_q, proj_k, proj_hs, w.pooled_raw, w.pooled_q,
-                                       w.pooled_k, s),
+      SLA_LAUNCH(sla::launch_pool_proj(D, proj_q, proj_k, proj_hs, w.pooled_raw, w.pooled_q, w.pooled_k, s),
                  "pool/proj kernel");
       pq = w.pooled_q;
       pk = w.pooled_k;
-    } else {
-      SLA_LAUNCH(sla::launch_pool_sum(D, Q, K, w.pooled_raw, s), "pool kernel");
     }
     SLA_LAUNCH(mark(1), "event record");
     SLA_LAUNCH(sla::launch_select(D, pq, pk, mask_out, (dbg && dbg->logits) ? dbg->logits : w.logits, s),

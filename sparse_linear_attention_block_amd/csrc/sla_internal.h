@@ -53,9 +53,9 @@ size_t carve(const Dims& D, void* base, Work* w);  // returns bytes needed (base
 // ---- launchers (each enqueues one or more kernels on `s`, returns hipError_t)
 hipError_t launch_pool_sum(const Dims& D, const void* Q, const void* K, double* raw,
                            hipStream_t s);
-hipError_t launch_pool_proj(const Dims& D, const void* Q, const void* K, const float* proj_q,
-                            const float* proj_k, int proj_hs, double* raw, double* pq, double* pk,
-                            hipStream_t s);
+// the router projection of the block means launch_pool_sum wrote to raw
+hipError_t launch_pool_proj(const Dims& D, const float* proj_q, const float* proj_k, int proj_hs,
+                            const double* raw, double* pq, double* pk, hipStream_t s);
 hipError_t launch_qk_mean(const Dims& D, const Work& w, hipStream_t s);
 hipError_t launch_sparse_q8(const Dims& D, const void* Q, const int8_t* mask, const float* alpha,
                             const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
