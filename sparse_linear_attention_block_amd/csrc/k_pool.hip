@@ -13,8 +13,9 @@
 //   workgroup sums 2 blocks with every 16-byte load of a thread issued before
 //   the first add; the means go to raw[z][bh][block][d] (the 8-bit sparse
 //   branch also takes its per-head channel means of Q and K from them).
-// k_pool_proj: grid (ceil(Nb/16), B*H, 2); float64 MFMA 16x16x4 against the
-//   head's router matrix (f32 [in][out]), 16 block means per workgroup.
+// k_pool_proj: grid (ceil(Nb/64), B*H, 2 * d/64); float64 MFMA 16x16x4
+//   against the head's router matrix (f32 [in][out]), 64 block means and a
+//   64-column slice of the matrix (staged in LDS) per workgroup.
 #include "sla_internal.h"
 #include "dev_common.h"
 
@@ -22,7 +23,6 @@ namespace sla {
 namespace {
 
 constexpr int kG = 2;      // blocks per summing workgroup
-constexpr int kPR = 16;    // block means per projecting workgroup
 
 template <typename T>
 __device__ __forceinline__ void add_chunk(const uint4& v, double* acc);
@@ -96,11 +96,13 @@ __global__ __launch_bounds__(256) void k_pool_sum(const T* __restrict__ Q, const
   }
 }
 
-// pooled[row][col] = sum_k raw[row][k] * P[k][col] on float64 MFMA 16x16x4:
-// a workgroup owns 16 consecutive block means, wave w the column tiles w and
-// w + 4 (d = 128) or w (d = 64). Every operand goes straight from global memory to registers, all
-// loads issued before the first product (the router matrix is f32 [in][out],
-// widened to f64 per operand).
+// pooled[row][col] = sum_k raw[row][k] * P[k][col] on float64 MFMA 16x16x4.
+// A workgroup owns 64 block means (wave w rows 16w .. 16w+15) and 64 output
+// columns: the router matrix's 64-column slice (f32, all D rows) is staged once
+// in LDS with its rows padded to 80 floats, so the four k groups of a B
+// fragment (rows 4ks + g) fall 16 banks apart; each wave reads its own means
+// straight from global memory (all loads issued before the first product)
+// and runs four independent MFMA chains, one per 16-column tile.
 template <int D>
 __global__ __launch_bounds__(256) void k_pool_proj(const double* __restrict__ raw,
                                                    const float* __restrict__ proj_q,
@@ -108,37 +110,44 @@ __global__ __launch_bounds__(256) void k_pool_proj(const double* __restrict__ ra
                                                    double* __restrict__ pq, double* __restrict__ pk,
                                                    int H, int Nb, int BH) {
   constexpr int KS = D / 4;        // k steps
-  constexpr int CPW = D / 64;      // column tiles per wave (8 or 4 tiles over 4 waves)
+  constexpr int CW = 64;           // output columns per workgroup
+  constexpr int PS = CW + 16;      // LDS row stride of the slice (floats)
+  __shared__ float ps[D * PS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int z = blockIdx.z, bh = blockIdx.y;
+  const int z = blockIdx.z & 1, c0 = (blockIdx.z >> 1) * CW, bh = blockIdx.y;
   const float* Pg = (z ? proj_k : proj_q) + (size_t)(bh % H) * proj_hs;
-  const int r0 = blockIdx.x * kPR;
+  // the slice: D rows x 64 columns as float4, 16 per row
+  for (int x = tid; x < D * CW / 4; x += 256) {
+    const int r = x / (CW / 4), c4 = x % (CW / 4);
+    *reinterpret_cast<float4*>(&ps[r * PS + 4 * c4]) =
+        *reinterpret_cast<const float4*>(Pg + (size_t)r * D + c0 + 4 * c4);
+  }
+  const int r0 = blockIdx.x * 64 + 16 * wave;
   const int row = min(r0 + l16, Nb - 1);           // rows past Nb are never stored
   const double* src = raw + (((size_t)z * BH + bh) * Nb + row) * D;
   double a[KS];                                    // A[row l16][k = 4ks + g]
-  float b[CPW][KS];                                // B[k = 4ks + g][16 ct + l16]
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) a[ks] = src[4 * ks + g];
-#pragma unroll
-  for (int u = 0; u < CPW; ++u)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b[u][ks] = Pg[(4 * ks + g) * D + 16 * (wave + 4 * u) + l16];
+  __syncthreads();
   typedef double f64x4 __attribute__((__vector_size__(4 * sizeof(double))));
+  f64x4 acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[ks], (double)ps[(4 * ks + g) * PS + 16 * ct + l16],
+                                                     acc[ct], 0, 0, 0);
   double* out = (z ? pk : pq) + ((size_t)bh * Nb) * D;
 #pragma unroll
-  for (int u = 0; u < CPW; ++u) {
-    const int ct = wave + 4 * u;
-    f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[ks], (double)b[u][ks], acc, 0, 0, 0);
+  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = r0 + g + 4 * e;                // f64 16x16 layout: D[g + 4e][l16]
-      if (r < Nb) out[(size_t)r * D + 16 * ct + l16] = acc[e];
+      if (r < Nb) out[(size_t)r * D + c0 + 16 * ct + l16] = acc[ct][e];
     }
-  }
 }
 
 }  // namespace
@@ -163,7 +172,7 @@ hipError_t launch_pool_sum(const Dims& D, const void* Q, const void* K, double* 
 
 hipError_t launch_pool_proj(const Dims& D, const float* proj_q, const float* proj_k, int proj_hs,
                             const double* raw, double* pq, double* pk, hipStream_t s) {
-  dim3 g2((D.Nb + kPR - 1) / kPR, D.BH, 2);
+  dim3 g2((D.Nb + 63) / 64, D.BH, 2 * (D.d / 64));  // z: (column slice, Q or K)
   if (D.d == 128)
     hipLaunchKernelGGL(k_pool_proj<128>, g2, dim3(256), 0, s, raw, proj_q, proj_k, proj_hs, pq, pk,
                        D.H, D.Nb, D.BH);
