@@ -92,11 +92,13 @@ typedef struct {
 
 /* Debug outputs of sla_forward_debug. Every pointer is a device buffer or NULL.
  * pooled_q, pooled_k: [B, H, Nb, d] float64, the router-projected block means
- *                     (Eq. 1's pool(Q), pool(K));
+ *                     (Eq. 1's pool(Q), pool(K)); the plain block means when
+ *                     the router matrices are NULL;
  * logits:             [B, H, Nb, Nb] float64, pool(Q) pool(K)^T / sqrt(d);
  * o_s, o_l:           [B, H, N, d] float32, the sparse and linear branch outputs
- *                     before the mix. pooled_q/pooled_k/logits are only written
- *                     when the mask is computed (mask_in == NULL).
+ *                     before the mix (for sla1_forward_debug, o_l is Proj(O_l)).
+ *                     pooled_q/pooled_k/logits are only written when the mask
+ *                     is computed (mask_in == NULL).
  * events:             caller-owned hipEvent_t handles (or NULL), recorded on
  *                     `stream`: events[0] before the pooling kernel and
  *                     events[k] after kernel k = 1 pooling, 2 scores/selection,
