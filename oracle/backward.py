@@ -1,0 +1,88 @@
+"""Float64 CPU oracle of the SLA2 backward pass (gradients for a fixed mask).
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package: imported by the tests
+and by the benchmark's cpu_baseline leg, never by the product path; it shares
+no code with the HIP path.
+
+The pages describe the backward only in outline (SLA explainer, section 2.3:
+the FlashAttention backward restricted to the blocks with Mc = 1 for the
+sparse path, the chain rule through phi(Q), phi(K) and V with per-block
+accumulation for the linear path; SLA paper summary, Fig. 6's backward-kernel
+speed). They print no formulas for it, so the oracle is the definition: the
+explicit forward of sla_oracle.forward (masked softmax over the critical
+tokens, explicit phi(Q) phi(K)^T restricted to marginal tokens and
+row-normalised, the alpha mix), written with torch float64 operations on the
+CPU and differentiated by autograd. The mask is an input (it is a hard,
+piecewise-constant function of Q and K, so no gradient flows through the
+router, the pooling or the ranking).
+"""
+
+from typing import Dict, Tuple
+
+import numpy as np
+import torch
+
+BLOCK = 64
+
+
+def _token_masks(mask_row: np.ndarray, N: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    m = torch.from_numpy(np.repeat(np.asarray(mask_row), BLOCK)[:N])
+    return m == 1, m == 0
+
+
+def forward_torch(Q, K, V, alpha, mask, phi: str = "softmax"):
+    """Explicit forward in torch float64 for a fixed block mask [B, H, Nb, Nb];
+    Q, K, V [B, H, N, d] float64 tensors (requires_grad as wanted), alpha [H].
+    Returns (O, O_s, O_l)."""
+    B, H, N, d = Q.shape
+    Nb = (N + BLOCK - 1) // BLOCK
+    outs, outs_s, outs_l = [], [], []
+    for b in range(B):
+        ob, osb, olb = [], [], []
+        for h in range(H):
+            q, k, v = Q[b, h], K[b, h], V[b, h]
+            S = (q @ k.T) / np.sqrt(d)
+            if phi == "softmax":
+                fq, fk = torch.softmax(q, dim=-1), torch.softmax(k, dim=-1)
+            else:
+                fq, fk = torch.nn.functional.elu(q) + 1.0, torch.nn.functional.elu(k) + 1.0
+            A = fq @ fk.T
+            rows_s, rows_l = [], []
+            for i in range(Nb):
+                t0, t1 = i * BLOCK, min((i + 1) * BLOCK, N)
+                crit, marg = _token_masks(mask[b, h, i], N)
+                if crit.any():
+                    Si = S[t0:t1].masked_fill(~crit[None, :], float("-inf"))
+                    rows_s.append(torch.softmax(Si, dim=-1) @ v)
+                else:
+                    rows_s.append(torch.zeros(t1 - t0, d, dtype=Q.dtype))
+                if marg.any():
+                    Ai = A[t0:t1] * marg[None, :].to(Q.dtype)
+                    rows_l.append((Ai @ v) / Ai.sum(dim=-1, keepdim=True))
+                else:
+                    rows_l.append(torch.zeros(t1 - t0, d, dtype=Q.dtype))
+            Os, Ol = torch.cat(rows_s), torch.cat(rows_l)
+            osb.append(Os)
+            olb.append(Ol)
+            ob.append(alpha[h] * Os + (1.0 - alpha[h]) * Ol)
+        outs.append(torch.stack(ob))
+        outs_s.append(torch.stack(osb))
+        outs_l.append(torch.stack(olb))
+    return torch.stack(outs), torch.stack(outs_s), torch.stack(outs_l)
+
+
+def backward(Q, K, V, alpha, mask, dO, phi: str = "softmax") -> Dict[str, np.ndarray]:
+    """Gradients of sum(O * dO) with respect to Q, K, V and alpha, float64.
+    Inputs are upcast exactly (bf16 / f32 -> f64). Returns numpy arrays dQ, dK,
+    dV [B, H, N, d] and dalpha [H] (summed over the batch)."""
+    f64 = lambda x: (x.detach().to("cpu", torch.float64) if hasattr(x, "detach")
+                     else torch.from_numpy(np.asarray(x, dtype=np.float64)))
+    q = f64(Q).requires_grad_(True)
+    k = f64(K).requires_grad_(True)
+    v = f64(V).requires_grad_(True)
+    a = f64(alpha).reshape(-1).requires_grad_(True)
+    g = f64(dO)
+    O, _, _ = forward_torch(q, k, v, a, np.asarray(mask), phi)
+    (O * g).sum().backward()
+    return {"dQ": q.grad.numpy(), "dK": k.grad.numpy(), "dV": v.grad.numpy(),
+            "dalpha": a.grad.numpy()}

@@ -1,0 +1,87 @@
+"""Pins of the backward oracle (oracle/backward.py): the torch re-statement of
+the forward against the pinned numpy oracle, autograd against central finite
+differences, the mixing ratio's gradient against its closed form, and the
+all-critical case against the autograd of torch's own attention routine."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from oracle import backward as ob
+
+
+def _case(N, d, H=2, seed=0):
+    rng = np.random.default_rng(seed)
+    Q, K, V = (rng.standard_normal((1, H, N, d)) for _ in range(3))
+    Nb = (N + 63) // 64
+    mask = rng.choice(np.array([1, 0, -1], dtype=np.int8), size=(1, H, Nb, Nb))
+    mask[..., 0] = 1            # every row has a critical block
+    mask[..., Nb - 1] = 0       # and a marginal one (the ragged block when N % 64)
+    alpha = rng.uniform(0.2, 0.8, size=H)
+    dO = rng.standard_normal((1, H, N, d))
+    return Q, K, V, alpha, mask, dO
+
+
+@pytest.mark.parametrize("phi", ["softmax", "elu1"])
+def test_torch_forward_equals_the_numpy_oracle(phi):
+    Q, K, V, alpha, mask, _ = _case(200, 16)
+    t = lambda x: torch.from_numpy(x)
+    O, Os, Ol = ob.forward_torch(t(Q), t(K), t(V), t(alpha), mask, phi)
+    r = orc.forward(Q, K, V, np.eye(16), np.eye(16), alpha, 0.0, 0.0, mask_in=mask, feature=phi)
+    for h in range(2):
+        np.testing.assert_allclose(O[0, h].numpy(), r.O[(0, h)], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(Os[0, h].numpy(), r.O_s[(0, h)], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(Ol[0, h].numpy(), r.O_l[(0, h)], rtol=1e-12, atol=1e-13)
+
+
+def test_gradients_against_finite_differences():
+    Q, K, V, alpha, mask, dO = _case(70, 8, H=1, seed=3)
+    g = ob.backward(Q, K, V, alpha, mask, dO)
+    t = lambda x: torch.from_numpy(np.array(x))
+
+    def loss(Q_, K_, V_, a_):
+        O, _, _ = ob.forward_torch(t(Q_), t(K_), t(V_), t(a_), mask)
+        return float((O.numpy() * dO).sum())
+
+    rng = np.random.default_rng(4)
+    eps = 1e-6
+    for name, arr, idx in [("dQ", Q, 0), ("dK", K, 1), ("dV", V, 2)]:
+        for _ in range(6):
+            pos = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            args = [Q, K, V, alpha]
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[idx][pos] += eps
+            minus[idx][pos] -= eps
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            assert abs(fd - g[name][pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, g[name][pos])
+    ap, am = alpha.copy(), alpha.copy()
+    ap[0] += eps
+    am[0] -= eps
+    fd = (loss(Q, K, V, ap) - loss(Q, K, V, am)) / (2 * eps)
+    assert abs(fd - g["dalpha"][0]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_alpha_gradient_closed_form():
+    # O = alpha O_s + (1 - alpha) O_l: dL/dalpha_h = sum dO * (O_s - O_l) over the head
+    Q, K, V, alpha, mask, dO = _case(260, 16, H=3, seed=5)
+    g = ob.backward(Q, K, V, alpha, mask, dO)
+    r = orc.forward(Q, K, V, np.eye(16), np.eye(16), alpha, 0.0, 0.0, mask_in=mask)
+    for h in range(3):
+        ref = float((dO[0, h] * (r.O_s[(0, h)] - r.O_l[(0, h)])).sum())
+        assert abs(g["dalpha"][h] - ref) <= 1e-10 * max(1.0, abs(ref))
+
+
+def test_all_critical_equals_attention_autograd():
+    # every block critical, alpha = 1: the gradients of dense softmax attention
+    rng = np.random.default_rng(6)
+    N, d = 192, 16
+    Q, K, V, dO = (rng.standard_normal((1, 1, N, d)) for _ in range(4))
+    mask = np.ones((1, 1, 3, 3), dtype=np.int8)
+    g = ob.backward(Q, K, V, np.ones(1), mask, dO)
+    q, k, v = (torch.from_numpy(x).requires_grad_(True) for x in (Q, K, V))
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+    (out * torch.from_numpy(dO)).sum().backward()
+    for name, t in (("dQ", q), ("dK", k), ("dV", v)):
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-12)
