@@ -186,6 +186,33 @@ int sla1_forward_debug(const sla_problem* p,
                        void* workspace, size_t workspace_bytes,
                        void* stream, const sla_debug* dbg);
 
+/* Workspace that sla_backward needs for `p` (host only, no device work).
+ * Returns SLA_OK or the validation error sla_backward would return. */
+int sla_backward_workspace_bytes(const sla_problem* p, size_t* bytes);
+
+/* The SLA2 backward pass for a fixed block mask: the gradients of
+ * sum(O * dO) with O = alpha O_s + (1 - alpha) O_l (SLA explainer, section 2.3:
+ * the FlashAttention backward over the critical blocks and the chain rule
+ * through phi(Q), phi(K) and V for the marginal ones, accumulated per block).
+ *  Q, K, V   device, dtype, [B, H, N, d]: the forward pass's inputs.
+ *  alpha     device float32 [H].
+ *  mask      device int8 [B, H, Nb, Nb]: the forward pass's block mask (the
+ *            mask is piecewise constant in Q and K: no gradient flows through
+ *            the router, the pooling or the ranking, so proj_q / proj_k get none).
+ *  dO        device, dtype, [B, H, N, d]: the gradient of the output.
+ *  dQ, dK,   device float32 [B, H, N, d] outputs (rows past N untouched).
+ *  dV
+ *  dalpha    device float32 [H] output, summed over the batch.
+ *  workspace device scratch of at least sla_backward_workspace_bytes(p) bytes.
+ * fp32 arithmetic. Requires quant == SLA_QUANT_NONE and phi == SLA_PHI_SOFTMAX
+ * (SLA_ERR_UNSUPPORTED otherwise). Errors as for sla_forward. */
+int sla_backward(const sla_problem* p,
+                 const void* Q, const void* K, const void* V, const float* alpha,
+                 const int8_t* mask, const void* dO,
+                 float* dQ, float* dK, float* dV, float* dalpha,
+                 void* workspace, size_t workspace_bytes,
+                 void* stream);
+
 /* SoftTop-k of the compressed attention map, the differentiable stand-in for
  * Eq. 2's top-k in SLA2's first training stage (SLA2 article, the two-stage
  * training paragraphs, stage 1: a sigmoid with a temperature; SLA2

@@ -11,9 +11,9 @@ argument-marshalling binding.
 """
 
 from ._binding import (  # noqa: F401
-    LIB_PATH, HipEvents, Plan, SLAError, block_counts, forward, forward_sla1, load_library,
+    LIB_PATH, HipEvents, Plan, SLAError, backward, block_counts, forward, forward_sla1, load_library,
     make_problem, soft_topk, workspace_bytes,
 )
 
-__all__ = ["forward", "forward_sla1", "soft_topk", "Plan", "HipEvents", "block_counts", "workspace_bytes", "load_library",
+__all__ = ["forward", "forward_sla1", "backward", "soft_topk", "Plan", "HipEvents", "block_counts", "workspace_bytes", "load_library",
            "make_problem", "SLAError", "LIB_PATH"]

@@ -68,6 +68,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sla1_forward.restype = ctypes.c_int
     lib.sla1_forward_debug.argtypes = _FWD_ARGS + [ctypes.POINTER(Debug)]
     lib.sla1_forward_debug.restype = ctypes.c_int
+    lib.sla_backward_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
+    lib.sla_backward_workspace_bytes.restype = ctypes.c_int
+    lib.sla_backward.argtypes = [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                                                      ctypes.c_void_p]
+    lib.sla_backward.restype = ctypes.c_int
     lib.sla_soft_topk.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                   ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.sla_soft_topk.restype = ctypes.c_int
@@ -250,6 +255,40 @@ def soft_topk(logits: torch.Tensor, k: float, tau: float, *, out: Optional[torch
         rc = lib.sla_soft_topk(_ptr(logits), rows, C, float(k), float(tau), _ptr(out), _ptr(lam), stream)
     _check(rc)
     return out, lam
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+             mask: torch.Tensor, dO: torch.Tensor, *, workspace: Optional[torch.Tensor] = None):
+    """SLA2 backward on the GPU (sla_backward) for the block mask the forward
+    pass used: returns (dQ, dK, dV float32 [B, H, N, d], dalpha float32 [H])."""
+    lib = load_library()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or dO.shape != q.shape:
+        raise ValueError("q, k, v and dO must share one [B, H, N, d] shape")
+    if q.dtype not in (torch.bfloat16, torch.float32) or any(t.dtype != q.dtype for t in (k, v, dO)):
+        raise ValueError("q, k, v and dO must all be bfloat16 or all float32")
+    B, H, N, d = q.shape
+    Nb = (N + 63) // 64
+    if mask.dtype != torch.int8 or tuple(mask.shape) != (B, H, Nb, Nb):
+        raise ValueError("mask must be int8 [B, H, Nb, Nb]")
+    if alpha.dtype != torch.float32 or alpha.numel() != H:
+        raise ValueError("alpha must be float32 with H entries")
+    q, k, v, dO, mask, alpha = (t.contiguous() for t in (q, k, v, dO, mask, alpha))
+    p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", 0.0, 0.0)
+    n = ctypes.c_size_t()
+    _check(lib.sla_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    if workspace is None or workspace.numel() * workspace.element_size() < n.value:
+        workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=q.device)
+    dQ = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dK = torch.empty_like(dQ)
+    dV = torch.empty_like(dQ)
+    dalpha = torch.empty(H, dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+        rc = lib.sla_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mask), _ptr(dO),
+                              _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dalpha), _ptr(workspace),
+                              ctypes.c_size_t(workspace.numel() * workspace.element_size()), stream)
+    _check(rc)
+    return dQ, dK, dV, dalpha
 
 
 class Plan:

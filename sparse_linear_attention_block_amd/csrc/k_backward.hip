@@ -1,0 +1,431 @@
+// Backward pass of SLA2 for a fixed block mask: dQ, dK, dV and dalpha of
+// sum(O * dO), with O = alpha O_s + (1 - alpha) O_l.
+//
+// SLA explainer (intelliparadigm.com), section 2.3: the sparse path takes the
+// FlashAttention backward over the blocks with Mc = 1 only, the linear path
+// the chain rule through phi(Q), phi(K) and V with per-block accumulation.
+// Written out, per head, with dO_s = alpha dO and dO_l = (1 - alpha) dO:
+//  sparse (query t, its critical keys s; P = exp(S - lse_t), S = q.k / sqrt(d)):
+//    D_t = dO_s[t] . O_s[t],  dS = P (dO_s[t] . v_s - D_t),
+//    dq_t += sum_s dS k_s / sqrt(d),  dk_s += sum_t dS q_t / sqrt(d),
+//    dv_s += sum_t P dO_s[t];
+//  linear (query t in block i, u = phi(q_t), num = u H_i, den = u . Z_i):
+//    dnum = dO_l[t] / den,  dden = -(dO_l[t] . O_l[t]) / den,
+//    du = H_i dnum + Z_i dden,  dH_i += u^T dnum,  dZ_i += u dden;
+//    dh_j = sum over query blocks i with Mc[i, j] = 0 of dH_i (dz_j likewise),
+//    taken as the head's total minus the blocks with Mc != 0;
+//    key s in block j, w = phi(k_s): dw = dh_j v_s + dz_j, dv_s += w dh_j;
+//  feature map (softmax over the features): dx = phi (dphi - dphi . phi);
+//  dalpha_h = sum over the head of dO . (O_s - O_l).
+//
+// fp32 arithmetic throughout (bf16 or f32 inputs), four threads per query or
+// key token, each holding d/4 features (the layout of the forward's f32
+// kernel). H_i and Z_i come from the forward's own h/z and marginal-sum
+// kernels. k_bwd_q (one workgroup per query block) recomputes the sparse
+// forward for its log-sum-exp and O_s, then produces dQ, dH_i / dZ_i and the
+// block's dalpha partial; k_bwd_htot sums dH_i per head; k_bwd_kv (one
+// workgroup per key block) produces dK and dV; k_bwd_alpha sums the partials
+// per head in a fixed order.
+#include "sla_internal.h"
+#include "dev_common.h"
+
+namespace sla {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T* p);
+template <>
+__device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) { return bf2f(*p); }
+
+__device__ __forceinline__ float sum4(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  return v;
+}
+__device__ __forceinline__ float max4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  return v;
+}
+
+// value r of a 4-thread group's d features (thread k of the group holds
+// features k P .. k P + P - 1 in x[])
+template <int P>
+__device__ __forceinline__ float group_get(const float (&x)[P], int r, int lane) {
+  float v = 0.f;
+#pragma unroll
+  for (int e = 0; e < P; ++e)
+    if (e == r % P) v = x[e];
+  return __shfl(v, (lane & ~3) | (r / P));
+}
+
+// softmax over the d features held by a 4-thread group
+template <int P>
+__device__ __forceinline__ void feature_softmax(const float (&x)[P], float (&f)[P]) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < P; ++e) m = fmaxf(m, x[e]);
+  m = max4(m);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    f[e] = expf(x[e] - m);
+    s += f[e];
+  }
+  const float inv = 1.0f / sum4(s);
+#pragma unroll
+  for (int e = 0; e < P; ++e) f[e] *= inv;
+}
+
+// The 64 keys of block j (f32, zero past N) into Ks / Vs.
+template <typename T, int D>
+__device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, int j, int N, float (*Ks)[D],
+                                         float (*Vs)[D]) {
+  for (int x = threadIdx.x; x < kBlock * D; x += 256) {
+    const int key = x / D, c = x % D, tk = j * kBlock + key;
+    Ks[key][c] = tk < N ? ldf<T>(Kb + (size_t)tk * D + c) : 0.f;
+    Vs[key][c] = tk < N ? ldf<T>(Vb + (size_t)tk * D + c) : 0.f;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_q(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int8_t* __restrict__ mask, const T* __restrict__ Hx, const float* __restrict__ alpha,
+    const T* __restrict__ dO, float* __restrict__ dQ, float* __restrict__ lse_out,
+    float* __restrict__ dt_out, float* __restrict__ dHx, float* __restrict__ dal, int H, int N, int Nb) {
+  constexpr int P = D / 4;
+  constexpr int NN = D * D + D;
+  __shared__ float Ks[kBlock][D];  // key tiles; then phi(Q) of the block
+  __shared__ float Vs[kBlock][D];  // value tiles; then dnum of the block
+  __shared__ float dd[kBlock];     // dden of the block
+  __shared__ uint16_t list[kMaxNb];
+  __shared__ int wsum[4];
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int bh = blockIdx.y, i = blockIdx.x, h = bh % H;
+  const int row = tid >> 2, part = tid & 3;
+  const int t = i * kBlock + row;
+  const bool valid = t < N;
+  const size_t base = (size_t)bh * N * D;
+  const int ncrit = compact_row(mask + ((size_t)bh * Nb + i) * Nb, Nb, (int8_t)1, list, wsum);
+  float q[P], g[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    q[e] = valid ? ldf<T>(Q + base + (size_t)t * D + part * P + e) : 0.f;
+    g[e] = valid ? ldf<T>(dO + base + (size_t)t * D + part * P + e) : 0.f;
+  }
+  const float al = alpha[h];
+  const float scale = 1.0f / sqrtf((float)D);
+  const T* Kb = K + base;
+  const T* Vb = V + base;
+
+  // sparse forward again: log-sum-exp and O_s of the query
+  float m = -INFINITY, l = 0.f, acc[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) acc[e] = 0.f;
+  for (int c = 0; c < ncrit; ++c) {
+    const int j = list[c];
+    __syncthreads();
+    stage_kv<T, D>(Kb, Vb, j, N, Ks, Vs);
+    __syncthreads();
+    const int nk = min(kBlock, N - j * kBlock);
+    for (int key = 0; key < nk; ++key) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) s = fmaf(q[e], Ks[key][part * P + e], s);
+      s = sum4(s) * scale;
+      const float mn = fmaxf(m, s);
+      const float corr = expf(m - mn), p = expf(s - mn);
+      l = l * corr + p;
+#pragma unroll
+      for (int e = 0; e < P; ++e) acc[e] = fmaf(p, Vs[key][part * P + e], acc[e] * corr);
+      m = mn;
+    }
+  }
+  const bool has_crit = ncrit > 0 && l > 0.f;
+  const float inv_l = has_crit ? 1.0f / l : 0.f;
+  const float lse = has_crit ? m + logf(l) : INFINITY;  // no critical key: every P is 0
+  float os[P], gs[P];
+  float dtp = 0.f;
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    os[e] = acc[e] * inv_l;
+    gs[e] = al * g[e];
+    dtp = fmaf(gs[e], os[e], dtp);
+  }
+  const float Dt = sum4(dtp);
+
+  // sparse dq: dS = P (dO_s . v - D_t), dq += dS k / sqrt(d)
+  float dq[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) dq[e] = 0.f;
+  for (int c = 0; c < ncrit; ++c) {
+    const int j = list[c];
+    __syncthreads();
+    stage_kv<T, D>(Kb, Vb, j, N, Ks, Vs);
+    __syncthreads();
+    const int nk = min(kBlock, N - j * kBlock);
+    for (int key = 0; key < nk; ++key) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        s = fmaf(q[e], Ks[key][part * P + e], s);
+        dp = fmaf(gs[e], Vs[key][part * P + e], dp);
+      }
+      s = sum4(s) * scale;
+      dp = sum4(dp);
+      const float ds = expf(s - lse) * (dp - Dt) * scale;
+#pragma unroll
+      for (int e = 0; e < P; ++e) dq[e] = fmaf(ds, Ks[key][part * P + e], dq[e]);
+    }
+  }
+
+  // linear branch: u = phi(q), num = u H_i, den = u . Z_i (H_i^T stored c-major: Hrow[n D + r] = H_i[r][n])
+  const T* Hrow = Hx + ((size_t)bh * Nb + i) * NN;
+  float u[P];
+  feature_softmax<P>(q, u);
+  float den = 0.f;
+#pragma unroll
+  for (int e = 0; e < P; ++e) den = fmaf(u[e], ldf<T>(Hrow + D * D + part * P + e), den);
+  den = sum4(den);
+  float num[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) num[e] = 0.f;
+  for (int r = 0; r < D; ++r) {
+    const float ur = group_get<P>(u, r, lane);
+#pragma unroll
+    for (int e = 0; e < P; ++e) num[e] = fmaf(ur, ldf<T>(Hrow + (size_t)(part * P + e) * D + r), num[e]);
+  }
+  const float inv_den = den > 0.f ? 1.0f / den : 0.f;
+  float ol[P], dnum[P];
+  float dop = 0.f, dap = 0.f;
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    ol[e] = num[e] * inv_den;
+    const float gl = (1.0f - al) * g[e];
+    dnum[e] = gl * inv_den;
+    dop = fmaf(gl, ol[e], dop);
+    dap = fmaf(g[e], os[e] - ol[e], dap);
+  }
+  const float dden = -sum4(dop) * inv_den;
+  // du[r] = sum_n H_i[r][n] dnum[n] + Z_i[r] dden, for the thread's features r
+  float du[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) du[e] = ldf<T>(Hrow + D * D + part * P + e) * dden;
+  for (int n = 0; n < D; ++n) {
+    const float dn = group_get<P>(dnum, n, lane);
+#pragma unroll
+    for (int e = 0; e < P; ++e) du[e] = fmaf(ldf<T>(Hrow + (size_t)n * D + part * P + e), dn, du[e]);
+  }
+  float dup = 0.f;
+#pragma unroll
+  for (int e = 0; e < P; ++e) dup = fmaf(du[e], u[e], dup);
+  dup = sum4(dup);
+#pragma unroll
+  for (int e = 0; e < P; ++e) dq[e] = fmaf(u[e], du[e] - dup, dq[e]);
+
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < P; ++e) dQ[base + (size_t)t * D + part * P + e] = dq[e];
+  }
+  const size_t tok = ((size_t)bh * Nb + i) * kBlock + row;
+  if (part == 0) {
+    lse_out[tok] = lse;
+    dt_out[tok] = Dt;
+  }
+
+  // dalpha partial of the block (rows past N hold zeros)
+  float da = valid ? dap : 0.f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) da += __shfl_xor(da, o);
+  __syncthreads();  // the key tiles are no longer needed
+  if (lane == 0) red[tid >> 6] = da;
+  // dH_i and dZ_i: phi(Q) and dnum of the block's queries (zero past N) in LDS
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    Ks[row][part * P + e] = valid ? u[e] : 0.f;
+    Vs[row][part * P + e] = valid ? dnum[e] : 0.f;
+  }
+  if (part == 0) dd[row] = valid ? dden : 0.f;
+  __syncthreads();
+  if (tid == 0) dal[(size_t)bh * Nb + i] = (red[0] + red[1]) + (red[2] + red[3]);
+  float* out = dHx + ((size_t)bh * Nb + i) * NN;
+  for (int x = tid; x < NN; x += 256) {
+    float s = 0.f;
+    if (x < D * D) {
+      const int n = x / D, r = x % D;  // dH_i[r][n], stored like H_i
+      for (int tq = 0; tq < kBlock; ++tq) s = fmaf(Ks[tq][r], Vs[tq][n], s);
+    } else {
+      const int r = x - D * D;
+      for (int tq = 0; tq < kBlock; ++tq) s = fmaf(Ks[tq][r], dd[tq], s);
+    }
+    out[x] = s;
+  }
+}
+
+// dH_tot[bh][x] = sum over the head's query blocks of dHx[bh][i][x]
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_htot(const float* __restrict__ dHx, float* __restrict__ dHtot,
+                                                  int Nb) {
+  constexpr int NN = D * D + D;
+  const int x = blockIdx.x * 256 + threadIdx.x, bh = blockIdx.y;
+  if (x >= NN) return;
+  double s = 0.0;
+  for (int i = 0; i < Nb; ++i) s += (double)dHx[((size_t)bh * Nb + i) * NN + x];
+  dHtot[(size_t)bh * NN + x] = (float)s;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_kv(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int8_t* __restrict__ mask, const float* __restrict__ alpha, const T* __restrict__ dO,
+    const float* __restrict__ lse_in, const float* __restrict__ dt_in, const float* __restrict__ dHx,
+    const float* __restrict__ dHtot, float* __restrict__ dK, float* __restrict__ dV, int H, int N,
+    int Nb) {
+  constexpr int P = D / 4;
+  constexpr int NN = D * D + D;
+  __shared__ float sm[NN > 2 * kBlock * D + 2 * kBlock ? NN : 2 * kBlock * D + 2 * kBlock];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int bh = blockIdx.y, j = blockIdx.x, h = bh % H;
+  const int row = tid >> 2, part = tid & 3;
+  const int s = j * kBlock + row;
+  const bool valid = s < N;
+  const size_t base = (size_t)bh * N * D;
+  float kk[P], vv[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    kk[e] = valid ? ldf<T>(K + base + (size_t)s * D + part * P + e) : 0.f;
+    vv[e] = valid ? ldf<T>(V + base + (size_t)s * D + part * P + e) : 0.f;
+  }
+  const float al = alpha[h];
+  const float scale = 1.0f / sqrtf((float)D);
+  float dk[P], dv[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) dk[e] = dv[e] = 0.f;
+
+  // linear branch: dh_j = dH_tot - sum of dH_i over the query blocks with Mc[i, j] != 0
+  float* DH = sm;  // [NN]: dh_j stored like H (DH[n D + r] = dh_j[r][n]), then dz_j
+  for (int x = tid; x < NN; x += 256) DH[x] = dHtot[(size_t)bh * NN + x];
+  for (int i = 0; i < Nb; ++i) {
+    if (mask[((size_t)bh * Nb + i) * Nb + j] == 0) continue;  // uniform
+    const float* src = dHx + ((size_t)bh * Nb + i) * NN;
+    for (int x = tid; x < NN; x += 256) DH[x] -= src[x];  // each thread owns its x
+  }
+  __syncthreads();
+  float w[P];
+  feature_softmax<P>(kk, w);
+  // dw[r] = sum_n dh_j[r][n] v[n] + dz_j[r]; dv[n] += sum_r w[r] dh_j[r][n]
+  float dw[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) dw[e] = DH[D * D + part * P + e];
+  for (int n = 0; n < D; ++n) {
+    const float vn = group_get<P>(vv, n, lane);
+#pragma unroll
+    for (int e = 0; e < P; ++e) dw[e] = fmaf(DH[n * D + part * P + e], vn, dw[e]);
+  }
+  for (int r = 0; r < D; ++r) {
+    const float wr = group_get<P>(w, r, lane);
+#pragma unroll
+    for (int e = 0; e < P; ++e) dv[e] = fmaf(wr, DH[(part * P + e) * D + r], dv[e]);
+  }
+  float dwp = 0.f;
+#pragma unroll
+  for (int e = 0; e < P; ++e) dwp = fmaf(dw[e], w[e], dwp);
+  dwp = sum4(dwp);
+#pragma unroll
+  for (int e = 0; e < P; ++e) dk[e] = w[e] * (dw[e] - dwp);
+
+  // sparse branch over the query blocks that hold key block j as critical
+  float (*Qs)[D] = reinterpret_cast<float (*)[D]>(sm);
+  float (*Gs)[D] = reinterpret_cast<float (*)[D]>(sm + kBlock * D);
+  float* Ls = sm + 2 * kBlock * D;
+  float* Ds = Ls + kBlock;
+  for (int i = 0; i < Nb; ++i) {
+    if (mask[((size_t)bh * Nb + i) * Nb + j] != 1) continue;  // uniform
+    __syncthreads();
+    for (int x = tid; x < kBlock * D; x += 256) {
+      const int tq = x / D, c = x % D, tt = i * kBlock + tq;
+      Qs[tq][c] = tt < N ? ldf<T>(Q + base + (size_t)tt * D + c) : 0.f;
+      Gs[tq][c] = tt < N ? al * ldf<T>(dO + base + (size_t)tt * D + c) : 0.f;
+    }
+    if (tid < kBlock) {
+      Ls[tid] = lse_in[((size_t)bh * Nb + i) * kBlock + tid];
+      Ds[tid] = dt_in[((size_t)bh * Nb + i) * kBlock + tid];
+    }
+    __syncthreads();
+    const int nq = min(kBlock, N - i * kBlock);
+    for (int tq = 0; tq < nq; ++tq) {
+      float sc = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        sc = fmaf(kk[e], Qs[tq][part * P + e], sc);
+        dp = fmaf(vv[e], Gs[tq][part * P + e], dp);
+      }
+      sc = sum4(sc) * scale;
+      dp = sum4(dp);
+      const float p = expf(sc - Ls[tq]);
+      const float ds = p * (dp - Ds[tq]) * scale;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        dv[e] = fmaf(p, Gs[tq][part * P + e], dv[e]);
+        dk[e] = fmaf(ds, Qs[tq][part * P + e], dk[e]);
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      dK[base + (size_t)s * D + part * P + e] = dk[e];
+      dV[base + (size_t)s * D + part * P + e] = dv[e];
+    }
+  }
+}
+
+// dalpha[h] = sum over batches and query blocks of the partials, in that order
+__global__ void k_bwd_alpha(const float* __restrict__ dal, float* __restrict__ dalpha, int B, int H,
+                            int Nb) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  double s = 0.0;
+  for (int b = 0; b < B; ++b)
+    for (int i = 0; i < Nb; ++i) s += (double)dal[((size_t)b * H + h) * Nb + i];
+  dalpha[h] = (float)s;
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_t(const Dims& Dm, const void* Q, const void* K, const void* V, const int8_t* mask,
+                        const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
+                        float* dK, float* dV, float* dalpha, hipStream_t s) {
+  constexpr int NN = D * D + D;
+  const dim3 grid(Dm.Nb, Dm.BH);
+  hipLaunchKernelGGL((k_bwd_q<T, D>), grid, dim3(256), 0, s, (const T*)Q, (const T*)K, (const T*)V, mask,
+                     (const T*)w.Hx, alpha, (const T*)dO, dQ, bw.lse, bw.dt, bw.dHx, bw.dal, Dm.H, Dm.N, Dm.Nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bwd_htot<D>, dim3((NN + 255) / 256, Dm.BH), dim3(256), 0, s, bw.dHx, bw.dHtot, Dm.Nb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bwd_kv<T, D>), grid, dim3(256), 0, s, (const T*)Q, (const T*)K, (const T*)V, mask,
+                     alpha, (const T*)dO, bw.lse, bw.dt, bw.dHx, bw.dHtot, dK, dV, Dm.H, Dm.N, Dm.Nb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bwd_alpha, dim3((Dm.H + 63) / 64), dim3(64), 0, s, bw.dal, dalpha, Dm.B, Dm.H, Dm.Nb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
+                           const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
+                           float* dK, float* dV, float* dalpha, hipStream_t s) {
+  if (D.bf16)
+    return D.d == 128 ? launch_bwd_t<uint16_t, 128>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s)
+                      : launch_bwd_t<uint16_t, 64>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s);
+  return D.d == 128 ? launch_bwd_t<float, 128>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s)
+                    : launch_bwd_t<float, 64>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s);
+}
+
+}  // namespace sla

@@ -112,6 +112,25 @@ size_t carve(const Dims& D, void* base, Work* w) {
   return off;
 }
 
+size_t carve_bwd(const Dims& D, void* base, Work* w, BwdWork* bw) {
+  size_t off = carve(D, base, w);
+  char* b = (char*)base;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = b ? (void*)(b + off) : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  const size_t BH = (size_t)D.BH, T = BH * D.Nb * kBlock;
+  BwdWork x = {};
+  x.lse = (float*)take(T * sizeof(float));
+  x.dt = (float*)take(T * sizeof(float));
+  x.dHx = (float*)take(BH * D.Nb * D.NN * sizeof(float));
+  x.dHtot = (float*)take(BH * D.NN * sizeof(float));
+  x.dal = (float*)take(BH * D.Nb * sizeof(float));
+  if (bw) *bw = x;
+  return off;
+}
+
 }  // namespace sla
 
 extern "C" {
@@ -311,6 +330,61 @@ int sla_soft_topk(const double* logits, int32_t rows, int32_t cols, double k, do
   const hipError_t e = sla::launch_soft_topk(logits, rows, cols, (float)k, (float)tau, out, lambda,
                                              (hipStream_t)stream);
   if (e != hipSuccess) return fail(SLA_ERR_HIP, "soft top-k kernel: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return SLA_OK;
+}
+
+// Validation shared by the backward entry points; SLA_OK or an error code.
+static int make_bwd_dims(const sla_problem* p, sla::Dims* D) {
+  const int rc = make_dims(p, D);
+  if (rc != SLA_OK) return rc;
+  if (D->quant) return fail(SLA_ERR_UNSUPPORTED, "the backward pass is built without the 8-bit branch");
+  if (D->elu) return fail(SLA_ERR_UNSUPPORTED, "the backward pass is built for the softmax feature map");
+  return SLA_OK;
+}
+
+int sla_backward_workspace_bytes(const sla_problem* p, size_t* bytes) {
+  sla::Dims D;
+  const int rc = make_bwd_dims(p, &D);
+  if (rc != SLA_OK) return rc;
+  if (!bytes) return fail(SLA_ERR_ARG, "bytes is NULL");
+  *bytes = sla::carve_bwd(D, nullptr, nullptr, nullptr);
+  g_err[0] = 0;
+  return SLA_OK;
+}
+
+int sla_backward(const sla_problem* p, const void* Q, const void* K, const void* V, const float* alpha,
+                 const int8_t* mask, const void* dO, float* dQ, float* dK, float* dV, float* dalpha,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  sla::Dims D;
+  const int rc = make_bwd_dims(p, &D);
+  if (rc != SLA_OK) return rc;
+  if (!Q || !K || !V || !alpha || !mask || !dO || !dQ || !dK || !dV || !dalpha)
+    return fail(SLA_ERR_ARG, "Q, K, V, alpha, mask, dO, dQ, dK, dV and dalpha must not be NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(dO, 16) || !aligned(dQ, 16) ||
+      !aligned(dK, 16) || !aligned(dV, 16) || !aligned(alpha, 4) || !aligned(dalpha, 4))
+    return fail(SLA_ERR_ARG, "tensors must be 16-byte aligned, alpha and dalpha 4-byte aligned");
+  const size_t need = sla::carve_bwd(D, nullptr, nullptr, nullptr);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    return fail(SLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu at %p)",
+                need, workspace_bytes, workspace);
+  sla::Work w;
+  sla::BwdWork bw;
+  sla::carve_bwd(D, workspace, &w, &bw);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();  // a stale error from earlier work is not ours to report
+#define SLA_LAUNCH(call, what)                                                            \
+  do {                                                                                    \
+    hipError_t e_ = (call);                                                               \
+    if (e_ != hipSuccess) return fail(SLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e_)); \
+  } while (0)
+  // the linear branch's per-query-block state H_i, Z_i, as in the forward pass
+  SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
+  if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
+  SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
+  SLA_LAUNCH(sla::launch_backward(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s),
+             "backward kernels");
+#undef SLA_LAUNCH
   g_err[0] = 0;
   return SLA_OK;
 }

@@ -50,6 +50,16 @@ struct Work {
 
 size_t carve(const Dims& D, void* base, Work* w);  // returns bytes needed (base may be NULL)
 
+// Backward-pass regions, carved after the forward's (k_backward.hip).
+struct BwdWork {
+  float* lse;    // [BH, Nb*64] log-sum-exp of each query's critical scores (+inf if none)
+  float* dt;     // [BH, Nb*64] dO_s . O_s of each query
+  float* dHx;    // [BH, Nb, NN] dH_i (stored like H_i^T) then dZ_i, per query block
+  float* dHtot;  // [BH, NN] their sum over the head's query blocks
+  float* dal;    // [BH, Nb] partial dalpha of each query block
+};
+size_t carve_bwd(const Dims& D, void* base, Work* w, BwdWork* bw);  // forward + backward bytes
+
 // ---- launchers (each enqueues one or more kernels on `s`, returns hipError_t)
 hipError_t launch_pool_sum(const Dims& D, const void* Q, const void* K, double* raw,
                            hipStream_t s);
@@ -74,6 +84,9 @@ hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const 
                              const int8_t* mask, const float* alpha, const float* proj_o,
                              const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
 
+hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
+                           const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
+                           float* dK, float* dV, float* dalpha, hipStream_t s);
 // SoftTop-k rows of a float64 logit matrix (k_soft_topk.hip); cols <= 4096
 hipError_t launch_soft_topk(const double* logits, int rows, int cols, float k, float tau, float* out,
                             float* lambda, hipStream_t s);
