@@ -22,7 +22,8 @@ oracle timed on a bounded sample of the same workload.
 branches fused as O = O_s + Proj(O_l) with a seeded d x d Proj), --phi elu1
 the ELU+1 feature map of the linear branch. --op soft_topk times SoftTop-k
 (sla_soft_topk) on the compressed logits of the workload instead of the
-forward pass, and prints that op's own line.
+forward pass, and prints that op's own line; --op backward times the
+backward pass (sla_backward) for the forward's mask and a seeded dO.
 """
 
 import argparse
@@ -264,6 +265,94 @@ def bench_soft_topk(args, cfg, x, torch, sla):
     print(json.dumps(line), flush=True)
 
 
+# fp32 FMA on the VALU without packed operations: 64 lanes x 2 flops per CU
+# per clock, 256 CUs at 2.4 GHz
+PEAK_F32_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+
+
+def backward_flops(B, H, Nb, n_h, d):
+    """Algorithmic flops of the backward pass: per (query block, critical tile)
+    the five 64 x 64 x d products of the FlashAttention backward (S, dP, dV,
+    dK, dQ), and per block the linear branch's five 64 x d x d products
+    (num, du and dH_i on the query side, dw and dv on the key side)."""
+    return 10.0 * B * H * Nb * n_h * 64 * 64 * d + 10.0 * B * H * Nb * 64 * d * d
+
+
+def bench_backward(args, cfg, x, torch, sla):
+    """sla_backward at the workload's shape, for the mask its forward pass
+    computes and a seeded dO; one JSON line."""
+    from oracle import backward as ob
+    dev = torch.device("cuda:0")
+    q, k, v, al = x.q.to(dev), x.k.to(dev), x.v.to(dev), x.alpha.to(dev)
+    _, mask = sla.forward(q, k, v, x.proj_q.to(dev), x.proj_k.to(dev), al, x.kh, x.kl)
+    g = np.random.default_rng(cfg.seed + 7).standard_normal(tuple(x.q.shape))
+    dO = torch.from_numpy(g.astype(np.float32)).to(x.q.dtype)
+    dO_d = dO.to(dev)
+    B, H, N, d = x.q.shape
+    Nb = cfg.Nb
+    n_h = sla.block_counts(N, x.kh, x.kl, B=B, H=H, d=d, dtype=cfg.dtype)[1]
+    p = sla.make_problem(B, H, N, d, cfg.dtype, 0.0, 0.0)
+    n = ctypes_size(sla, p)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        sla.backward(q, k, v, al, mask, dO_d, workspace=ws)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        sla.backward(q, k, v, al, mask, dO_d, workspace=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    F = backward_flops(B, H, Nb, n_h, d)
+    achieved = F / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "SLA2 backward ms & dense-equivalent TFLOPS (10*B*H*N^2*d per backward)",
+        "value": round(10.0 * B * H * N * N * d / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s (dense-equivalent backward)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 (" + cfg.dtype + " inputs)",
+        "data": "synthetic: the seeded workload, its forward mask and a seeded N(0,1) dO",
+        "config": {"workload": cfg.name + "_backward", "B": B, "H": H, "N": N, "d": d, "Nb": Nb,
+                   "n_h": n_h, "kh": x.kh, "kl": x.kl},
+        "roofline": {"kernel": "sla_backward (all its kernels)", "bound": "alu",
+                     "achieved": round(achieved, 3), "peak": round(PEAK_F32_VALU_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_VALU_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": F, "ms_per_launch": round(ms, 4)},
+    }
+    if not args.no_cpu:
+        import threadpoolctl
+        cores = max([pp.get("num_threads", 1) for pp in threadpoolctl.threadpool_info()] or [1])
+        mk = mask.cpu().numpy()
+        t0 = time.perf_counter()
+        done = 0
+        for i in range(0, Nb, 7):
+            ob.dq_rows(x.q, x.k, x.v, x.alpha, mk, dO, 0, 0, [i])
+            done += 1
+            if time.perf_counter() - t0 > args.cpu_seconds and done >= 2:
+                break
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": round(10.0 * 64 * N * d * done / dt / 1e12, 6), "unit": "TFLOP/s (dense-equivalent backward)",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{cfg.name}, head (0,0): the float64 autograd oracle's dQ for {done} of {Nb} query "
+                      f"blocks in {dt:.1f} s, counted as 10*64*N*d per block (dK and dV are not formed "
+                      f"by this sample, so the rate flatters the oracle)"}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+def ctypes_size(sla, p):
+    import ctypes
+    n = ctypes.c_size_t()
+    rc = sla.load_library().sla_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n))
+    if rc != 0:
+        raise RuntimeError("sla_backward_workspace_bytes failed")
+    return max(int(n.value), 256)
+
+
 def step_distribution(torch, plan, hev, steps, flush_mib):
     """Per-step times after the timed region: each step bracketed by two
     fence-free HIP events on its stream. The unflushed steps run back to back;
@@ -306,8 +395,9 @@ def main():
                          "O = O_s + Proj(O_l) (sla1_forward)")
     ap.add_argument("--phi", choices=["softmax", "elu1"], default="softmax",
                     help="feature map of the linear branch")
-    ap.add_argument("--op", choices=["forward", "soft_topk"], default="forward",
-                    help="forward: the whole forward pass; soft_topk: SoftTop-k on its logits")
+    ap.add_argument("--op", choices=["forward", "soft_topk", "backward"], default="forward",
+                    help="forward: the whole forward pass; soft_topk: SoftTop-k on its logits; "
+                         "backward: the backward pass")
     ap.add_argument("--tau", type=float, default=1e-3, help="SoftTop-k temperature (Pc units)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--flush-mib", type=int, default=512,
@@ -340,6 +430,12 @@ def main():
     print(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     if args.op == "soft_topk":
         bench_soft_topk(args, cfg, x, torch, sla)
+        return
+    if args.op == "backward":
+        if cfg.quant:
+            print("the backward pass is built without the 8-bit branch", file=sys.stderr)
+            sys.exit(2)
+        bench_backward(args, cfg, x, torch, sla)
         return
     dev = torch.device("cuda:0")
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)

@@ -86,3 +86,33 @@ def backward(Q, K, V, alpha, mask, dO, phi: str = "softmax") -> Dict[str, np.nda
     (O * g).sum().backward()
     return {"dQ": q.grad.numpy(), "dK": k.grad.numpy(), "dV": v.grad.numpy(),
             "dalpha": a.grad.numpy()}
+
+
+def dq_rows(Q, K, V, alpha, mask, dO, b: int, h: int, blocks, phi: str = "softmax") -> Dict[int, np.ndarray]:
+    """dQ of the given query blocks of head (b, h), float64. The rows of O in
+    query block i depend on q only through that block's own rows, so the
+    gradient of sum(O_i * dO_i) with respect to them is dQ there; only those
+    rows' forward is formed (the same explicit definition as forward_torch)."""
+    f64 = lambda x: (x.detach().to("cpu", torch.float64) if hasattr(x, "detach")
+                     else torch.from_numpy(np.asarray(x, dtype=np.float64)))
+    k, v = f64(K[b, h]), f64(V[b, h])
+    a = float(f64(alpha).reshape(-1)[h])
+    N, d = k.shape
+    fk = torch.softmax(k, dim=-1) if phi == "softmax" else torch.nn.functional.elu(k) + 1.0
+    out = {}
+    for i in blocks:
+        t0, t1 = i * BLOCK, min((i + 1) * BLOCK, N)
+        qi = f64(Q[b, h, t0:t1]).requires_grad_(True)
+        gi = f64(dO[b, h, t0:t1])
+        crit, marg = _token_masks(np.asarray(mask)[b, h, i], N)
+        O = torch.zeros(t1 - t0, d, dtype=torch.float64)
+        if crit.any():
+            S = ((qi @ k.T) / np.sqrt(d)).masked_fill(~crit[None, :], float("-inf"))
+            O = O + a * (torch.softmax(S, dim=-1) @ v)
+        if marg.any():
+            fq = torch.softmax(qi, dim=-1) if phi == "softmax" else torch.nn.functional.elu(qi) + 1.0
+            A = (fq @ fk.T) * marg[None, :].to(torch.float64)
+            O = O + (1.0 - a) * ((A @ v) / A.sum(dim=-1, keepdim=True))
+        (O * gi).sum().backward()
+        out[int(i)] = qi.grad.numpy()
+    return out

@@ -89,3 +89,37 @@ def test_fp32_d128():
     x = make_inputs(cfg, H=2, N=300)
     x.q, x.k, x.v = x.q.float(), x.k.float(), x.v.float()
     _check(x, 1e-4)
+
+
+def test_full_size_sampled():
+    """The Wan2.1-1.3B shape (B=1, H=12, N=32760) in the launch shape the
+    benchmark times: dQ on sampled query blocks of three heads against the
+    oracle's per-block gradient, and the sum of dV over the keys against its
+    closed form, sum_t (alpha [t has a critical block] + (1 - alpha) [t has
+    a marginal one]) dO[t], on every head."""
+    cfg = CONFIGS[3]
+    x = make_inputs(cfg)
+    mask = run_gpu(x, debug=False)["mask"]
+    dO = _grad_out(x, 11)
+    dQ, dK, dV, da = sla.backward(x.q.cuda(), x.k.cuda(), x.v.cuda(), x.alpha.cuda(),
+                                  torch.from_numpy(mask).cuda(), dO.cuda())
+    torch.cuda.synchronize()
+    dQ, dV = dQ.cpu().numpy(), dV.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(12)
+    for h in (0, 5, 11):
+        blocks = sorted(rng.choice(cfg.Nb, 3, replace=False).tolist()) + [cfg.Nb - 1]
+        ref = ob.dq_rows(x.q, x.k, x.v, x.alpha, mask, dO, 0, h, blocks)
+        for i, r in ref.items():
+            e = rel_l1(dQ[0, h, 64 * i:64 * i + r.shape[0]], r)
+            _flush(f"head {h} block {i}: dQ rel-L1 {e:.2e}")
+            assert e <= 1e-2, (h, i, e)
+    g = dO.double().numpy()
+    al = x.alpha.double().numpy()
+    for h in range(cfg.H):
+        c = np.repeat((mask[0, h] == 1).any(axis=1), 64)[:x.N].astype(float)
+        m = np.repeat((mask[0, h] == 0).any(axis=1), 64)[:x.N].astype(float)
+        w = al[h] * c + (1 - al[h]) * m
+        expect = (w[:, None] * g[0, h]).sum(axis=0)
+        e = rel_l1(dV[0, h].sum(axis=0), expect)
+        assert e <= 1e-3, (h, e)
+    _flush(f"sum of dV over the keys matches its closed form on all {cfg.H} heads")

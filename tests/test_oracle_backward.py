@@ -85,3 +85,26 @@ def test_all_critical_equals_attention_autograd():
     (out * torch.from_numpy(dO)).sum().backward()
     for name, t in (("dQ", q), ("dK", k), ("dV", v)):
         np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_dq_rows_equal_the_full_gradient():
+    Q, K, V, alpha, mask, dO = _case(300, 16, H=2, seed=9)
+    g = ob.backward(Q, K, V, alpha, mask, dO)
+    rows = ob.dq_rows(Q, K, V, alpha, mask, dO, 0, 1, [0, 2, 4])
+    for i, r in rows.items():
+        np.testing.assert_allclose(r, g["dQ"][0, 1, 64 * i:64 * i + 64], rtol=1e-11, atol=1e-13)
+
+
+def test_value_gradient_sum_closed_form():
+    # both branches are row-normalised maps of V: summed over the keys, dV is
+    # sum_t (alpha [t has a critical block] + (1 - alpha) [t has a marginal one]) dO[t]
+    Q, K, V, alpha, mask, dO = _case(330, 16, H=2, seed=10)
+    mask[0, 1, 2] = -1
+    mask[0, 1, 3, :] = 1
+    g = ob.backward(Q, K, V, alpha, mask, dO)
+    for h in range(2):
+        c = np.repeat((mask[0, h] == 1).any(axis=1), 64)[:330].astype(float)
+        m = np.repeat((mask[0, h] == 0).any(axis=1), 64)[:330].astype(float)
+        w = alpha[h] * c + (1 - alpha[h]) * m
+        np.testing.assert_allclose(g["dV"][0, h].sum(axis=0), (w[:, None] * dO[0, h]).sum(axis=0),
+                                   rtol=1e-11, atol=1e-11)
