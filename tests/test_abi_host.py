@@ -167,3 +167,44 @@ def _stk(lg=0x10000, rows=4, cols=64, k=3.0, tau=1e-3, out=0x10000, lam=None):
 def test_soft_topk_argument_errors(kw):
     assert _stk(**kw) == B.SLA_ERR_ARG
     assert sla.load_library().sla_last_error()
+
+
+def _bwd(p, Q=0x10000, K=0x10000, V=0x10000, al=0x10000, m=0x10000, dO=0x10000, dQ=0x10000,
+         dK=0x10000, dV=0x10000, da=0x10000, ws=0x10000, wsb=0):
+    lib = sla.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.sla_backward(ctypes.byref(p), vp(Q), vp(K), vp(V), vp(al), vp(m), vp(dO), vp(dQ), vp(dK),
+                            vp(dV), vp(da), vp(ws), ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=None), B.SLA_ERR_ARG),            # the forward's mask is required
+    (dict(dO=None), B.SLA_ERR_ARG),
+    (dict(dK=None), B.SLA_ERR_ARG),
+    (dict(da=None), B.SLA_ERR_ARG),
+    (dict(dQ=0x10004), B.SLA_ERR_ARG),        # misaligned
+    (dict(al=0x10001), B.SLA_ERR_ARG),
+    (dict(quant=True), B.SLA_ERR_UNSUPPORTED),
+    (dict(elu=True), B.SLA_ERR_UNSUPPORTED),
+    (dict(), B.SLA_ERR_WORKSPACE),            # valid up to the workspace
+    (dict(ws=0x10080, wsb=1 << 40), B.SLA_ERR_WORKSPACE),
+])
+def test_backward_errors(kw, code):
+    p = good()
+    if kw.pop("quant", False):
+        p.quant = B.SLA_QUANT_I8QK_F8PV
+    if kw.pop("elu", False):
+        p.phi = B.SLA_PHI_ELU1
+    assert _bwd(p, **kw) == code
+    assert sla.load_library().sla_last_error()
+
+
+def test_backward_workspace_covers_the_forward():
+    lib = sla.load_library()
+    p = sla.make_problem(1, 12, 32760, 128, "bf16", 0.05, 0.10)
+    fwd, bwd = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(fwd)) == 0
+    assert lib.sla_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(bwd)) == 0
+    # the forward's regions plus lse, D_t, dH_i per query block, their total and the partials
+    Nb, NN = 512, 128 * 128 + 128
+    assert bwd.value >= fwd.value + 12 * Nb * NN * 4 and bwd.value % 256 == 0
