@@ -18,9 +18,9 @@
 //  feature map (softmax over the features): dx = phi (dphi - dphi . phi);
 //  dalpha_h = sum over the head of dO . (O_s - O_l).
 //
-// fp32 arithmetic throughout (bf16 or f32 inputs), four threads per query or
-// key token, each holding d/4 features (the layout of the forward's f32
-// kernel). H_i and Z_i come from the forward's own h/z and marginal-sum
+// fp32 arithmetic throughout (bf16 or f32 inputs), eight threads per query or
+// key token, each holding d/8 features (with four, a thread's state filled
+// 256 VGPRs and one wave ran per SIMD). H_i and Z_i come from the forward's own h/z and marginal-sum
 // kernels. k_bwd_q (one workgroup per query block) recomputes the sparse
 // forward for its log-sum-exp and O_s, then produces dQ, dH_i / dZ_i and the
 // block's dalpha partial; k_bwd_htot sums dH_i per head; k_bwd_kv (one
@@ -32,6 +32,9 @@
 namespace sla {
 namespace {
 
+constexpr int kTpt = 8;              // threads per query / key token
+constexpr int kThreads = kBlock * kTpt;  // one 64-token block per workgroup
+
 template <typename T>
 __device__ __forceinline__ float ldf(const T* p);
 template <>
@@ -39,18 +42,19 @@ __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) { return bf2f(*p); }
 
+// over the kTpt threads of a token
 __device__ __forceinline__ float sum4(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
+#pragma unroll
+  for (int o = 1; o < kTpt; o <<= 1) v += __shfl_xor(v, o);
   return v;
 }
 __device__ __forceinline__ float max4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
+#pragma unroll
+  for (int o = 1; o < kTpt; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
 
-// value r of a 4-thread group's d features (thread k of the group holds
+// value r of a token group's d features (thread k of the group holds
 // features k P .. k P + P - 1 in x[])
 template <int P>
 __device__ __forceinline__ float group_get(const float (&x)[P], int r, int lane) {
@@ -58,10 +62,10 @@ __device__ __forceinline__ float group_get(const float (&x)[P], int r, int lane)
 #pragma unroll
   for (int e = 0; e < P; ++e)
     if (e == r % P) v = x[e];
-  return __shfl(v, (lane & ~3) | (r / P));
+  return __shfl(v, (lane & ~(kTpt - 1)) | (r / P));
 }
 
-// softmax over the d features held by a 4-thread group
+// softmax over the d features held by a token group
 template <int P>
 __device__ __forceinline__ void feature_softmax(const float (&x)[P], float (&f)[P]) {
   float m = -INFINITY;
@@ -79,11 +83,34 @@ __device__ __forceinline__ void feature_softmax(const float (&x)[P], float (&f)[
   for (int e = 0; e < P; ++e) f[e] *= inv;
 }
 
+// The block indices j of a mask row with mrow[j] == value, in ascending order,
+// into list (for workgroups of kThreads); returns their number.
+__device__ int compact_row_wg(const int8_t* __restrict__ mrow, int Nb, int8_t value, uint16_t* list,
+                              int* wsum) {
+  constexpr int NW = kThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int total = 0;
+  for (int base = 0; base < Nb; base += kThreads) {
+    const int j = base + tid;
+    const bool f = (j < Nb) && (mrow[j] == value);
+    const uint64_t bal = __ballot(f);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int off = total;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (f) list[off + before] = (uint16_t)j;
+    for (int w = 0; w < NW; ++w) total += wsum[w];
+    __syncthreads();
+  }
+  return total;
+}
+
 // The 64 keys of block j (f32, zero past N) into Ks / Vs.
 template <typename T, int D>
 __device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, int j, int N, float (*Ks)[D],
                                          float (*Vs)[D]) {
-  for (int x = threadIdx.x; x < kBlock * D; x += 256) {
+  for (int x = threadIdx.x; x < kBlock * D; x += kThreads) {
     const int key = x / D, c = x % D, tk = j * kBlock + key;
     Ks[key][c] = tk < N ? ldf<T>(Kb + (size_t)tk * D + c) : 0.f;
     Vs[key][c] = tk < N ? ldf<T>(Vb + (size_t)tk * D + c) : 0.f;
@@ -91,26 +118,26 @@ __device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, int j, int N,
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_bwd_q(
+__global__ __launch_bounds__(kThreads) void k_bwd_q(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int8_t* __restrict__ mask, const T* __restrict__ Hx, const float* __restrict__ alpha,
     const T* __restrict__ dO, float* __restrict__ dQ, float* __restrict__ lse_out,
     float* __restrict__ dt_out, float* __restrict__ dHx, float* __restrict__ dal, int H, int N, int Nb) {
-  constexpr int P = D / 4;
+  constexpr int P = D / kTpt;
   constexpr int NN = D * D + D;
   __shared__ float Ks[kBlock][D];  // key tiles; then phi(Q) of the block
   __shared__ float Vs[kBlock][D];  // value tiles; then dnum of the block
   __shared__ float dd[kBlock];     // dden of the block
   __shared__ uint16_t list[kMaxNb];
-  __shared__ int wsum[4];
-  __shared__ float red[4];
+  __shared__ int wsum[kThreads / 64];
+  __shared__ float red[kThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int bh = blockIdx.y, i = blockIdx.x, h = bh % H;
-  const int row = tid >> 2, part = tid & 3;
+  const int row = tid / kTpt, part = tid % kTpt;
   const int t = i * kBlock + row;
   const bool valid = t < N;
   const size_t base = (size_t)bh * N * D;
-  const int ncrit = compact_row(mask + ((size_t)bh * Nb + i) * Nb, Nb, (int8_t)1, list, wsum);
+  const int ncrit = compact_row_wg(mask + ((size_t)bh * Nb + i) * Nb, Nb, (int8_t)1, list, wsum);
   float q[P], g[P];
 #pragma unroll
   for (int e = 0; e < P; ++e) {
@@ -251,9 +278,13 @@ __global__ __launch_bounds__(256) void k_bwd_q(
   }
   if (part == 0) dd[row] = valid ? dden : 0.f;
   __syncthreads();
-  if (tid == 0) dal[(size_t)bh * Nb + i] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (tid == 0) {
+    float sdal = 0.f;
+    for (int wv = 0; wv < kThreads / 64; ++wv) sdal += red[wv];
+    dal[(size_t)bh * Nb + i] = sdal;
+  }
   float* out = dHx + ((size_t)bh * Nb + i) * NN;
-  for (int x = tid; x < NN; x += 256) {
+  for (int x = tid; x < NN; x += kThreads) {
     float s = 0.f;
     if (x < D * D) {
       const int n = x / D, r = x % D;  // dH_i[r][n], stored like H_i
@@ -279,18 +310,18 @@ __global__ __launch_bounds__(256) void k_bwd_htot(const float* __restrict__ dHx,
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_bwd_kv(
+__global__ __launch_bounds__(kThreads) void k_bwd_kv(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int8_t* __restrict__ mask, const float* __restrict__ alpha, const T* __restrict__ dO,
     const float* __restrict__ lse_in, const float* __restrict__ dt_in, const float* __restrict__ dHx,
     const float* __restrict__ dHtot, float* __restrict__ dK, float* __restrict__ dV, int H, int N,
     int Nb) {
-  constexpr int P = D / 4;
+  constexpr int P = D / kTpt;
   constexpr int NN = D * D + D;
   __shared__ float sm[NN > 2 * kBlock * D + 2 * kBlock ? NN : 2 * kBlock * D + 2 * kBlock];
   const int tid = threadIdx.x, lane = tid & 63;
   const int bh = blockIdx.y, j = blockIdx.x, h = bh % H;
-  const int row = tid >> 2, part = tid & 3;
+  const int row = tid / kTpt, part = tid % kTpt;
   const int s = j * kBlock + row;
   const bool valid = s < N;
   const size_t base = (size_t)bh * N * D;
@@ -308,11 +339,11 @@ __global__ __launch_bounds__(256) void k_bwd_kv(
 
   // linear branch: dh_j = dH_tot - sum of dH_i over the query blocks with Mc[i, j] != 0
   float* DH = sm;  // [NN]: dh_j stored like H (DH[n D + r] = dh_j[r][n]), then dz_j
-  for (int x = tid; x < NN; x += 256) DH[x] = dHtot[(size_t)bh * NN + x];
+  for (int x = tid; x < NN; x += kThreads) DH[x] = dHtot[(size_t)bh * NN + x];
   for (int i = 0; i < Nb; ++i) {
     if (mask[((size_t)bh * Nb + i) * Nb + j] == 0) continue;  // uniform
     const float* src = dHx + ((size_t)bh * Nb + i) * NN;
-    for (int x = tid; x < NN; x += 256) DH[x] -= src[x];  // each thread owns its x
+    for (int x = tid; x < NN; x += kThreads) DH[x] -= src[x];  // each thread owns its x
   }
   __syncthreads();
   float w[P];
@@ -346,7 +377,7 @@ __global__ __launch_bounds__(256) void k_bwd_kv(
   for (int i = 0; i < Nb; ++i) {
     if (mask[((size_t)bh * Nb + i) * Nb + j] != 1) continue;  // uniform
     __syncthreads();
-    for (int x = tid; x < kBlock * D; x += 256) {
+    for (int x = tid; x < kBlock * D; x += kThreads) {
       const int tq = x / D, c = x % D, tt = i * kBlock + tq;
       Qs[tq][c] = tt < N ? ldf<T>(Q + base + (size_t)tt * D + c) : 0.f;
       Gs[tq][c] = tt < N ? al * ldf<T>(dO + base + (size_t)tt * D + c) : 0.f;
@@ -401,14 +432,14 @@ hipError_t launch_bwd_t(const Dims& Dm, const void* Q, const void* K, const void
                         float* dK, float* dV, float* dalpha, hipStream_t s) {
   constexpr int NN = D * D + D;
   const dim3 grid(Dm.Nb, Dm.BH);
-  hipLaunchKernelGGL((k_bwd_q<T, D>), grid, dim3(256), 0, s, (const T*)Q, (const T*)K, (const T*)V, mask,
+  hipLaunchKernelGGL((k_bwd_q<T, D>), grid, dim3(kThreads), 0, s, (const T*)Q, (const T*)K, (const T*)V, mask,
                      (const T*)w.Hx, alpha, (const T*)dO, dQ, bw.lse, bw.dt, bw.dHx, bw.dal, Dm.H, Dm.N, Dm.Nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_htot<D>, dim3((NN + 255) / 256, Dm.BH), dim3(256), 0, s, bw.dHx, bw.dHtot, Dm.Nb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_kv<T, D>), grid, dim3(256), 0, s, (const T*)Q, (const T*)K, (const T*)V, mask,
+  hipLaunchKernelGGL((k_bwd_kv<T, D>), grid, dim3(kThreads), 0, s, (const T*)Q, (const T*)K, (const T*)V, mask,
                      alpha, (const T*)dO, bw.lse, bw.dt, bw.dHx, bw.dHtot, dK, dV, Dm.H, Dm.N, Dm.Nb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
