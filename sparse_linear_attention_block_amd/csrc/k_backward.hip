@@ -20,7 +20,8 @@
 //
 // fp32 arithmetic throughout (bf16 or f32 inputs), eight threads per query or
 // key token, each holding d/8 features (with four, a thread's state filled
-// 256 VGPRs and one wave ran per SIMD). H_i and Z_i come from the forward's own h/z and marginal-sum
+// 256 VGPRs and one wave ran per SIMD); a token's dot products are summed
+// across its 8 lanes with DPP moves. H_i and Z_i come from the forward's own h/z and marginal-sum
 // kernels. k_bwd_q (one workgroup per query block) recomputes the sparse
 // forward for its log-sum-exp and O_s, then produces dQ, dH_i / dZ_i and the
 // block's dalpha partial; k_bwd_htot sums dH_i per head; k_bwd_kv (one
@@ -42,15 +43,27 @@ __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) { return bf2f(*p); }
 
-// over the kTpt threads of a token
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum and max over the kTpt = 8 threads of a token (8 consecutive lanes),
+// with DPP moves instead of LDS permutes: partners at lane distance 1 and 2
+// (quad permutations), then the other quad of the 8 (half-row mirror). Every
+// step combines two values both partners hold, so all 8 lanes end with the
+// same bits.
+static_assert(kTpt == 8, "the DPP reductions span 8 lanes");
 __device__ __forceinline__ float sum4(float v) {
-#pragma unroll
-  for (int o = 1; o < kTpt; o <<= 1) v += __shfl_xor(v, o);
+  v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp<0x141>(v);  // row_half_mirror
   return v;
 }
 __device__ __forceinline__ float max4(float v) {
-#pragma unroll
-  for (int o = 1; o < kTpt; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
   return v;
 }
 
