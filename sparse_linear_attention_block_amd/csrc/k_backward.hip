@@ -21,7 +21,8 @@
 // fp32 arithmetic throughout (bf16 or f32 inputs), eight threads per query or
 // key token, each holding d/8 features (with four, a thread's state filled
 // 256 VGPRs and one wave ran per SIMD); a token's dot products are summed
-// across its 8 lanes with DPP moves. H_i and Z_i come from the forward's own h/z and marginal-sum
+// across its 8 lanes with DPP moves; the per-key exponentials use the
+// hardware base-2 exponential (__expf, a few ulp). H_i and Z_i come from the forward's own h/z and marginal-sum
 // kernels. k_bwd_q (one workgroup per query block) recomputes the sparse
 // forward for its log-sum-exp and O_s, then produces dQ, dH_i / dZ_i and the
 // block's dalpha partial; k_bwd_htot sums dH_i per head; k_bwd_kv (one
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
       for (int e = 0; e < P; ++e) s = fmaf(q[e], Ks[key][part * P + e], s);
       s = sum4(s) * scale;
       const float mn = fmaxf(m, s);
-      const float corr = expf(m - mn), p = expf(s - mn);
+      const float corr = __expf(m - mn), p = __expf(s - mn);
       l = l * corr + p;
 #pragma unroll
       for (int e = 0; e < P; ++e) acc[e] = fmaf(p, Vs[key][part * P + e], acc[e] * corr);
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
       }
       s = sum4(s) * scale;
       dp = sum4(dp);
-      const float ds = expf(s - lse) * (dp - Dt) * scale;
+      const float ds = __expf(s - lse) * (dp - Dt) * scale;
 #pragma unroll
       for (int e = 0; e < P; ++e) dq[e] = fmaf(ds, Ks[key][part * P + e], dq[e]);
     }
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_kv(
       }
       sc = sum4(sc) * scale;
       dp = sum4(dp);
-      const float p = expf(sc - Ls[tq]);
+      const float p = __expf(sc - Ls[tq]);
       const float ds = p * (dp - Ds[tq]) * scale;
 #pragma unroll
       for (int e = 0; e < P; ++e) {
