@@ -123,3 +123,8 @@ def test_full_size_sampled():
         e = rel_l1(dV[0, h].sum(axis=0), expect)
         assert e <= 1e-3, (h, e)
     _flush(f"sum of dV over the keys matches its closed form on all {cfg.H} heads")
+
+
+def test_bf16_batch_of_two():
+    # the CFG-batch recipe (B = 2, per-head alpha): dalpha sums over the batch
+    _check(make_inputs(CONFIGS[4], H=3, N=500), 1e-2)
