@@ -3,6 +3,7 @@
 // kernels on the caller's stream (SLA2 and SLA formulations), and the
 // SoftTop-k entry point. No device memory is allocated here and no call
 // synchronises.
+#include <float.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -326,8 +327,15 @@ int sla_soft_topk(const double* logits, int32_t rows, int32_t cols, double k, do
     return fail(SLA_ERR_ARG, "rows must be >= 1 and cols in [1, %d] (got %d, %d)", sla::kMaxNb, rows, cols);
   if (!(k >= 0.0 && k <= (double)cols)) return fail(SLA_ERR_ARG, "k must lie in [0, cols] (got %g)", k);
   if (!(tau >= 1e-20 && tau <= 1e20)) return fail(SLA_ERR_ARG, "tau must lie in [1e-20, 1e20] (got %g)", tau);
+  // the kernel searches in float32: a budget strictly inside (0, cols) stays
+  // strictly inside when rounded, so only k = 0 and k = cols take the edge cases
+  float kf = (float)k;
+  if (k > 0.0 && k < (double)cols) {
+    if (!(kf > 0.f)) kf = FLT_MIN;
+    if (kf >= (float)cols) kf = nextafterf((float)cols, 0.f);
+  }
   (void)hipGetLastError();  // a stale error from earlier work is not ours to report
-  const hipError_t e = sla::launch_soft_topk(logits, rows, cols, (float)k, (float)tau, out, lambda,
+  const hipError_t e = sla::launch_soft_topk(logits, rows, cols, kf, (float)tau, out, lambda,
                                              (hipStream_t)stream);
   if (e != hipSuccess) return fail(SLA_ERR_HIP, "soft top-k kernel: %s", hipGetErrorString(e));
   g_err[0] = 0;

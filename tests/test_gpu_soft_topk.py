@@ -114,3 +114,14 @@ def test_deterministic():
     a = sla.soft_topk(lg, 10.0, 1e-3)[0]
     b = sla.soft_topk(lg, 10.0, 1e-3)[0]
     assert torch.equal(a, b)
+
+
+def test_budgets_next_to_the_edges():
+    # budgets a hair inside (0, cols) keep a finite threshold, as in the oracle
+    rng = np.random.default_rng(10)
+    lg = rng.standard_normal((4, 96))
+    for k in (96.0 - 1e-9, 1e-9):
+        g, lam = sla.soft_topk(torch.from_numpy(lg).cuda(), k, 1e-2)
+        torch.cuda.synchronize()
+        assert np.isfinite(lam.cpu().numpy()).all(), k
+        assert abs(float(g.sum(dim=-1).max()) - k) <= 1e-3 * max(1.0, k / 10), k
