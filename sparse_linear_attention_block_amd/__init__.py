@@ -1,13 +1,13 @@
-"""MI355X (gfx950) forward pass of SLA / SLA2 sparse-linear attention.
+"""MI355X (gfx950) SLA / SLA2 sparse-linear attention.
 
-Five hand-written HIP kernels behind the C ABI of include/sla.h:
+Hand-written HIP kernels behind the C ABI of include/sla.h. The forward pass:
 router projection + block mean pooling, compressed scores + three-way block
 classification, per-key-block linear state h_j / z_j, the marginal-block
 sums (one MFMA product per head), and block-sparse online-softmax attention
 over the critical blocks with the linear-branch output and the SLA2 mix (or
-the SLA output fusion O = O_s + Proj(O_l)) fused into its epilogue; and the
-SoftTop-k relaxation of the block selection. This package is the
-argument-marshalling binding.
+the SLA output fusion O = O_s + Proj(O_l)) fused into its epilogue. Also the
+backward pass for a fixed mask and the SoftTop-k relaxation of the block
+selection. This package is the argument-marshalling binding.
 """
 
 from ._binding import (  # noqa: F401
