@@ -122,47 +122,88 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _run(q, k, v, proj_q, proj_k, alpha, proj_o, kh, kl, mask_in, quant, out, mask_out,
-         workspace, debug, phi):
-    lib = load_library()
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+def _same_device(name, t, dev):
+    if t is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, not on q's device {dev}")
+
+
+def _check_router(name, t, H, d):
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    if tuple(t.shape) not in ((d, d), (H, d, d)):
+        raise ValueError(f"{name} must be [d, d] or [H, d, d] = [{d}, {d}] or [{H}, {d}, {d}] "
+                         f"(got {list(t.shape)})")
+
+
+def validate_forward_args(q, k, v, proj_q=None, proj_k=None, alpha=None, proj_o=None,
+                          mask_in=None, out=None, mask_out=None, require_device=True) -> int:
+    """Checks every tensor argument of a forward call before any pointer
+    reaches the library (a host tensor, or one of the wrong shape, would be
+    read out of bounds by the kernels). Returns the router / output-map head
+    stride in elements (0 or d*d); raises ValueError otherwise.
+    require_device=False skips only the "is a GPU tensor" test, so that the
+    remaining rules can be exercised on host tensors."""
+    if q.dim() != 4 or tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if require_device and not q.is_cuda:
         raise ValueError("q, k, v must be device tensors")
     if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must all be bfloat16 or all float32")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous")
     B, H, N, d = q.shape
     Nb = (N + 63) // 64
     dev = q.device
+    for name, t in (("k", k), ("v", v), ("proj_q", proj_q), ("proj_k", proj_k), ("alpha", alpha),
+                    ("proj_o", proj_o), ("mask_in", mask_in), ("out", out), ("mask_out", mask_out)):
+        _same_device(name, t, dev)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
     hs = 0
     if (proj_q is None) != (proj_k is None):
         raise ValueError("proj_q and proj_k are both given or both None")
     if proj_q is not None:
-        if proj_q.dtype != torch.float32 or proj_k.shape != proj_q.shape:
-            raise ValueError("proj_q and proj_k must be float32 tensors of one shape")
-        proj_q, proj_k = proj_q.contiguous(), proj_k.contiguous()
+        _check_router("proj_q", proj_q, H, d)
+        _check_router("proj_k", proj_k, H, d)
+        if proj_k.shape != proj_q.shape:
+            raise ValueError("proj_q and proj_k must have one shape")
         hs = d * d if proj_q.dim() == 3 else 0
     if proj_o is not None:
-        if proj_o.dtype != torch.float32 or proj_o.shape[-2:] != (d, d) or proj_o.dim() not in (2, 3):
-            raise ValueError("proj_o must be float32 [d, d] or [H, d, d]")
-        if proj_o.dim() == 3 and proj_o.shape[0] != H:
-            raise ValueError("a per-head proj_o must have H matrices")
+        _check_router("proj_o", proj_o, H, d)
         ohs = d * d if proj_o.dim() == 3 else 0
         if proj_q is not None and ohs != hs:
             raise ValueError("proj_q, proj_k and proj_o share one head stride: all [d, d] or all [H, d, d]")
         hs = ohs
+    else:
+        if alpha is None or alpha.dtype != torch.float32 or alpha.numel() != H:
+            raise ValueError("alpha must be float32 with H entries")
+    if mask_in is not None and (mask_in.dtype != torch.int8 or tuple(mask_in.shape) != (B, H, Nb, Nb)):
+        raise ValueError("mask_in must be int8 [B, H, Nb, Nb]")
+    if out is not None and (out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape)
+                            or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor of q's dtype and shape")
+    if mask_out is not None and (mask_out.dtype != torch.int8 or tuple(mask_out.shape) != (B, H, Nb, Nb)
+                                 or not mask_out.is_contiguous()):
+        raise ValueError("mask_out must be a contiguous int8 [B, H, Nb, Nb] tensor")
+    return hs
+
+
+def _run(q, k, v, proj_q, proj_k, alpha, proj_o, kh, kl, mask_in, quant, out, mask_out,
+         workspace, debug, phi):
+    lib = load_library()
+    hs = validate_forward_args(q, k, v, proj_q, proj_k, alpha, proj_o, mask_in, out, mask_out)
+    B, H, N, d = q.shape
+    Nb = (N + 63) // 64
+    dev = q.device
+    if proj_q is not None:
+        proj_q, proj_k = proj_q.contiguous(), proj_k.contiguous()
+    if proj_o is not None:
         proj_o = proj_o.contiguous()
     else:
-        if alpha.dtype != torch.float32 or alpha.numel() != H:
-            raise ValueError("alpha must be float32 with H entries")
         alpha = alpha.contiguous()
     if mask_in is not None:
-        if mask_in.dtype != torch.int8 or tuple(mask_in.shape) != (B, H, Nb, Nb):
-            raise ValueError("mask_in must be int8 [B, H, Nb, Nb]")
         mask_in = mask_in.contiguous()
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", kh, kl,
                      quant, hs, phi)
     need = workspace_bytes(p)
@@ -272,6 +313,10 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Ten
         raise ValueError("mask must be int8 [B, H, Nb, Nb]")
     if alpha.dtype != torch.float32 or alpha.numel() != H:
         raise ValueError("alpha must be float32 with H entries")
+    if not q.is_cuda:
+        raise ValueError("q, k, v and dO must be device tensors")
+    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("mask", mask), ("dO", dO), ("workspace", workspace)):
+        _same_device(name, t, q.device)
     q, k, v, dO, mask, alpha = (t.contiguous() for t in (q, k, v, dO, mask, alpha))
     p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", 0.0, 0.0)
     n = ctypes.c_size_t()
@@ -299,11 +344,14 @@ class Plan:
     def __init__(self, q, k, v, proj_q, proj_k, alpha, kh, kl, mask_in=None, quant=False,
                  phi="softmax", proj_o=None):
         lib = load_library()
+        hs = validate_forward_args(q, k, v, proj_q, proj_k, alpha, proj_o, mask_in)
+        for name, t in (("proj_q", proj_q), ("proj_k", proj_k), ("alpha", alpha), ("proj_o", proj_o),
+                        ("mask_in", mask_in)):
+            if t is not None and not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous (a Plan keeps raw pointers to it)")
         B, H, N, d = q.shape
         Nb = (N + 63) // 64
         dev = q.device
-        hs = d * d if ((proj_q is not None and proj_q.dim() == 3) or
-                       (proj_o is not None and proj_o.dim() == 3)) else 0
         self.problem = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32",
                                     kh, kl, quant, hs, phi)
         self.sla1 = proj_o is not None

@@ -208,3 +208,80 @@ def test_backward_workspace_covers_the_forward():
     # the forward's regions plus lse, D_t, dH_i per query block, their total and the partials
     Nb, NN = 512, 128 * 128 + 128
     assert bwd.value >= fwd.value + 12 * Nb * NN * 4 and bwd.value % 256 == 0
+
+
+# ---- the Python binding's argument checks (host tensors; require_device=False
+# lets every other rule be exercised without a GPU)
+
+def _fwd_tensors(B=1, H=2, N=100, d=64, dtype=None):
+    import torch
+    dt = dtype or torch.bfloat16
+    q = torch.zeros(B, H, N, d, dtype=dt)
+    Nb = (N + 63) // 64
+    return dict(q=q, k=q.clone(), v=q.clone(), proj_q=torch.eye(d), proj_k=torch.eye(d),
+                alpha=torch.full((H,), 0.5), mask_in=torch.zeros(B, H, Nb, Nb, dtype=torch.int8),
+                out=torch.empty_like(q), mask_out=torch.empty(B, H, Nb, Nb, dtype=torch.int8))
+
+
+def test_binding_accepts_valid_arguments():
+    import torch
+    t = _fwd_tensors()
+    assert B.validate_forward_args(**t, require_device=False) == 0
+    t["proj_q"] = torch.zeros(2, 64, 64)
+    t["proj_k"] = torch.zeros(2, 64, 64)
+    assert B.validate_forward_args(**t, require_device=False) == 64 * 64
+    t = _fwd_tensors()
+    t.update(proj_q=None, proj_k=None, alpha=None, proj_o=torch.eye(64))
+    assert B.validate_forward_args(**t, require_device=False) == 0
+
+
+def _bad(change):
+    import torch
+    t = _fwd_tensors()
+    change(t, torch)
+    return t
+
+
+@pytest.mark.parametrize("change,match", [
+    (lambda t, torch: t.update(k=torch.zeros(1, 2, 99, 64, dtype=torch.bfloat16)), "share one"),
+    (lambda t, torch: t.update(v=t["v"].float()), "bfloat16 or all float32"),
+    (lambda t, torch: t.update(q=t["q"].half(), k=t["k"].half(), v=t["v"].half(),
+                               out=t["out"].half()), "bfloat16 or all float32"),
+    (lambda t, torch: t.update(q=t["q"].transpose(2, 3).contiguous().transpose(2, 3)), "contiguous"),
+    (lambda t, torch: t.update(proj_q=torch.eye(32), proj_k=torch.eye(32)), r"\[d, d\] or \[H, d, d\]"),
+    (lambda t, torch: t.update(proj_q=torch.zeros(3, 64, 64), proj_k=torch.zeros(3, 64, 64)),
+     r"\[d, d\] or \[H, d, d\]"),
+    (lambda t, torch: t.update(proj_q=torch.eye(64, dtype=torch.float64)), "float32"),
+    (lambda t, torch: t.update(proj_k=torch.zeros(2, 64, 64)), "one shape"),
+    (lambda t, torch: t.update(proj_k=None), "both given"),
+    (lambda t, torch: t.update(alpha=torch.full((3,), 0.5)), "alpha"),
+    (lambda t, torch: t.update(alpha=torch.full((2,), 0.5, dtype=torch.float64)), "alpha"),
+    (lambda t, torch: t.update(alpha=None), "alpha"),
+    (lambda t, torch: t.update(proj_o=torch.eye(64), proj_q=torch.zeros(2, 64, 64),
+                               proj_k=torch.zeros(2, 64, 64)), "head stride"),
+    (lambda t, torch: t.update(proj_o=torch.eye(48)), r"\[d, d\] or \[H, d, d\]"),
+    (lambda t, torch: t.update(mask_in=torch.zeros(1, 2, 2, 3, dtype=torch.int8)), "mask_in"),
+    (lambda t, torch: t.update(mask_in=torch.zeros(1, 2, 2, 2, dtype=torch.int32)), "mask_in"),
+    (lambda t, torch: t.update(out=torch.empty(1, 2, 100, 64)), "out"),
+    (lambda t, torch: t.update(out=torch.empty(1, 2, 99, 64, dtype=torch.bfloat16)), "out"),
+    (lambda t, torch: t.update(mask_out=torch.empty(1, 2, 2, 2, dtype=torch.int16)), "mask_out"),
+    (lambda t, torch: t.update(mask_out=torch.empty(1, 2, 3, 2, dtype=torch.int8)), "mask_out"),
+    (lambda t, torch: t.update(alpha=torch.full((2,), 0.5, device="meta")), "not on q's device"),
+    (lambda t, torch: t.update(proj_q=torch.eye(64, device="meta")), "not on q's device"),
+    (lambda t, torch: t.update(out=torch.empty(1, 2, 100, 64, dtype=torch.bfloat16, device="meta")),
+     "not on q's device"),
+])
+def test_binding_rejects(change, match):
+    with pytest.raises(ValueError, match=match):
+        B.validate_forward_args(**_bad(change), require_device=False)
+
+
+def test_binding_requires_device_tensors():
+    with pytest.raises(ValueError, match="device tensors"):
+        B.validate_forward_args(**_fwd_tensors())
+    import torch
+    t = _fwd_tensors()
+    with pytest.raises(ValueError, match="device tensors"):
+        sla.backward(t["q"], t["k"], t["v"], t["alpha"], t["mask_in"], t["q"])
+    with pytest.raises(ValueError, match="device tensors"):
+        sla.forward(t["q"], t["k"], t["v"], t["proj_q"], t["proj_k"], t["alpha"], 0.25, 0.25)
