@@ -37,6 +37,8 @@
  *  - The library allocates no device memory and keeps no state between calls:
  *    the caller owns every buffer, including the workspace sized by
  *    sla_workspace_bytes(). Calls are reentrant if their workspaces differ.
+ *    The one exception is sla_forward_noalloc, whose scratch is a fixed array
+ *    that the library holds on each GPU (see its declaration).
  *  - Argument errors are reported before anything is enqueued, with outputs
  *    untouched. No C++ exception crosses this interface.
  */
@@ -185,6 +187,27 @@ int sla1_forward_debug(const sla_problem* p,
                        void* O, int8_t* mask_out,
                        void* workspace, size_t workspace_bytes,
                        void* stream, const sla_debug* dbg);
+
+/* Bytes of device scratch that sla_forward_noalloc holds per GPU (160 MiB). */
+#define SLA_NOALLOC_SCRATCH_BYTES (160u * 1024u * 1024u)
+
+/* sla_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Every argument is as for sla_forward. The
+ * intermediate buffers live in a scratch array of SLA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it is loaded on, until the process ends;
+ * the current device's copy is used (the stream must belong to that device).
+ * No device memory is allocated or freed by this call. Problems whose
+ * workspace (sla_workspace_bytes) exceeds the scratch return SLA_ERR_WORKSPACE
+ * before any work. All calls on one GPU share its scratch and it keeps the
+ * last call's contents: calls that overlap on one GPU (two streams, or two
+ * host threads) race and must be serialised by the caller. */
+int sla_forward_noalloc(const sla_problem* p,
+                        const void* Q, const void* K, const void* V,
+                        const float* proj_q, const float* proj_k, const float* alpha,
+                        const int8_t* mask_in,
+                        void* O, int8_t* mask_out,
+                        void* stream);
 
 /* Workspace that sla_backward needs for `p` (host only, no device work).
  * Returns SLA_OK or the validation error sla_backward would return. */

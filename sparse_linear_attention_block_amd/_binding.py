@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sla1_forward.restype = ctypes.c_int
     lib.sla1_forward_debug.argtypes = _FWD_ARGS + [ctypes.POINTER(Debug)]
     lib.sla1_forward_debug.restype = ctypes.c_int
+    lib.sla_forward_noalloc.argtypes = _FWD_ARGS[:10] + [ctypes.c_void_p]
+    lib.sla_forward_noalloc.restype = ctypes.c_int
     lib.sla_backward_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
     lib.sla_backward_workspace_bytes.restype = ctypes.c_int
     lib.sla_backward.argtypes = [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 + [ctypes.c_void_p, ctypes.c_size_t,
@@ -254,6 +256,39 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """
     return _run(q, k, v, proj_q, proj_k, alpha, None, kh, kl, mask_in, quant, out, mask_out,
                 workspace, debug, phi)
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the per-GPU scratch that forward_noalloc uses (SLA_NOALLOC_SCRATCH_BYTES)."""
+    return 160 * 1024 * 1024
+
+
+def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    proj_q: Optional[torch.Tensor], proj_k: Optional[torch.Tensor], alpha: torch.Tensor,
+                    kh: float, kl: float, out: torch.Tensor, mask_in: Optional[torch.Tensor] = None,
+                    mask_out: Optional[torch.Tensor] = None, *, quant: bool = False,
+                    phi: str = "softmax"):
+    """SLA2 forward without a workspace (sla_forward_noalloc): the library's
+    per-GPU scratch holds the intermediates, so this call allocates nothing on
+    the device. The caller passes the output `out` (q's dtype and shape) and,
+    unless mask_in is given, `mask_out` (int8 [B, H, Nb, Nb]). Returns
+    (out, mask). Calls that overlap on one GPU race on the shared scratch."""
+    lib = load_library()
+    validate_forward_args(q, k, v, proj_q, proj_k, alpha, None, mask_in, out, mask_out)
+    if out is None or (mask_in is None and mask_out is None):
+        raise ValueError("forward_noalloc needs out, and mask_out unless mask_in is given")
+    for name, t in (("proj_q", proj_q), ("proj_k", proj_k), ("alpha", alpha), ("mask_in", mask_in)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (this call may not copy)")
+    B, H, N, d = q.shape
+    hs = d * d if (proj_q is not None and proj_q.dim() == 3) else 0
+    p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", kh, kl, quant, hs, phi)
+    with torch.cuda.device(q.device):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+        rc = lib.sla_forward_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q), _ptr(proj_k),
+                                     _ptr(alpha), _ptr(mask_in), _ptr(out), _ptr(mask_out), stream)
+    _check(rc)
+    return out, (mask_out if mask_out is not None else mask_in)
 
 
 def forward_sla1(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj_o: torch.Tensor,

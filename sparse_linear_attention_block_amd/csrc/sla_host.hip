@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sla_internal.h"
 
 namespace {
@@ -316,6 +318,72 @@ int sla1_forward(const sla_problem* p, const void* Q, const void* K, const void*
                  size_t workspace_bytes, void* stream) {
   return sla1_forward_debug(p, Q, K, V, proj_q, proj_k, proj_o, mask_in, O, mask_out, workspace,
                             workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free forward pass
+//
+// Scratch of sla_forward_noalloc: one file-scope device array per GPU (every
+// device that loads this library holds its own copy until the process ends).
+// Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in symbol); it resolves the device address once per device with
+// hipGetSymbolAddress and uses that.
+static __device__ __align__(256) unsigned char scratch[SLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, resolved on its first use on that
+// device (with the device current); nullptr on failure (g_err set).
+void* scratch_ptr(int* status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = fail(SLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = fail(SLA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev,
+                   kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *status = fail(SLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int sla_forward_noalloc(const sla_problem* p, const void* Q, const void* K, const void* V,
+                        const float* proj_q, const float* proj_k, const float* alpha,
+                        const int8_t* mask_in, void* O, int8_t* mask_out, void* stream) {
+  sla::Dims D;
+  const int rc = make_dims(p, &D);
+  if (rc != SLA_OK) return rc;
+  const size_t need = sla::carve(D, nullptr, nullptr);
+  if (need > (size_t)SLA_NOALLOC_SCRATCH_BYTES)
+    return fail(SLA_ERR_WORKSPACE,
+                "this problem needs %zu bytes of scratch; sla_forward_noalloc holds %zu (use sla_forward "
+                "with a workspace)", need, (size_t)SLA_NOALLOC_SCRATCH_BYTES);
+  int status = SLA_OK;
+  void* ws = scratch_ptr(&status);
+  if (!ws) return status;
+  return run_forward(p, Q, K, V, proj_q, proj_k, alpha, nullptr, mask_in, O, mask_out, ws,
+                     (size_t)SLA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int sla_soft_topk(const double* logits, int32_t rows, int32_t cols, double k, double tau, float* out,

@@ -285,3 +285,23 @@ def test_binding_requires_device_tensors():
         sla.backward(t["q"], t["k"], t["v"], t["alpha"], t["mask_in"], t["q"])
     with pytest.raises(ValueError, match="device tensors"):
         sla.forward(t["q"], t["k"], t["v"], t["proj_q"], t["proj_k"], t["alpha"], 0.25, 0.25)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "sla.h")).read()
+    m = re.search(r"#define SLA_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", text)
+    assert m and int(m.group(1)) * 2 ** 20 == sla.noalloc_scratch_bytes()
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """Host-only: the size check returns before any device work."""
+    lib = sla.load_library()
+    p = sla.make_problem(1, 12, 32760, 128, "bf16", 0.05, 0.10)
+    assert sla.workspace_bytes(p) > sla.noalloc_scratch_bytes()
+    fake = ctypes.c_void_p(0x10000)
+    rc = lib.sla_forward_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake, fake, None)
+    assert rc == B.SLA_ERR_WORKSPACE
+    assert b"scratch" in lib.sla_last_error()
+    bad = sla.make_problem(1, 12, 100, 96, "bf16", 0.05, 0.10)   # d = 96 is not built
+    assert lib.sla_forward_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, fake, fake,
+                                   None) == B.SLA_ERR_UNSUPPORTED
