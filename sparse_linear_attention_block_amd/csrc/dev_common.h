@@ -212,41 +212,45 @@ __device__ inline int compact_row(const int8_t* __restrict__ mrow, int Nb, int8_
 
 // The same compaction in two parts, so that a kernel can load the mask row
 // first, issue its other prologue loads, and wait only for the mask: mask_load
-// reads bytes j = tid + 256 k of the row for k < kMaskPre (every load is issued;
+// reads bytes j = tid + NT k of the row for k < kMaskPre (every load is issued;
 // indices past the row re-read its last byte and are ignored), compact_loaded
 // builds the list from them with one barrier for all chunks; rows longer than
-// 256 kMaskPre blocks finish chunk by chunk as in compact_row. wsum holds
-// 4 kMaskPre ints.
+// NT kMaskPre blocks finish chunk by chunk as in compact_row. NT is the
+// workgroup's thread count (a multiple of 64); wsum holds (NT / 64) kMaskPre ints.
 constexpr int kMaskPre = 8;
+template <int NT = 256>
 __device__ __forceinline__ void mask_load(const int8_t* __restrict__ mrow, int Nb,
                                           int8_t (&mv)[kMaskPre]) {
 #pragma unroll
-  for (int k = 0; k < kMaskPre; ++k) mv[k] = mrow[min((int)threadIdx.x + 256 * k, Nb - 1)];
+  for (int k = 0; k < kMaskPre; ++k) mv[k] = mrow[min((int)threadIdx.x + NT * k, Nb - 1)];
 }
+template <int NT = 256>
 __device__ inline int compact_loaded(const int8_t (&mv)[kMaskPre], const int8_t* __restrict__ mrow,
                                      int Nb, int8_t value, uint16_t* list, int* wsum) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int before[kMaskPre];
   uint32_t fbits = 0;
 #pragma unroll
   for (int k = 0; k < kMaskPre; ++k) {
-    const bool f = tid + 256 * k < Nb && mv[k] == value;
+    const bool f = tid + NT * k < Nb && mv[k] == value;
     const uint64_t bal = __ballot(f);
     before[k] = __popcll(bal & ((1ull << lane) - 1ull));
     fbits |= (uint32_t)f << k;
-    if (lane == 0) wsum[4 * k + wave] = __popcll(bal);
+    if (lane == 0) wsum[NW * k + wave] = __popcll(bal);
   }
   __syncthreads();
   int total = 0;
 #pragma unroll
   for (int k = 0; k < kMaskPre; ++k) {
     int off = total;
-    for (int w = 0; w < wave; ++w) off += wsum[4 * k + w];
-    if ((fbits >> k) & 1) list[off + before[k]] = (uint16_t)(tid + 256 * k);
-    total += wsum[4 * k] + wsum[4 * k + 1] + wsum[4 * k + 2] + wsum[4 * k + 3];
+    for (int w = 0; w < wave; ++w) off += wsum[NW * k + w];
+    if ((fbits >> k) & 1) list[off + before[k]] = (uint16_t)(tid + NT * k);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) total += wsum[NW * k + w];
   }
   __syncthreads();
-  for (int base = 256 * kMaskPre; base < Nb; base += 256) {
+  for (int base = NT * kMaskPre; base < Nb; base += NT) {
     const int j = base + tid;
     const bool f = (j < Nb) && (mrow[j] == value);
     const uint64_t bal = __ballot(f);
@@ -256,7 +260,8 @@ __device__ inline int compact_loaded(const int8_t (&mv)[kMaskPre], const int8_t*
     int off = total;
     for (int w = 0; w < wave; ++w) off += wsum[w];
     if (f) list[off + bef] = (uint16_t)j;
-    total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) total += wsum[w];
     __syncthreads();
   }
   return total;

@@ -52,6 +52,8 @@
 // key tiles, which then come from the XCD's L2.
 //
 // f32 path: 4 threads per query, plain FMA, one key at a time.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "sla_internal.h"
@@ -62,33 +64,41 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D>
+template <int D, int NW>
 struct FaCfg {
+  static constexpr int NT = 64 * NW;               // threads of a workgroup
+  static constexpr int QG = 4 / NW;                // 16-query groups a wave owns
   static constexpr int C = D / 8;                  // 16-byte chunks per K row
   static constexpr int HT = 32 * D;                // elements of one half tile (32 keys) of K or of V^T
-  static constexpr int INSTR = HT / 8 / 256;       // 16-byte async copies per lane per operand and step
+  static constexpr int INSTR = HT / 8 / NT;        // 16-byte async copies per lane per operand and step
   static constexpr int NN = D * D + D;
   static constexpr int KSTEPS = D / 32;
   static constexpr int FT = D / 16;                // feature tiles of O
   static constexpr int OS = D + 8;                 // LDS row stride of the staged output
   static constexpr int HROWS = 2 * HT / D;         // rows of H_i^T one step buffer holds (64)
   static constexpr int HPARTS = D / HROWS;         // buffers H_i^T takes (2 at d = 128, 1 at d = 64)
-  static constexpr int HINSTR = HROWS * D / 8 / 256;  // 16-byte copies per lane of one part
+  static constexpr int HINSTR = HROWS * D / 8 / NT;  // 16-byte copies per lane of one part
 };
 
-// Workgroup: 4 waves, one query block (64 queries). Wave w owns queries
-// 16w .. 16w+15 against every key, so its softmax needs no partner; the keys
-// of a critical tile are taken 32 at a time (a step), so that each product is a
-// full-rate 16x16x32 MFMA (P.V contracts over the step's 32 keys), the step
-// buffers are 16 KB and three workgroups fit on a CU.
-template <int D, bool PROJ, bool ELU>
-__global__ __launch_bounds__(256, 3) void k_sparse_bf16(
+// Workgroup: NW waves, one query block (64 queries). Wave w owns the QG = 4/NW
+// groups of 16 queries 16 QG w .. 16 QG w + 16 QG - 1 against every key, so
+// its softmax needs no partner; every K and V^T fragment a wave reads from LDS
+// feeds the products of all its query groups, so two groups per wave (NW = 2)
+// halve the LDS bytes per flop of one group per wave (NW = 4). The keys of a
+// critical tile are taken 32 at a time (a step), so that each product is a
+// full-rate 16x16x32 MFMA (P.V contracts over the step's 32 keys) and the step
+// buffers are 16 KB. The critical list lives in dynamic LDS of
+// max(2 Nb, 2 D) bytes.
+template <int D, int NW, bool PROJ, bool ELU>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 2 : 3, NW == 2 ? 2 : 3)))
+void k_sparse_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const int8_t* __restrict__ mask,
     const uint16_t* __restrict__ Hx, const float* __restrict__ alpha,
     const uint16_t* __restrict__ wo, int wo_hs, uint16_t* __restrict__ O,
     float* __restrict__ dbg_os, float* __restrict__ dbg_ol, int H, int N, int Nb) {
-  using Cf = FaCfg<D>;
+  using Cf = FaCfg<D, NW>;
+  constexpr int NT = Cf::NT, QG = Cf::QG;
   constexpr int C = Cf::C, HT = Cf::HT, INSTR = Cf::INSTR, NN = Cf::NN;
   constexpr int KSTEPS = Cf::KSTEPS, FT = Cf::FT, OS = Cf::OS;
   constexpr int HROWS = Cf::HROWS, HPARTS = Cf::HPARTS, HINSTR = Cf::HINSTR;
@@ -98,8 +108,8 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
   // asynchronous copies into the other.
   __shared__ __attribute__((aligned(16))) uint16_t bufA[2 * HT];
   __shared__ __attribute__((aligned(16))) uint16_t bufB[2 * HT];
-  __shared__ __attribute__((aligned(16))) uint16_t list[kMaxNb];  // critical list, then Z_i
-  __shared__ int wsum[4 * kMaskPre];
+  extern __shared__ __attribute__((aligned(16))) uint16_t list[];  // critical list, then Z_i
+  __shared__ int wsum[NW * kMaskPre];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS addresses
@@ -108,20 +118,21 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
   const int bh = id / Nb, i = id - bh * Nb;
   const int h = bh % H;
 
-  // the mask row first, then the wave's 16 queries as MFMA B operands:
+  // the mask row first, then the wave's queries as MFMA B operands:
   // Q[t][32ks + 8g .. +7] (they land while the critical list is compacted)
   const int8_t* mrow = mask + ((size_t)bh * Nb + i) * Nb;
   int8_t mv[kMaskPre];
-  mask_load(mrow, Nb, mv);
-  uint4 qr[KSTEPS];
-  {
-    const int t = min(i * kBlock + 16 * wave + l16, N - 1);  // rows past N are never stored
+  mask_load<NT>(mrow, Nb, mv);
+  uint4 qr[QG][KSTEPS];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const int t = min(i * kBlock + 16 * (QG * wave + qg) + l16, N - 1);  // rows past N are never stored
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
-      qr[ks] = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + t) * D + 32 * ks + 8 * g);
+      qr[qg][ks] = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + t) * D + 32 * ks + 8 * g);
   }
 
-  const int ncrit = compact_loaded(mv, mrow, Nb, (int8_t)1, list, wsum);
+  const int ncrit = compact_loaded<NT>(mv, mrow, Nb, (int8_t)1, list, wsum);
   const int nstep = 2 * ncrit;  // step s: keys 32 (s & 1) .. +31 of critical tile s >> 1
 
   const uint16_t* Kb = K + (size_t)bh * N * D;
@@ -133,7 +144,7 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
   int koff[INSTR];
 #pragma unroll
   for (int u = 0; u < INSTR; ++u) {
-    const int G = 64 * (4 * u + wave) + lane;
+    const int G = 64 * (NW * u + wave) + lane;
     const int r = G / C, sch = G % C;
     koff[u] = r * D + (sch ^ (r & (C - 1))) * 8;
   }
@@ -152,14 +163,14 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
 #pragma unroll
       for (int u = 0; u < INSTR; ++u) {
         const int off = koff[u] - max(0, koff[u] / D + over) * D;
-        load_lds16_buf(krs, 2 * off, sk, dst + 512 * (4 * u + wave));
-        load_lds16_buf(vrs, (64 * (4 * u + wave) + lane) * 16, sv, dst + HT + 512 * (4 * u + wave));
+        load_lds16_buf(krs, 2 * off, sk, dst + 512 * (NW * u + wave));
+        load_lds16_buf(vrs, (64 * (NW * u + wave) + lane) * 16, sv, dst + HT + 512 * (NW * u + wave));
       }
     } else {
 #pragma unroll
       for (int u = 0; u < INSTR; ++u) {
-        load_lds16_buf(krs, 2 * koff[u], sk, dst + 512 * (4 * u + wave));
-        load_lds16_buf(vrs, (64 * (4 * u + wave) + lane) * 16, sv, dst + HT + 512 * (4 * u + wave));
+        load_lds16_buf(krs, 2 * koff[u], sk, dst + 512 * (NW * u + wave));
+        load_lds16_buf(vrs, (64 * (NW * u + wave) + lane) * 16, sv, dst + HT + 512 * (NW * u + wave));
       }
     }
   };
@@ -170,27 +181,34 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
   auto issueH = [&](int part, uint16_t* dst) {
 #pragma unroll
     for (int u = 0; u < HINSTR; ++u) {
-      const int G = 64 * (4 * u + wave) + lane;
+      const int G = 64 * (NW * u + wave) + lane;
       const int r = G / C, sch = G % C;
-      load_lds16(Hrow + (part * HROWS + r) * D + (sch ^ (r & (C - 1))) * 8, dst + 512 * (4 * u + wave));
+      load_lds16(Hrow + (part * HROWS + r) * D + (sch ^ (r & (C - 1))) * 8, dst + 512 * (NW * u + wave));
     }
     if (part == 0 && wave == 0 && lane < C) load_lds16(Hrow + D * D + 8 * lane, zbuf);
   };
 
   const float sc = kLog2e / sqrtf((float)D);
-  f32x4 acc[FT];
+  f32x4 acc[QG][FT];
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) acc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mref = -INFINITY;
+  for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) acc[qg][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mref[QG];
   // Row sums of P come out of the MFMA unit: an A operand whose row 0 is all
   // ones gives sum_k P[k][q] in row 0 of the product (lane group 0, register 0)
   // and is rescaled together with acc.
-  f32x4 accl = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accl[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    mref[qg] = -INFINITY;
+    accl[qg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const uint32_t one2 = l16 == 0 ? 0x3f803f80u : 0u;  // two bf16 ones in row 0
   const uint4 ones = make_uint4(one2, one2, one2, one2);
 
   // one step: wait for its half tile, start the copy of the next one into the
-  // other buffer, S^T, online softmax against the wave's reference max,
+  // other buffer, S^T, online softmax against each group's reference max,
   // O^T += V^T P^T
   auto step = [&](int s, const uint16_t* cur, uint16_t* nxt) {
     const int j = __builtin_amdgcn_readfirstlane((int)list[s >> 1]);
@@ -214,12 +232,15 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     else
       issueH(0, nxt);  // every wave has read list[s >> 1]: the list area is free
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 sv[2];  // [key tile]
-    sv[0] = sv[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 sv[QG][2];  // [query group][key tile]
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) sv[qg][0] = sv[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) sv[kt] = mfma_bf16(ka[ks][kt], qr[ks], sv[kt]);
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) sv[qg][kt] = mfma_bf16(ka[ks][kt], qr[qg][ks], sv[qg][kt]);
     // the V^T fragments of the step load while the softmax runs
     const uint16_t* vtile = cur + HT;
     uint4 va[FT];
@@ -232,35 +253,53 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     if (j * kBlock + 32 * hh + 32 > N) {  // ragged last block: keys past N take no part
       const int kbase = j * kBlock + 32 * hh + 4 * g;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv[kt][r] = kbase + 16 * kt + r >= N ? -INFINITY : sv[kt][r];
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sv[qg][kt][r] = kbase + 16 * kt + r >= N ? -INFINITY : sv[qg][kt][r];
     }
     // Reference max: raised only when some score exceeds it by more than 2^8
     // (rare after the first step); the 4 lane groups of a query then agree on
     // the new value through a cross-group max, and acc / l are rescaled.
-    const float lmax = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                             fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3]))) * sc;
-    if (__ballot(lmax > mref + TAU)) {
-      const float tm = group4_max(lmax);
-      const float nref = tm > mref + TAU ? tm : mref;
-      const float fac = nref == mref ? 1.0f : __builtin_amdgcn_exp2f(mref - nref);
-      mref = nref;
-      accl *= fac;
+    float lmax[QG];
+    bool raise = false;
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) acc[ft] *= fac;
+    for (int qg = 0; qg < QG; ++qg) {
+      lmax[qg] = fmaxf(fmaxf(fmaxf(sv[qg][0][0], sv[qg][0][1]), fmaxf(sv[qg][0][2], sv[qg][0][3])),
+                       fmaxf(fmaxf(sv[qg][1][0], sv[qg][1][1]), fmaxf(sv[qg][1][2], sv[qg][1][3]))) * sc;
+      raise = raise || lmax[qg] > mref[qg] + TAU;
     }
-    const float meff = mref == -INFINITY ? 0.0f : mref;  // no valid key yet: every p is 0
-    float p[2][4];
+    if (__ballot(raise)) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int qg = 0; qg < QG; ++qg) {
+        const float tm = group4_max(lmax[qg]);
+        const float nref = tm > mref[qg] + TAU ? tm : mref[qg];
+        const float fac = nref == mref[qg] ? 1.0f : __builtin_amdgcn_exp2f(mref[qg] - nref);
+        mref[qg] = nref;
+        accl[qg] *= fac;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[kt][r] = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], sc, -meff));
-    const uint4 pb = make_uint4(pack_bf2(p[0][0], p[0][1]), pack_bf2(p[0][2], p[0][3]),
-                                pack_bf2(p[1][0], p[1][1]), pack_bf2(p[1][2], p[1][3]));
+        for (int ft = 0; ft < FT; ++ft) acc[qg][ft] *= fac;
+      }
+    }
+    uint4 pb[QG];
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) acc[ft] = mfma_bf16(va[ft], pb, acc[ft]);
-    accl = mfma_bf16(ones, pb, accl);
+    for (int qg = 0; qg < QG; ++qg) {
+      const float meff = mref[qg] == -INFINITY ? 0.0f : mref[qg];  // no valid key yet: every p is 0
+      float p[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[kt][r] = __builtin_amdgcn_exp2f(fmaf(sv[qg][kt][r], sc, -meff));
+      pb[qg] = make_uint4(pack_bf2(p[0][0], p[0][1]), pack_bf2(p[0][2], p[0][3]),
+                          pack_bf2(p[1][0], p[1][1]), pack_bf2(p[1][2], p[1][3]));
+    }
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) acc[qg][ft] = mfma_bf16(va[ft], pb[qg], acc[qg][ft]);
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) accl[qg] = mfma_bf16(ones, pb[qg], accl[qg]);
   };
   if (nstep > 0)
     issue(list[0], 0, bufA);
@@ -271,50 +310,57 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     step(s + 1, bufB, bufA);
   }
 
-  // ---- epilogue: O_s = acc / l; phi(Q) of the wave's 16 queries; den =
+  // ---- epilogue: O_s = acc / l; phi(Q) of the wave's queries; den =
   // phi(Q).Z_i and num^T = H_i^T phi(Q)^T on MFMA; the mix; full-row stores.
   // H_i^T part 0 went into bufA during the last step (in the prologue when
   // there was no step); part 1 (d = 128) follows into bufB.
-  const float lw = __shfl(accl[0], l16);  // from lane group 0
-  const float inv_l = lw > 0.f ? 1.0f / lw : 0.f;
+  float inv_l[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const float lw = __shfl(accl[qg][0], l16);  // from lane group 0
+    inv_l[qg] = lw > 0.f ? 1.0f / lw : 0.f;
+  }
   if constexpr (HPARTS == 2) {
     lds_barrier();  // every wave is done with bufB
     issueH(1, bufB);
   }
-  float qf[KSTEPS * 8];
+  uint4 fq[QG][KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    const uint32_t w4[4] = {qr[ks].x, qr[ks].y, qr[ks].z, qr[ks].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qf[ks * 8 + 2 * e] = bf_lo(w4[e]);
-      qf[ks * 8 + 2 * e + 1] = bf_hi(w4[e]);
-    }
-  }
-  uint4 fq[KSTEPS];
-  if constexpr (ELU) {  // phi = elu + 1, elementwise
+  for (int qg = 0; qg < QG; ++qg) {
+    float qf[KSTEPS * 8];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      uint32_t w4[4];
+      const uint32_t w4[4] = {qr[qg][ks].x, qr[qg][ks].y, qr[qg][ks].z, qr[qg][ks].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w4[e] = pack_bf2(elu1(qf[ks * 8 + 2 * e]), elu1(qf[ks * 8 + 2 * e + 1]));
-      fq[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      for (int e = 0; e < 4; ++e) {
+        qf[ks * 8 + 2 * e] = bf_lo(w4[e]);
+        qf[ks * 8 + 2 * e + 1] = bf_hi(w4[e]);
+      }
     }
-  } else {
-    float qm = -INFINITY;
+    if constexpr (ELU) {  // phi = elu + 1, elementwise
 #pragma unroll
-    for (int e = 0; e < KSTEPS * 8; ++e) qm = fmaxf(qm, qf[e]);
-    qm = group4_max(qm) * kLog2e;
-    // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
-    // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        uint32_t w4[4];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      uint32_t w4[4];
+        for (int e = 0; e < 4; ++e) w4[e] = pack_bf2(elu1(qf[ks * 8 + 2 * e]), elu1(qf[ks * 8 + 2 * e + 1]));
+        fq[qg][ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+    } else {
+      float qm = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w4[e] = pack_bf2(__builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e], kLog2e, -qm)),
-                         __builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e + 1], kLog2e, -qm)));
-      fq[ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      for (int e = 0; e < KSTEPS * 8; ++e) qm = fmaxf(qm, qf[e]);
+      qm = group4_max(qm) * kLog2e;
+      // e = exp(q - max q); phi(Q) = e / sum(e), but the sum cancels between the
+      // numerator phi(Q) H_i and the denominator phi(Q) Z_i, so e enters both unscaled
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w4[e] = pack_bf2(__builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e], kLog2e, -qm)),
+                           __builtin_amdgcn_exp2f(fmaf(qf[ks * 8 + 2 * e + 1], kLog2e, -qm)));
+        fq[qg][ks] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
     }
   }
   // part 0 of H_i^T and Z_i have landed (part 1's copies, issued after them, may not)
@@ -324,26 +370,38 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_barrier();
   // den: an A operand whose row 0 is Z_i gives phi(Q).Z_i in row 0 of the product
-  f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float inv_den[QG];
+  {
+    f32x4 dacc[QG];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    const uint4 z = *reinterpret_cast<const uint4*>(zbuf + 32 * ks + 8 * g);
-    dacc = mfma_bf16(l16 == 0 ? z : make_uint4(0u, 0u, 0u, 0u), fq[ks], dacc);
+    for (int qg = 0; qg < QG; ++qg) dacc[qg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const uint4 z = *reinterpret_cast<const uint4*>(zbuf + 32 * ks + 8 * g);
+      const uint4 za = l16 == 0 ? z : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) dacc[qg] = mfma_bf16(za, fq[qg][ks], dacc[qg]);
+    }
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      const float den = __shfl(dacc[qg][0], l16);  // from lane group 0
+      inv_den[qg] = den > 0.f ? 1.0f / den : 0.f;
+    }
   }
-  const float den = __shfl(dacc[0], l16);  // from lane group 0
-  const float inv_den = den > 0.f ? 1.0f / den : 0.f;
-  f32x4 nm[FT];
+  f32x4 nm[QG][FT];
   auto numpart = [&](auto PART, const uint16_t* hb) {
     constexpr int part = decltype(PART)::value;
 #pragma unroll
     for (int f = 0; f < FT / HPARTS; ++f) {
       const int ft = part * (FT / HPARTS) + f;
-      nm[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) nm[qg][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int hr = 16 * f + l16;  // row within the part
         const uint4 a = *reinterpret_cast<const uint4*>(hb + (hr * C + ((4 * ks + g) ^ (hr & (C - 1)))) * 8);
-        nm[ft] = mfma_bf16(a, fq[ks], nm[ft]);
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) nm[qg][ft] = mfma_bf16(a, fq[qg][ks], nm[qg][ft]);
       }
     }
   };
@@ -353,18 +411,21 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
     lds_barrier();
     numpart(std::integral_constant<int, 1>{}, bufB);
   }
-  float cs, cl;
+  float cs[QG], cl[QG];
   if constexpr (PROJ) {
     // Proj(O_l) = O_l W. B operand: num^T rounded to bf16, its k slots the
     // features {4g..4g+3, 16+4g..16+4g+3} of each 32-feature step; A operand:
     // W^T in the same feature order (k_pack_proj), one fragment set per output
     // tile, the next tile's fragments in flight while the current one multiplies.
-    uint4 nb[KSTEPS];
+    uint4 nb[QG][KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      nb[ks] = make_uint4(pack_bf2(nm[2 * ks][0], nm[2 * ks][1]), pack_bf2(nm[2 * ks][2], nm[2 * ks][3]),
-                          pack_bf2(nm[2 * ks + 1][0], nm[2 * ks + 1][1]),
-                          pack_bf2(nm[2 * ks + 1][2], nm[2 * ks + 1][3]));
+    for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        nb[qg][ks] = make_uint4(pack_bf2(nm[qg][2 * ks][0], nm[qg][2 * ks][1]),
+                                pack_bf2(nm[qg][2 * ks][2], nm[qg][2 * ks][3]),
+                                pack_bf2(nm[qg][2 * ks + 1][0], nm[qg][2 * ks + 1][1]),
+                                pack_bf2(nm[qg][2 * ks + 1][2], nm[qg][2 * ks + 1][3]));
     const uint4* wf = reinterpret_cast<const uint4*>(wo + (size_t)h * wo_hs) + lane;
     uint4 wa[2][KSTEPS];
 #pragma unroll
@@ -375,46 +436,59 @@ __global__ __launch_bounds__(256, 3) void k_sparse_bf16(
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) wa[(nt + 1) & 1][ks] = wf[((nt + 1) * KSTEPS + ks) * 64];
       }
-      nm[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) nm[nt] = mfma_bf16(wa[nt & 1][ks], nb[ks], nm[nt]);
+      for (int qg = 0; qg < QG; ++qg) {
+        nm[qg][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) nm[qg][nt] = mfma_bf16(wa[nt & 1][ks], nb[qg][ks], nm[qg][nt]);
+      }
     }
-    cs = inv_l;  // O = O_s + Proj(O_l)
-    cl = inv_den;
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      cs[qg] = inv_l[qg];  // O = O_s + Proj(O_l)
+      cl[qg] = inv_den[qg];
+    }
   } else {
     const float al = alpha[h];
-    cs = al * inv_l;
-    cl = (1.0f - al) * inv_den;
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      cs[qg] = al * inv_l[qg];
+      cl[qg] = (1.0f - al) * inv_den[qg];
+    }
   }
   lds_barrier();  // every wave has read H_i^T: the buffers become the output stage
-  // wave w stages its 16 rows in buffer w / 2 and writes them back itself
-  uint16_t* ost = ((wave >> 1) ? bufB : bufA) + (wave & 1) * 16 * OS;
-  const int q = 16 * wave + l16;
-  const int t = i * kBlock + q;
-  const bool dbg = (dbg_os || dbg_ol) && t < N;
+  // the waves' 16 QG rows each, NW / 2 waves per buffer; each wave writes back its own rows
+  constexpr int WPB = NW / 2;
+  uint16_t* ost = ((wave / WPB) ? bufB : bufA) + (wave % WPB) * 16 * QG * OS;
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    float o[4];
+  for (int qg = 0; qg < QG; ++qg) {
+    const int t = i * kBlock + 16 * (QG * wave + qg) + l16;
+    const bool dbg = (dbg_os || dbg_ol) && t < N;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = fmaf(acc[ft][r], cs, nm[ft][r] * cl);
-    *reinterpret_cast<uint2*>(ost + l16 * OS + 16 * ft + 4 * g) =
-        make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
-    if (dbg) {
-      const size_t off = ((size_t)bh * N + t) * D + 16 * ft + 4 * g;
-      if (dbg_os)
-        *reinterpret_cast<float4*>(dbg_os + off) =
-            make_float4(acc[ft][0] * inv_l, acc[ft][1] * inv_l, acc[ft][2] * inv_l, acc[ft][3] * inv_l);
-      if (dbg_ol)
-        *reinterpret_cast<float4*>(dbg_ol + off) =
-            make_float4(nm[ft][0] * inv_den, nm[ft][1] * inv_den, nm[ft][2] * inv_den, nm[ft][3] * inv_den);
+    for (int ft = 0; ft < FT; ++ft) {
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = fmaf(acc[qg][ft][r], cs[qg], nm[qg][ft][r] * cl[qg]);
+      *reinterpret_cast<uint2*>(ost + (16 * qg + l16) * OS + 16 * ft + 4 * g) =
+          make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+      if (dbg) {
+        const size_t off = ((size_t)bh * N + t) * D + 16 * ft + 4 * g;
+        const float il = inv_l[qg], id_ = inv_den[qg];
+        if (dbg_os)
+          *reinterpret_cast<float4*>(dbg_os + off) =
+              make_float4(acc[qg][ft][0] * il, acc[qg][ft][1] * il, acc[qg][ft][2] * il, acc[qg][ft][3] * il);
+        if (dbg_ol)
+          *reinterpret_cast<float4*>(dbg_ol + off) =
+              make_float4(nm[qg][ft][0] * id_, nm[qg][ft][1] * id_, nm[qg][ft][2] * id_, nm[qg][ft][3] * id_);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // a wave reads back only its own rows
   // full-row 16-byte stores of the wave's staged rows
-  const int nrow = min(16, N - (i * kBlock + 16 * wave));
-  uint16_t* Ob = O + ((size_t)bh * N + (size_t)i * kBlock + 16 * wave) * D;
+  const int nrow = min(16 * QG, N - (i * kBlock + 16 * QG * wave));
+  uint16_t* Ob = O + ((size_t)bh * N + (size_t)i * kBlock + 16 * QG * wave) * D;
 #pragma unroll
-  for (int x0 = 0; x0 < 16 * C; x0 += 64) {
+  for (int x0 = 0; x0 < 16 * QG * C; x0 += 64) {
     const int x = x0 + lane;
     const int row = x / C, ch = x % C;
     if (row < nrow)
@@ -585,25 +659,46 @@ __global__ __launch_bounds__(256) void k_pack_proj(const float* __restrict__ W,
   }
 }
 
-template <int D, bool PROJ, bool ELU>
+// waves per workgroup of the bf16 sparse kernel (2: two 16-query groups per
+// wave; 4: one); SLA_SPARSE_WAVES in the environment overrides it for timing
+int sparse_waves() {
+  static int nw = [] {
+    const char* e = getenv("SLA_SPARSE_WAVES");
+    return (e && atoi(e) == 4) ? 4 : 2;
+  }();
+  return nw;
+}
+
+template <int D, int NW, bool PROJ, bool ELU>
 hipError_t launch_bf16(const Dims& D_, const void* Q, const void* K, const int8_t* mask,
                        const float* alpha, const Work& w, void* O, float* dbg_os, float* dbg_ol,
                        hipStream_t s) {
-  hipLaunchKernelGGL((k_sparse_bf16<D, PROJ, ELU>), dim3(D_.BH * D_.Nb), dim3(256), 0, s,
+  // dynamic LDS: the critical list (2 Nb bytes), later Z_i (2 D bytes)
+  const size_t lbytes = ((size_t)2 * (D_.Nb > D ? D_.Nb : D) + 15) / 16 * 16;
+  hipLaunchKernelGGL((k_sparse_bf16<D, NW, PROJ, ELU>), dim3(D_.BH * D_.Nb), dim3(64 * NW), lbytes, s,
                      (const uint16_t*)Q, (const uint16_t*)K, w.vt, mask, (const uint16_t*)w.Hx, alpha,
                      w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, D_.H, D_.N, D_.Nb);
   return hipGetLastError();
+}
+
+template <int D, int NW>
+hipError_t launch_bf16_nw(const Dims& D_, const void* Q, const void* K, const int8_t* mask,
+                          const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
+                          float* dbg_ol, hipStream_t s) {
+  if (proj)
+    return D_.elu ? launch_bf16<D, NW, true, true>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s)
+                  : launch_bf16<D, NW, true, false>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s);
+  return D_.elu ? launch_bf16<D, NW, false, true>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s)
+                : launch_bf16<D, NW, false, false>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s);
 }
 
 template <int D>
 hipError_t launch_bf16_d(const Dims& D_, const void* Q, const void* K, const int8_t* mask,
                          const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
                          float* dbg_ol, hipStream_t s) {
-  if (proj)
-    return D_.elu ? launch_bf16<D, true, true>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s)
-                  : launch_bf16<D, true, false>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s);
-  return D_.elu ? launch_bf16<D, false, true>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s)
-                : launch_bf16<D, false, false>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s);
+  if (sparse_waves() == 4)
+    return launch_bf16_nw<D, 4>(D_, Q, K, mask, alpha, proj, w, O, dbg_os, dbg_ol, s);
+  return launch_bf16_nw<D, 2>(D_, Q, K, mask, alpha, proj, w, O, dbg_os, dbg_ol, s);
 }
 
 }  // namespace
