@@ -15,6 +15,14 @@ row-normalised, the alpha mix), written with torch float64 operations on the
 CPU and differentiated by autograd. The mask is an input (it is a hard,
 piecewise-constant function of Q and K, so no gradient flows through the
 router, the pooling or the ranking).
+
+The SLA formulation (SLA paper summary, section 4, step 4 and its
+final-output formula) fuses the branches as O = O_s + O_l W with a learned
+d x d map W indexed [in, out] (one shared matrix or one per head); with
+proj_o given, the same explicit forward uses that fusion and the gradients
+include dW (summed over the batch, and over the heads when W is shared). Both
+formulations take phi = softmax over the features or elu + 1 elementwise
+(SLA paper summary, Eq. 3's symbols and Table 2).
 """
 
 from typing import Dict, Tuple
@@ -30,10 +38,11 @@ def _token_masks(mask_row: np.ndarray, N: int) -> Tuple[torch.Tensor, torch.Tens
     return m == 1, m == 0
 
 
-def forward_torch(Q, K, V, alpha, mask, phi: str = "softmax"):
+def forward_torch(Q, K, V, alpha, mask, phi: str = "softmax", proj_o=None):
     """Explicit forward in torch float64 for a fixed block mask [B, H, Nb, Nb];
-    Q, K, V [B, H, N, d] float64 tensors (requires_grad as wanted), alpha [H].
-    Returns (O, O_s, O_l)."""
+    Q, K, V [B, H, N, d] float64 tensors (requires_grad as wanted), alpha [H]
+    (SLA2 mix) or, with proj_o ([d, d] or [H, d, d]), the SLA fusion
+    O = O_s + O_l proj_o (alpha unused). Returns (O, O_s, O_l)."""
     B, H, N, d = Q.shape
     Nb = (N + BLOCK - 1) // BLOCK
     outs, outs_s, outs_l = [], [], []
@@ -64,31 +73,45 @@ def forward_torch(Q, K, V, alpha, mask, phi: str = "softmax"):
             Os, Ol = torch.cat(rows_s), torch.cat(rows_l)
             osb.append(Os)
             olb.append(Ol)
-            ob.append(alpha[h] * Os + (1.0 - alpha[h]) * Ol)
+            if proj_o is None:
+                ob.append(alpha[h] * Os + (1.0 - alpha[h]) * Ol)
+            else:
+                ob.append(Os + Ol @ (proj_o[h] if proj_o.dim() == 3 else proj_o))
         outs.append(torch.stack(ob))
         outs_s.append(torch.stack(osb))
         outs_l.append(torch.stack(olb))
     return torch.stack(outs), torch.stack(outs_s), torch.stack(outs_l)
 
 
-def backward(Q, K, V, alpha, mask, dO, phi: str = "softmax") -> Dict[str, np.ndarray]:
-    """Gradients of sum(O * dO) with respect to Q, K, V and alpha, float64.
-    Inputs are upcast exactly (bf16 / f32 -> f64). Returns numpy arrays dQ, dK,
-    dV [B, H, N, d] and dalpha [H] (summed over the batch)."""
+def backward(Q, K, V, alpha, mask, dO, phi: str = "softmax", proj_o=None) -> Dict[str, np.ndarray]:
+    """Gradients of sum(O * dO) with respect to Q, K, V and alpha (SLA2) or
+    proj_o (SLA, when proj_o is given), float64. Inputs are upcast exactly
+    (bf16 / f32 -> f64). Returns numpy arrays dQ, dK, dV [B, H, N, d] and
+    dalpha [H] (summed over the batch) or dproj_o (proj_o's shape)."""
     f64 = lambda x: (x.detach().to("cpu", torch.float64) if hasattr(x, "detach")
                      else torch.from_numpy(np.asarray(x, dtype=np.float64)))
     q = f64(Q).requires_grad_(True)
     k = f64(K).requires_grad_(True)
     v = f64(V).requires_grad_(True)
-    a = f64(alpha).reshape(-1).requires_grad_(True)
     g = f64(dO)
-    O, _, _ = forward_torch(q, k, v, a, np.asarray(mask), phi)
+    if proj_o is None:
+        a = f64(alpha).reshape(-1).requires_grad_(True)
+        w = None
+    else:
+        a = None
+        w = f64(proj_o).requires_grad_(True)
+    O, _, _ = forward_torch(q, k, v, a, np.asarray(mask), phi, w)
     (O * g).sum().backward()
-    return {"dQ": q.grad.numpy(), "dK": k.grad.numpy(), "dV": v.grad.numpy(),
-            "dalpha": a.grad.numpy()}
+    out = {"dQ": q.grad.numpy(), "dK": k.grad.numpy(), "dV": v.grad.numpy()}
+    if w is None:
+        out["dalpha"] = a.grad.numpy()
+    else:
+        out["dproj_o"] = w.grad.numpy()
+    return out
 
 
-def dq_rows(Q, K, V, alpha, mask, dO, b: int, h: int, blocks, phi: str = "softmax") -> Dict[int, np.ndarray]:
+def dq_rows(Q, K, V, alpha, mask, dO, b: int, h: int, blocks, phi: str = "softmax",
+            proj_o=None) -> Dict[int, np.ndarray]:
     """dQ of the given query blocks of head (b, h), float64. The rows of O in
     query block i depend on q only through that block's own rows, so the
     gradient of sum(O_i * dO_i) with respect to them is dQ there; only those
@@ -96,7 +119,11 @@ def dq_rows(Q, K, V, alpha, mask, dO, b: int, h: int, blocks, phi: str = "softma
     f64 = lambda x: (x.detach().to("cpu", torch.float64) if hasattr(x, "detach")
                      else torch.from_numpy(np.asarray(x, dtype=np.float64)))
     k, v = f64(K[b, h]), f64(V[b, h])
-    a = float(f64(alpha).reshape(-1)[h])
+    if proj_o is None:
+        a, wo = float(f64(alpha).reshape(-1)[h]), None
+    else:
+        wo = f64(proj_o)
+        wo = wo[h] if wo.dim() == 3 else wo
     N, d = k.shape
     fk = torch.softmax(k, dim=-1) if phi == "softmax" else torch.nn.functional.elu(k) + 1.0
     out = {}
@@ -108,11 +135,13 @@ def dq_rows(Q, K, V, alpha, mask, dO, b: int, h: int, blocks, phi: str = "softma
         O = torch.zeros(t1 - t0, d, dtype=torch.float64)
         if crit.any():
             S = ((qi @ k.T) / np.sqrt(d)).masked_fill(~crit[None, :], float("-inf"))
-            O = O + a * (torch.softmax(S, dim=-1) @ v)
+            Os = torch.softmax(S, dim=-1) @ v
+            O = O + (Os if wo is not None else a * Os)
         if marg.any():
             fq = torch.softmax(qi, dim=-1) if phi == "softmax" else torch.nn.functional.elu(qi) + 1.0
             A = (fq @ fk.T) * marg[None, :].to(torch.float64)
-            O = O + (1.0 - a) * ((A @ v) / A.sum(dim=-1, keepdim=True))
+            Ol = (A @ v) / A.sum(dim=-1, keepdim=True)
+            O = O + (Ol @ wo if wo is not None else (1.0 - a) * Ol)
         (O * gi).sum().backward()
         out[int(i)] = qi.grad.numpy()
     return out
