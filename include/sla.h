@@ -227,14 +227,34 @@ int sla_backward_workspace_bytes(const sla_problem* p, size_t* bytes);
  *  dV
  *  dalpha    device float32 [H] output, summed over the batch.
  *  workspace device scratch of at least sla_backward_workspace_bytes(p) bytes.
- * fp32 arithmetic. Requires quant == SLA_QUANT_NONE and phi == SLA_PHI_SOFTMAX
- * (SLA_ERR_UNSUPPORTED otherwise). Errors as for sla_forward. */
+ * fp32 arithmetic; either feature map (p->phi). Requires quant ==
+ * SLA_QUANT_NONE (SLA_ERR_UNSUPPORTED otherwise). Errors as for sla_forward. */
 int sla_backward(const sla_problem* p,
                  const void* Q, const void* K, const void* V, const float* alpha,
                  const int8_t* mask, const void* dO,
                  float* dQ, float* dK, float* dV, float* dalpha,
                  void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/* Workspace that sla1_backward needs for `p` (host only, no device work): that
+ * of sla_backward plus one d x d float32 part of dproj_o per query block. */
+int sla1_backward_workspace_bytes(const sla_problem* p, size_t* bytes);
+
+/* The backward pass of the SLA formulation O = O_s + O_l proj_o (SLA paper
+ * summary, section 4, step 4 and its final-output formula) for a fixed block
+ * mask: dO_s = dO, dO_l = dO proj_o^T, and
+ *  dproj_o   device float32 output of proj_o's shape ([d, d], or [H, d, d]
+ *            with proj_head_stride = d*d): the sum over tokens of O_l^T dO,
+ *            over the batch, and over the heads when proj_o is shared.
+ *  proj_o    device float32 [d, d] or [H, d, d], indexed [in, out]; required.
+ * Every other argument is as for sla_backward (there is no alpha or dalpha).
+ * The router matrices get no gradient (the mask is held fixed). */
+int sla1_backward(const sla_problem* p,
+                  const void* Q, const void* K, const void* V, const float* proj_o,
+                  const int8_t* mask, const void* dO,
+                  float* dQ, float* dK, float* dV, float* dproj_o,
+                  void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /* SoftTop-k of the compressed attention map, the differentiable stand-in for
  * Eq. 2's top-k in SLA2's first training stage (SLA2 article, the two-stage

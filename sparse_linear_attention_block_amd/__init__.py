@@ -11,9 +11,9 @@ selection. This package is the argument-marshalling binding.
 """
 
 from ._binding import (  # noqa: F401
-    LIB_PATH, HipEvents, Plan, SLAError, backward, block_counts, forward, forward_noalloc, forward_sla1,
+    LIB_PATH, HipEvents, Plan, SLAError, backward, backward_sla1, block_counts, forward, forward_noalloc, forward_sla1,
     load_library, make_problem, noalloc_scratch_bytes, soft_topk, workspace_bytes,
 )
 
-__all__ = ["forward", "forward_noalloc", "noalloc_scratch_bytes", "forward_sla1", "backward", "soft_topk", "Plan", "HipEvents", "block_counts", "workspace_bytes", "load_library",
+__all__ = ["forward", "forward_noalloc", "noalloc_scratch_bytes", "forward_sla1", "backward", "backward_sla1", "soft_topk", "Plan", "HipEvents", "block_counts", "workspace_bytes", "load_library",
            "make_problem", "SLAError", "LIB_PATH"]

@@ -75,6 +75,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sla_backward.argtypes = [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 10 + [ctypes.c_void_p, ctypes.c_size_t,
                                                                                       ctypes.c_void_p]
     lib.sla_backward.restype = ctypes.c_int
+    lib.sla1_backward_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
+    lib.sla1_backward_workspace_bytes.restype = ctypes.c_int
+    lib.sla1_backward.argtypes = lib.sla_backward.argtypes
+    lib.sla1_backward.restype = ctypes.c_int
     lib.sla_soft_topk.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                   ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.sla_soft_topk.restype = ctypes.c_int
@@ -333,10 +337,7 @@ def soft_topk(logits: torch.Tensor, k: float, tau: float, *, out: Optional[torch
     return out, lam
 
 
-def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
-             mask: torch.Tensor, dO: torch.Tensor, *, workspace: Optional[torch.Tensor] = None):
-    """SLA2 backward on the GPU (sla_backward) for the block mask the forward
-    pass used: returns (dQ, dK, dV float32 [B, H, N, d], dalpha float32 [H])."""
+def _backward(q, k, v, alpha, proj_o, mask, dO, workspace, phi):
     lib = load_library()
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or dO.shape != q.shape:
         raise ValueError("q, k, v and dO must share one [B, H, N, d] shape")
@@ -346,29 +347,62 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Ten
     Nb = (N + 63) // 64
     if mask.dtype != torch.int8 or tuple(mask.shape) != (B, H, Nb, Nb):
         raise ValueError("mask must be int8 [B, H, Nb, Nb]")
-    if alpha.dtype != torch.float32 or alpha.numel() != H:
-        raise ValueError("alpha must be float32 with H entries")
+    hs = 0
+    if proj_o is None:
+        if alpha is None or alpha.dtype != torch.float32 or alpha.numel() != H:
+            raise ValueError("alpha must be float32 with H entries")
+    else:
+        _check_router("proj_o", proj_o, H, d)
+        hs = d * d if proj_o.dim() == 3 else 0
     if not q.is_cuda:
         raise ValueError("q, k, v and dO must be device tensors")
-    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("mask", mask), ("dO", dO), ("workspace", workspace)):
+    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("proj_o", proj_o), ("mask", mask), ("dO", dO),
+                    ("workspace", workspace)):
         _same_device(name, t, q.device)
-    q, k, v, dO, mask, alpha = (t.contiguous() for t in (q, k, v, dO, mask, alpha))
-    p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", 0.0, 0.0)
+    q, k, v, dO, mask = (t.contiguous() for t in (q, k, v, dO, mask))
+    alpha = None if alpha is None else alpha.contiguous()
+    proj_o = None if proj_o is None else proj_o.contiguous()
+    p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", 0.0, 0.0,
+                     proj_head_stride=hs, phi=phi)
     n = ctypes.c_size_t()
-    _check(lib.sla_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    size_fn = lib.sla_backward_workspace_bytes if proj_o is None else lib.sla1_backward_workspace_bytes
+    _check(size_fn(ctypes.byref(p), ctypes.byref(n)))
     if workspace is None or workspace.numel() * workspace.element_size() < n.value:
         workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=q.device)
     dQ = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dK = torch.empty_like(dQ)
     dV = torch.empty_like(dQ)
-    dalpha = torch.empty(H, dtype=torch.float32, device=q.device)
+    if proj_o is None:
+        dpar = torch.empty(H, dtype=torch.float32, device=q.device)
+    else:
+        dpar = torch.empty(proj_o.shape, dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
         stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
-        rc = lib.sla_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(mask), _ptr(dO),
-                              _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dalpha), _ptr(workspace),
-                              ctypes.c_size_t(workspace.numel() * workspace.element_size()), stream)
+        fn = lib.sla_backward if proj_o is None else lib.sla1_backward
+        rc = fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha if proj_o is None else proj_o), _ptr(mask),
+                _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dpar), _ptr(workspace),
+                ctypes.c_size_t(workspace.numel() * workspace.element_size()), stream)
     _check(rc)
-    return dQ, dK, dV, dalpha
+    return dQ, dK, dV, dpar
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+             mask: torch.Tensor, dO: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
+             phi: str = "softmax"):
+    """SLA2 backward on the GPU (sla_backward) for the block mask the forward
+    pass used: returns (dQ, dK, dV float32 [B, H, N, d], dalpha float32 [H])."""
+    return _backward(q, k, v, alpha, None, mask, dO, workspace, phi)
+
+
+def backward_sla1(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj_o: torch.Tensor,
+                  mask: torch.Tensor, dO: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
+                  phi: str = "softmax"):
+    """Backward of the SLA formulation O = O_s + O_l proj_o on the GPU
+    (sla1_backward): returns (dQ, dK, dV float32 [B, H, N, d], dproj_o float32
+    of proj_o's shape)."""
+    if proj_o is None:
+        raise ValueError("proj_o is required")
+    return _backward(q, k, v, None, proj_o, mask, dO, workspace, phi)
 
 
 class Plan:

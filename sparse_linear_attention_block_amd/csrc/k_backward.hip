@@ -15,8 +15,12 @@
 //    dh_j = sum over query blocks i with Mc[i, j] = 0 of dH_i (dz_j likewise),
 //    taken as the head's total minus the blocks with Mc != 0;
 //    key s in block j, w = phi(k_s): dw = dh_j v_s + dz_j, dv_s += w dh_j;
-//  feature map (softmax over the features): dx = phi (dphi - dphi . phi);
+//  feature map: softmax over the features, dx = phi (dphi - dphi . phi); or
+//  elu + 1 elementwise, dx = dphi * (1 if x > 0 else exp(x));
 //  dalpha_h = sum over the head of dO . (O_s - O_l).
+// The SLA fusion O = O_s + O_l W (SLA paper summary, section 4, step 4):
+// dO_s = dO, dO_l = dO W^T, and dW = sum over tokens of O_l^T dO, formed per
+// query block (k_bwd_q) and summed in a fixed order (k_bwd_dw); no dalpha.
 //
 // fp32 arithmetic throughout (bf16 or f32 inputs), eight threads per query or
 // key token, each holding d/8 features (with four, a thread's state filled
@@ -97,6 +101,13 @@ __device__ __forceinline__ void feature_softmax(const float (&x)[P], float (&f)[
   for (int e = 0; e < P; ++e) f[e] *= inv;
 }
 
+// elu + 1 of a thread's features and its derivative (1 above zero, exp(x) at or below)
+template <int P>
+__device__ __forceinline__ void feature_elu1(const float (&x)[P], float (&f)[P]) {
+#pragma unroll
+  for (int e = 0; e < P; ++e) f[e] = x[e] > 0.f ? x[e] + 1.0f : expf(x[e]);
+}
+
 // The block indices j of a mask row with mrow[j] == value, in ascending order,
 // into list (for workgroups of kThreads); returns their number.
 __device__ int compact_row_wg(const int8_t* __restrict__ mrow, int Nb, int8_t value, uint16_t* list,
@@ -131,12 +142,14 @@ __device__ __forceinline__ void stage_kv(const T* Kb, const T* Vb, int j, int N,
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ELU, bool PROJ>
 __global__ __launch_bounds__(kThreads) void k_bwd_q(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int8_t* __restrict__ mask, const T* __restrict__ Hx, const float* __restrict__ alpha,
+    const float* __restrict__ proj_o, int proj_hs,
     const T* __restrict__ dO, float* __restrict__ dQ, float* __restrict__ lse_out,
-    float* __restrict__ dt_out, float* __restrict__ dHx, float* __restrict__ dal, int H, int N, int Nb) {
+    float* __restrict__ dt_out, float* __restrict__ dHx, float* __restrict__ dal, float* __restrict__ dWp,
+    int H, int N, int Nb) {
   constexpr int P = D / kTpt;
   constexpr int NN = D * D + D;
   __shared__ float Ks[kBlock][D];  // key tiles; then phi(Q) of the block
@@ -158,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
     q[e] = valid ? ldf<T>(Q + base + (size_t)t * D + part * P + e) : 0.f;
     g[e] = valid ? ldf<T>(dO + base + (size_t)t * D + part * P + e) : 0.f;
   }
-  const float al = alpha[h];
+  const float al = PROJ ? 1.0f : alpha[h];  // the SLA fusion weighs O_s by 1
   const float scale = 1.0f / sqrtf((float)D);
   const T* Kb = K + base;
   const T* Vb = V + base;
@@ -227,7 +240,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
   // linear branch: u = phi(q), num = u H_i, den = u . Z_i (H_i^T stored c-major: Hrow[n D + r] = H_i[r][n])
   const T* Hrow = Hx + ((size_t)bh * Nb + i) * NN;
   float u[P];
-  feature_softmax<P>(q, u);
+  if constexpr (ELU)
+    feature_elu1<P>(q, u);
+  else
+    feature_softmax<P>(q, u);
   float den = 0.f;
 #pragma unroll
   for (int e = 0; e < P; ++e) den = fmaf(u[e], ldf<T>(Hrow + D * D + part * P + e), den);
@@ -241,14 +257,28 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
     for (int e = 0; e < P; ++e) num[e] = fmaf(ur, ldf<T>(Hrow + (size_t)(part * P + e) * D + r), num[e]);
   }
   const float inv_den = den > 0.f ? 1.0f / den : 0.f;
+  // dO_l: (1 - alpha) dO, or dO W^T for the SLA fusion (W [in][out]: dO_l[c] = sum_n W[c][n] dO[n])
+  float gl[P];
+  if constexpr (PROJ) {
+    const float* W = proj_o + (size_t)h * proj_hs;
+#pragma unroll
+    for (int e = 0; e < P; ++e) gl[e] = 0.f;
+    for (int n = 0; n < D; ++n) {
+      const float gn = group_get<P>(g, n, lane);
+#pragma unroll
+      for (int e = 0; e < P; ++e) gl[e] = fmaf(W[(size_t)(part * P + e) * D + n], gn, gl[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < P; ++e) gl[e] = (1.0f - al) * g[e];
+  }
   float ol[P], dnum[P];
   float dop = 0.f, dap = 0.f;
 #pragma unroll
   for (int e = 0; e < P; ++e) {
     ol[e] = num[e] * inv_den;
-    const float gl = (1.0f - al) * g[e];
-    dnum[e] = gl * inv_den;
-    dop = fmaf(gl, ol[e], dop);
+    dnum[e] = gl[e] * inv_den;
+    dop = fmaf(gl[e], ol[e], dop);
     dap = fmaf(g[e], os[e] - ol[e], dap);
   }
   const float dden = -sum4(dop) * inv_den;
@@ -261,12 +291,17 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
 #pragma unroll
     for (int e = 0; e < P; ++e) du[e] = fmaf(ldf<T>(Hrow + (size_t)n * D + part * P + e), dn, du[e]);
   }
-  float dup = 0.f;
+  if constexpr (ELU) {
 #pragma unroll
-  for (int e = 0; e < P; ++e) dup = fmaf(du[e], u[e], dup);
-  dup = sum4(dup);
+    for (int e = 0; e < P; ++e) dq[e] = fmaf(du[e], q[e] > 0.f ? 1.0f : u[e], dq[e]);
+  } else {
+    float dup = 0.f;
 #pragma unroll
-  for (int e = 0; e < P; ++e) dq[e] = fmaf(u[e], du[e] - dup, dq[e]);
+    for (int e = 0; e < P; ++e) dup = fmaf(du[e], u[e], dup);
+    dup = sum4(dup);
+#pragma unroll
+    for (int e = 0; e < P; ++e) dq[e] = fmaf(u[e], du[e] - dup, dq[e]);
+  }
 
   if (valid) {
 #pragma unroll
@@ -292,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
   }
   if (part == 0) dd[row] = valid ? dden : 0.f;
   __syncthreads();
-  if (tid == 0) {
+  if (!PROJ && tid == 0) {
     float sdal = 0.f;
     for (int wv = 0; wv < kThreads / 64; ++wv) sdal += red[wv];
     dal[(size_t)bh * Nb + i] = sdal;
@@ -309,6 +344,37 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
     }
     out[x] = s;
   }
+  if constexpr (PROJ) {
+    // the block's part of dW = O_l^T dO: O_l and dO of its queries (zero past N) in LDS
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      Ks[row][part * P + e] = valid ? ol[e] : 0.f;
+      Vs[row][part * P + e] = valid ? g[e] : 0.f;
+    }
+    __syncthreads();
+    float* wout = dWp + ((size_t)bh * Nb + i) * D * D;
+    for (int x = tid; x < D * D; x += kThreads) {
+      const int c = x / D, n = x % D;  // dW[c][n], W indexed [in][out]
+      float s = 0.f;
+      for (int tq = 0; tq < kBlock; ++tq) s = fmaf(Ks[tq][c], Vs[tq][n], s);
+      wout[x] = s;
+    }
+  }
+}
+
+// dW = sum of the per-block parts over batches and query blocks (and over the
+// heads when W is shared), in that order, in float64
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_dw(const float* __restrict__ dWp, float* __restrict__ dW, int B,
+                                                int H, int Nb, int per_head) {
+  const int x = blockIdx.x * 256 + threadIdx.x, hw = blockIdx.y;
+  if (x >= D * D) return;
+  double s = 0.0;
+  for (int b = 0; b < B; ++b)
+    for (int h = per_head ? hw : 0; h < (per_head ? hw + 1 : H); ++h)
+      for (int i = 0; i < Nb; ++i) s += (double)dWp[(((size_t)b * H + h) * Nb + i) * D * D + x];
+  dW[(size_t)hw * D * D + x] = (float)s;
 }
 
 // dH_tot[bh][x] = sum over the head's query blocks of dHx[bh][i][x]
@@ -323,7 +389,7 @@ __global__ __launch_bounds__(256) void k_bwd_htot(const float* __restrict__ dHx,
   dHtot[(size_t)bh * NN + x] = (float)s;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ELU>
 __global__ __launch_bounds__(kThreads) void k_bwd_kv(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int8_t* __restrict__ mask, const float* __restrict__ alpha, const T* __restrict__ dO,
@@ -345,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_kv(
     kk[e] = valid ? ldf<T>(K + base + (size_t)s * D + part * P + e) : 0.f;
     vv[e] = valid ? ldf<T>(V + base + (size_t)s * D + part * P + e) : 0.f;
   }
-  const float al = alpha[h];
+  const float al = alpha ? alpha[h] : 1.0f;  // the SLA fusion (no alpha) weighs O_s by 1
   const float scale = 1.0f / sqrtf((float)D);
   float dk[P], dv[P];
 #pragma unroll
@@ -361,7 +427,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_kv(
   }
   __syncthreads();
   float w[P];
-  feature_softmax<P>(kk, w);
+  if constexpr (ELU)
+    feature_elu1<P>(kk, w);
+  else
+    feature_softmax<P>(kk, w);
   // dw[r] = sum_n dh_j[r][n] v[n] + dz_j[r]; dv[n] += sum_r w[r] dh_j[r][n]
   float dw[P];
 #pragma unroll
@@ -376,12 +445,17 @@ __global__ __launch_bounds__(kThreads) void k_bwd_kv(
 #pragma unroll
     for (int e = 0; e < P; ++e) dv[e] = fmaf(wr, DH[(part * P + e) * D + r], dv[e]);
   }
-  float dwp = 0.f;
+  if constexpr (ELU) {
 #pragma unroll
-  for (int e = 0; e < P; ++e) dwp = fmaf(dw[e], w[e], dwp);
-  dwp = sum4(dwp);
+    for (int e = 0; e < P; ++e) dk[e] = dw[e] * (kk[e] > 0.f ? 1.0f : w[e]);
+  } else {
+    float dwp = 0.f;
 #pragma unroll
-  for (int e = 0; e < P; ++e) dk[e] = w[e] * (dw[e] - dwp);
+    for (int e = 0; e < P; ++e) dwp = fmaf(dw[e], w[e], dwp);
+    dwp = sum4(dwp);
+#pragma unroll
+    for (int e = 0; e < P; ++e) dk[e] = w[e] * (dw[e] - dwp);
+  }
 
   // sparse branch over the query blocks that hold key block j as critical
   float (*Qs)[D] = reinterpret_cast<float (*)[D]>(sm);
@@ -440,37 +514,67 @@ __global__ void k_bwd_alpha(const float* __restrict__ dal, float* __restrict__ d
   dalpha[h] = (float)s;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ELU, bool PROJ>
 hipError_t launch_bwd_t(const Dims& Dm, const void* Q, const void* K, const void* V, const int8_t* mask,
-                        const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
-                        float* dK, float* dV, float* dalpha, hipStream_t s) {
+                        const float* alpha, const float* proj_o, const void* dO, const Work& w,
+                        const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,
+                        hipStream_t s) {
   constexpr int NN = D * D + D;
   const dim3 grid(Dm.Nb, Dm.BH);
-  hipLaunchKernelGGL((k_bwd_q<T, D>), grid, dim3(kThreads), 0, s, (const T*)Q, (const T*)K, (const T*)V, mask,
-                     (const T*)w.Hx, alpha, (const T*)dO, dQ, bw.lse, bw.dt, bw.dHx, bw.dal, Dm.H, Dm.N, Dm.Nb);
+  hipLaunchKernelGGL((k_bwd_q<T, D, ELU, PROJ>), grid, dim3(kThreads), 0, s, (const T*)Q, (const T*)K,
+                     (const T*)V, mask, (const T*)w.Hx, alpha, proj_o, Dm.proj_hs, (const T*)dO, dQ, bw.lse,
+                     bw.dt, bw.dHx, bw.dal, bw.dWp, Dm.H, Dm.N, Dm.Nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_htot<D>, dim3((NN + 255) / 256, Dm.BH), dim3(256), 0, s, bw.dHx, bw.dHtot, Dm.Nb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_kv<T, D>), grid, dim3(kThreads), 0, s, (const T*)Q, (const T*)K, (const T*)V, mask,
-                     alpha, (const T*)dO, bw.lse, bw.dt, bw.dHx, bw.dHtot, dK, dV, Dm.H, Dm.N, Dm.Nb);
+  hipLaunchKernelGGL((k_bwd_kv<T, D, ELU>), grid, dim3(kThreads), 0, s, (const T*)Q, (const T*)K, (const T*)V,
+                     mask, PROJ ? nullptr : alpha, (const T*)dO, bw.lse, bw.dt, bw.dHx, bw.dHtot, dK, dV, Dm.H,
+                     Dm.N, Dm.Nb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bwd_alpha, dim3((Dm.H + 63) / 64), dim3(64), 0, s, bw.dal, dalpha, Dm.B, Dm.H, Dm.Nb);
+  if constexpr (PROJ) {
+    const int hs = Dm.proj_hs ? Dm.H : 1;
+    hipLaunchKernelGGL(k_bwd_dw<D>, dim3((D * D + 255) / 256, hs), dim3(256), 0, s, bw.dWp, dproj_o, Dm.B,
+                       Dm.H, Dm.Nb, Dm.proj_hs ? 1 : 0);
+  } else {
+    hipLaunchKernelGGL(k_bwd_alpha, dim3((Dm.H + 63) / 64), dim3(64), 0, s, bw.dal, dalpha, Dm.B, Dm.H, Dm.Nb);
+  }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_td(const Dims& Dm, const void* Q, const void* K, const void* V, const int8_t* mask,
+                         const float* alpha, const float* proj_o, const void* dO, const Work& w,
+                         const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,
+                         hipStream_t s) {
+  if (proj_o)
+    return Dm.elu ? launch_bwd_t<T, D, true, true>(Dm, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV,
+                                                   dalpha, dproj_o, s)
+                  : launch_bwd_t<T, D, false, true>(Dm, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV,
+                                                    dalpha, dproj_o, s);
+  return Dm.elu ? launch_bwd_t<T, D, true, false>(Dm, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV,
+                                                  dalpha, dproj_o, s)
+                : launch_bwd_t<T, D, false, false>(Dm, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV,
+                                                   dalpha, dproj_o, s);
 }
 
 }  // namespace
 
 hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
-                           const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
-                           float* dK, float* dV, float* dalpha, hipStream_t s) {
+                           const float* alpha, const float* proj_o, const void* dO, const Work& w,
+                           const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,
+                           hipStream_t s) {
   if (D.bf16)
-    return D.d == 128 ? launch_bwd_t<uint16_t, 128>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s)
-                      : launch_bwd_t<uint16_t, 64>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s);
-  return D.d == 128 ? launch_bwd_t<float, 128>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s)
-                    : launch_bwd_t<float, 64>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s);
+    return D.d == 128 ? launch_bwd_td<uint16_t, 128>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV,
+                                                      dalpha, dproj_o, s)
+                      : launch_bwd_td<uint16_t, 64>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV,
+                                                     dalpha, dproj_o, s);
+  return D.d == 128 ? launch_bwd_td<float, 128>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, dalpha,
+                                                dproj_o, s)
+                    : launch_bwd_td<float, 64>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, dalpha,
+                                               dproj_o, s);
 }
 
 }  // namespace sla

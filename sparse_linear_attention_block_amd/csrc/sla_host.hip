@@ -115,7 +115,7 @@ size_t carve(const Dims& D, void* base, Work* w) {
   return off;
 }
 
-size_t carve_bwd(const Dims& D, void* base, Work* w, BwdWork* bw) {
+size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw) {
   size_t off = carve(D, base, w);
   char* b = (char*)base;
   auto take = [&](size_t bytes) -> void* {
@@ -130,6 +130,7 @@ size_t carve_bwd(const Dims& D, void* base, Work* w, BwdWork* bw) {
   x.dHx = (float*)take(BH * D.Nb * D.NN * sizeof(float));
   x.dHtot = (float*)take(BH * D.NN * sizeof(float));
   x.dal = (float*)take(BH * D.Nb * sizeof(float));
+  if (proj) x.dWp = (float*)take(BH * D.Nb * D.d * D.d * sizeof(float));
   if (bw) *bw = x;
   return off;
 }
@@ -415,7 +416,6 @@ static int make_bwd_dims(const sla_problem* p, sla::Dims* D) {
   const int rc = make_dims(p, D);
   if (rc != SLA_OK) return rc;
   if (D->quant) return fail(SLA_ERR_UNSUPPORTED, "the backward pass is built without the 8-bit branch");
-  if (D->elu) return fail(SLA_ERR_UNSUPPORTED, "the backward pass is built for the softmax feature map");
   return SLA_OK;
 }
 
@@ -424,29 +424,48 @@ int sla_backward_workspace_bytes(const sla_problem* p, size_t* bytes) {
   const int rc = make_bwd_dims(p, &D);
   if (rc != SLA_OK) return rc;
   if (!bytes) return fail(SLA_ERR_ARG, "bytes is NULL");
-  *bytes = sla::carve_bwd(D, nullptr, nullptr, nullptr);
+  *bytes = sla::carve_bwd(D, false, nullptr, nullptr, nullptr);
   g_err[0] = 0;
   return SLA_OK;
 }
 
-int sla_backward(const sla_problem* p, const void* Q, const void* K, const void* V, const float* alpha,
-                 const int8_t* mask, const void* dO, float* dQ, float* dK, float* dV, float* dalpha,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+int sla1_backward_workspace_bytes(const sla_problem* p, size_t* bytes) {
   sla::Dims D;
   const int rc = make_bwd_dims(p, &D);
   if (rc != SLA_OK) return rc;
-  if (!Q || !K || !V || !alpha || !mask || !dO || !dQ || !dK || !dV || !dalpha)
-    return fail(SLA_ERR_ARG, "Q, K, V, alpha, mask, dO, dQ, dK, dV and dalpha must not be NULL");
+  if (!bytes) return fail(SLA_ERR_ARG, "bytes is NULL");
+  *bytes = sla::carve_bwd(D, true, nullptr, nullptr, nullptr);
+  g_err[0] = 0;
+  return SLA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Both formulations: proj_o == NULL is SLA2 (dalpha), otherwise SLA (dproj_o).
+int run_backward(const sla_problem* p, const void* Q, const void* K, const void* V, const float* alpha,
+                 const float* proj_o, const int8_t* mask, const void* dO, float* dQ, float* dK, float* dV,
+                 float* dalpha, float* dproj_o, void* workspace, size_t workspace_bytes, void* stream) {
+  sla::Dims D;
+  const int rc = make_bwd_dims(p, &D);
+  if (rc != SLA_OK) return rc;
+  const bool sla1 = proj_o != nullptr;
+  if (!Q || !K || !V || !mask || !dO || !dQ || !dK || !dV)
+    return fail(SLA_ERR_ARG, "Q, K, V, mask, dO, dQ, dK and dV must not be NULL");
+  if (!sla1 && (!alpha || !dalpha)) return fail(SLA_ERR_ARG, "alpha and dalpha must not be NULL");
+  if (sla1 && !dproj_o) return fail(SLA_ERR_ARG, "dproj_o must not be NULL");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(dO, 16) || !aligned(dQ, 16) ||
-      !aligned(dK, 16) || !aligned(dV, 16) || !aligned(alpha, 4) || !aligned(dalpha, 4))
-    return fail(SLA_ERR_ARG, "tensors must be 16-byte aligned, alpha and dalpha 4-byte aligned");
-  const size_t need = sla::carve_bwd(D, nullptr, nullptr, nullptr);
+      !aligned(dK, 16) || !aligned(dV, 16) || (alpha && !aligned(alpha, 4)) || (dalpha && !aligned(dalpha, 4)) ||
+      (proj_o && !aligned(proj_o, 4)) || (dproj_o && !aligned(dproj_o, 4)))
+    return fail(SLA_ERR_ARG, "tensors must be 16-byte aligned, alpha, proj_o and their gradients 4-byte aligned");
+  const size_t need = sla::carve_bwd(D, sla1, nullptr, nullptr, nullptr);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
     return fail(SLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu at %p)",
                 need, workspace_bytes, workspace);
   sla::Work w;
   sla::BwdWork bw;
-  sla::carve_bwd(D, workspace, &w, &bw);
+  sla::carve_bwd(D, sla1, workspace, &w, &bw);
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();  // a stale error from earlier work is not ours to report
 #define SLA_LAUNCH(call, what)                                                            \
@@ -458,11 +477,31 @@ int sla_backward(const sla_problem* p, const void* Q, const void* K, const void*
   SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
   if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
   SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
-  SLA_LAUNCH(sla::launch_backward(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, dalpha, s),
+  SLA_LAUNCH(sla::launch_backward(D, Q, K, V, mask, sla1 ? nullptr : alpha, proj_o, dO, w, bw, dQ, dK, dV,
+                                  dalpha, dproj_o, s),
              "backward kernels");
 #undef SLA_LAUNCH
   g_err[0] = 0;
   return SLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sla_backward(const sla_problem* p, const void* Q, const void* K, const void* V, const float* alpha,
+                 const int8_t* mask, const void* dO, float* dQ, float* dK, float* dV, float* dalpha,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return run_backward(p, Q, K, V, alpha, nullptr, mask, dO, dQ, dK, dV, dalpha, nullptr, workspace,
+                      workspace_bytes, stream);
+}
+
+int sla1_backward(const sla_problem* p, const void* Q, const void* K, const void* V, const float* proj_o,
+                  const int8_t* mask, const void* dO, float* dQ, float* dK, float* dV, float* dproj_o,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!proj_o) return fail(SLA_ERR_ARG, "proj_o must not be NULL");
+  return run_backward(p, Q, K, V, nullptr, proj_o, mask, dO, dQ, dK, dV, nullptr, dproj_o, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -57,8 +57,10 @@ struct BwdWork {
   float* dHx;    // [BH, Nb, NN] dH_i (stored like H_i^T) then dZ_i, per query block
   float* dHtot;  // [BH, NN] their sum over the head's query blocks
   float* dal;    // [BH, Nb] partial dalpha of each query block
+  float* dWp;    // SLA fusion only: [BH, Nb, d, d] each query block's part of dW = O_l^T dO
 };
-size_t carve_bwd(const Dims& D, void* base, Work* w, BwdWork* bw);  // forward + backward bytes
+// forward + backward bytes; proj: the SLA fusion's dW parts are included
+size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw);
 
 // ---- launchers (each enqueues one or more kernels on `s`, returns hipError_t)
 hipError_t launch_pool_sum(const Dims& D, const void* Q, const void* K, double* raw,
@@ -84,9 +86,12 @@ hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const 
                              const int8_t* mask, const float* alpha, const float* proj_o,
                              const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
 
+// proj_o == NULL: SLA2 (dalpha written, dproj_o unused); else the SLA fusion (dproj_o
+// written, alpha and dalpha unused)
 hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
-                           const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
-                           float* dK, float* dV, float* dalpha, hipStream_t s);
+                           const float* alpha, const float* proj_o, const void* dO, const Work& w,
+                           const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,
+                           hipStream_t s);
 // SoftTop-k rows of a float64 logit matrix (k_soft_topk.hip); cols <= 4096
 hipError_t launch_soft_topk(const double* logits, int rows, int cols, float k, float tau, float* out,
                             float* lambda, hipStream_t s);

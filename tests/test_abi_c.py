@@ -1,6 +1,7 @@
 """The C ABI from C: a C99 program includes include/sla.h, links libsla.so and
 makes the host-only calls (version, block counts, workspace sizes, status
-text and the error paths that return before any device work)."""
+text and the error paths that return before any device work, including those
+of the SLA backward and the allocation-free forward)."""
 
 import os
 import shutil
@@ -31,7 +32,14 @@ int main(void) {
   p.phi = 7;
   if (sla_forward(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != SLA_ERR_ARG) return 6;
   p.phi = SLA_PHI_ELU1;
-  if (sla_backward_workspace_bytes(&p, &bwd) != SLA_ERR_UNSUPPORTED) return 7;
+  size_t bwd1 = 0;
+  if (sla_backward_workspace_bytes(&p, &bwd) != SLA_OK || sla1_backward_workspace_bytes(&p, &bwd1) != SLA_OK ||
+      bwd1 <= bwd) return 7;
+  p.quant = SLA_QUANT_I8QK_F8PV;
+  if (sla1_backward_workspace_bytes(&p, &bwd1) != SLA_ERR_UNSUPPORTED) return 11;
+  if (sla1_backward(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != SLA_ERR_ARG) return 12;
+  if (sla_forward_noalloc(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != SLA_ERR_WORKSPACE) return 13;  /* too big */
+  p.quant = SLA_QUANT_NONE;
   if (sla1_forward(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != SLA_ERR_ARG) return 8;
   if (sla_soft_topk(0, 1, 1, 0.5, 1.0, 0, 0, 0) != SLA_ERR_ARG) return 9;
   if (!strstr(sla_status_str(SLA_ERR_WORKSPACE), "WORKSPACE")) return 10;

@@ -185,7 +185,7 @@ def _bwd(p, Q=0x10000, K=0x10000, V=0x10000, al=0x10000, m=0x10000, dO=0x10000, 
     (dict(dQ=0x10004), B.SLA_ERR_ARG),        # misaligned
     (dict(al=0x10001), B.SLA_ERR_ARG),
     (dict(quant=True), B.SLA_ERR_UNSUPPORTED),
-    (dict(elu=True), B.SLA_ERR_UNSUPPORTED),
+    (dict(elu=True), B.SLA_ERR_WORKSPACE),    # elu + 1 is built: valid up to the workspace
     (dict(), B.SLA_ERR_WORKSPACE),            # valid up to the workspace
     (dict(ws=0x10080, wsb=1 << 40), B.SLA_ERR_WORKSPACE),
 ])
@@ -197,6 +197,42 @@ def test_backward_errors(kw, code):
         p.phi = B.SLA_PHI_ELU1
     assert _bwd(p, **kw) == code
     assert sla.load_library().sla_last_error()
+
+
+def _bwd1(p, Q=0x10000, K=0x10000, V=0x10000, W=0x10000, m=0x10000, dO=0x10000, dQ=0x10000,
+          dK=0x10000, dV=0x10000, dW=0x10000, ws=None, wsb=0):
+    lib = sla.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.sla1_backward(ctypes.byref(p), vp(Q), vp(K), vp(V), vp(W), vp(m), vp(dO), vp(dQ), vp(dK),
+                             vp(dV), vp(dW), vp(ws), ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), B.SLA_ERR_ARG),            # the output map is required
+    (dict(dW=None), B.SLA_ERR_ARG),
+    (dict(m=None), B.SLA_ERR_ARG),
+    (dict(dW=0x10002), B.SLA_ERR_ARG),        # misaligned
+    (dict(quant=True), B.SLA_ERR_UNSUPPORTED),
+    (dict(), B.SLA_ERR_WORKSPACE),
+    (dict(elu=True), B.SLA_ERR_WORKSPACE),
+])
+def test_sla1_backward_errors(kw, code):
+    p = good()
+    if kw.pop("quant", False):
+        p.quant = B.SLA_QUANT_I8QK_F8PV
+    if kw.pop("elu", False):
+        p.phi = B.SLA_PHI_ELU1
+    assert _bwd1(p, **kw) == code
+    assert sla.load_library().sla_last_error()
+
+
+def test_sla1_backward_workspace_adds_the_map_parts():
+    lib = sla.load_library()
+    p = sla.make_problem(1, 12, 32760, 128, "bf16", 0.05, 0.10)
+    b2, b1 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sla_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(b2)) == 0
+    assert lib.sla1_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(b1)) == 0
+    assert b1.value == b2.value + 12 * 512 * 128 * 128 * 4
 
 
 def test_backward_workspace_covers_the_forward():

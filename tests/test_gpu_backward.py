@@ -1,11 +1,13 @@
-"""GPU parity of the SLA2 backward pass (sla_backward) against the float64
+"""GPU parity of the backward passes (sla_backward for SLA2, sla1_backward
+for the SLA fusion O = O_s + O_l W, either feature map) against the float64
 autograd oracle (oracle/backward.py), for the block mask the forward pass
 computes (or an injected one), through the C ABI.
 
 Bounds, per (batch, head), on rel-L1 = sum |x - y| / sum |y|: fp32 inputs 1e-4
 (fp32 arithmetic over sums of at most a few thousand terms); bf16 inputs 1e-2,
 the forward's bf16 bound (the linear branch's H_i and Z_i are the forward's
-bf16 ones). dalpha to 1e-4 (fp32) or 1e-2 (bf16) relative.
+bf16 ones). dalpha to 1e-4 (fp32) or 1e-2 (bf16) relative; dW to the same
+rel-L1 bounds.
 """
 
 import numpy as np
@@ -128,3 +130,82 @@ def test_full_size_sampled():
 def test_bf16_batch_of_two():
     # the CFG-batch recipe (B = 2, per-head alpha): dalpha sums over the batch
     _check(make_inputs(CONFIGS[4], H=3, N=500), 1e-2)
+
+
+# ---- ELU+1 and the SLA formulation O = O_s + O_l W (sla1_backward)
+
+def _check_sla1(x, tol, W, phi="softmax", mask=None, seed=21):
+    if mask is None:
+        mask = run_gpu(x, debug=False, proj_o=W, router=False, phi=phi)["mask"]
+    dO = _grad_out(x, seed)
+    ref = ob.backward(x.q, x.k, x.v, None, mask, dO, phi=phi, proj_o=W)
+    dQ, dK, dV, dW = sla.backward_sla1(x.q.cuda(), x.k.cuda(), x.v.cuda(), W.cuda(),
+                                       torch.from_numpy(np.ascontiguousarray(mask)).cuda(), dO.cuda(), phi=phi)
+    torch.cuda.synchronize()
+    got = {"dQ": dQ.cpu().numpy(), "dK": dK.cpu().numpy(), "dV": dV.cpu().numpy()}
+    worst = 0.0
+    for name in ("dQ", "dK", "dV"):
+        for b in range(x.B):
+            for h in range(x.H):
+                e = rel_l1(got[name][b, h], ref[name][b, h])
+                worst = max(worst, e)
+                assert e <= tol, (name, b, h, e)
+    eW = rel_l1(dW.cpu().numpy(), ref["dproj_o"])
+    _flush(f"SLA {phi} W{list(W.shape)} B={x.B} H={x.H} N={x.N} d={x.d} {x.q.dtype}: worst rel-L1 {worst:.2e}, "
+           f"dW {eW:.2e}")
+    assert eW <= tol, eW
+
+
+def _proj(d, H=None, seed=5):
+    rng = np.random.default_rng(seed)
+    shape = (d, d) if H is None else (H, d, d)
+    return torch.from_numpy((np.eye(d) + 0.3 * rng.standard_normal(shape) / np.sqrt(d)).astype(np.float32))
+
+
+@pytest.mark.parametrize("N", [100, 1000])
+def test_elu1_sla2_bf16(N):
+    x = make_inputs(CONFIGS[2], H=2, N=N)
+    mask = run_gpu(x, debug=False, phi="elu1")["mask"]
+    dO = _grad_out(x, 9)
+    ref = ob.backward(x.q, x.k, x.v, x.alpha, mask, dO, phi="elu1")
+    dQ, dK, dV, da = sla.backward(x.q.cuda(), x.k.cuda(), x.v.cuda(), x.alpha.cuda(),
+                                  torch.from_numpy(mask).cuda(), dO.cuda(), phi="elu1")
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dQ), ("dK", dK), ("dV", dV)):
+        for h in range(2):
+            e = rel_l1(t.cpu().numpy()[0, h], ref[name][0, h])
+            assert e <= 1e-2, (name, h, e)
+    eda = float(np.abs(da.cpu().numpy() - ref["dalpha"]).max() / np.abs(ref["dalpha"]).max())
+    _flush(f"SLA2 elu1 N={N}: dalpha {eda:.2e}")
+    assert eda <= 1e-2
+
+
+def test_sla1_fp32_tiny():
+    x = make_inputs(CONFIGS[1])
+    _check_sla1(x, 1e-4, _proj(64))
+    _check_sla1(x, 1e-4, _proj(64, H=2), phi="elu1")
+
+
+@pytest.mark.parametrize("phi", ["softmax", "elu1"])
+@pytest.mark.parametrize("per_head", [False, True])
+def test_sla1_bf16(phi, per_head):
+    x = make_inputs(CONFIGS[2], H=3, N=1000)
+    _check_sla1(x, 1e-2, _proj(128, H=3 if per_head else None), phi=phi)
+
+
+def test_sla1_batch_of_two_injected_mask():
+    # dW sums over the batch (and the heads, W shared); rows with empty sets
+    x = make_inputs(CONFIGS[4], H=2, N=500)
+    Nb = 8
+    rng = np.random.default_rng(22)
+    mask = rng.choice(np.array([1, 0, -1], dtype=np.int8), size=(2, 2, Nb, Nb))
+    mask[0, 0, 2] = -1
+    mask[1, 1, 3] = 0
+    mask[1, 0, 4] = 1
+    _check_sla1(x, 1e-2, _proj(128), mask=mask)
+
+
+def test_sla1_fp32_d128():
+    x = make_inputs(CONFIGS[2], H=2, N=300)
+    x.q, x.k, x.v = x.q.float(), x.k.float(), x.v.float()
+    _check_sla1(x, 1e-4, _proj(128, H=2), phi="elu1")
