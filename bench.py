@@ -416,6 +416,8 @@ def main():
     ap.add_argument("--op", choices=["forward", "soft_topk", "backward"], default="forward",
                     help="forward: the whole forward pass; soft_topk: SoftTop-k on its logits; "
                          "backward: the backward pass")
+    ap.add_argument("--linear", choices=["gemm", "chain"], default="gemm",
+                    help="marginal sums: gemm (indicator product per head) or chain (row-to-row updates)")
     ap.add_argument("--tau", type=float, default=1e-3, help="SoftTop-k temperature (Pc units)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--flush-mib", type=int, default=512,
@@ -446,7 +448,8 @@ def main():
     if cfg.quant:
         print("note: the 8-bit sparse branch is timed with quant=True", file=sys.stderr)
     # the name the profiles of this workload are filed under
-    wl_name = cfg.name + ("_sla1" if sla1 else "") + ("_elu1" if args.phi == "elu1" else "")
+    wl_name = (cfg.name + ("_sla1" if sla1 else "") + ("_elu1" if args.phi == "elu1" else "")
+               + ("_chain" if args.linear == "chain" else ""))
     t0 = time.time()
     x = make_inputs(cfg)
     print(f"[bench] inputs {cfg.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -464,9 +467,10 @@ def main():
     pq, pk, al = x.proj_q.to(dev), x.proj_k.to(dev), x.alpha.to(dev)
     proj_o = make_proj_o(cfg) if sla1 else None
     if sla1:
-        plan = sla.Plan(q, k, v, None, None, None, x.kh, x.kl, phi=args.phi, proj_o=proj_o.to(dev))
+        plan = sla.Plan(q, k, v, None, None, None, x.kh, x.kl, phi=args.phi, proj_o=proj_o.to(dev),
+                        linear=args.linear)
     else:
-        plan = sla.Plan(q, k, v, pq, pk, al, x.kh, x.kl, quant=cfg.quant, phi=args.phi)
+        plan = sla.Plan(q, k, v, pq, pk, al, x.kh, x.kl, quant=cfg.quant, phi=args.phi, linear=args.linear)
     B, H, N, d, Nb = plan.dims
     _, n_h, n_l = sla.block_counts(N, x.kh, x.kl, B=B, H=H, d=d, dtype=cfg.dtype)
     if args.hbm_calib_mib > 0:
@@ -554,7 +558,7 @@ def main():
                                    else "SLA2: O = alpha O_s + (1 - alpha) O_l, "
                                         + ("identity router matrices" if cfg.router == "identity"
                                            else "learned router matrices I + 0.1 N(0, 1/d)")),
-                   "phi": args.phi},
+                   "phi": args.phi, "linear_sums": args.linear},
         "roofline": {"kernel": "sparse_attn_mix", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "flops_per_launch": k5_flops, "ms_per_launch": round(k5_ms, 5)},

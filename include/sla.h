@@ -82,6 +82,16 @@ typedef enum {
   SLA_PHI_ELU1 = 1      /* elementwise elu(x) + 1: x + 1 for x > 0, exp(x) else */
 } sla_phi;
 
+/* How the per-query-block marginal sums H_i, Z_i of the linear branch are
+ * formed (the result is the same up to float32 rounding order). */
+typedef enum {
+  SLA_LINEAR_GEMM = 0,   /* one 0/1-indicator matrix product per head on MFMA      */
+  SLA_LINEAR_CHAIN = 1   /* each row from the previous one: add the blocks that
+                          * became marginal, subtract those that stopped being so
+                          * (SLA explainer, section 2.3, on sparse per-row sums);
+                          * bf16 only, Nb <= 1216 (SLA_ERR_UNSUPPORTED otherwise) */
+} sla_linear_sums;
+
 typedef struct {
   int32_t B, H, N, d;         /* d in {64, 128}                                  */
   int32_t dtype;              /* sla_dtype of Q, K, V, O                         */
@@ -90,6 +100,7 @@ typedef struct {
                               /* matrix for all heads; d*d: they are [H, d, d]   */
   int32_t phi;                /* sla_phi                                         */
   double  kh, kl;             /* critical / negligible fractions in [0, 1]       */
+  int32_t linear_sums;        /* sla_linear_sums (0, the default, is the GEMM)   */
 } sla_problem;
 
 /* Debug outputs of sla_forward_debug. Every pointer is a device buffer or NULL.
@@ -284,7 +295,7 @@ const char* sla_status_str(int status);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* sla_last_error(void);
 
-/* Interface version: (major << 16) | minor. */
+/* Interface version: (major << 16) | minor (1.2 added sla_problem.linear_sums). */
 int sla_version(void);
 
 #ifdef __cplusplus

@@ -18,13 +18,15 @@ SLA_F32, SLA_BF16 = 0, 1
 SLA_QUANT_NONE, SLA_QUANT_I8QK_F8PV = 0, 1
 SLA_PHI_SOFTMAX, SLA_PHI_ELU1 = 0, 1
 _PHI = {"softmax": SLA_PHI_SOFTMAX, "elu1": SLA_PHI_ELU1}
+SLA_LINEAR_GEMM, SLA_LINEAR_CHAIN = 0, 1
+_LINEAR = {"gemm": SLA_LINEAR_GEMM, "chain": SLA_LINEAR_CHAIN}
 
 
 class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("quant", ctypes.c_int32),
                 ("proj_head_stride", ctypes.c_int32), ("phi", ctypes.c_int32),
-                ("kh", ctypes.c_double), ("kl", ctypes.c_double)]
+                ("kh", ctypes.c_double), ("kl", ctypes.c_double), ("linear_sums", ctypes.c_int32)]
 
 
 class Debug(ctypes.Structure):
@@ -99,12 +101,15 @@ def _check(rc: int) -> None:
 
 
 def make_problem(B: int, H: int, N: int, d: int, dtype: str, kh: float, kl: float,
-                 quant: bool = False, proj_head_stride: int = 0, phi: str = "softmax") -> Problem:
+                 quant: bool = False, proj_head_stride: int = 0, phi: str = "softmax",
+                 linear: str = "gemm") -> Problem:
     if phi not in _PHI:
         raise ValueError(f"phi must be one of {sorted(_PHI)}")
+    if linear not in _LINEAR:
+        raise ValueError(f"linear must be one of {sorted(_LINEAR)}")
     return Problem(B, H, N, d, SLA_BF16 if dtype in ("bf16", torch.bfloat16) else SLA_F32,
                    SLA_QUANT_I8QK_F8PV if quant else SLA_QUANT_NONE, proj_head_stride, _PHI[phi],
-                   float(kh), float(kl))
+                   float(kh), float(kl), _LINEAR[linear])
 
 
 def block_counts(N: int, kh: float, kl: float, *, B: int = 1, H: int = 1, d: int = 128,
@@ -194,7 +199,7 @@ def validate_forward_args(q, k, v, proj_q=None, proj_k=None, alpha=None, proj_o=
 
 
 def _run(q, k, v, proj_q, proj_k, alpha, proj_o, kh, kl, mask_in, quant, out, mask_out,
-         workspace, debug, phi):
+         workspace, debug, phi, linear="gemm"):
     lib = load_library()
     hs = validate_forward_args(q, k, v, proj_q, proj_k, alpha, proj_o, mask_in, out, mask_out)
     B, H, N, d = q.shape
@@ -211,7 +216,7 @@ def _run(q, k, v, proj_q, proj_k, alpha, proj_o, kh, kl, mask_in, quant, out, ma
     if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on q's device")
     p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", kh, kl,
-                     quant, hs, phi)
+                     quant, hs, phi, linear)
     need = workspace_bytes(p)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -250,16 +255,18 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             kh: float, kl: float, mask_in: Optional[torch.Tensor] = None, *,
             quant: bool = False, out: Optional[torch.Tensor] = None,
             mask_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            debug: bool = False, phi: str = "softmax"):
+            debug: bool = False, phi: str = "softmax", linear: str = "gemm"):
     """SLA2 forward on the GPU (sla_forward): returns (O, mask) or (O, mask, debug dict).
 
     q, k, v: [B, H, N, d] contiguous bf16 or float32 device tensors.
     proj_q, proj_k: float32 [d, d] or [H, d, d], or both None (no router projection).
     alpha: float32 [H]. mask_in: optional int8 [B, H, Nb, Nb] in {1, 0, -1}.
     phi: the linear branch's feature map, "softmax" or "elu1".
+    linear: how the marginal sums are formed, "gemm" (the indicator product)
+    or "chain" (row-to-row updates).
     """
     return _run(q, k, v, proj_q, proj_k, alpha, None, kh, kl, mask_in, quant, out, mask_out,
-                workspace, debug, phi)
+                workspace, debug, phi, linear)
 
 
 def noalloc_scratch_bytes() -> int:
@@ -300,7 +307,7 @@ def forward_sla1(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj_o: torc
                  proj_q: Optional[torch.Tensor] = None, proj_k: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None, mask_out: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None, debug: bool = False,
-                 phi: str = "softmax"):
+                 phi: str = "softmax", linear: str = "gemm"):
     """SLA forward on the GPU (sla1_forward): O = O_s + O_l proj_o.
 
     proj_o: float32 [d, d] or [H, d, d], indexed [in, out]. The router matrices
@@ -311,7 +318,7 @@ def forward_sla1(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj_o: torc
     if proj_o is None:
         raise ValueError("proj_o is required")
     return _run(q, k, v, proj_q, proj_k, None, proj_o, kh, kl, mask_in, False, out, mask_out,
-                workspace, debug, phi)
+                workspace, debug, phi, linear)
 
 
 def soft_topk(logits: torch.Tensor, k: float, tau: float, *, out: Optional[torch.Tensor] = None,
@@ -411,7 +418,7 @@ class Plan:
     (used by the benchmark and by callers that run the same shape often)."""
 
     def __init__(self, q, k, v, proj_q, proj_k, alpha, kh, kl, mask_in=None, quant=False,
-                 phi="softmax", proj_o=None):
+                 phi="softmax", proj_o=None, linear="gemm"):
         lib = load_library()
         hs = validate_forward_args(q, k, v, proj_q, proj_k, alpha, proj_o, mask_in)
         for name, t in (("proj_q", proj_q), ("proj_k", proj_k), ("alpha", alpha), ("proj_o", proj_o),
@@ -422,7 +429,7 @@ class Plan:
         Nb = (N + 63) // 64
         dev = q.device
         self.problem = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32",
-                                    kh, kl, quant, hs, phi)
+                                    kh, kl, quant, hs, phi, linear)
         self.sla1 = proj_o is not None
         self.nbytes = workspace_bytes(self.problem)
         self.workspace = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=dev)

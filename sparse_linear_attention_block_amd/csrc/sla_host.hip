@@ -57,6 +57,11 @@ int make_dims(const sla_problem* p, sla::Dims* D) {
     return fail(SLA_ERR_ARG, "kh and kl select %d + %d > %d blocks per row", n_h, n_l, Nb);
   if (p->quant == SLA_QUANT_I8QK_F8PV && p->dtype != SLA_BF16)
     return fail(SLA_ERR_UNSUPPORTED, "the 8-bit sparse branch needs bf16 inputs");
+  if (p->linear_sums != SLA_LINEAR_GEMM && p->linear_sums != SLA_LINEAR_CHAIN)
+    return fail(SLA_ERR_ARG, "unknown linear_sums %d", p->linear_sums);
+  if (p->linear_sums == SLA_LINEAR_CHAIN && (p->dtype != SLA_BF16 || (Nb + 31) / 32 * 32 > sla::kChainMaxNbp))
+    return fail(SLA_ERR_UNSUPPORTED, "the chain form of the marginal sums is built for bf16 and Nb <= %d",
+                sla::kChainMaxNbp);
   D->B = p->B;
   D->H = p->H;
   D->N = p->N;
@@ -72,6 +77,7 @@ int make_dims(const sla_problem* p, sla::Dims* D) {
   D->quant = p->quant == SLA_QUANT_I8QK_F8PV;
   D->elu = p->phi == SLA_PHI_ELU1;
   D->proj_hs = p->proj_head_stride;
+  D->chain = p->linear_sums == SLA_LINEAR_CHAIN;
   return SLA_OK;
 }
 
@@ -99,6 +105,10 @@ size_t carve(const Dims& D, void* base, Work* w) {
     if (!D.quant) x.vt = (uint16_t*)take(BH * D.Nb * D.d * kBlock * sizeof(uint16_t));
     x.ind = (uint32_t*)take(BH * (D.Nbp / 32) * D.Nb128 * sizeof(uint32_t));
     x.wo = (uint16_t*)take((size_t)(D.proj_hs ? D.H : 1) * D.d * D.d * sizeof(uint16_t));
+    if (D.chain) {
+      x.chain_lists = (uint16_t*)take(BH * D.Nb * D.Nb * sizeof(uint16_t));
+      x.chain_cnt = (uint32_t*)take(BH * D.Nb * sizeof(uint32_t));
+    }
   } else {
     x.hx = take(BH * D.Nb * D.NN * sizeof(float));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(float));
@@ -139,7 +149,7 @@ size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw) {
 
 extern "C" {
 
-int sla_version(void) { return (1 << 16) | 1; }
+int sla_version(void) { return (1 << 16) | 2; }
 
 const char* sla_status_str(int status) {
   switch (status) {
@@ -164,6 +174,7 @@ int sla_block_counts(const sla_problem* p, int32_t* nb, int32_t* n_h, int32_t* n
   if (q.d != 64 && q.d != 128) q.d = 64;
   q.proj_head_stride = 0;
   q.phi = SLA_PHI_SOFTMAX;
+  q.linear_sums = SLA_LINEAR_GEMM;
   const int rc = make_dims(&q, &D);
   if (rc != SLA_OK) return rc;
   if (nb) *nb = D.Nb;
@@ -266,8 +277,12 @@ int run_forward(const sla_problem* p, const void* Q, const void* K, const void* 
   if (D.quant) SLA_LAUNCH(sla::launch_qk_mean(D, w, s), "channel-mean kernel");
   SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
   SLA_LAUNCH(mark(3), "event record");
-  if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
-  SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
+  if (D.chain) {
+    SLA_LAUNCH(sla::launch_chain(D, mask, w, s), "chain kernels");
+  } else {
+    if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
+    SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
+  }
   SLA_LAUNCH(mark(4), "event record");
   float* dos = dbg ? dbg->o_s : nullptr;
   float* dol = dbg ? dbg->o_l : nullptr;
@@ -475,8 +490,12 @@ int run_backward(const sla_problem* p, const void* Q, const void* K, const void*
   } while (0)
   // the linear branch's per-query-block state H_i, Z_i, as in the forward pass
   SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
-  if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
-  SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
+  if (D.chain) {
+    SLA_LAUNCH(sla::launch_chain(D, mask, w, s), "chain kernels");
+  } else {
+    if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
+    SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
+  }
   SLA_LAUNCH(sla::launch_backward(D, Q, K, V, mask, sla1 ? nullptr : alpha, proj_o, dO, w, bw, dQ, dK, dV,
                                   dalpha, dproj_o, s),
              "backward kernels");

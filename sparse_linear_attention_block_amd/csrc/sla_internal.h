@@ -23,6 +23,7 @@ struct Dims {
   bool quant;
   bool elu;         // feature map elu(x) + 1 instead of the softmax over the features
   int proj_hs;      // head stride of proj_q / proj_k / proj_o in elements: 0 or d*d
+  bool chain;       // marginal sums by the row-to-row chain (k_chain.hip) instead of the GEMM
 };
 
 // Device workspace regions, carved from the caller's buffer.
@@ -46,6 +47,8 @@ struct Work {
   float* vs;          // quant only: [BH, Nb] per-block scales of V
   uint16_t* wo;       // bf16 only: [Hs, d/16, d/32, 64, 8] the SLA output map Proj in bf16 MFMA
                       // A-operand fragments (Hs = H if it is per head, else 1; k_sparse.hip)
+  uint16_t* chain_lists;  // chain only: [BH, Nb, Nb] per row, the blocks to add (front) and subtract (back)
+  uint32_t* chain_cnt;    // chain only: [BH, Nb] their counts, n_add | n_sub << 16
 };
 
 size_t carve(const Dims& D, void* base, Work* w);  // returns bytes needed (base may be NULL)
@@ -76,6 +79,10 @@ hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8
 hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w, hipStream_t s);
 hipError_t launch_indicator(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
 hipError_t launch_linear(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
+// the chain form of the marginal sums (bf16, Nbp <= kChainMaxNbp), and its LDS bytes per workgroup
+constexpr int kChainMaxNbp = 1216;
+size_t chain_lds_bytes(int Nbp);
+hipError_t launch_chain(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
 // proj_o == NULL: the SLA2 mix with alpha; else O = O_s + O_l proj_o (alpha unused; the
 // bf16 kernel reads the fragments that launch_pack_proj wrote to w.wo)
 hipError_t launch_pack_proj(const Dims& D, const float* proj_o, const Work& w, hipStream_t s);

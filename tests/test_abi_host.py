@@ -341,3 +341,26 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     bad = sla.make_problem(1, 12, 100, 96, "bf16", 0.05, 0.10)   # d = 96 is not built
     assert lib.sla_forward_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, fake, fake,
                                    None) == B.SLA_ERR_UNSUPPORTED
+
+
+def test_linear_sums_field():
+    lib = sla.load_library()
+    n = ctypes.c_size_t()
+    g = sla.make_problem(1, 12, 32760, 128, "bf16", 0.05, 0.10)
+    c = sla.make_problem(1, 12, 32760, 128, "bf16", 0.05, 0.10, linear="chain")
+    assert lib.sla_workspace_bytes(ctypes.byref(g), ctypes.byref(n)) == 0
+    ng = n.value
+    assert lib.sla_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == 0
+    # the chain's per-row lists and counts (the indicator and its product still have their regions)
+    assert n.value >= ng + 12 * 512 * 512 * 2 + 12 * 512 * 4
+    bad = sla.make_problem(1, 2, 1000, 64, "bf16", 0.2, 0.2)
+    bad.linear_sums = 7
+    assert lib.sla_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == B.SLA_ERR_ARG
+    f32 = sla.make_problem(1, 2, 1000, 64, "f32", 0.2, 0.2, linear="chain")
+    assert lib.sla_workspace_bytes(ctypes.byref(f32), ctypes.byref(n)) == B.SLA_ERR_UNSUPPORTED
+    ok = sla.make_problem(1, 2, 1216 * 64, 64, "bf16", 0.01, 0.01, linear="chain")
+    assert lib.sla_workspace_bytes(ctypes.byref(ok), ctypes.byref(n)) == 0
+    big = sla.make_problem(1, 2, 1216 * 64 + 1, 64, "bf16", 0.01, 0.01, linear="chain")
+    assert lib.sla_workspace_bytes(ctypes.byref(big), ctypes.byref(n)) == B.SLA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        sla.make_problem(1, 2, 100, 64, "bf16", 0.2, 0.2, linear="lut")
