@@ -88,7 +88,6 @@ def kernel_bytes(B, H, N, d, Nb, n_h, quant=False):
     Nbp = (Nb + 31) // 32 * 32
     hx = 2.0 * BH * Nbp * NN
     Hx = 2.0 * BH * Nb * NN
-    vt = 2.0 * BH * Nb * d * 64
     X8 = BH * Nb * 64 * d * 1.0     # one 8-bit copy, whole blocks
     kbias = 4.0 * BH * Nb * 64
     if quant:
@@ -102,11 +101,10 @@ def kernel_bytes(B, H, N, d, Nb, n_h, quant=False):
     return {
         "pool_proj": 2 * X + 2 * 8.0 * BH * Nb * d,
         "score_select": 2 * 8.0 * BH * Nb * d + BH * Nb * Nb,
-        # the method's own bytes: K and V read, h_j and z_j written (the V^T copy the
-        # sparse kernel reads is a layout of ours, not counted)
+        # K and V read, h_j and z_j written
         "hz": 2 * X + hx,
         "linear_sum": hx + Hx + BH * Nb * Nb,
-        "sparse_attn_mix": X + X + vt + Hx + X,  # Q, K tiles, V^T tiles, H_i, O (K/V once each)
+        "sparse_attn_mix": X + X + X + Hx + X,  # Q, K tiles, V tiles, H_i, O (K/V once each)
     }
 
 

@@ -20,11 +20,9 @@
 //     linear-branch GEMM's k operand, 4 consecutive key blocks, contiguous);
 //     the workgroups of the two halves run on one XCD, so the halves meet in
 //     its L2;
-//  3. z_j[r] (from the same bf16 phi values) goes to column d*d + r;
-//  4. the V^T tile of each block is copied to vt for the sparse kernel, whose
-//     P.V product needs the token index contiguous: for each half of the keys
-//     a [d][32] block, keys permuted into that kernel's MFMA k-slot order and
-//     16-byte chunks swizzled against LDS bank conflicts.
+//  3. z_j[r] (from the same bf16 phi values) goes to column d*d + r.
+//  (A V^T copy for the sparse kernel can still be written through `vt`; the
+//  bf16 sparse kernel now reads the V rows themselves, so it is passed NULL.)
 // Tokens past N and blocks past Nb are zero in LDS, so they add nothing.
 // 8-bit sparse branch: from the K rows already in registers the same pass forms
 // K - mean(K), its int8 codes with one absmax scale per block and the per-key
@@ -449,11 +447,11 @@ hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w,
     dim3 grid(D.Nbp / 4 * 2 * D.BH);
     if (D.d == 128)
       hipLaunchKernelGGL(k_hz_bf16<128>, grid, dim3(HzCfg<128>::NT), 0, s, (const uint16_t*)K,
-                         (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4,
+                         (const uint16_t*)V, (uint16_t*)w.hx, nullptr, D.N, D.Nb, D.Nbp / 4,
                          D.quant ? w.v8t : nullptr, w.vs, w.qkmean, w.k8, w.ks, w.kb, D.BH, D.elu ? 1 : 0);
     else
       hipLaunchKernelGGL(k_hz_bf16<64>, grid, dim3(HzCfg<64>::NT), 0, s, (const uint16_t*)K,
-                         (const uint16_t*)V, (uint16_t*)w.hx, D.quant ? nullptr : w.vt, D.N, D.Nb, D.Nbp / 4,
+                         (const uint16_t*)V, (uint16_t*)w.hx, nullptr, D.N, D.Nb, D.Nbp / 4,
                          D.quant ? w.v8t : nullptr, w.vs, w.qkmean, w.k8, w.ks, w.kb, D.BH, D.elu ? 1 : 0);
   } else {
     dim3 grid(D.Nb, D.BH);

@@ -15,9 +15,9 @@
 // on chip per query block). One workgroup of 4 waves owns a query block; wave
 // w owns queries 16w .. 16w+15 against every key, so its online softmax needs
 // no partner. The keys of a critical tile are taken 32 at a time (a step):
-// the K rows and V^T columns of a step arrive by direct global->LDS copies (no
+// the K rows and V rows of a step arrive by direct global->LDS copies (no
 // register staging) into one of two 16 KB buffers, one step ahead, one barrier
-// per step, and three workgroups fit on a CU. Per step:
+// per step. Per step:
 //   S^T = K Q^T    MFMA 16x16x32, the step's 32 keys as A (row-swizzled LDS),
 //                  the wave's 16 queries (registers) as B; a lane gets 4 keys
 //                  of one query per 16-key tile;
@@ -27,11 +27,14 @@
 //                  not depend on the reference); the row sums of P come from
 //                  one more MFMA with an A operand whose row 0 is all ones;
 //   O^T += V^T P^T MFMA 16x16x32 with P^T straight from registers: a lane's 8
-//                  k slots are its keys {4g..4g+3, 16+4g..16+4g+3}, and the h/z
-//                  kernel stored V^T in that key order.
+//                  k slots are its keys {4g..4g+3, 16+4g..16+4g+3}; the V^T
+//                  operand comes from the V rows in LDS through gfx950's
+//                  transposed LDS reads (ds_read_b64_tr_b16), in that key order.
 // All K fragments of a step are read before the next step's copies are issued
 // and before its first product, and the V^T fragments right after the last
-// one, so their LDS latency overlaps. During the last step the first half of
+// one, so their LDS latency overlaps. Each wave owns two 16-query groups (two
+// waves per query block), so every fragment it reads from LDS feeds two
+// products. During the last step the first half of
 // H_i^T (from K4's output, rows swizzled like K) is copied into the idle buffer
 // and Z_i into the spent critical list; the second half follows into the other
 // buffer while phi(Q) is formed. Each wave then finishes its 16 queries:
@@ -64,6 +67,34 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef short s16x4_v __attribute__((ext_vector_type(4)));
+
+// The A operand of O^T += V^T P^T for feature tile ft of a 32-key step, from
+// the step's V rows in LDS (row-major; 16-byte chunk q of row r at position
+// q ^ (r % C), like the K rows): lane (l16, g) holds feature 16 ft + l16 of keys
+// 4g .. 4g+3 (k slots 0-3) and 16+4g .. 16+4g+3 (k slots 4-7), the key order of
+// P^T's B operand. gfx950's transposed LDS read gives lane i of a 16-lane group
+// element k of source lane 4k + i/4's four 16-bit values at position i % 4, so
+// source lane s reads the 8 bytes of features 16 ft + 4 (s % 4) .. +3 of key
+// row 4g + s / 4 (and of the row 16 below it). xb is the lane's byte offset for
+// ft = 0; the swizzle and the row occupy disjoint bits, so tile ft is at
+// xb ^ 32 ft.
+template <int D>
+__device__ __forceinline__ int vt_base(int g, int s) {
+  constexpr int C = D / 8;
+  const int r = 4 * g + (s >> 2), m = r & (C - 1);
+  return r * 2 * D + 32 * (m >> 1) + 16 * (((s & 3) >> 1) ^ (m & 1)) + 8 * (s & 1);
+}
+template <int D>
+__device__ __forceinline__ uint4 vt_frag(const uint16_t* vrows, int xb, int ft) {
+  const char* p0 = reinterpret_cast<const char*>(vrows) + (xb ^ (32 * ft));
+  const char* p1 = p0 + 16 * 2 * D;  // 16 key rows further
+  const s16x4_v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_v*)p0);
+  const s16x4_v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_v*)p1);
+  const uint2 lo = __builtin_bit_cast(uint2, a), hi = __builtin_bit_cast(uint2, b);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 template <int D, int NW>
 struct FaCfg {
   static constexpr int NT = 64 * NW;               // threads of a workgroup
@@ -93,7 +124,7 @@ template <int D, int NW, bool PROJ, bool ELU>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 2 : 3, NW == 2 ? 2 : 3)))
 void k_sparse_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ vt, const int8_t* __restrict__ mask,
+    const uint16_t* __restrict__ V, const int8_t* __restrict__ mask,
     const uint16_t* __restrict__ Hx, const float* __restrict__ alpha,
     const uint16_t* __restrict__ wo, int wo_hs, uint16_t* __restrict__ O,
     float* __restrict__ dbg_os, float* __restrict__ dbg_ol, int H, int N, int Nb) {
@@ -136,11 +167,12 @@ void k_sparse_bf16(
   const int nstep = 2 * ncrit;  // step s: keys 32 (s & 1) .. +31 of critical tile s >> 1
 
   const uint16_t* Kb = K + (size_t)bh * N * D;
-  const uint16_t* Vb = vt + (size_t)bh * Nb * 2 * HT;
-  // K rows land in LDS with their 16-byte chunks XOR-swizzled by the row
-  // index (16 lanes reading 16 rows at one column hit distinct banks); the
-  // V^T half tile is copied as laid out by the h/z kernel. The per-lane source
-  // offsets within a half tile are the same for every step.
+  const uint16_t* Vb = V + (size_t)bh * N * D;
+  // K and V rows land in LDS with their 16-byte chunks XOR-swizzled by the row
+  // index (16 lanes reading 16 rows at one chunk hit distinct banks, and a
+  // transposed read of 32 bytes from each of 16 V rows takes the two cycles
+  // its 512 bytes need). The per-lane source offsets within a half tile are the
+  // same for every step and for K and V.
   int koff[INSTR];
 #pragma unroll
   for (int u = 0; u < INSTR; ++u) {
@@ -148,29 +180,30 @@ void k_sparse_bf16(
     const int r = G / C, sch = G % C;
     koff[u] = r * D + (sch ^ (r & (C - 1))) * 8;
   }
-  // Copies go through buffer resources over this head's K rows and V^T half
-  // tiles: the per-lane byte offsets stay in registers and the step's offset
+  const int vxb = vt_base<D>(g, l16);
+  // Copies go through buffer resources over this head's K and V rows: the
+  // per-lane byte offsets stay in registers and the step's offset
   // (wave-uniform) is the scalar offset.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, N * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, Nb * 2 * HT * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, N * D * 2);
   auto issue = [&](int jv, int hv, uint16_t* dst) {
     const int j = __builtin_amdgcn_readfirstlane(jv);
     const int hh = __builtin_amdgcn_readfirstlane(hv);
     const int row0 = j * kBlock + 32 * hh;
-    const int sk = row0 * D * 2, sv = (2 * j + hh) * HT * 2;
-    if (row0 + 32 > N) {  // ragged: rows past N re-read row N-1 (masked below)
+    const int sk = row0 * D * 2;
+    if (row0 + 32 > N) {  // ragged: rows past N re-read row N-1 (their P is 0)
       const int over = row0 - (N - 1);
 #pragma unroll
       for (int u = 0; u < INSTR; ++u) {
         const int off = koff[u] - max(0, koff[u] / D + over) * D;
         load_lds16_buf(krs, 2 * off, sk, dst + 512 * (NW * u + wave));
-        load_lds16_buf(vrs, (64 * (NW * u + wave) + lane) * 16, sv, dst + HT + 512 * (NW * u + wave));
+        load_lds16_buf(vrs, 2 * off, sk, dst + HT + 512 * (NW * u + wave));
       }
     } else {
 #pragma unroll
       for (int u = 0; u < INSTR; ++u) {
         load_lds16_buf(krs, 2 * koff[u], sk, dst + 512 * (NW * u + wave));
-        load_lds16_buf(vrs, (64 * (NW * u + wave) + lane) * 16, sv, dst + HT + 512 * (NW * u + wave));
+        load_lds16_buf(vrs, 2 * koff[u], sk, dst + HT + 512 * (NW * u + wave));
       }
     }
   };
@@ -241,14 +274,12 @@ void k_sparse_bf16(
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) sv[qg][kt] = mfma_bf16(ka[ks][kt], qr[qg][ks], sv[qg][kt]);
-    // the V^T fragments of the step load while the softmax runs
+    // the V^T fragments of the step (transposed reads of the V rows) load
+    // while the softmax runs
     const uint16_t* vtile = cur + HT;
     uint4 va[FT];
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      const int c = 16 * ft + l16;
-      va[ft] = *reinterpret_cast<const uint4*>(vtile + c * 32 + 8 * (g ^ ((c >> 1) & 3)));
-    }
+    for (int ft = 0; ft < FT; ++ft) va[ft] = vt_frag<D>(vtile, vxb, ft);
     __builtin_amdgcn_sched_barrier(0);
     if (j * kBlock + 32 * hh + 32 > N) {  // ragged last block: keys past N take no part
       const int kbase = j * kBlock + 32 * hh + 4 * g;
@@ -670,35 +701,35 @@ int sparse_waves() {
 }
 
 template <int D, int NW, bool PROJ, bool ELU>
-hipError_t launch_bf16(const Dims& D_, const void* Q, const void* K, const int8_t* mask,
+hipError_t launch_bf16(const Dims& D_, const void* Q, const void* K, const void* V, const int8_t* mask,
                        const float* alpha, const Work& w, void* O, float* dbg_os, float* dbg_ol,
                        hipStream_t s) {
   // dynamic LDS: the critical list (2 Nb bytes), later Z_i (2 D bytes)
   const size_t lbytes = ((size_t)2 * (D_.Nb > D ? D_.Nb : D) + 15) / 16 * 16;
   hipLaunchKernelGGL((k_sparse_bf16<D, NW, PROJ, ELU>), dim3(D_.BH * D_.Nb), dim3(64 * NW), lbytes, s,
-                     (const uint16_t*)Q, (const uint16_t*)K, w.vt, mask, (const uint16_t*)w.Hx, alpha,
+                     (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, mask, (const uint16_t*)w.Hx, alpha,
                      w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, D_.H, D_.N, D_.Nb);
   return hipGetLastError();
 }
 
 template <int D, int NW>
-hipError_t launch_bf16_nw(const Dims& D_, const void* Q, const void* K, const int8_t* mask,
+hipError_t launch_bf16_nw(const Dims& D_, const void* Q, const void* K, const void* V, const int8_t* mask,
                           const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
                           float* dbg_ol, hipStream_t s) {
   if (proj)
-    return D_.elu ? launch_bf16<D, NW, true, true>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s)
-                  : launch_bf16<D, NW, true, false>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s);
-  return D_.elu ? launch_bf16<D, NW, false, true>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s)
-                : launch_bf16<D, NW, false, false>(D_, Q, K, mask, alpha, w, O, dbg_os, dbg_ol, s);
+    return D_.elu ? launch_bf16<D, NW, true, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, s)
+                  : launch_bf16<D, NW, true, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, s);
+  return D_.elu ? launch_bf16<D, NW, false, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, s)
+                : launch_bf16<D, NW, false, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, s);
 }
 
 template <int D>
-hipError_t launch_bf16_d(const Dims& D_, const void* Q, const void* K, const int8_t* mask,
+hipError_t launch_bf16_d(const Dims& D_, const void* Q, const void* K, const void* V, const int8_t* mask,
                          const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
                          float* dbg_ol, hipStream_t s) {
   if (sparse_waves() == 4)
-    return launch_bf16_nw<D, 4>(D_, Q, K, mask, alpha, proj, w, O, dbg_os, dbg_ol, s);
-  return launch_bf16_nw<D, 2>(D_, Q, K, mask, alpha, proj, w, O, dbg_os, dbg_ol, s);
+    return launch_bf16_nw<D, 4>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, s);
+  return launch_bf16_nw<D, 2>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, s);
 }
 
 }  // namespace
@@ -713,13 +744,13 @@ hipError_t launch_pack_proj(const Dims& D, const float* proj_o, const Work& w, h
   return hipGetLastError();
 }
 
-hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const int8_t* mask,
+hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                          const float* alpha, const float* proj_o, const Work& w, void* O,
                          float* dbg_os, float* dbg_ol, hipStream_t s) {
-  // the f32 path reads V directly; vt is not formed
   if (!D.bf16) return hipErrorInvalidValue;
-  if (D.d == 128) return launch_bf16_d<128>(D, Q, K, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
-  return launch_bf16_d<64>(D, Q, K, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
+  if (D.d == 128)
+    return launch_bf16_d<128>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
+  return launch_bf16_d<64>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
 }
 
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,

@@ -102,7 +102,6 @@ size_t carve(const Dims& D, void* base, Work* w) {
   if (D.bf16) {
     x.hx = take(BH * (D.Nbp / 4) * D.NN * 4 * sizeof(uint16_t));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(uint16_t));
-    if (!D.quant) x.vt = (uint16_t*)take(BH * D.Nb * D.d * kBlock * sizeof(uint16_t));
     x.ind = (uint32_t*)take(BH * (D.Nbp / 32) * D.Nb128 * sizeof(uint32_t));
     x.wo = (uint16_t*)take((size_t)(D.proj_hs ? D.H : 1) * D.d * D.d * sizeof(uint16_t));
     if (D.chain) {
@@ -290,7 +289,7 @@ int run_forward(const sla_problem* p, const void* Q, const void* K, const void* 
   if (D.quant)
     SLA_LAUNCH(sla::launch_sparse_q8(D, Q, mask, alpha, w, O, dos, dol, s), "8-bit sparse kernel");
   else if (D.bf16)
-    SLA_LAUNCH(sla::launch_sparse(D, Q, K, mask, alpha, proj_o, w, O, dos, dol, s), "sparse kernel");
+    SLA_LAUNCH(sla::launch_sparse(D, Q, K, V, mask, alpha, proj_o, w, O, dos, dol, s), "sparse kernel");
   else
     SLA_LAUNCH(sla::launch_sparse_f32(D, Q, K, V, mask, alpha, proj_o, w, O, dos, dol, s), "sparse kernel");
   SLA_LAUNCH(mark(5), "event record");

@@ -37,7 +37,6 @@ struct Work {
   void* Hx;           // [BH, Nb, NN] per query block: H_i^T (c-major) then Z_i; bf16 or f32
   uint32_t* ind;      // bf16 only: [BH, Nbp/32, Nb128/128, 16, 8] marginal indicator (Mc == 0)
                       // as bits, one 32-bit word per (32-key step, query block) (k_linear.hip)
-  uint16_t* vt;       // bf16 without quant: [BH, Nb, d, 64] V^T of every key block (zero past N)
   float* qkmean;      // quant only: [2, BH, d] channel means of Q and K over the N tokens
   int8_t* k8;         // quant only: [BH, Nb*64, d] int8 of K - mean(K), zero rows past N;
                       // bytes of each row in the score product's k-slot order (k_quant.hip)
@@ -86,7 +85,7 @@ hipError_t launch_chain(const Dims& D, const int8_t* mask, const Work& w, hipStr
 // proj_o == NULL: the SLA2 mix with alpha; else O = O_s + O_l proj_o (alpha unused; the
 // bf16 kernel reads the fragments that launch_pack_proj wrote to w.wo)
 hipError_t launch_pack_proj(const Dims& D, const float* proj_o, const Work& w, hipStream_t s);
-hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const int8_t* mask,
+hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                          const float* alpha, const float* proj_o, const Work& w, void* O,
                          float* dbg_os, float* dbg_ol, hipStream_t s);
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,
