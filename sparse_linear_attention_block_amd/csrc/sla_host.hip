@@ -98,7 +98,9 @@ size_t carve(const Dims& D, void* base, Work* w) {
   x.pooled_q = (double*)take(BH * D.Nb * D.d * sizeof(double));
   x.pooled_k = (double*)take(BH * D.Nb * D.d * sizeof(double));
   x.pooled_raw = (double*)take(2 * BH * D.Nb * D.d * sizeof(double));
-  x.logits = (double*)take(BH * D.Nb * D.Nb * sizeof(double));
+  x.hilo = (uint16_t*)take(4 * BH * D.Nb * D.d * sizeof(uint16_t));
+  x.est = (float*)take(BH * D.Nb * D.Nb * sizeof(float));
+  x.norms = (float*)take(BH * (D.Nb + (D.Nb + 63) / 64) * sizeof(float));
   if (D.bf16) {
     x.hx = take(BH * (D.Nbp / 4) * D.NN * 4 * sizeof(uint16_t));
     x.Hx = take(BH * D.Nb * D.NN * sizeof(uint16_t));
@@ -257,7 +259,7 @@ int run_forward(const sla_problem* p, const void* Q, const void* K, const void* 
       pk = w.pooled_k;
     }
     SLA_LAUNCH(mark(1), "event record");
-    SLA_LAUNCH(sla::launch_select(D, pq, pk, mask_out, (dbg && dbg->logits) ? dbg->logits : w.logits, s),
+    SLA_LAUNCH(sla::launch_select(D, pq, pk, mask_out, w.hilo, w.est, w.norms, dbg ? dbg->logits : nullptr, s),
                "score/select kernel");
     SLA_LAUNCH(mark(2), "event record");
     if (dbg && dbg->pooled_q)

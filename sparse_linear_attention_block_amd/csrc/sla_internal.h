@@ -31,7 +31,11 @@ struct Work {
   double* pooled_q;   // [BH, Nb, d]
   double* pooled_k;   // [BH, Nb, d]
   double* pooled_raw; // [2, BH, Nb, d] block means before the router projection
-  double* logits;     // [BH, Nb, Nb] pooled logits pool(Q) pool(K)^T / sqrt(d)
+  uint16_t* hilo;     // [4, BH, Nb, d] bf16 two-term split of the pooled queries (hi, lo), then keys
+  float* est;         // [BH, Nb, Nb] float32 estimates of the pooled logits
+                      // pool(Q) pool(K)^T / sqrt(d) (k_select.hip)
+  float* norms;       // [BH, Nb] norms of the pooled queries, then [BH, ceil(Nb / 64)] the
+                      // largest norm of each 64 pooled keys
   void* hx;           // bf16: [BH, Nbp/4, NN, 4] (four key blocks interleaved per column)
                       // f32:  [BH, Nb, NN]
   void* Hx;           // [BH, Nb, NN] per query block: H_i^T (c-major) then Z_i; bf16 or f32
@@ -73,8 +77,9 @@ hipError_t launch_pool_proj(const Dims& D, const float* proj_q, const float* pro
 hipError_t launch_qk_mean(const Dims& D, const Work& w, hipStream_t s);
 hipError_t launch_sparse_q8(const Dims& D, const void* Q, const int8_t* mask, const float* alpha,
                             const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
+// the mask from the pooled vectors; dbg_lg (may be NULL): [BH, Nb, Nb] float64 logits, written
 hipError_t launch_select(const Dims& D, const double* pq, const double* pk, int8_t* mask,
-                         double* lg, hipStream_t s);  // lg: [BH, Nb, Nb] float64 logits (written)
+                         uint16_t* hilo, float* est, float* norms, double* dbg_lg, hipStream_t s);
 hipError_t launch_hz(const Dims& D, const void* K, const void* V, const Work& w, hipStream_t s);
 hipError_t launch_indicator(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);
 hipError_t launch_linear(const Dims& D, const int8_t* mask, const Work& w, hipStream_t s);

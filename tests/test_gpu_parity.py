@@ -124,6 +124,25 @@ def test_duplicate_key_blocks_tie():
     _check_all_rows(x, BF16_REL_L1, BF16_MAX_ABS)
 
 
+def test_zero_queries_band_wider_than_a_wave():
+    # every logit 0 on 150 blocks: the whole row is the undecided band at both
+    # boundaries (150 candidates, ranked in three 64-lane chunks) and the order
+    # falls back to the index
+    x = _custom(150 * 64, 0.3, 0.2)
+    x.q.zero_()
+    ref, g, _ = _check_all_rows(x, BF16_REL_L1, BF16_MAX_ABS)
+    expect = np.array([1] * 45 + [0] * 75 + [-1] * 30, dtype=np.int8)
+    assert (g["mask"] == expect).all()
+
+
+def test_duplicate_key_blocks_in_the_band():
+    x = _custom(150 * 64, 0.1, 0.1)
+    # blocks 2, 71 and 140 identical in every head: equal logits wherever they fall
+    for j in (71, 140):
+        x.k[:, :, 64 * j:64 * j + 64] = x.k[:, :, 128:192]
+    _check_all_rows(x, BF16_REL_L1, BF16_MAX_ABS)
+
+
 def test_mask_in_arbitrary_rows():
     x = _custom(1000, 0.2, 0.2)
     Nb = 16
