@@ -322,19 +322,22 @@ def bench_backward(args, cfg, x, torch, sla):
     ms = start.elapsed_time(stop) / args.steps
     F = backward_flops(B, H, Nb, n_h, d)
     achieved = F / (ms * 1e-3) / 1e12
+    # bf16 inputs: every product on bf16 MFMA (float32 accumulation); float32 inputs: the VALU kernels
+    mfma = cfg.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_F32_VALU_TFLOPS
     line = {
         "metric": "SLA2 backward ms & dense-equivalent TFLOPS (10*B*H*N^2*d per backward)",
         "value": round(10.0 * B * H * N * N * d / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s (dense-equivalent backward)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32 (" + cfg.dtype + " inputs)",
+        "vs_baseline": None, "dtype": "bf16 MFMA, f32 accumulate" if mfma else "f32 (" + cfg.dtype + " inputs)",
         "data": "synthetic: the seeded workload, its forward mask and a seeded N(0,1) dO",
         "config": {"workload": cfg.name + "_backward", "B": B, "H": H, "N": N, "d": d, "Nb": Nb,
                    "n_h": n_h, "kh": x.kh, "kl": x.kl},
-        "roofline": {"kernel": "sla_backward (all its kernels)", "bound": "alu",
-                     "achieved": round(achieved, 3), "peak": round(PEAK_F32_VALU_TFLOPS, 1),
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F32_VALU_TFLOPS, 4),
+        "roofline": {"kernel": "sla_backward (all its kernels)", "bound": "mfma" if mfma else "alu",
+                     "achieved": round(achieved, 3), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": None, "flops_per_launch": F, "ms_per_launch": round(ms, 4)},
     }
     if not args.no_cpu:

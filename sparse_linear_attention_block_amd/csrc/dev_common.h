@@ -210,6 +210,35 @@ __device__ inline int compact_row(const int8_t* __restrict__ mrow, int Nb, int8_
   return total;
 }
 
+typedef short s16x4_v __attribute__((ext_vector_type(4)));
+
+// The A operand of O^T += V^T P^T for feature tile ft of a 32-key step (or any
+// product that contracts over 32 rows held row-major in LDS), from the step's V
+// rows in LDS (row-major; 16-byte chunk q of row r at position
+// q ^ (r % C), like the K rows): lane (l16, g) holds feature 16 ft + l16 of keys
+// 4g .. 4g+3 (k slots 0-3) and 16+4g .. 16+4g+3 (k slots 4-7), the key order of
+// P^T's B operand. gfx950's transposed LDS read gives lane i of a 16-lane group
+// element k of source lane 4k + i/4's four 16-bit values at position i % 4, so
+// source lane s reads the 8 bytes of features 16 ft + 4 (s % 4) .. +3 of key
+// row 4g + s / 4 (and of the row 16 below it). xb is the lane's byte offset for
+// ft = 0; the swizzle and the row occupy disjoint bits, so tile ft is at
+// xb ^ 32 ft.
+template <int D>
+__device__ __forceinline__ int vt_base(int g, int s) {
+  constexpr int C = D / 8;
+  const int r = 4 * g + (s >> 2), m = r & (C - 1);
+  return r * 2 * D + 32 * (m >> 1) + 16 * (((s & 3) >> 1) ^ (m & 1)) + 8 * (s & 1);
+}
+template <int D>
+__device__ __forceinline__ uint4 vt_frag(const uint16_t* vrows, int xb, int ft) {
+  const char* p0 = reinterpret_cast<const char*>(vrows) + (xb ^ (32 * ft));
+  const char* p1 = p0 + 16 * 2 * D;  // 16 key rows further
+  const s16x4_v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_v*)p0);
+  const s16x4_v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_v*)p1);
+  const uint2 lo = __builtin_bit_cast(uint2, a), hi = __builtin_bit_cast(uint2, b);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // The same compaction in two parts, so that a kernel can load the mask row
 // first, issue its other prologue loads, and wait only for the mask: mask_load
 // reads bytes j = tid + NT k of the row for k < kMaskPre (every load is issued;

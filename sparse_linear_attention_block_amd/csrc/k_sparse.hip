@@ -67,34 +67,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-typedef short s16x4_v __attribute__((ext_vector_type(4)));
-
-// The A operand of O^T += V^T P^T for feature tile ft of a 32-key step, from
-// the step's V rows in LDS (row-major; 16-byte chunk q of row r at position
-// q ^ (r % C), like the K rows): lane (l16, g) holds feature 16 ft + l16 of keys
-// 4g .. 4g+3 (k slots 0-3) and 16+4g .. 16+4g+3 (k slots 4-7), the key order of
-// P^T's B operand. gfx950's transposed LDS read gives lane i of a 16-lane group
-// element k of source lane 4k + i/4's four 16-bit values at position i % 4, so
-// source lane s reads the 8 bytes of features 16 ft + 4 (s % 4) .. +3 of key
-// row 4g + s / 4 (and of the row 16 below it). xb is the lane's byte offset for
-// ft = 0; the swizzle and the row occupy disjoint bits, so tile ft is at
-// xb ^ 32 ft.
-template <int D>
-__device__ __forceinline__ int vt_base(int g, int s) {
-  constexpr int C = D / 8;
-  const int r = 4 * g + (s >> 2), m = r & (C - 1);
-  return r * 2 * D + 32 * (m >> 1) + 16 * (((s & 3) >> 1) ^ (m & 1)) + 8 * (s & 1);
-}
-template <int D>
-__device__ __forceinline__ uint4 vt_frag(const uint16_t* vrows, int xb, int ft) {
-  const char* p0 = reinterpret_cast<const char*>(vrows) + (xb ^ (32 * ft));
-  const char* p1 = p0 + 16 * 2 * D;  // 16 key rows further
-  const s16x4_v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_v*)p0);
-  const s16x4_v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_v*)p1);
-  const uint2 lo = __builtin_bit_cast(uint2, a), hi = __builtin_bit_cast(uint2, b);
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
 template <int D, int NW>
 struct FaCfg {
   static constexpr int NT = 64 * NW;               // threads of a workgroup
@@ -127,7 +99,7 @@ void k_sparse_bf16(
     const uint16_t* __restrict__ V, const int8_t* __restrict__ mask,
     const uint16_t* __restrict__ Hx, const float* __restrict__ alpha,
     const uint16_t* __restrict__ wo, int wo_hs, uint16_t* __restrict__ O,
-    float* __restrict__ dbg_os, float* __restrict__ dbg_ol, int H, int N, int Nb) {
+    float* __restrict__ dbg_os, float* __restrict__ dbg_ol, float* __restrict__ lse_out, int H, int N, int Nb) {
   using Cf = FaCfg<D, NW>;
   constexpr int NT = Cf::NT, QG = Cf::QG;
   constexpr int C = Cf::C, HT = Cf::HT, INSTR = Cf::INSTR, NN = Cf::NN;
@@ -350,6 +322,12 @@ void k_sparse_bf16(
   for (int qg = 0; qg < QG; ++qg) {
     const float lw = __shfl(accl[qg][0], l16);  // from lane group 0
     inv_l[qg] = lw > 0.f ? 1.0f / lw : 0.f;
+    if (lse_out && g == 0) {  // log2 of the softmax normaliser: P = exp2(s log2(e) / sqrt(d) - lse2)
+      const int tq = 16 * (QG * wave + qg) + l16;
+      const float meff = mref[qg] == -INFINITY ? 0.0f : mref[qg];
+      lse_out[((size_t)bh * Nb + i) * kBlock + tq] =
+          (lw > 0.f && i * kBlock + tq < N) ? meff + __log2f(lw) : INFINITY;
+    }
   }
   if constexpr (HPARTS == 2) {
     lds_barrier();  // every wave is done with bufB
@@ -516,7 +494,7 @@ void k_sparse_bf16(
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // a wave reads back only its own rows
   // full-row 16-byte stores of the wave's staged rows
-  const int nrow = min(16 * QG, N - (i * kBlock + 16 * QG * wave));
+  const int nrow = O ? min(16 * QG, N - (i * kBlock + 16 * QG * wave)) : 0;
   uint16_t* Ob = O + ((size_t)bh * N + (size_t)i * kBlock + 16 * QG * wave) * D;
 #pragma unroll
   for (int x0 = 0; x0 < 16 * QG * C; x0 += 64) {
@@ -703,33 +681,33 @@ int sparse_waves() {
 template <int D, int NW, bool PROJ, bool ELU>
 hipError_t launch_bf16(const Dims& D_, const void* Q, const void* K, const void* V, const int8_t* mask,
                        const float* alpha, const Work& w, void* O, float* dbg_os, float* dbg_ol,
-                       hipStream_t s) {
+                       float* lse_out, hipStream_t s) {
   // dynamic LDS: the critical list (2 Nb bytes), later Z_i (2 D bytes)
   const size_t lbytes = ((size_t)2 * (D_.Nb > D ? D_.Nb : D) + 15) / 16 * 16;
   hipLaunchKernelGGL((k_sparse_bf16<D, NW, PROJ, ELU>), dim3(D_.BH * D_.Nb), dim3(64 * NW), lbytes, s,
                      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, mask, (const uint16_t*)w.Hx, alpha,
-                     w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, D_.H, D_.N, D_.Nb);
+                     w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, lse_out, D_.H, D_.N, D_.Nb);
   return hipGetLastError();
 }
 
 template <int D, int NW>
 hipError_t launch_bf16_nw(const Dims& D_, const void* Q, const void* K, const void* V, const int8_t* mask,
                           const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
-                          float* dbg_ol, hipStream_t s) {
+                          float* dbg_ol, float* lse_out, hipStream_t s) {
   if (proj)
-    return D_.elu ? launch_bf16<D, NW, true, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, s)
-                  : launch_bf16<D, NW, true, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, s);
-  return D_.elu ? launch_bf16<D, NW, false, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, s)
-                : launch_bf16<D, NW, false, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, s);
+    return D_.elu ? launch_bf16<D, NW, true, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, s)
+                  : launch_bf16<D, NW, true, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, s);
+  return D_.elu ? launch_bf16<D, NW, false, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, s)
+                : launch_bf16<D, NW, false, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, s);
 }
 
 template <int D>
 hipError_t launch_bf16_d(const Dims& D_, const void* Q, const void* K, const void* V, const int8_t* mask,
                          const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
-                         float* dbg_ol, hipStream_t s) {
+                         float* dbg_ol, float* lse_out, hipStream_t s) {
   if (sparse_waves() == 4)
-    return launch_bf16_nw<D, 4>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, s);
-  return launch_bf16_nw<D, 2>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, s);
+    return launch_bf16_nw<D, 4>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, lse_out, s);
+  return launch_bf16_nw<D, 2>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, lse_out, s);
 }
 
 }  // namespace
@@ -746,11 +724,11 @@ hipError_t launch_pack_proj(const Dims& D, const float* proj_o, const Work& w, h
 
 hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                          const float* alpha, const float* proj_o, const Work& w, void* O,
-                         float* dbg_os, float* dbg_ol, hipStream_t s) {
+                         float* dbg_os, float* dbg_ol, hipStream_t s, float* lse_out) {
   if (!D.bf16) return hipErrorInvalidValue;
   if (D.d == 128)
-    return launch_bf16_d<128>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
-  return launch_bf16_d<64>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, s);
+    return launch_bf16_d<128>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, lse_out, s);
+  return launch_bf16_d<64>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, lse_out, s);
 }
 
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,

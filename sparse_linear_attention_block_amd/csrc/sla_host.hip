@@ -141,6 +141,10 @@ size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw) {
   x.dHx = (float*)take(BH * D.Nb * D.NN * sizeof(float));
   x.dHtot = (float*)take(BH * D.NN * sizeof(float));
   x.dal = (float*)take(BH * D.Nb * sizeof(float));
+  if (D.bf16) {  // the MFMA path (SLA2; carved for both formulations so that the SLA fusion only adds dW)
+    x.Os = (float*)take(BH * D.N * D.d * sizeof(float));
+    x.maskT = (int8_t*)take(BH * D.Nb * D.Nb);
+  }
   if (proj) x.dWp = (float*)take(BH * D.Nb * D.d * D.d * sizeof(float));
   if (bw) *bw = x;
   return off;

@@ -64,6 +64,8 @@ struct BwdWork {
   float* dHtot;  // [BH, NN] their sum over the head's query blocks
   float* dal;    // [BH, Nb] partial dalpha of each query block
   float* dWp;    // SLA fusion only: [BH, Nb, d, d] each query block's part of dW = O_l^T dO
+  float* Os;     // bf16 only: [BH, N, d] O_s of the forward recompute (k_backward_mfma.hip)
+  int8_t* maskT; // bf16 only: [BH, Nb, Nb] the transposed mask
 };
 // forward + backward bytes; proj: the SLA fusion's dW parts are included
 size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw);
@@ -90,15 +92,23 @@ hipError_t launch_chain(const Dims& D, const int8_t* mask, const Work& w, hipStr
 // proj_o == NULL: the SLA2 mix with alpha; else O = O_s + O_l proj_o (alpha unused; the
 // bf16 kernel reads the fragments that launch_pack_proj wrote to w.wo)
 hipError_t launch_pack_proj(const Dims& D, const float* proj_o, const Work& w, hipStream_t s);
+// O may be NULL (nothing stored); lse_out (may be NULL): [BH, Nb*64] log2 of each query's softmax
+// normaliser over its critical keys, P = exp2(s log2(e) / sqrt(d) - lse2) (+inf past N or with no
+// critical key)
 hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                          const float* alpha, const float* proj_o, const Work& w, void* O,
-                         float* dbg_os, float* dbg_ol, hipStream_t s);
+                         float* dbg_os, float* dbg_ol, hipStream_t s, float* lse_out = nullptr);
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,
                              const int8_t* mask, const float* alpha, const float* proj_o,
                              const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
 
 // proj_o == NULL: SLA2 (dalpha written, dproj_o unused); else the SLA fusion (dproj_o
 // written, alpha and dalpha unused)
+// bf16 SLA2 (no output map): the MFMA kernels of k_backward_mfma.hip; writes dQ, dK, dV and the
+// per-block dalpha partials (bw.dal); uses bw.lse / bw.dt as lse2 / D_t and bw.dHx as bf16 dH
+hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
+                                const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
+                                float* dK, float* dV, hipStream_t s);
 hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                            const float* alpha, const float* proj_o, const void* dO, const Work& w,
                            const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,

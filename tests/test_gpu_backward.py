@@ -7,7 +7,10 @@ Bounds, per (batch, head), on rel-L1 = sum |x - y| / sum |y|: fp32 inputs 1e-4
 (fp32 arithmetic over sums of at most a few thousand terms); bf16 inputs 1e-2,
 the forward's bf16 bound (the linear branch's H_i and Z_i are the forward's
 bf16 ones). dalpha to 1e-4 (fp32) or 1e-2 (bf16) relative; dW to the same
-rel-L1 bounds.
+rel-L1 bounds. For bf16 inputs without the output map the products run on
+bf16 MFMA: P, dS, phi and the linear-branch gradients enter them rounded to
+bf16 (relative 2^-9), so the closed form of the sum of dV over the keys, whose
+error is that of the few dominant weights of each row, is held to 3e-3.
 """
 
 import numpy as np
@@ -117,14 +120,16 @@ def test_full_size_sampled():
             assert e <= 1e-2, (h, i, e)
     g = dO.double().numpy()
     al = x.alpha.double().numpy()
+    worst = 0.0
     for h in range(cfg.H):
         c = np.repeat((mask[0, h] == 1).any(axis=1), 64)[:x.N].astype(float)
         m = np.repeat((mask[0, h] == 0).any(axis=1), 64)[:x.N].astype(float)
         w = al[h] * c + (1 - al[h]) * m
         expect = (w[:, None] * g[0, h]).sum(axis=0)
         e = rel_l1(dV[0, h].sum(axis=0), expect)
-        assert e <= 1e-3, (h, e)
-    _flush(f"sum of dV over the keys matches its closed form on all {cfg.H} heads")
+        worst = max(worst, e)
+        assert e <= 3e-3, (h, e)
+    _flush(f"sum of dV over the keys matches its closed form on all {cfg.H} heads (worst {worst:.2e})")
 
 
 def test_bf16_batch_of_two():
