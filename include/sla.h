@@ -238,8 +238,11 @@ int sla_backward_workspace_bytes(const sla_problem* p, size_t* bytes);
  *  dV
  *  dalpha    device float32 [H] output, summed over the batch.
  *  workspace device scratch of at least sla_backward_workspace_bytes(p) bytes.
- * fp32 arithmetic; either feature map (p->phi). Requires quant ==
- * SLA_QUANT_NONE (SLA_ERR_UNSUPPORTED otherwise). Errors as for sla_forward. */
+ * Arithmetic: with bf16 inputs every product runs on bf16 matrix cores with
+ * float32 accumulation (P, dS, phi and the linear-branch gradients rounded to
+ * bf16); with float32 inputs, float32 throughout. Either feature map
+ * (p->phi). Requires quant == SLA_QUANT_NONE (SLA_ERR_UNSUPPORTED otherwise).
+ * Errors as for sla_forward. */
 int sla_backward(const sla_problem* p,
                  const void* Q, const void* K, const void* V, const float* alpha,
                  const int8_t* mask, const void* dO,
@@ -248,7 +251,8 @@ int sla_backward(const sla_problem* p,
                  void* stream);
 
 /* Workspace that sla1_backward needs for `p` (host only, no device work): that
- * of sla_backward plus one d x d float32 part of dproj_o per query block. */
+ * of sla_backward plus one d x d float32 part of dproj_o per query block (and,
+ * with bf16 inputs, proj_o once in bf16). */
 int sla1_backward_workspace_bytes(const sla_problem* p, size_t* bytes);
 
 /* The backward pass of the SLA formulation O = O_s + O_l proj_o (SLA paper

@@ -566,10 +566,20 @@ hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const vo
                            const float* alpha, const float* proj_o, const void* dO, const Work& w,
                            const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,
                            hipStream_t s) {
-  if (D.bf16 && !proj_o) {  // SLA2 on bf16 inputs: the MFMA kernels (k_backward_mfma.hip)
-    hipError_t e = launch_backward_mfma(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, s);
+  if (D.bf16) {  // bf16 inputs: the MFMA kernels (k_backward_mfma.hip)
+    hipError_t e = launch_backward_mfma(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bwd_alpha, dim3((D.H + 63) / 64), dim3(64), 0, s, bw.dal, dalpha, D.B, D.H, D.Nb);
+    if (proj_o) {
+      const int hs = D.proj_hs ? D.H : 1;
+      if (D.d == 128)
+        hipLaunchKernelGGL(k_bwd_dw<128>, dim3((128 * 128 + 255) / 256, hs), dim3(256), 0, s, bw.dWp, dproj_o,
+                           D.B, D.H, D.Nb, D.proj_hs ? 1 : 0);
+      else
+        hipLaunchKernelGGL(k_bwd_dw<64>, dim3((64 * 64 + 255) / 256, hs), dim3(256), 0, s, bw.dWp, dproj_o, D.B,
+                           D.H, D.Nb, D.proj_hs ? 1 : 0);
+    } else {
+      hipLaunchKernelGGL(k_bwd_alpha, dim3((D.H + 63) / 64), dim3(64), 0, s, bw.dal, dalpha, D.B, D.H, D.Nb);
+    }
     return hipGetLastError();
   }
   if (D.bf16)

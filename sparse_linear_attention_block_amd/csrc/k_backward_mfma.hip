@@ -28,6 +28,11 @@
 //    hold the key block as critical (the transposed mask row), S = Q K^T and
 //    dP = dO V^T (Q and dO rows in LDS, keys as the B operand), P and dS from
 //    lse2 and D_t, dV^T += dO^T (alpha P), dK^T += Q^T dS / sqrt(d).
+// The SLA fusion O = O_s + O_l W (SLA paper summary, section 4, step 4) takes
+// the same kernels with alpha = 1 for the sparse side, dO_l = dO W^T on MFMA
+// (W packed once into A-operand fragments) and each query block's part of
+// dW = O_l^T dO (O_l and dO rows in LDS, both operands by transposed reads),
+// summed in float64 by k_bwd_dw.
 // Every product takes bf16 operands and accumulates in float32.
 #include "sla_internal.h"
 #include "dev_common.h"
@@ -205,13 +210,13 @@ __device__ __forceinline__ void phi_vjp(const float (&x)[BwCfg<D>::FT][4], const
   }
 }
 
-template <int D, bool ELU>
+template <int D, bool ELU, bool PROJ>
 __global__ __launch_bounds__(256) void k_bwdq_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const int8_t* __restrict__ mask, const uint16_t* __restrict__ Hx,
     const float* __restrict__ Os, const float* __restrict__ lse2, const float* __restrict__ alpha,
-    float* __restrict__ dQ, float* __restrict__ Dt, uint16_t* __restrict__ dH, float* __restrict__ dal, int H,
-    int N, int Nb) {
+    const uint16_t* __restrict__ wq, int wq_hs, float* __restrict__ dQ, float* __restrict__ Dt,
+    uint16_t* __restrict__ dH, float* __restrict__ dal, float* __restrict__ dWp, int H, int N, int Nb) {
   using Cf = BwCfg<D>;
   constexpr int NT = Cf::NT, HT = Cf::HT, INSTR = Cf::INSTR, KS = Cf::KS, FT = Cf::FT;
   constexpr int HPARTS = Cf::HPARTS, NN = Cf::NN;
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(256) void k_bwdq_mfma(
     os[ft] = *reinterpret_cast<const float4*>(Os + qrow + 16 * ft + 4 * g);
   }
   const float l2 = lse2[((size_t)bh * Nb + i) * kBlock + 16 * wave + l16];
-  const float al = alpha[h];
+  const float al = PROJ ? 1.0f : alpha[h];  // the SLA fusion weighs O_s by 1
   const int ncrit = compact_loaded<NT>(mv, mrow, Nb, (int8_t)1, list, wsum);
   float qf[FT][4], gf[FT][4];
 #pragma unroll
@@ -372,14 +377,34 @@ __global__ __launch_bounds__(256) void k_bwdq_mfma(
     den = __shfl(dacc[0], l16);  // row 0 of the product, from lane group 0
   }
   const float inv_den = den > 0.f ? 1.0f / den : 0.f;
-  float dnm[FT][4];
+  // dO_l: (1 - alpha) dO, or dO W^T for the SLA fusion (A: W's rows c from the
+  // packed fragments, B: dO with the features 32 ks + 8 g .. +7)
+  float glf[FT][4];
+  if constexpr (PROJ) {
+    const uint4* wf = reinterpret_cast<const uint4*>(wq + (size_t)h * wq_hs) + lane;
+#pragma unroll
+    for (int ct = 0; ct < FT; ++ct) {
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a = mfma_bf16(wf[(ct * KS + ks) * 64], gr[ks], a);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) glf[ct][e] = a[e];
+    }
+  } else {
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) glf[ft][e] = (1.0f - al) * gf[ft][e];
+  }
+  float dnm[FT][4], olf[FT][4];
   float dop = 0.f, dol = 0.f;
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float ol = nm[ft][e] * inv_den;
-      const float gl = (1.0f - al) * gf[ft][e];
+      const float gl = glf[ft][e];
+      olf[ft][e] = qv ? ol : 0.f;
       dnm[ft][e] = qv ? gl * inv_den : 0.f;
       dop = fmaf(gl, ol, dop);
       dol = fmaf(gf[ft][e], ol, dol);
@@ -429,11 +454,13 @@ __global__ __launch_bounds__(256) void k_bwdq_mfma(
     }
     if (g == 0) ddn[row] = dden;
   }
-  float da = (qv && g == 0) ? dos - dool : 0.f;  // this query's dO . (O_s - O_l)
-  da = wsum64(da);
-  if (lane == 0) red[wave] = da;
+  if constexpr (!PROJ) {
+    float da = (qv && g == 0) ? dos - dool : 0.f;  // this query's dO . (O_s - O_l)
+    da = wsum64(da);
+    if (lane == 0) red[wave] = da;
+  }
   lds_barrier();
-  if (tid == 0) dal[(size_t)bh * Nb + i] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (!PROJ && tid == 0) dal[(size_t)bh * Nb + i] = (red[0] + red[1]) + (red[2] + red[3]);
   // D[r][n] = sum_q u[q][r] dnum[q][n]: A = u^T, B = dnum, both by transposed
   // reads of the staged rows; lane (l16 = n, g) holds r = 16 rt + 4 g .. +3,
   // four consecutive entries of dH_i^T's row n
@@ -475,6 +502,40 @@ __global__ __launch_bounds__(256) void k_bwdq_mfma(
       for (int kq = 0; kq < 2; ++kq) a = mfma_bf16(ua[rt][kq], bz[kq], a);
       if (l16 == 0)
         *reinterpret_cast<uint2*>(dHrow + D * D + 16 * rt + 4 * g) = make_uint2(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]));
+    }
+  }
+  if constexpr (PROJ) {
+    // the block's part of dW = O_l^T dO (W indexed [in c][out n]): O_l rows into
+    // bufA and dO rows into bufB (zero past N); D[n][c] = sum_q dO[q][n] O_l[q][c]
+    // with A = dO^T and B = O_l by transposed reads, so lane (l16 = c, g) holds
+    // n = 16 nt + 4 g .. +3 of row c of dW
+    lds_barrier();  // every wave has read the u and dnum rows
+    {
+      const int row = 16 * wave + l16;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        const int o = swz<D>(row, 2 * ft + (g >> 1)) + 4 * (g & 1);
+        *reinterpret_cast<uint2*>(bufA + o) =
+            make_uint2(pack_bf2(olf[ft][0], olf[ft][1]), pack_bf2(olf[ft][2], olf[ft][3]));
+        *reinterpret_cast<uint2*>(bufB + o) = qv ? ga2[ft] : make_uint2(0u, 0u);
+      }
+    }
+    lds_barrier();
+    float* wout = dWp + ((size_t)bh * Nb + i) * D * D;
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+      const int ct = NTW * wave + x;
+      uint4 ob[2];
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) ob[kq] = vt_frag<D>(bufA + 32 * kq * D, vxb, ct);
+#pragma unroll
+      for (int nt = 0; nt < FT; ++nt) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) a = mfma_bf16(vt_frag<D>(bufB + 32 * kq * D, vxb, nt), ob[kq], a);
+        *reinterpret_cast<float4*>(wout + (size_t)(16 * ct + l16) * D + 16 * nt + 4 * g) =
+            make_float4(a[0], a[1], a[2], a[3]);
+      }
     }
   }
 }
@@ -520,7 +581,7 @@ __global__ __launch_bounds__(256) void k_bwdkv_mfma(
   uint2 ka2[FT];
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) ka2[ft] = *reinterpret_cast<const uint2*>(K + krow + 16 * ft + 4 * g);
-  const float al = alpha[h];
+  const float al = alpha ? alpha[h] : 1.0f;  // the SLA fusion (no alpha) weighs O_s by 1
   const int ncol = compact_loaded<NT>(mv, mrow, Nb, (int8_t)1, list, wsum);
   const int vxb = vt_base<D>(g, l16);
 
@@ -688,17 +749,40 @@ __global__ __launch_bounds__(256) void k_dh_interleave(const uint16_t* __restric
       make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
 }
 
-template <int D, bool ELU>
+// W ([in c][out n], float32, one matrix or one per head) as bf16 A-operand
+// fragments of dO_l^T = W dO^T: fragment (ct, ks) of lane (l16, g) holds
+// W[16 ct + l16][32 ks + 8 g .. +7]; [Hs][FT][KS][64] uint4
+template <int D>
+__global__ __launch_bounds__(256) void k_pack_w(const float* __restrict__ W, uint16_t* __restrict__ wq) {
+  constexpr int FT = D / 16, KS = D / 32;
+  const float* Wh = W + (size_t)blockIdx.x * D * D;
+  uint4* out = reinterpret_cast<uint4*>(wq + (size_t)blockIdx.x * D * D);
+  for (int x = threadIdx.x; x < FT * KS * 64; x += 256) {
+    const int lane = x & 63, ks = (x >> 6) % KS, ct = (x >> 6) / KS;
+    const float* src = Wh + (size_t)(16 * ct + (lane & 15)) * D + 32 * ks + 8 * (lane >> 4);
+    out[x] = make_uint4(pack_bf2(src[0], src[1]), pack_bf2(src[2], src[3]), pack_bf2(src[4], src[5]),
+                        pack_bf2(src[6], src[7]));
+  }
+}
+
+template <int D, bool ELU, bool PROJ>
 hipError_t launch_mfma_t(const Dims& Dm, const void* Q, const void* K, const void* V, const int8_t* mask,
-                         const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
-                         float* dK, float* dV, hipStream_t s) {
+                         const float* alpha, const float* proj_o, const void* dO, const Work& w, const BwdWork& bw,
+                         float* dQ, float* dK, float* dV, hipStream_t s) {
   const size_t lbytes = ((size_t)2 * Dm.Nb + 15) / 16 * 16;
   const dim3 grid(Dm.BH * Dm.Nb);
   uint16_t* dH = reinterpret_cast<uint16_t*>(bw.dHx);
-  hipLaunchKernelGGL((k_bwdq_mfma<D, ELU>), grid, dim3(256), lbytes, s, (const uint16_t*)Q, (const uint16_t*)K,
-                     (const uint16_t*)V, (const uint16_t*)dO, mask, (const uint16_t*)w.Hx, bw.Os, bw.lse, alpha, dQ,
-                     bw.dt, dH, bw.dal, Dm.H, Dm.N, Dm.Nb);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if constexpr (PROJ) {
+    hipLaunchKernelGGL(k_pack_w<D>, dim3(Dm.proj_hs ? Dm.H : 1), dim3(256), 0, s, proj_o, bw.wq);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_bwdq_mfma<D, ELU, PROJ>), grid, dim3(256), lbytes, s, (const uint16_t*)Q,
+                     (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)dO, mask, (const uint16_t*)w.Hx, bw.Os,
+                     bw.lse, alpha, (const uint16_t*)bw.wq, Dm.proj_hs, dQ, bw.dt, dH, bw.dal, bw.dWp, Dm.H, Dm.N,
+                     Dm.Nb);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nt = (Dm.Nb + 63) / 64;
   hipLaunchKernelGGL(k_mask_t, dim3(nt, nt, Dm.BH), dim3(256), 0, s, mask, bw.maskT, Dm.Nb);
@@ -716,25 +800,35 @@ hipError_t launch_mfma_t(const Dims& Dm, const void* Q, const void* K, const voi
   e = launch_linear(Dm, bw.maskT, w, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_bwdkv_mfma<D, ELU>), grid, dim3(256), lbytes, s, (const uint16_t*)Q, (const uint16_t*)K,
-                     (const uint16_t*)V, (const uint16_t*)dO, bw.maskT, bw.lse, bw.dt, (const uint16_t*)w.Hx, alpha,
-                     dK, dV, Dm.H, Dm.N, Dm.Nb);
+                     (const uint16_t*)V, (const uint16_t*)dO, bw.maskT, bw.lse, bw.dt, (const uint16_t*)w.Hx,
+                     PROJ ? nullptr : alpha, dK, dV, Dm.H, Dm.N, Dm.Nb);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
-                                const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
-                                float* dK, float* dV, hipStream_t s) {
+                                const float* alpha, const float* proj_o, const void* dO, const Work& w,
+                                const BwdWork& bw, float* dQ, float* dK, float* dV, hipStream_t s) {
   if (!D.bf16) return hipErrorInvalidValue;
-  // O_s and lse2 from the forward sparse kernel with this mask (O itself is not stored)
-  hipError_t e = launch_sparse(D, Q, K, V, mask, alpha, nullptr, w, nullptr, bw.Os, nullptr, s, bw.lse);
+  // O_s and lse2 from the forward sparse kernel with this mask (O itself is not stored, so
+  // the SLA2 mix runs with any alpha: the SLA fusion passes a workspace array in its place)
+  hipError_t e = launch_sparse(D, Q, K, V, mask, proj_o ? bw.dal : alpha, nullptr, w, nullptr, bw.Os, nullptr, s,
+                               bw.lse);
   if (e != hipSuccess) return e;
-  if (D.d == 128)
-    return D.elu ? launch_mfma_t<128, true>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, s)
-                 : launch_mfma_t<128, false>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, s);
-  return D.elu ? launch_mfma_t<64, true>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, s)
-               : launch_mfma_t<64, false>(D, Q, K, V, mask, alpha, dO, w, bw, dQ, dK, dV, s);
+  const bool p = proj_o != nullptr;
+  if (D.d == 128) {
+    if (p)
+      return D.elu ? launch_mfma_t<128, true, true>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s)
+                   : launch_mfma_t<128, false, true>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s);
+    return D.elu ? launch_mfma_t<128, true, false>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s)
+                 : launch_mfma_t<128, false, false>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s);
+  }
+  if (p)
+    return D.elu ? launch_mfma_t<64, true, true>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s)
+                 : launch_mfma_t<64, false, true>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s);
+  return D.elu ? launch_mfma_t<64, true, false>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s)
+               : launch_mfma_t<64, false, false>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s);
 }
 
 }  // namespace sla

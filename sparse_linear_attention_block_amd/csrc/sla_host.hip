@@ -145,7 +145,10 @@ size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw) {
     x.Os = (float*)take(BH * D.N * D.d * sizeof(float));
     x.maskT = (int8_t*)take(BH * D.Nb * D.Nb);
   }
-  if (proj) x.dWp = (float*)take(BH * D.Nb * D.d * D.d * sizeof(float));
+  if (proj) {
+    x.dWp = (float*)take(BH * D.Nb * D.d * D.d * sizeof(float));
+    if (D.bf16) x.wq = (uint16_t*)take((size_t)(D.proj_hs ? D.H : 1) * D.d * D.d * sizeof(uint16_t));
+  }
   if (bw) *bw = x;
   return off;
 }

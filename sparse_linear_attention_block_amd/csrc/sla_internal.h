@@ -66,6 +66,7 @@ struct BwdWork {
   float* dWp;    // SLA fusion only: [BH, Nb, d, d] each query block's part of dW = O_l^T dO
   float* Os;     // bf16 only: [BH, N, d] O_s of the forward recompute (k_backward_mfma.hip)
   int8_t* maskT; // bf16 only: [BH, Nb, Nb] the transposed mask
+  uint16_t* wq;  // bf16 SLA fusion only: [Hs, d, d] the output map as bf16 A-operand fragments
 };
 // forward + backward bytes; proj: the SLA fusion's dW parts are included
 size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw);
@@ -104,11 +105,12 @@ hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const 
 
 // proj_o == NULL: SLA2 (dalpha written, dproj_o unused); else the SLA fusion (dproj_o
 // written, alpha and dalpha unused)
-// bf16 SLA2 (no output map): the MFMA kernels of k_backward_mfma.hip; writes dQ, dK, dV and the
-// per-block dalpha partials (bw.dal); uses bw.lse / bw.dt as lse2 / D_t and bw.dHx as bf16 dH
+// bf16 inputs: the MFMA kernels of k_backward_mfma.hip; writes dQ, dK, dV and the per-block
+// dalpha partials (bw.dal; SLA2) or dW parts (bw.dWp; proj_o given); uses bw.lse / bw.dt as
+// lse2 / D_t and bw.dHx as bf16 dH
 hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
-                                const float* alpha, const void* dO, const Work& w, const BwdWork& bw, float* dQ,
-                                float* dK, float* dV, hipStream_t s);
+                                const float* alpha, const float* proj_o, const void* dO, const Work& w,
+                                const BwdWork& bw, float* dQ, float* dK, float* dV, hipStream_t s);
 hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                            const float* alpha, const float* proj_o, const void* dO, const Work& w,
                            const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,
