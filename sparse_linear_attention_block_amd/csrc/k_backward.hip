@@ -504,14 +504,17 @@ __global__ __launch_bounds__(kThreads) void k_bwd_kv(
 }
 
 // dalpha[h] = sum over batches and query blocks of the partials, in that order
-__global__ void k_bwd_alpha(const float* __restrict__ dal, float* __restrict__ dalpha, int B, int H,
-                            int Nb) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= H) return;
+// one wave per head: lane l sums the partials i = l (mod 64) of every batch in
+// order, then the lanes combine in a fixed butterfly (the same bits in every lane)
+__global__ __launch_bounds__(64) void k_bwd_alpha(const float* __restrict__ dal, float* __restrict__ dalpha,
+                                                  int B, int H, int Nb) {
+  const int h = blockIdx.x, lane = threadIdx.x;
   double s = 0.0;
   for (int b = 0; b < B; ++b)
-    for (int i = 0; i < Nb; ++i) s += (double)dal[((size_t)b * H + h) * Nb + i];
-  dalpha[h] = (float)s;
+    for (int i = lane; i < Nb; i += 64) s += (double)dal[((size_t)b * H + h) * Nb + i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) dalpha[h] = (float)s;
 }
 
 template <typename T, int D, bool ELU, bool PROJ>
@@ -539,7 +542,7 @@ hipError_t launch_bwd_t(const Dims& Dm, const void* Q, const void* K, const void
     hipLaunchKernelGGL(k_bwd_dw<D>, dim3((D * D + 255) / 256, hs), dim3(256), 0, s, bw.dWp, dproj_o, Dm.B,
                        Dm.H, Dm.Nb, Dm.proj_hs ? 1 : 0);
   } else {
-    hipLaunchKernelGGL(k_bwd_alpha, dim3((Dm.H + 63) / 64), dim3(64), 0, s, bw.dal, dalpha, Dm.B, Dm.H, Dm.Nb);
+    hipLaunchKernelGGL(k_bwd_alpha, dim3(Dm.H), dim3(64), 0, s, bw.dal, dalpha, Dm.B, Dm.H, Dm.Nb);
   }
   return hipGetLastError();
 }
@@ -578,7 +581,7 @@ hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const vo
         hipLaunchKernelGGL(k_bwd_dw<64>, dim3((64 * 64 + 255) / 256, hs), dim3(256), 0, s, bw.dWp, dproj_o, D.B,
                            D.H, D.Nb, D.proj_hs ? 1 : 0);
     } else {
-      hipLaunchKernelGGL(k_bwd_alpha, dim3((D.H + 63) / 64), dim3(64), 0, s, bw.dal, dalpha, D.B, D.H, D.Nb);
+      hipLaunchKernelGGL(k_bwd_alpha, dim3(D.H), dim3(64), 0, s, bw.dal, dalpha, D.B, D.H, D.Nb);
     }
     return hipGetLastError();
   }

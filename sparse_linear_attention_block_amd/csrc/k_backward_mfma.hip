@@ -211,7 +211,7 @@ __device__ __forceinline__ void phi_vjp(const float (&x)[BwCfg<D>::FT][4], const
 }
 
 template <int D, bool ELU, bool PROJ>
-__global__ __launch_bounds__(256) void k_bwdq_mfma(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwdq_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const int8_t* __restrict__ mask, const uint16_t* __restrict__ Hx,
     const float* __restrict__ Os, const float* __restrict__ lse2, const float* __restrict__ alpha,
@@ -304,6 +304,7 @@ __global__ __launch_bounds__(256) void k_bwdq_mfma(
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) sv[kt] = mfma_bf16(ka[ks][kt], qr[ks], sv[kt]);
+    __builtin_amdgcn_sched_barrier(0);  // one operand set in registers at a time
     uint4 vb[KS][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -314,6 +315,7 @@ __global__ __launch_bounds__(256) void k_bwdq_mfma(
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) dp[kt] = mfma_bf16(vb[ks][kt], gr[ks], dp[kt]);
+    __builtin_amdgcn_sched_barrier(0);
     uint4 kt_[FT];
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) kt_[ft] = vt_frag<D>(cur, vxb, ft);
@@ -541,7 +543,7 @@ __global__ __launch_bounds__(256) void k_bwdq_mfma(
 }
 
 template <int D, bool ELU>
-__global__ __launch_bounds__(256) void k_bwdkv_mfma(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwdkv_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const int8_t* __restrict__ maskT, const float* __restrict__ lse2,
     const float* __restrict__ Dt, const uint16_t* __restrict__ dh, const float* __restrict__ alpha,
@@ -660,6 +662,9 @@ __global__ __launch_bounds__(256) void k_bwdkv_mfma(
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) sv[qt] = mfma_bf16(qa[ks][qt], kr[ks], sv[qt]);
+    // one operand set in registers at a time (the phases are kept apart so that
+    // two waves fit on a SIMD)
+    __builtin_amdgcn_sched_barrier(0);
     uint4 ga[KS][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -670,12 +675,10 @@ __global__ __launch_bounds__(256) void k_bwdkv_mfma(
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) dp[qt] = mfma_bf16(ga[ks][qt], vr[ks], dp[qt]);
-    uint4 qtr[FT], gtr[FT];
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 gtr[FT];
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      qtr[ft] = vt_frag<D>(cur, vxb, ft);
-      gtr[ft] = vt_frag<D>(cur + HT, vxb, ft);
-    }
+    for (int ft = 0; ft < FT; ++ft) gtr[ft] = vt_frag<D>(cur + HT, vxb, ft);
     // lse2 and D_t of queries 16 qt + 4 g .. +3 (rows past N: lse2 = +inf, so P = 0)
     float p[2][4], ds[2][4];
 #pragma unroll
@@ -695,10 +698,13 @@ __global__ __launch_bounds__(256) void k_bwdkv_mfma(
     const uint4 db = make_uint4(pack_bf2(ds[0][0], ds[0][1]), pack_bf2(ds[0][2], ds[0][3]),
                                 pack_bf2(ds[1][0], ds[1][1]), pack_bf2(ds[1][2], ds[1][3]));
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      dv[ft] = mfma_bf16(gtr[ft], pb, dv[ft]);
-      dk[ft] = mfma_bf16(qtr[ft], db, dk[ft]);
-    }
+    for (int ft = 0; ft < FT; ++ft) dv[ft] = mfma_bf16(gtr[ft], pb, dv[ft]);
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 qtr[FT];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) qtr[ft] = vt_frag<D>(cur, vxb, ft);
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) dk[ft] = mfma_bf16(qtr[ft], db, dk[ft]);
   };
   if (nstep > 0) copy(0, bufA, lsA);
   for (int s = 0; s < nstep; s += 2) {  // nstep is even
