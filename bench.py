@@ -465,7 +465,13 @@ def main():
         return
     dev = torch.device("cuda:0")
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
-    pq, pk, al = x.proj_q.to(dev), x.proj_k.to(dev), x.alpha.to(dev)
+    # a workload whose router is the identity passes none (the block means are compared as
+    # they are: the same pooled vectors, without an identity product)
+    if cfg.router == "identity":
+        pq = pk = None
+    else:
+        pq, pk = x.proj_q.to(dev), x.proj_k.to(dev)
+    al = x.alpha.to(dev)
     proj_o = make_proj_o(cfg) if sla1 else None
     if sla1:
         plan = sla.Plan(q, k, v, None, None, None, x.kh, x.kl, phi=args.phi, proj_o=proj_o.to(dev),
@@ -557,7 +563,8 @@ def main():
                    "sparsity": round(1 - n_h / Nb, 4),
                    "formulation": ("SLA: no router, O = O_s + Proj(O_l)" if sla1
                                    else "SLA2: O = alpha O_s + (1 - alpha) O_l, "
-                                        + ("identity router matrices" if cfg.router == "identity"
+                                        + ("identity router (none applied: the block means are compared)"
+                                           if cfg.router == "identity"
                                            else "learned router matrices I + 0.1 N(0, 1/d)")),
                    "phi": args.phi, "linear_sums": args.linear},
         "roofline": {"kernel": "sparse_attn_mix", "bound": "mfma", "achieved": round(achieved, 2),

@@ -92,7 +92,9 @@ struct FaCfg {
 // full-rate 16x16x32 MFMA (P.V contracts over the step's 32 keys) and the step
 // buffers are 16 KB. The critical list lives in dynamic LDS of
 // max(2 Nb, 2 D) bytes.
-template <int D, int NW, bool PROJ, bool ELU>
+// LSE: also write each query's log2 softmax normaliser (the backward pass's
+// recompute; a separate instance so that the forward pays nothing for it).
+template <int D, int NW, bool PROJ, bool ELU, bool LSE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 2 : 3, NW == 2 ? 2 : 3)))
 void k_sparse_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -322,7 +324,7 @@ void k_sparse_bf16(
   for (int qg = 0; qg < QG; ++qg) {
     const float lw = __shfl(accl[qg][0], l16);  // from lane group 0
     inv_l[qg] = lw > 0.f ? 1.0f / lw : 0.f;
-    if (lse_out && g == 0) {  // log2 of the softmax normaliser: P = exp2(s log2(e) / sqrt(d) - lse2)
+    if (LSE && g == 0) {  // log2 of the softmax normaliser: P = exp2(s log2(e) / sqrt(d) - lse2)
       const int tq = 16 * (QG * wave + qg) + l16;
       const float meff = mref[qg] == -INFINITY ? 0.0f : mref[qg];
       lse_out[((size_t)bh * Nb + i) * kBlock + tq] =
@@ -684,9 +686,18 @@ hipError_t launch_bf16(const Dims& D_, const void* Q, const void* K, const void*
                        float* lse_out, hipStream_t s) {
   // dynamic LDS: the critical list (2 Nb bytes), later Z_i (2 D bytes)
   const size_t lbytes = ((size_t)2 * (D_.Nb > D ? D_.Nb : D) + 15) / 16 * 16;
-  hipLaunchKernelGGL((k_sparse_bf16<D, NW, PROJ, ELU>), dim3(D_.BH * D_.Nb), dim3(64 * NW), lbytes, s,
+  if constexpr (!PROJ) {  // the backward's recompute runs the SLA2 form
+    if (lse_out) {
+      hipLaunchKernelGGL((k_sparse_bf16<D, NW, PROJ, ELU, true>), dim3(D_.BH * D_.Nb), dim3(64 * NW), lbytes, s,
+                         (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, mask, (const uint16_t*)w.Hx,
+                         alpha, w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, lse_out, D_.H, D_.N, D_.Nb);
+      return hipGetLastError();
+    }
+  }
+  if (lse_out) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_sparse_bf16<D, NW, PROJ, ELU, false>), dim3(D_.BH * D_.Nb), dim3(64 * NW), lbytes, s,
                      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, mask, (const uint16_t*)w.Hx, alpha,
-                     w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, lse_out, D_.H, D_.N, D_.Nb);
+                     w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, nullptr, D_.H, D_.N, D_.Nb);
   return hipGetLastError();
 }
 
