@@ -547,7 +547,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const int8_t* __restrict__ maskT, const float* __restrict__ lse2,
     const float* __restrict__ Dt, const uint16_t* __restrict__ dh, const float* __restrict__ alpha,
-    float* __restrict__ dK, float* __restrict__ dV, int H, int N, int Nb) {
+    const int* __restrict__ order, float* __restrict__ dK, float* __restrict__ dV, int H, int N, int Nb) {
   using Cf = BwCfg<D>;
   constexpr int NT = Cf::NT, HT = Cf::HT, INSTR = Cf::INSTR, KS = Cf::KS, FT = Cf::FT;
   constexpr int HPARTS = Cf::HPARTS, NN = Cf::NN;
@@ -562,7 +562,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  // key blocks in order of falling critical count (the longest first)
+  const int id = order[blockIdx.x];
   const int bh = id / Nb, j = id - bh * Nb, h = bh % H;
   const int8_t* mrow = maskT + ((size_t)bh * Nb + j) * Nb;
   int8_t mv[kMaskPre];
@@ -755,6 +756,51 @@ __global__ __launch_bounds__(256) void k_dh_interleave(const uint16_t* __restric
       make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
 }
 
+// cnt[row] = number of critical entries of row `row` of the transposed mask
+// (the query blocks that take key block row % Nb as critical); one wave per row
+__global__ __launch_bounds__(256) void k_col_count(const int8_t* __restrict__ maskT, int* __restrict__ cnt,
+                                                   int Nb, int rows) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;  // whole wave
+  const int8_t* m = maskT + (size_t)row * Nb;
+  int c = 0;
+  for (int x0 = 0; x0 < Nb; x0 += 64) c += __popcll(__ballot(x0 + lane < Nb && m[x0 + lane] == 1));
+  if (lane == 0) cnt[row] = c;
+}
+
+// order = the rows sorted by falling count (a counting sort over 0 .. Nb in one
+// workgroup; rows of equal count in any order), so that the key blocks with the
+// most critical query blocks start first
+__global__ __launch_bounds__(1024) void k_lpt_order(const int* __restrict__ cnt, int* __restrict__ order, int Nb,
+                                                    int rows) {
+  __shared__ int bins[kMaxNb + 1];
+  const int tid = threadIdx.x;
+  for (int x = tid; x <= Nb; x += 1024) bins[x] = 0;
+  __syncthreads();
+  for (int r = tid; r < rows; r += 1024) atomicAdd(&bins[cnt[r]], 1);
+  __syncthreads();
+  if (tid < 64) {  // exclusive scan from the highest count down, 64 lanes over contiguous ranges
+    const int per = (Nb + 1 + 63) / 64;
+    const int hi = Nb - per * tid, lo = max(hi - per, -1);  // bins hi .. lo + 1
+    int sum = 0;
+    for (int c = hi; c > lo; --c) sum += bins[c];
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (tid >= o) incl += v;
+    }
+    int run = incl - sum;
+    for (int c = hi; c > lo; --c) {
+      const int n = bins[c];
+      bins[c] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < rows; r += 1024) order[atomicAdd(&bins[cnt[r]], 1)] = r;
+}
+
 // W ([in c][out n], float32, one matrix or one per head) as bf16 A-operand
 // fragments of dO_l^T = W dO^T: fragment (ct, ks) of lane (l16, g) holds
 // W[16 ct + l16][32 ks + 8 g .. +7]; [Hs][FT][KS][64] uint4
@@ -805,9 +851,16 @@ hipError_t launch_mfma_t(const Dims& Dm, const void* Q, const void* K, const voi
   if (e != hipSuccess) return e;
   e = launch_linear(Dm, bw.maskT, w, s);
   if (e != hipSuccess) return e;
+  const int rows = Dm.BH * Dm.Nb;
+  hipLaunchKernelGGL(k_col_count, dim3((rows + 3) / 4), dim3(256), 0, s, bw.maskT, bw.kvcnt, Dm.Nb, rows);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_lpt_order, dim3(1), dim3(1024), 0, s, bw.kvcnt, bw.kvorder, Dm.Nb, rows);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_bwdkv_mfma<D, ELU>), grid, dim3(256), lbytes, s, (const uint16_t*)Q, (const uint16_t*)K,
                      (const uint16_t*)V, (const uint16_t*)dO, bw.maskT, bw.lse, bw.dt, (const uint16_t*)w.Hx,
-                     PROJ ? nullptr : alpha, dK, dV, Dm.H, Dm.N, Dm.Nb);
+                     PROJ ? nullptr : alpha, bw.kvorder, dK, dV, Dm.H, Dm.N, Dm.Nb);
   return hipGetLastError();
 }
 

@@ -345,18 +345,28 @@ __device__ void find_bin(const uint32_t* h, bool from_top, int need, int& bin, i
 // first the whole row), the cell becomes the bin that holds the rank, and the
 // rank is counted inside it, until the cell's range is at most tol wide or
 // four levels are done. Bins are a monotone function of the value, so equal
-// values share a bin and a higher bin never holds a smaller value.
+// values share a bin and a higher bin never holds a smaller value. Once a cell
+// holds at most 64 elements they move to one per lane (through tmp, the
+// wave's 64 floats of LDS), so the later levels cost one value per lane
+// instead of a sweep over the row.
 template <int kMaxE>
 __device__ void locate(const float (&a)[kMaxE], int E, uint64_t cell, int rank, bool from_top, float tol,
-                       uint32_t* __restrict__ hist, float& lo, float& hi) {
+                       uint32_t* __restrict__ hist, float* __restrict__ tmp, float& lo, float& hi) {
   const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  bool packed = false, xin = false;
+  float x = 0.f;
   for (int level = 0;; ++level) {
     float mn = INFINITY, mx = -INFINITY;
+    if (packed) {
+      if (xin) mn = mx = x;
+    } else {
 #pragma unroll
-    for (int e = 0; e < kMaxE; ++e) {
-      if ((cell >> e) & 1ull) {
-        mn = fminf(mn, a[e]);
-        mx = fmaxf(mx, a[e]);
+      for (int e = 0; e < kMaxE; ++e) {
+        if ((cell >> e) & 1ull) {
+          mn = fminf(mn, a[e]);
+          mx = fmaxf(mx, a[e]);
+        }
       }
     }
     lo = wave_min(mn);
@@ -367,20 +377,45 @@ __device__ void locate(const float (&a)[kMaxE], int E, uint64_t cell, int rank, 
 #pragma unroll
     for (int q = 0; q < 4; ++q) hist[64 * q + lane] = 0u;
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (packed) {
+      if (xin) atomicAdd(&hist[min(255, (int)((x - lo) * sc))], 1u);
+    } else {
 #pragma unroll
-    for (int e = 0; e < kMaxE; ++e) {
-      if ((cell >> e) & 1ull) atomicAdd(&hist[min(255, (int)((a[e] - lo) * sc))], 1u);
+      for (int e = 0; e < kMaxE; ++e) {
+        if ((cell >> e) & 1ull) atomicAdd(&hist[min(255, (int)((a[e] - lo) * sc))], 1u);
+      }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     int bin, before;
     find_bin(hist, from_top, rank, bin, before);
     rank -= before;
+    if (packed) {
+      xin = xin && min(255, (int)((x - lo) * sc)) == bin;
+      continue;
+    }
     uint64_t nc = 0ull;
+    int cnt = 0;
 #pragma unroll
     for (int e = 0; e < kMaxE; ++e) {
-      if (((cell >> e) & 1ull) && min(255, (int)((a[e] - lo) * sc)) == bin) nc |= 1ull << e;
+      const bool in = ((cell >> e) & 1ull) && min(255, (int)((a[e] - lo) * sc)) == bin;
+      if (in) nc |= 1ull << e;
+      cnt += __popcll(__ballot(in));
     }
     cell = nc;
+    if (cnt <= 64) {  // one element of the new cell per lane
+      int pos = 0;
+#pragma unroll
+      for (int e = 0; e < kMaxE; ++e) {
+        const bool in = (nc >> e) & 1ull;
+        const uint64_t b = __ballot(in);
+        if (in) tmp[pos + __popcll(b & below)] = a[e];
+        pos += __popcll(b);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      xin = lane < cnt;
+      x = xin ? tmp[lane] : 0.f;
+      packed = true;
+    }
   }
 }
 
@@ -480,6 +515,7 @@ __global__ __launch_bounds__(256) void k_classify_band(const float* __restrict__
                                                        const double* __restrict__ pk, int8_t* __restrict__ mask,
                                                        int Nb, int nt, int D, int n_h, int n_l, int rows) {
   __shared__ uint32_t hist[4][256];
+  __shared__ float tmp[4][64];             // a located cell, one element per lane
   __shared__ uint16_t lst[4][64 * kMaxE];  // a band's candidates, per wave
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
@@ -502,13 +538,13 @@ __global__ __launch_bounds__(256) void k_classify_band(const float* __restrict__
   uint64_t top = 0ull, bot = 0ull;
   if (n_h > 0) {
     float lo = 0.f, hi = 0.f;
-    if (!wide) locate<kMaxE>(a, E, valid, n_h, true, eps, hist[wave], lo, hi);
+    if (!wide) locate<kMaxE>(a, E, valid, n_h, true, eps, hist[wave], tmp[wave], lo, hi);
     top = band_select<true, kMaxE>(a, E, valid, lo, hi, 2.0f * eps, wide, n_h, D, qrow, pkh, lst[wave]);
   }
   if (n_l > 0) {
     const uint64_t rest = valid & ~top;
     float lo = 0.f, hi = 0.f;
-    if (!wide) locate<kMaxE>(a, E, rest, n_l, false, eps, hist[wave], lo, hi);
+    if (!wide) locate<kMaxE>(a, E, rest, n_l, false, eps, hist[wave], tmp[wave], lo, hi);
     bot = band_select<false, kMaxE>(a, E, rest, lo, hi, 2.0f * eps, wide, n_l, D, qrow, pkh, lst[wave]);
   }
   int8_t* mrow = mask + (size_t)row * Nb;

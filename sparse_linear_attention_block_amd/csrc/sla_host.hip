@@ -144,6 +144,8 @@ size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw) {
   if (D.bf16) {  // the MFMA path (SLA2; carved for both formulations so that the SLA fusion only adds dW)
     x.Os = (float*)take(BH * D.N * D.d * sizeof(float));
     x.maskT = (int8_t*)take(BH * D.Nb * D.Nb);
+    x.kvcnt = (int*)take(BH * D.Nb * sizeof(int));
+    x.kvorder = (int*)take(BH * D.Nb * sizeof(int));
   }
   if (proj) {
     x.dWp = (float*)take(BH * D.Nb * D.d * D.d * sizeof(float));

@@ -67,6 +67,8 @@ struct BwdWork {
   float* Os;     // bf16 only: [BH, N, d] O_s of the forward recompute (k_backward_mfma.hip)
   int8_t* maskT; // bf16 only: [BH, Nb, Nb] the transposed mask
   uint16_t* wq;  // bf16 SLA fusion only: [Hs, d, d] the output map as bf16 A-operand fragments
+  int* kvcnt;    // bf16 only: [BH * Nb] critical query blocks per key block
+  int* kvorder;  // bf16 only: [BH * Nb] key blocks by falling count (the dK/dV launch order)
 };
 // forward + backward bytes; proj: the SLA fusion's dW parts are included
 size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw);
