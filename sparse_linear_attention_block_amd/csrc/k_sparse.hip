@@ -160,12 +160,11 @@ void k_sparse_bf16(
   // (wave-uniform) is the scalar offset.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kb, N * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vb, N * D * 2);
-  auto issue = [&](int jv, int hv, uint16_t* dst) {
-    const int j = __builtin_amdgcn_readfirstlane(jv);
-    const int hh = __builtin_amdgcn_readfirstlane(hv);
+  auto issue = [&](auto RAGc, int j, int hh, uint16_t* dst) {
+    constexpr bool RAG = decltype(RAGc)::value;
     const int row0 = j * kBlock + 32 * hh;
     const int sk = row0 * D * 2;
-    if (row0 + 32 > N) {  // ragged: rows past N re-read row N-1 (their P is 0)
+    if constexpr (RAG) {  // ragged: rows past N re-read row N-1 (their P is 0)
       const int over = row0 - (N - 1);
 #pragma unroll
       for (int u = 0; u < INSTR; ++u) {
@@ -234,20 +233,43 @@ void k_sparse_bf16(
         ka[ks][kt] = *reinterpret_cast<const uint4*>(cur + (row * C + ((4 * ks + g) ^ (row & (C - 1)))) * 8);
       }
     __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < nstep)
-      issue(jn, (s + 1) & 1, nxt);
-    else
-      issueH(0, nxt);  // every wave has read list[s >> 1]: the list area is free
-    __builtin_amdgcn_sched_barrier(0);
+    // S^T products; the copies of the next step are issued between them, so
+    // that a copy waiting for the memory pipeline holds up no product
     f32x4 sv[QG][2];  // [query group][key tile]
+    auto sprod = [&]() {
 #pragma unroll
-    for (int qg = 0; qg < QG; ++qg) sv[qg][0] = sv[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qg = 0; qg < QG; ++qg) sv[qg][0] = sv[qg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
+      for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) sv[qg][kt] = mfma_bf16(ka[ks][kt], qr[qg][ks], sv[qg][kt]);
+          for (int qg = 0; qg < QG; ++qg) sv[qg][kt] = mfma_bf16(ka[ks][kt], qr[qg][ks], sv[qg][kt]);
+    };
+    auto spread = [&]() {
+#pragma unroll
+      for (int u = 0; u < 2 * INSTR; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * KSTEPS * QG / (2 * INSTR), 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    };
+    if (s + 1 < nstep) {
+      const int jnu = __builtin_amdgcn_readfirstlane(jn);
+      const int hn = (s + 1) & 1;
+      if (jnu * kBlock + 32 * hn + 32 > N) {
+        issue(std::true_type{}, jnu, hn, nxt);
+        sprod();
+        spread();
+      } else {
+        issue(std::false_type{}, jnu, hn, nxt);
+        sprod();
+        spread();
+      }
+    } else {
+      issueH(0, nxt);  // every wave has read list[s >> 1]: the list area is free
+      sprod();
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // the V^T fragments of the step (transposed reads of the V rows) load
     // while the softmax runs
     const uint16_t* vtile = cur + HT;
@@ -306,8 +328,13 @@ void k_sparse_bf16(
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) accl[qg] = mfma_bf16(ones, pb[qg], accl[qg]);
   };
-  if (nstep > 0)
-    issue(list[0], 0, bufA);
+  if (nstep > 0) {
+    const int j0 = __builtin_amdgcn_readfirstlane((int)list[0]);
+    if (j0 * kBlock + 32 > N)
+      issue(std::true_type{}, j0, 0, bufA);
+    else
+      issue(std::false_type{}, j0, 0, bufA);
+  }
   else
     issueH(0, bufA);
   for (int s = 0; s < nstep; s += 2) {  // nstep is even
