@@ -294,53 +294,68 @@ def backward_flops(B, H, Nb, n_h, d):
     return 10.0 * B * H * Nb * n_h * 64 * 64 * d + 10.0 * B * H * Nb * 64 * d * d
 
 
-def bench_backward(args, cfg, x, torch, sla):
-    """sla_backward at the workload's shape, for the mask its forward pass
-    computes and a seeded dO; one JSON line."""
+def bench_backward(args, cfg, x, torch, sla, proj_o=None):
+    """sla_backward (or, with proj_o, sla1_backward) at the workload's shape,
+    for the mask its forward pass computes and a seeded dO; one JSON line."""
     from oracle import backward as ob
     dev = torch.device("cuda:0")
     q, k, v, al = x.q.to(dev), x.k.to(dev), x.v.to(dev), x.alpha.to(dev)
-    _, mask = sla.forward(q, k, v, x.proj_q.to(dev), x.proj_k.to(dev), al, x.kh, x.kl)
+    sla1 = proj_o is not None
+    if sla1:
+        proj_o = proj_o.to(dev)
+        _, mask = sla.forward_sla1(q, k, v, proj_o, x.kh, x.kl, proj_q=x.proj_q.to(dev),
+                                   proj_k=x.proj_k.to(dev))
+    else:
+        _, mask = sla.forward(q, k, v, x.proj_q.to(dev), x.proj_k.to(dev), al, x.kh, x.kl)
     g = np.random.default_rng(cfg.seed + 7).standard_normal(tuple(x.q.shape))
     dO = torch.from_numpy(g.astype(np.float32)).to(x.q.dtype)
     dO_d = dO.to(dev)
     B, H, N, d = x.q.shape
     Nb = cfg.Nb
     n_h = sla.block_counts(N, x.kh, x.kl, B=B, H=H, d=d, dtype=cfg.dtype)[1]
-    p = sla.make_problem(B, H, N, d, cfg.dtype, 0.0, 0.0)
-    n = ctypes_size(sla, p)
+    p = sla.make_problem(B, H, N, d, cfg.dtype, 0.0, 0.0,
+                         proj_head_stride=(d * d if sla1 and proj_o.dim() == 3 else 0))
+    n = ctypes_size(sla, p, sla1)
     ws = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def run():
+        if sla1:
+            sla.backward_sla1(q, k, v, proj_o, mask, dO_d, workspace=ws)
+        else:
+            sla.backward(q, k, v, al, mask, dO_d, workspace=ws)
     for _ in range(args.warmup):
-        sla.backward(q, k, v, al, mask, dO_d, workspace=ws)
+        run()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
-        sla.backward(q, k, v, al, mask, dO_d, workspace=ws)
+        run()
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
-    F = backward_flops(B, H, Nb, n_h, d)
+    # the SLA fusion adds the output map's two products per token: dO_l = dO W^T and dW = O_l^T dO
+    F = backward_flops(B, H, Nb, n_h, d) + (4.0 * B * H * N * d * d if sla1 else 0.0)
     achieved = F / (ms * 1e-3) / 1e12
     # bf16 inputs: every product on bf16 MFMA (float32 accumulation); float32 inputs: the VALU kernels
     mfma = cfg.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if mfma else PEAK_F32_VALU_TFLOPS
     line = {
-        "metric": "SLA2 backward ms & dense-equivalent TFLOPS (10*B*H*N^2*d per backward)",
+        "metric": ("SLA" if sla1 else "SLA2") + " backward ms & dense-equivalent TFLOPS (10*B*H*N^2*d per backward)",
         "value": round(10.0 * B * H * N * N * d / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s (dense-equivalent backward)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 MFMA, f32 accumulate" if mfma else "f32 (" + cfg.dtype + " inputs)",
         "data": "synthetic: the seeded workload, its forward mask and a seeded N(0,1) dO",
-        "config": {"workload": cfg.name + "_backward", "B": B, "H": H, "N": N, "d": d, "Nb": Nb,
+        "config": {"workload": cfg.name + ("_sla1" if sla1 else "") + "_backward", "B": B, "H": H, "N": N, "d": d, "Nb": Nb,
                    "n_h": n_h, "kh": x.kh, "kl": x.kl},
-        "roofline": {"kernel": "sla_backward (all its kernels)", "bound": "mfma" if mfma else "alu",
+        "roofline": {"kernel": ("sla1_backward" if sla1 else "sla_backward") + " (all its kernels)",
+                     "bound": "mfma" if mfma else "alu",
                      "achieved": round(achieved, 3), "peak": round(peak, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": None, "flops_per_launch": F, "ms_per_launch": round(ms, 4)},
     }
-    if not args.no_cpu:
+    if not args.no_cpu and not sla1:
         import threadpoolctl
         cores = max([pp.get("num_threads", 1) for pp in threadpoolctl.threadpool_info()] or [1])
         mk = mask.cpu().numpy()
@@ -363,10 +378,12 @@ def bench_backward(args, cfg, x, torch, sla):
     print(json.dumps(line), flush=True)
 
 
-def ctypes_size(sla, p):
+def ctypes_size(sla, p, sla1=False):
     import ctypes
     n = ctypes.c_size_t()
-    rc = sla.load_library().sla_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n))
+    lib = sla.load_library()
+    fn = lib.sla1_backward_workspace_bytes if sla1 else lib.sla_backward_workspace_bytes
+    rc = fn(ctypes.byref(p), ctypes.byref(n))
     if rc != 0:
         raise RuntimeError("sla_backward_workspace_bytes failed")
     return max(int(n.value), 256)
@@ -461,7 +478,7 @@ def main():
         if cfg.quant:
             print("the backward pass is built without the 8-bit branch", file=sys.stderr)
             sys.exit(2)
-        bench_backward(args, cfg, x, torch, sla)
+        bench_backward(args, cfg, x, torch, sla, make_proj_o(cfg) if sla1 else None)
         return
     dev = torch.device("cuda:0")
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)

@@ -20,7 +20,8 @@
 //  dalpha_h = sum over the head of dO . (O_s - O_l).
 // The SLA fusion O = O_s + O_l W (SLA paper summary, section 4, step 4):
 // dO_s = dO, dO_l = dO W^T, and dW = sum over tokens of O_l^T dO, formed per
-// query block (k_bwd_q) and summed in a fixed order (k_bwd_dw); no dalpha.
+// query block (k_bwd_q) and summed in a fixed order (k_bwd_dw_part and
+// k_bwd_dw_fin); no dalpha.
 //
 // fp32 arithmetic throughout (bf16 or f32 inputs), eight threads per query or
 // key token, each holding d/8 features (with four, a thread's state filled
@@ -364,17 +365,46 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
 }
 
 // dW = sum of the per-block parts over batches and query blocks (and over the
-// heads when W is shared), in that order, in float64
+// heads when W is shared), in float64 and a fixed order: the parts, in the
+// order (batch, head, query block), are cut into kDwSplit consecutive ranges;
+// k_bwd_dw_part sums each range (one thread per entry of W, 256 consecutive
+// entries per workgroup, so every part is read as whole rows), k_bwd_dw_fin
+// the kDwSplit range sums in range order.
 template <int D>
-__global__ __launch_bounds__(256) void k_bwd_dw(const float* __restrict__ dWp, float* __restrict__ dW, int B,
-                                                int H, int Nb, int per_head) {
+__global__ __launch_bounds__(256) void k_bwd_dw_part(const float* __restrict__ dWp, double* __restrict__ dWs,
+                                                     int B, int H, int Nb, int per_head) {
+  const int x = blockIdx.x * 256 + threadIdx.x, r = blockIdx.y, hw = blockIdx.z;
+  if (x >= D * D) return;
+  const int P = per_head ? B * Nb : B * H * Nb;  // parts summed into this W
+  const int per = (P + kDwSplit - 1) / kDwSplit;
+  const int p0 = r * per, p1 = min(P, p0 + per);
+  double s = 0.0;
+  for (int q = p0; q < p1; ++q) {
+    // part q: (batch, head, block) = (q / (H Nb), q / Nb % H, q % Nb) for a shared W,
+    // (q / Nb, hw, q % Nb) for head hw's own
+    const size_t part = per_head ? ((size_t)(q / Nb) * H + hw) * Nb + q % Nb : (size_t)q;
+    s += (double)dWp[part * D * D + x];
+  }
+  dWs[((size_t)hw * kDwSplit + r) * D * D + x] = s;
+}
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_dw_fin(const double* __restrict__ dWs, float* __restrict__ dW) {
   const int x = blockIdx.x * 256 + threadIdx.x, hw = blockIdx.y;
   if (x >= D * D) return;
   double s = 0.0;
-  for (int b = 0; b < B; ++b)
-    for (int h = per_head ? hw : 0; h < (per_head ? hw + 1 : H); ++h)
-      for (int i = 0; i < Nb; ++i) s += (double)dWp[(((size_t)b * H + h) * Nb + i) * D * D + x];
+  for (int r = 0; r < kDwSplit; ++r) s += dWs[((size_t)hw * kDwSplit + r) * D * D + x];
   dW[(size_t)hw * D * D + x] = (float)s;
+}
+
+template <int D>
+hipError_t launch_dw(const Dims& Dm, const BwdWork& bw, float* dW, hipStream_t s) {
+  const int hs = Dm.proj_hs ? Dm.H : 1;
+  hipLaunchKernelGGL(k_bwd_dw_part<D>, dim3((D * D + 255) / 256, kDwSplit, hs), dim3(256), 0, s, bw.dWp, bw.dWs,
+                     Dm.B, Dm.H, Dm.Nb, Dm.proj_hs ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bwd_dw_fin<D>, dim3((D * D + 255) / 256, hs), dim3(256), 0, s, bw.dWs, dW);
+  return hipGetLastError();
 }
 
 // dH_tot[bh][x] = sum over the head's query blocks of dHx[bh][i][x]
@@ -538,9 +568,8 @@ hipError_t launch_bwd_t(const Dims& Dm, const void* Q, const void* K, const void
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (PROJ) {
-    const int hs = Dm.proj_hs ? Dm.H : 1;
-    hipLaunchKernelGGL(k_bwd_dw<D>, dim3((D * D + 255) / 256, hs), dim3(256), 0, s, bw.dWp, dproj_o, Dm.B,
-                       Dm.H, Dm.Nb, Dm.proj_hs ? 1 : 0);
+    e = launch_dw<D>(Dm, bw, dproj_o, s);
+    if (e != hipSuccess) return e;
   } else {
     hipLaunchKernelGGL(k_bwd_alpha, dim3(Dm.H), dim3(64), 0, s, bw.dal, dalpha, Dm.B, Dm.H, Dm.Nb);
   }
@@ -573,13 +602,8 @@ hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const vo
     hipError_t e = launch_backward_mfma(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s);
     if (e != hipSuccess) return e;
     if (proj_o) {
-      const int hs = D.proj_hs ? D.H : 1;
-      if (D.d == 128)
-        hipLaunchKernelGGL(k_bwd_dw<128>, dim3((128 * 128 + 255) / 256, hs), dim3(256), 0, s, bw.dWp, dproj_o,
-                           D.B, D.H, D.Nb, D.proj_hs ? 1 : 0);
-      else
-        hipLaunchKernelGGL(k_bwd_dw<64>, dim3((64 * 64 + 255) / 256, hs), dim3(256), 0, s, bw.dWp, dproj_o, D.B,
-                           D.H, D.Nb, D.proj_hs ? 1 : 0);
+      e = D.d == 128 ? launch_dw<128>(D, bw, dproj_o, s) : launch_dw<64>(D, bw, dproj_o, s);
+      if (e != hipSuccess) return e;
     } else {
       hipLaunchKernelGGL(k_bwd_alpha, dim3(D.H), dim3(64), 0, s, bw.dal, dalpha, D.B, D.H, D.Nb);
     }

@@ -32,7 +32,7 @@
 // the same kernels with alpha = 1 for the sparse side, dO_l = dO W^T on MFMA
 // (W packed once into A-operand fragments) and each query block's part of
 // dW = O_l^T dO (O_l and dO rows in LDS, both operands by transposed reads),
-// summed in float64 by k_bwd_dw.
+// summed in float64 by k_bwd_dw_part and k_bwd_dw_fin.
 // Every product takes bf16 operands and accumulates in float32.
 #include "sla_internal.h"
 #include "dev_common.h"

@@ -149,6 +149,7 @@ size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw) {
   }
   if (proj) {
     x.dWp = (float*)take(BH * D.Nb * D.d * D.d * sizeof(float));
+    x.dWs = (double*)take((size_t)(D.proj_hs ? D.H : 1) * kDwSplit * D.d * D.d * sizeof(double));
     if (D.bf16) x.wq = (uint16_t*)take((size_t)(D.proj_hs ? D.H : 1) * D.d * D.d * sizeof(uint16_t));
   }
   if (bw) *bw = x;

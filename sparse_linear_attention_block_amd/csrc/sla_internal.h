@@ -64,12 +64,15 @@ struct BwdWork {
   float* dHtot;  // [BH, NN] their sum over the head's query blocks
   float* dal;    // [BH, Nb] partial dalpha of each query block
   float* dWp;    // SLA fusion only: [BH, Nb, d, d] each query block's part of dW = O_l^T dO
+  double* dWs;   // SLA fusion only: [Hs, kDwSplit, d, d] sums of consecutive ranges of those parts
   float* Os;     // bf16 only: [BH, N, d] O_s of the forward recompute (k_backward_mfma.hip)
   int8_t* maskT; // bf16 only: [BH, Nb, Nb] the transposed mask
   uint16_t* wq;  // bf16 SLA fusion only: [Hs, d, d] the output map as bf16 A-operand fragments
   int* kvcnt;    // bf16 only: [BH * Nb] critical query blocks per key block
   int* kvorder;  // bf16 only: [BH * Nb] key blocks by falling count (the dK/dV launch order)
 };
+// ranges the SLA fusion's dW parts are summed in before the ranges are added
+constexpr int kDwSplit = 32;
 // forward + backward bytes; proj: the SLA fusion's dW parts are included
 size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw);
 

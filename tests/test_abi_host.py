@@ -233,7 +233,8 @@ def test_sla1_backward_workspace_adds_the_map_parts():
     assert lib.sla_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(b2)) == 0
     assert lib.sla1_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(b1)) == 0
     # dW's per-block parts (float32) and the map's bf16 fragments for the MFMA kernels
-    assert b1.value == b2.value + 12 * 512 * 128 * 128 * 4 + 128 * 128 * 2
+    # dW parts of every query block, the range sums (32 ranges, float64) and W as bf16 fragments
+    assert b1.value == b2.value + 12 * 512 * 128 * 128 * 4 + 32 * 128 * 128 * 8 + 128 * 128 * 2
 
 
 def test_backward_workspace_covers_the_forward():
