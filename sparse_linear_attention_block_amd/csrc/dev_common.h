@@ -212,10 +212,34 @@ __device__ inline int compact_row(const int8_t* __restrict__ mrow, int Nb, int8_
 
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
 
+// Row-major tiles of d-wide bf16 rows (K, V, H_i^T, Q, dO rows) sit in LDS
+// with their 16-byte chunks XOR-swizzled by the row: chunk c of row r at
+// position c ^ row_swz(r). At d = 128 (16 chunks, one row spans all 64 banks)
+// row_swz(r) = 2 ((r % 8) ^ 4 h) + h with h = (r / 8) % 2, found by measuring
+// LDS bank conflicts of both reads the kernels make on gfx950:
+//  - a transposed read (ds_read_b64_tr_b16) takes 32-byte chunk pairs from
+//    8 consecutive rows per 256-byte cycle, so those rows must sit on 8
+//    distinct pairs: the pair index row_swz(r) / 2 = (r % 8) ^ 4 h is a
+//    permutation of r % 8 for either h;
+//  - a 16-byte fragment read (ds_read_b128) of 16 rows at one chunk is free
+//    of conflicts only when rows r and r + 8 fall in different 128-byte
+//    halves of the row (the 4 h term).
+// The plain r % 16 swizzle meets the second and costs the first two extra
+// cycles per read; (r % 8) << 1 | h the reverse. At d = 64 it is r % 8.
+template <int D>
+__device__ __forceinline__ int row_swz(int r) {
+  if constexpr (D == 128) {
+    const int h = (r >> 3) & 1;
+    return (((r & 7) ^ (h << 2)) << 1) | h;
+  } else {
+    return r & (D / 8 - 1);
+  }
+}
+
 // The A operand of O^T += V^T P^T for feature tile ft of a 32-key step (or any
 // product that contracts over 32 rows held row-major in LDS), from the step's V
 // rows in LDS (row-major; 16-byte chunk q of row r at position
-// q ^ (r % C), like the K rows): lane (l16, g) holds feature 16 ft + l16 of keys
+// q ^ row_swz(r), like the K rows): lane (l16, g) holds feature 16 ft + l16 of keys
 // 4g .. 4g+3 (k slots 0-3) and 16+4g .. 16+4g+3 (k slots 4-7), the key order of
 // P^T's B operand. gfx950's transposed LDS read gives lane i of a 16-lane group
 // element k of source lane 4k + i/4's four 16-bit values at position i % 4, so
@@ -225,8 +249,7 @@ typedef short s16x4_v __attribute__((ext_vector_type(4)));
 // xb ^ 32 ft.
 template <int D>
 __device__ __forceinline__ int vt_base(int g, int s) {
-  constexpr int C = D / 8;
-  const int r = 4 * g + (s >> 2), m = r & (C - 1);
+  const int r = 4 * g + (s >> 2), m = row_swz<D>(r);
   return r * 2 * D + 32 * (m >> 1) + 16 * (((s & 3) >> 1) ^ (m & 1)) + 8 * (s & 1);
 }
 template <int D>

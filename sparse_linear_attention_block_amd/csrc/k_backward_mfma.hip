@@ -63,15 +63,15 @@ __device__ __forceinline__ float wsum64(float v) {
 }
 
 // Row r, 16-byte chunk c of a row-major tile in LDS whose chunks are
-// XOR-swizzled by the row (the layout of the forward's K rows), as an element offset.
+// XOR-swizzled by the row (row_swz, the layout of the forward's K rows), as an element offset.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   constexpr int C = D / 8;
-  return (r * C + (c ^ (r & (C - 1)))) * 8;
+  return (r * C + (c ^ row_swz<D>(r))) * 8;
 }
 
 // Per-lane element offsets of the copies of 32 rows (row r, chunk sch of the
-// global rows lands at LDS chunk r C + sch ^ (r % C)), the same for every step.
+// global rows lands at LDS chunk r C + sch ^ row_swz(r)), the same for every step.
 template <int D>
 __device__ __forceinline__ void row_offsets(int wave, int lane, int (&koff)[BwCfg<D>::INSTR]) {
   constexpr int C = D / 8;
@@ -79,7 +79,7 @@ __device__ __forceinline__ void row_offsets(int wave, int lane, int (&koff)[BwCf
   for (int u = 0; u < BwCfg<D>::INSTR; ++u) {
     const int G = 64 * (BwCfg<D>::NW * u + wave) + lane;
     const int r = G / C, sch = G % C;
-    koff[u] = r * D + (sch ^ (r & (C - 1))) * 8;
+    koff[u] = r * D + (sch ^ row_swz<D>(r)) * 8;
   }
 }
 
@@ -120,7 +120,7 @@ __device__ __forceinline__ void copy_tile_part(const uint16_t* src, int part, ui
   for (int u = 0; u < Cf::HINSTR; ++u) {
     const int G = 64 * (Cf::NW * u + wave) + lane;
     const int r = G / C, sch = G % C;
-    load_lds16(src + (part * 64 + r) * D + (sch ^ (r & (C - 1))) * 8, dst + 512 * (Cf::NW * u + wave));
+    load_lds16(src + (part * 64 + r) * D + (sch ^ row_swz<D>(r)) * 8, dst + 512 * (Cf::NW * u + wave));
   }
   if (part == 0 && wave == 0 && lane < C) load_lds16(src + D * D + 8 * lane, zbuf);
 }

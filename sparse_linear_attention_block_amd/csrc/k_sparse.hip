@@ -152,7 +152,7 @@ void k_sparse_bf16(
   for (int u = 0; u < INSTR; ++u) {
     const int G = 64 * (NW * u + wave) + lane;
     const int r = G / C, sch = G % C;
-    koff[u] = r * D + (sch ^ (r & (C - 1))) * 8;
+    koff[u] = r * D + (sch ^ row_swz<D>(r)) * 8;
   }
   const int vxb = vt_base<D>(g, l16);
   // Copies go through buffer resources over this head's K and V rows: the
@@ -189,7 +189,7 @@ void k_sparse_bf16(
     for (int u = 0; u < HINSTR; ++u) {
       const int G = 64 * (NW * u + wave) + lane;
       const int r = G / C, sch = G % C;
-      load_lds16(Hrow + (part * HROWS + r) * D + (sch ^ (r & (C - 1))) * 8, dst + 512 * (NW * u + wave));
+      load_lds16(Hrow + (part * HROWS + r) * D + (sch ^ row_swz<D>(r)) * 8, dst + 512 * (NW * u + wave));
     }
     if (part == 0 && wave == 0 && lane < C) load_lds16(Hrow + D * D + 8 * lane, zbuf);
   };
@@ -230,7 +230,7 @@ void k_sparse_bf16(
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int row = 16 * kt + l16;
-        ka[ks][kt] = *reinterpret_cast<const uint4*>(cur + (row * C + ((4 * ks + g) ^ (row & (C - 1)))) * 8);
+        ka[ks][kt] = *reinterpret_cast<const uint4*>(cur + (row * C + ((4 * ks + g) ^ row_swz<D>(row))) * 8);
       }
     __builtin_amdgcn_sched_barrier(0);
     // S^T products; the copies of the next step are issued between them, so
@@ -437,7 +437,7 @@ void k_sparse_bf16(
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int hr = 16 * f + l16;  // row within the part
-        const uint4 a = *reinterpret_cast<const uint4*>(hb + (hr * C + ((4 * ks + g) ^ (hr & (C - 1)))) * 8);
+        const uint4 a = *reinterpret_cast<const uint4*>(hb + (hr * C + ((4 * ks + g) ^ row_swz<D>(hr))) * 8);
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) nm[qg][ft] = mfma_bf16(a, fq[qg][ks], nm[qg][ft]);
       }
