@@ -739,21 +739,31 @@ __global__ __launch_bounds__(256) void k_mask_t(const int8_t* __restrict__ mask,
 }
 
 // dH (bf16 [BH, Nb, NN]) into the layout of hx that the indicator product reads
-// ([BH, Nbp / 4, NN, 4]: four consecutive blocks per 8-byte word), zero past Nb
+// ([BH, Nbp / 4, NN, 4]: four consecutive blocks per 8-byte word), zero past Nb.
+// A thread moves four consecutive n of four consecutive blocks: four 8-byte
+// loads, four 8-byte stores (NN is a multiple of 4).
 __global__ __launch_bounds__(256) void k_dh_interleave(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                                                        int Nb, int Nbp, int NN) {
   const int bh = blockIdx.y;
+  const int N4 = NN / 4;
   const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= (size_t)(Nbp / 4) * NN) return;
-  const int q = (int)(x / NN), n = (int)(x % NN);
-  uint32_t v[4];
+  if (x >= (size_t)(Nbp / 4) * N4) return;
+  const int q = (int)(x / N4), n = 4 * (int)(x % N4);
+  uint2 v[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = 4 * q + k;
-    v[k] = i < Nb ? (uint32_t)src[((size_t)bh * Nb + i) * NN + n] : 0u;
+    v[k] = i < Nb ? *reinterpret_cast<const uint2*>(src + ((size_t)bh * Nb + i) * NN + n) : make_uint2(0u, 0u);
   }
-  *reinterpret_cast<uint2*>(dst + (((size_t)bh * (Nbp / 4) + q) * NN + n) * 4) =
-      make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+  // v[k] holds blocks 4q + k at n .. n + 3 as (n, n+1 | n+2, n+3); word e of the output is
+  // (block 4q, 4q+1 | 4q+2, 4q+3) at n + e
+  uint2* out = reinterpret_cast<uint2*>(dst + (((size_t)bh * (Nbp / 4) + q) * NN + n) * 4);
+  auto lo16 = [](uint32_t w) { return w & 0xffffu; };
+  auto hi16 = [](uint32_t w) { return w >> 16; };
+  out[0] = make_uint2(lo16(v[0].x) | (lo16(v[1].x) << 16), lo16(v[2].x) | (lo16(v[3].x) << 16));
+  out[1] = make_uint2(hi16(v[0].x) | (hi16(v[1].x) << 16), hi16(v[2].x) | (hi16(v[3].x) << 16));
+  out[2] = make_uint2(lo16(v[0].y) | (lo16(v[1].y) << 16), lo16(v[2].y) | (lo16(v[3].y) << 16));
+  out[3] = make_uint2(hi16(v[0].y) | (hi16(v[1].y) << 16), hi16(v[2].y) | (hi16(v[3].y) << 16));
 }
 
 // cnt[row] = number of critical entries of row `row` of the transposed mask
@@ -844,7 +854,7 @@ hipError_t launch_mfma_t(const Dims& Dm, const void* Q, const void* K, const voi
   // with dH in the place of hx and dh written over H_i (no longer needed)
   e = launch_indicator(Dm, bw.maskT, w, s);
   if (e != hipSuccess) return e;
-  const size_t per = (size_t)(Dm.Nbp / 4) * Dm.NN;
+  const size_t per = (size_t)(Dm.Nbp / 4) * (Dm.NN / 4);
   hipLaunchKernelGGL(k_dh_interleave, dim3((unsigned)((per + 255) / 256), Dm.BH), dim3(256), 0, s, dH,
                      (uint16_t*)w.hx, Dm.Nb, Dm.Nbp, Dm.NN);
   e = hipGetLastError();
