@@ -49,11 +49,15 @@ template <typename T, int d>
 __global__ __launch_bounds__(256) void k_pool_sum(const T* __restrict__ Q, const T* __restrict__ K,
                                                   double* __restrict__ raw, int N, int Nb, int BH) {
   constexpr int E = 16 / sizeof(T);           // elements per 16-byte chunk
-  __shared__ double part[kG][4096 / sizeof(T)];  // row groups x d partial sums per block
+  constexpr int C = d / E, RG = 256 / C, RPT = kBlock / RG;  // rows per thread per block
+  // partial sums per block: row group rg, feature c E + e at rg (d + 16) + e C + c, so
+  // that the lanes of a row group write one e of consecutive c side by side and
+  // consecutive row groups fall 128 bytes apart in the banks
+  constexpr int PS = d + 16;
+  __shared__ double part[kG][RG * PS];
   const int tid = threadIdx.x;
   const int z = blockIdx.z, bh = blockIdx.y;
   const T* X = (z ? K : Q) + (size_t)bh * N * d;
-  constexpr int C = d / E, RG = 256 / C, RPT = kBlock / RG;  // rows per thread per block
   const int c = tid % C, rg = tid / C;
   const int blk0 = blockIdx.x * kG;
   uint4 v[kG][8];  // at most 8 rows per thread (f32, d = 128)
@@ -83,14 +87,15 @@ __global__ __launch_bounds__(256) void k_pool_sum(const T* __restrict__ Q, const
     for (int u = 0; u < 8; ++u)
       if (u < RPT) add_chunk<T>(v[b][u], acc);
 #pragma unroll
-    for (int e = 0; e < E; ++e) part[b][rg * d + c * E + e] = acc[e];
+    for (int e = 0; e < E; ++e) part[b][rg * PS + e * C + c] = acc[e];
   }
   __syncthreads();
   for (int o = tid; o < kG * d; o += 256) {
-    const int b = o / d, col = o % d, blk = blk0 + b;
+    // consecutive threads read consecutive positions l = e C + c of feature c E + e
+    const int b = o / d, l = o % d, col = (l % C) * E + l / C, blk = blk0 + b;
     if (blk >= Nb) continue;
     double sum = 0.0;
-    for (int u = 0; u < RG; ++u) sum += part[b][u * d + col];
+    for (int u = 0; u < RG; ++u) sum += part[b][u * PS + l];
     const int cnt = min(kBlock, N - blk * kBlock);
     raw[(((size_t)z * BH + bh) * Nb + blk) * d + col] = sum / (double)cnt;
   }
