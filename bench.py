@@ -80,8 +80,8 @@ def pages_flop_fraction(kh, N, d):
 def kernel_bytes(B, H, N, d, Nb, n_h, quant=False):
     """Compulsory HBM bytes of each bf16 kernel per launch (each tensor once).
     With the 8-bit sparse branch the h/z stage also writes int8 K and its key
-    bias (from the K rows it reads anyway) and fp8 V^T in place of bf16 V^T,
-    and the sparse kernel reads those 8-bit tiles."""
+    bias (from the K rows it reads anyway) and fp8 V^T (the bf16 sparse kernel
+    reads the V rows themselves), and the sparse kernel reads those 8-bit tiles."""
     X = 2.0 * B * H * N * d
     BH = B * H
     NN = d * d + d
