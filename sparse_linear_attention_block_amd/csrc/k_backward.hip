@@ -367,25 +367,46 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
 // dW = sum of the per-block parts over batches and query blocks (and over the
 // heads when W is shared), in float64 and a fixed order: the parts, in the
 // order (batch, head, query block), are cut into kDwSplit consecutive ranges;
-// k_bwd_dw_part sums each range (one thread per entry of W, 256 consecutive
-// entries per workgroup, so every part is read as whole rows), k_bwd_dw_fin
-// the kDwSplit range sums in range order.
+// k_bwd_dw_part sums each range (a thread owns four consecutive entries of W,
+// read as 16-byte words, eight parts' words in flight before they are added in
+// part order; 1024 consecutive entries per workgroup, so every part is read as
+// whole rows), k_bwd_dw_fin the kDwSplit range sums in range order.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_dw_part(const float* __restrict__ dWp, double* __restrict__ dWs,
                                                      int B, int H, int Nb, int per_head) {
-  const int x = blockIdx.x * 256 + threadIdx.x, r = blockIdx.y, hw = blockIdx.z;
+  const int x = 4 * (blockIdx.x * 256 + threadIdx.x), r = blockIdx.y, hw = blockIdx.z;
   if (x >= D * D) return;
   const int P = per_head ? B * Nb : B * H * Nb;  // parts summed into this W
   const int per = (P + kDwSplit - 1) / kDwSplit;
   const int p0 = r * per, p1 = min(P, p0 + per);
-  double s = 0.0;
-  for (int q = p0; q < p1; ++q) {
-    // part q: (batch, head, block) = (q / (H Nb), q / Nb % H, q % Nb) for a shared W,
-    // (q / Nb, hw, q % Nb) for head hw's own
-    const size_t part = per_head ? ((size_t)(q / Nb) * H + hw) * Nb + q % Nb : (size_t)q;
-    s += (double)dWp[part * D * D + x];
+  // part q: (batch, head, block) = (q / (H Nb), q / Nb % H, q % Nb) for a shared W,
+  // (q / Nb, hw, q % Nb) for head hw's own
+  auto part = [&](int q) -> size_t {
+    return per_head ? ((size_t)(q / Nb) * H + hw) * Nb + q % Nb : (size_t)q;
+  };
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  constexpr int U = 8;
+  for (int q0 = p0; q0 < p1; q0 += U) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = q0 + u < p1 ? *reinterpret_cast<const float4*>(dWp + part(q0 + u) * D * D + x)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (q0 + u < p1) {
+        s0 += (double)v[u].x;
+        s1 += (double)v[u].y;
+        s2 += (double)v[u].z;
+        s3 += (double)v[u].w;
+      }
+    }
   }
-  dWs[((size_t)hw * kDwSplit + r) * D * D + x] = s;
+  double* out = dWs + ((size_t)hw * kDwSplit + r) * D * D + x;
+  out[0] = s0;
+  out[1] = s1;
+  out[2] = s2;
+  out[3] = s3;
 }
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_dw_fin(const double* __restrict__ dWs, float* __restrict__ dW) {
@@ -399,7 +420,7 @@ __global__ __launch_bounds__(256) void k_bwd_dw_fin(const double* __restrict__ d
 template <int D>
 hipError_t launch_dw(const Dims& Dm, const BwdWork& bw, float* dW, hipStream_t s) {
   const int hs = Dm.proj_hs ? Dm.H : 1;
-  hipLaunchKernelGGL(k_bwd_dw_part<D>, dim3((D * D + 255) / 256, kDwSplit, hs), dim3(256), 0, s, bw.dWp, bw.dWs,
+  hipLaunchKernelGGL(k_bwd_dw_part<D>, dim3((D * D / 4 + 255) / 256, kDwSplit, hs), dim3(256), 0, s, bw.dWp, bw.dWs,
                      Dm.B, Dm.H, Dm.Nb, Dm.proj_hs ? 1 : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
