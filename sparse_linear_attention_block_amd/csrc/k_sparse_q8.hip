@@ -199,11 +199,19 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of pair p have landed
     lds_barrier();  // all copies of pair p are in LDS; every wave is done with pair p-1
     if (p + 1 < npair) issue(p + 1, nxt);
+    // The integer products accumulate onto the bit image of the float 1.5 * 2^23:
+    // with |n| <= 127^2 D < 2^22 the sum's bits read as the float 1.5 * 2^23 + n
+    // exactly, so no conversion is needed; fma(that, su, bias) then carries the
+    // tile constant C_t = 1.5 * 2^23 * su_t (rounded once, at the magnitude of
+    // C_t, an error below 1e-4 of the int8 codes' own rounding error), which is
+    // taken out of the tile maximum and added to the exponent offset.
+    constexpr int kMagic = 0x4B400000;
+    constexpr float kMagicF = 12582912.0f;
     i32x4 s[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) s[t][kt] = i32x4{0, 0, 0, 0};
+      for (int kt = 0; kt < 4; ++kt) s[t][kt] = i32x4{kMagic, kMagic, kMagic, kMagic};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       if (t == 1 && !has1) break;
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
         const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float v = fmaf((float)s[t][kt][r], su, bv[r]);
+          const float v = fmaf(__int_as_float(s[t][kt][r]), su, bv[r]);
           if constexpr (FAST) {
             sf[t][kt][r] = v;
           } else {
@@ -248,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
 #pragma unroll
       for (int x = 3; x + 1 < 16; x += 2)
         m = fmaxf(fmaxf(m, sf[t][x >> 2][x & 3]), sf[t][(x + 1) >> 2][(x + 1) & 3]);
-      tmax[t] = fmaxf(m, sf[t][3][3]);
+      tmax[t] = fmaxf(m, sf[t][3][3]) - kMagicF * su;  // -inf stays -inf
     }
     // the rest of the pair; called on both sides of the (rare) reference raise,
     // so that the common path keeps the accumulators where the products left them
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_q8(
       const float Mq = group4_max(fmaxf(tmax[0] + lsv0, tmax[1] + lsv1));
       constexpr float kLog2_448 = 8.807354922057604f;
       const float E = fminf(fmaxf(ceilf(Mq - meff - kLog2_448), -127.f), 127.f);
-      const float off0 = meff - lsv0 + E, off1 = meff - lsv1 + E;
+      const float off0 = (meff - lsv0 + E) + kMagicF * su0, off1 = (meff - lsv1 + E) + kMagicF * su1;
       float ssum[2] = {0.f, 0.f};
       i32x8 pb;
   #pragma unroll
