@@ -23,7 +23,10 @@ branches fused as O = O_s + Proj(O_l) with a seeded d x d Proj), --phi elu1
 the ELU+1 feature map of the linear branch. --op soft_topk times SoftTop-k
 (sla_soft_topk) on the compressed logits of the workload instead of the
 forward pass, and prints that op's own line; --op backward times the
-backward pass (sla_backward) for the forward's mask and a seeded dO.
+backward pass (sla_backward) for the forward's mask and a seeded dO, and
+--op backward --saved the backward from the state a saving forward pass
+(sla_forward_train) kept (sla_backward_saved), which does not run the
+forward again.
 """
 
 import argparse
@@ -301,12 +304,20 @@ def bench_backward(args, cfg, x, torch, sla, proj_o=None):
     dev = torch.device("cuda:0")
     q, k, v, al = x.q.to(dev), x.k.to(dev), x.v.to(dev), x.alpha.to(dev)
     sla1 = proj_o is not None
+    saved = args.saved
+    pq, pk = x.proj_q.to(dev), x.proj_k.to(dev)
+    ws_saved = None
     if sla1:
         proj_o = proj_o.to(dev)
-        _, mask = sla.forward_sla1(q, k, v, proj_o, x.kh, x.kl, proj_q=x.proj_q.to(dev),
-                                   proj_k=x.proj_k.to(dev))
+        if saved:
+            _, mask, ws_saved = sla.forward_sla1_train(q, k, v, proj_o, x.kh, x.kl, proj_q=pq, proj_k=pk)
+        else:
+            _, mask = sla.forward_sla1(q, k, v, proj_o, x.kh, x.kl, proj_q=pq, proj_k=pk)
     else:
-        _, mask = sla.forward(q, k, v, x.proj_q.to(dev), x.proj_k.to(dev), al, x.kh, x.kl)
+        if saved:
+            _, mask, ws_saved = sla.forward_train(q, k, v, pq, pk, al, x.kh, x.kl)
+        else:
+            _, mask = sla.forward(q, k, v, pq, pk, al, x.kh, x.kl)
     g = np.random.default_rng(cfg.seed + 7).standard_normal(tuple(x.q.shape))
     dO = torch.from_numpy(g.astype(np.float32)).to(x.q.dtype)
     dO_d = dO.to(dev)
@@ -318,8 +329,32 @@ def bench_backward(args, cfg, x, torch, sla, proj_o=None):
     n = ctypes_size(sla, p, sla1)
     ws = torch.empty(n, dtype=torch.uint8, device=dev)
 
+    if saved:
+        # the saving forward's own cost, for the record (not part of the timed backward)
+        def fwd_train():
+            if sla1:
+                sla.forward_sla1_train(q, k, v, proj_o, x.kh, x.kl, proj_q=pq, proj_k=pk, workspace=ws_saved)
+            else:
+                sla.forward_train(q, k, v, pq, pk, al, x.kh, x.kl, workspace=ws_saved)
+        for _ in range(3):
+            fwd_train()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fwd_train()
+        e1.record()
+        torch.cuda.synchronize()
+        print(f"[bench] saving forward ({'sla1_' if sla1 else 'sla_'}forward_train): "
+              f"{e0.elapsed_time(e1) / 10:.4f} ms per call", file=sys.stderr, flush=True)
+
     def run():
-        if sla1:
+        if saved:  # the state in ws_saved is only read, so every call sees the same inputs
+            if sla1:
+                sla.backward_sla1_saved(q, k, v, proj_o, mask, dO_d, ws_saved)
+            else:
+                sla.backward_saved(q, k, v, al, mask, dO_d, ws_saved)
+        elif sla1:
             sla.backward_sla1(q, k, v, proj_o, mask, dO_d, workspace=ws)
         else:
             sla.backward(q, k, v, al, mask, dO_d, workspace=ws)
@@ -347,9 +382,11 @@ def bench_backward(args, cfg, x, torch, sla, proj_o=None):
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 MFMA, f32 accumulate" if mfma else "f32 (" + cfg.dtype + " inputs)",
         "data": "synthetic: the seeded workload, its forward mask and a seeded N(0,1) dO",
-        "config": {"workload": cfg.name + ("_sla1" if sla1 else "") + "_backward", "B": B, "H": H, "N": N, "d": d, "Nb": Nb,
+        "config": {"workload": cfg.name + ("_sla1" if sla1 else "") + "_backward" + ("_saved" if saved else ""),
+                   "B": B, "H": H, "N": N, "d": d, "Nb": Nb,
                    "n_h": n_h, "kh": x.kh, "kl": x.kl},
-        "roofline": {"kernel": ("sla1_backward" if sla1 else "sla_backward") + " (all its kernels)",
+        "roofline": {"kernel": ("sla1_backward" if sla1 else "sla_backward") + ("_saved" if saved else "")
+                               + " (all its kernels)",
                      "bound": "mfma" if mfma else "alu",
                      "achieved": round(achieved, 3), "peak": round(peak, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -434,6 +471,9 @@ def main():
     ap.add_argument("--op", choices=["forward", "soft_topk", "backward"], default="forward",
                     help="forward: the whole forward pass; soft_topk: SoftTop-k on its logits; "
                          "backward: the backward pass")
+    ap.add_argument("--saved", action="store_true",
+                    help="with --op backward: time the backward from a saving forward's state "
+                         "(sla_forward_train, then sla_backward_saved)")
     ap.add_argument("--linear", choices=["gemm", "chain"], default="gemm",
                     help="marginal sums: gemm (indicator product per head) or chain (row-to-row updates)")
     ap.add_argument("--tau", type=float, default=1e-3, help="SoftTop-k temperature (Pc units)")

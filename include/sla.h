@@ -271,6 +271,59 @@ int sla1_backward(const sla_problem* p,
                   void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* The training pair: a forward pass that keeps what the backward pass needs,
+ * and a backward pass that takes it instead of running the forward again. The
+ * sparse path's backward follows FlashAttention's (SLA explainer, section 2.3),
+ * which takes the softmax normaliser that its forward saved; here the forward
+ * also keeps O_s (for D_t = dO_s . O_s) and the linear branch's h_j, z_j, H_i
+ * and Z_i.
+ *
+ * sla_forward_train / sla1_forward_train: as sla_forward / sla1_forward (same
+ * arguments, same O and mask), with a workspace of at least
+ * sla_backward_workspace_bytes(p) (sla1: sla1_backward_workspace_bytes(p))
+ * bytes; on completion it holds, besides the forward's intermediates, O_s as
+ * float32 and each query's log2 softmax normaliser over its critical keys.
+ * Requires dtype == SLA_BF16 and quant == SLA_QUANT_NONE
+ * (SLA_ERR_UNSUPPORTED otherwise).
+ *
+ * sla_backward_saved / sla1_backward_saved: as sla_backward / sla1_backward
+ * (same arguments and outputs), reading that state from `workspace` instead of
+ * recomputing it. The caller passes the workspace the forward_train call
+ * filled, unmodified since, and the same Q, K, V, alpha (sla1: proj_o), mask
+ * (mask_in, or the mask_out that call wrote) and the same B, H, N, d,
+ * proj_head_stride, phi and linear_sums; the library cannot check that the
+ * workspace holds that state, and anything else gives undefined gradients
+ * (the reads stay inside the workspace). The results equal those of
+ * sla_backward / sla1_backward for the same inputs. Requires dtype ==
+ * SLA_BF16. The workspace may be reused for the next forward_train once the
+ * backward has completed on `stream`. */
+int sla_forward_train(const sla_problem* p,
+                      const void* Q, const void* K, const void* V,
+                      const float* proj_q, const float* proj_k, const float* alpha,
+                      const int8_t* mask_in,
+                      void* O, int8_t* mask_out,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
+int sla1_forward_train(const sla_problem* p,
+                       const void* Q, const void* K, const void* V,
+                       const float* proj_q, const float* proj_k, const float* proj_o,
+                       const int8_t* mask_in,
+                       void* O, int8_t* mask_out,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
+int sla_backward_saved(const sla_problem* p,
+                       const void* Q, const void* K, const void* V, const float* alpha,
+                       const int8_t* mask, const void* dO,
+                       float* dQ, float* dK, float* dV, float* dalpha,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
+int sla1_backward_saved(const sla_problem* p,
+                        const void* Q, const void* K, const void* V, const float* proj_o,
+                        const int8_t* mask, const void* dO,
+                        float* dQ, float* dK, float* dV, float* dproj_o,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* SoftTop-k of the compressed attention map, the differentiable stand-in for
  * Eq. 2's top-k in SLA2's first training stage (SLA2 article, the two-stage
  * training paragraphs, stage 1: a sigmoid with a temperature; SLA2

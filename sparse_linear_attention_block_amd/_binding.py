@@ -81,6 +81,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sla1_backward_workspace_bytes.restype = ctypes.c_int
     lib.sla1_backward.argtypes = lib.sla_backward.argtypes
     lib.sla1_backward.restype = ctypes.c_int
+    # the training pair: a forward that keeps the backward's inputs in the workspace
+    for fn in (lib.sla_forward_train, lib.sla1_forward_train):
+        fn.argtypes = _FWD_ARGS
+        fn.restype = ctypes.c_int
+    for fn in (lib.sla_backward_saved, lib.sla1_backward_saved):
+        fn.argtypes = lib.sla_backward.argtypes
+        fn.restype = ctypes.c_int
     lib.sla_soft_topk.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                   ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.sla_soft_topk.restype = ctypes.c_int
@@ -199,7 +206,7 @@ def validate_forward_args(q, k, v, proj_q=None, proj_k=None, alpha=None, proj_o=
 
 
 def _run(q, k, v, proj_q, proj_k, alpha, proj_o, kh, kl, mask_in, quant, out, mask_out,
-         workspace, debug, phi, linear="gemm"):
+         workspace, debug, phi, linear="gemm", train=False):
     lib = load_library()
     hs = validate_forward_args(q, k, v, proj_q, proj_k, alpha, proj_o, mask_in, out, mask_out)
     B, H, N, d = q.shape
@@ -217,7 +224,13 @@ def _run(q, k, v, proj_q, proj_k, alpha, proj_o, kh, kl, mask_in, quant, out, ma
         raise ValueError("workspace must be a contiguous tensor on q's device")
     p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", kh, kl,
                      quant, hs, phi, linear)
-    need = workspace_bytes(p)
+    if train:
+        need = ctypes.c_size_t()
+        size_fn = lib.sla_backward_workspace_bytes if proj_o is None else lib.sla1_backward_workspace_bytes
+        _check(size_fn(ctypes.byref(p), ctypes.byref(need)))
+        need = need.value
+    else:
+        need = workspace_bytes(p)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if out is None:
@@ -239,12 +252,16 @@ def _run(q, k, v, proj_q, proj_k, alpha, proj_o, kh, kl, mask_in, quant, out, ma
         args = [ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q), _ptr(proj_k),
                 _ptr(alpha if proj_o is None else proj_o), _ptr(mask_in), _ptr(out), _ptr(mask_out),
                 _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()), stream]
-        if proj_o is None:
+        if train:
+            rc = (lib.sla_forward_train if proj_o is None else lib.sla1_forward_train)(*args)
+        elif proj_o is None:
             rc = lib.sla_forward_debug(*args, ctypes.byref(dbg)) if debug else lib.sla_forward(*args)
         else:
             rc = lib.sla1_forward_debug(*args, ctypes.byref(dbg)) if debug else lib.sla1_forward(*args)
     _check(rc)
     mask = mask_out if mask_out is not None else mask_in
+    if train:
+        return out, mask, workspace
     if debug:
         return out, mask, dbg_t
     return out, mask
@@ -267,6 +284,32 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """
     return _run(q, k, v, proj_q, proj_k, alpha, None, kh, kl, mask_in, quant, out, mask_out,
                 workspace, debug, phi, linear)
+
+
+def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  proj_q: Optional[torch.Tensor], proj_k: Optional[torch.Tensor], alpha: torch.Tensor,
+                  kh: float, kl: float, mask_in: Optional[torch.Tensor] = None, *,
+                  out: Optional[torch.Tensor] = None, mask_out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, phi: str = "softmax", linear: str = "gemm"):
+    """SLA2 forward that keeps the backward pass's inputs (sla_forward_train):
+    returns (O, mask, workspace). Pass the three, unchanged, with the same q, k,
+    v and alpha to backward_saved. bf16 inputs only."""
+    return _run(q, k, v, proj_q, proj_k, alpha, None, kh, kl, mask_in, False, out, mask_out,
+                workspace, False, phi, linear, train=True)
+
+
+def forward_sla1_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj_o: torch.Tensor,
+                       kh: float, kl: float, mask_in: Optional[torch.Tensor] = None, *,
+                       proj_q: Optional[torch.Tensor] = None, proj_k: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, mask_out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, phi: str = "softmax",
+                       linear: str = "gemm"):
+    """SLA forward that keeps the backward pass's inputs (sla1_forward_train):
+    returns (O, mask, workspace) for backward_sla1_saved. bf16 inputs only."""
+    if proj_o is None:
+        raise ValueError("proj_o is required")
+    return _run(q, k, v, proj_q, proj_k, None, proj_o, kh, kl, mask_in, False, out, mask_out,
+                workspace, False, phi, linear, train=True)
 
 
 def noalloc_scratch_bytes() -> int:
@@ -344,7 +387,7 @@ def soft_topk(logits: torch.Tensor, k: float, tau: float, *, out: Optional[torch
     return out, lam
 
 
-def _backward(q, k, v, alpha, proj_o, mask, dO, workspace, phi):
+def _backward(q, k, v, alpha, proj_o, mask, dO, workspace, phi, linear="gemm", saved=False):
     lib = load_library()
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or dO.shape != q.shape:
         raise ValueError("q, k, v and dO must share one [B, H, N, d] shape")
@@ -370,11 +413,14 @@ def _backward(q, k, v, alpha, proj_o, mask, dO, workspace, phi):
     alpha = None if alpha is None else alpha.contiguous()
     proj_o = None if proj_o is None else proj_o.contiguous()
     p = make_problem(B, H, N, d, "bf16" if q.dtype == torch.bfloat16 else "f32", 0.0, 0.0,
-                     proj_head_stride=hs, phi=phi)
+                     proj_head_stride=hs, phi=phi, linear=linear)
     n = ctypes.c_size_t()
     size_fn = lib.sla_backward_workspace_bytes if proj_o is None else lib.sla1_backward_workspace_bytes
     _check(size_fn(ctypes.byref(p), ctypes.byref(n)))
-    if workspace is None or workspace.numel() * workspace.element_size() < n.value:
+    if saved:
+        if workspace is None or not workspace.is_contiguous():
+            raise ValueError("the backward from saved state needs the workspace its forward_train filled")
+    elif workspace is None or workspace.numel() * workspace.element_size() < n.value:
         workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=q.device)
     dQ = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dK = torch.empty_like(dQ)
@@ -385,7 +431,10 @@ def _backward(q, k, v, alpha, proj_o, mask, dO, workspace, phi):
         dpar = torch.empty(proj_o.shape, dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
         stream = ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
-        fn = lib.sla_backward if proj_o is None else lib.sla1_backward
+        if saved:
+            fn = lib.sla_backward_saved if proj_o is None else lib.sla1_backward_saved
+        else:
+            fn = lib.sla_backward if proj_o is None else lib.sla1_backward
         rc = fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha if proj_o is None else proj_o), _ptr(mask),
                 _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dpar), _ptr(workspace),
                 ctypes.c_size_t(workspace.numel() * workspace.element_size()), stream)
@@ -395,21 +444,41 @@ def _backward(q, k, v, alpha, proj_o, mask, dO, workspace, phi):
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
              mask: torch.Tensor, dO: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
-             phi: str = "softmax"):
+             phi: str = "softmax", linear: str = "gemm"):
     """SLA2 backward on the GPU (sla_backward) for the block mask the forward
     pass used: returns (dQ, dK, dV float32 [B, H, N, d], dalpha float32 [H])."""
-    return _backward(q, k, v, alpha, None, mask, dO, workspace, phi)
+    return _backward(q, k, v, alpha, None, mask, dO, workspace, phi, linear)
 
 
 def backward_sla1(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj_o: torch.Tensor,
                   mask: torch.Tensor, dO: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
-                  phi: str = "softmax"):
+                  phi: str = "softmax", linear: str = "gemm"):
     """Backward of the SLA formulation O = O_s + O_l proj_o on the GPU
     (sla1_backward): returns (dQ, dK, dV float32 [B, H, N, d], dproj_o float32
     of proj_o's shape)."""
     if proj_o is None:
         raise ValueError("proj_o is required")
-    return _backward(q, k, v, None, proj_o, mask, dO, workspace, phi)
+    return _backward(q, k, v, None, proj_o, mask, dO, workspace, phi, linear)
+
+
+def backward_saved(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                   mask: torch.Tensor, dO: torch.Tensor, workspace: torch.Tensor, *,
+                   phi: str = "softmax", linear: str = "gemm"):
+    """SLA2 backward from the state forward_train left in `workspace`
+    (sla_backward_saved): the same results as backward(), without running the
+    forward again. q, k, v, alpha, mask, phi and linear must be those of the
+    forward_train call, and the workspace untouched since."""
+    return _backward(q, k, v, alpha, None, mask, dO, workspace, phi, linear, saved=True)
+
+
+def backward_sla1_saved(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, proj_o: torch.Tensor,
+                        mask: torch.Tensor, dO: torch.Tensor, workspace: torch.Tensor, *,
+                        phi: str = "softmax", linear: str = "gemm"):
+    """SLA backward from the state forward_sla1_train left in `workspace`
+    (sla1_backward_saved)."""
+    if proj_o is None:
+        raise ValueError("proj_o is required")
+    return _backward(q, k, v, None, proj_o, mask, dO, workspace, phi, linear, saved=True)
 
 
 class Plan:

@@ -618,9 +618,9 @@ hipError_t launch_bwd_td(const Dims& Dm, const void* Q, const void* K, const voi
 hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                            const float* alpha, const float* proj_o, const void* dO, const Work& w,
                            const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,
-                           hipStream_t s) {
+                           bool recompute, hipStream_t s) {
   if (D.bf16) {  // bf16 inputs: the MFMA kernels (k_backward_mfma.hip)
-    hipError_t e = launch_backward_mfma(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s);
+    hipError_t e = launch_backward_mfma(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, recompute, s);
     if (e != hipSuccess) return e;
     if (proj_o) {
       e = D.d == 128 ? launch_dw<128>(D, bw, dproj_o, s) : launch_dw<64>(D, bw, dproj_o, s);

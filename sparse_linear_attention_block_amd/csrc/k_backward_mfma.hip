@@ -878,13 +878,16 @@ hipError_t launch_mfma_t(const Dims& Dm, const void* Q, const void* K, const voi
 
 hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                                 const float* alpha, const float* proj_o, const void* dO, const Work& w,
-                                const BwdWork& bw, float* dQ, float* dK, float* dV, hipStream_t s) {
+                                const BwdWork& bw, float* dQ, float* dK, float* dV, bool recompute,
+                                hipStream_t s) {
   if (!D.bf16) return hipErrorInvalidValue;
-  // O_s and lse2 from the forward sparse kernel with this mask (O itself is not stored, so
-  // the SLA2 mix runs with any alpha: the SLA fusion passes a workspace array in its place)
-  hipError_t e = launch_sparse(D, Q, K, V, mask, proj_o ? bw.dal : alpha, nullptr, w, nullptr, bw.Os, nullptr, s,
-                               bw.lse);
-  if (e != hipSuccess) return e;
+  if (recompute) {
+    // O_s and lse2 from the forward sparse kernel with this mask (O itself is not stored, so
+    // the SLA2 mix runs with any alpha: the SLA fusion passes a workspace array in its place)
+    hipError_t e = launch_sparse(D, Q, K, V, mask, proj_o ? bw.dal : alpha, nullptr, w, nullptr, bw.Os, nullptr,
+                                 s, bw.lse);
+    if (e != hipSuccess) return e;
+  }
   const bool p = proj_o != nullptr;
   if (D.d == 128) {
     if (p)

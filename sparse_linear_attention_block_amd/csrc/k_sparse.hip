@@ -92,8 +92,8 @@ struct FaCfg {
 // full-rate 16x16x32 MFMA (P.V contracts over the step's 32 keys) and the step
 // buffers are 16 KB. The critical list lives in dynamic LDS of
 // max(2 Nb, 2 D) bytes.
-// LSE: also write each query's log2 softmax normaliser (the backward pass's
-// recompute; a separate instance so that the forward pays nothing for it).
+// LSE: also write each query's log2 softmax normaliser (for the backward pass;
+// a separate instance so that the plain forward pays nothing for it).
 template <int D, int NW, bool PROJ, bool ELU, bool LSE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 2 : 3, NW == 2 ? 2 : 3)))
 void k_sparse_bf16(
@@ -713,7 +713,7 @@ hipError_t launch_bf16(const Dims& D_, const void* Q, const void* K, const void*
                        float* lse_out, hipStream_t s) {
   // dynamic LDS: the critical list (2 Nb bytes), later Z_i (2 D bytes)
   const size_t lbytes = ((size_t)2 * (D_.Nb > D ? D_.Nb : D) + 15) / 16 * 16;
-  if constexpr (!PROJ) {  // the backward's recompute runs the SLA2 form
+  if constexpr (!PROJ || NW == 2) {  // the SLA fusion's saving forward: two-wave layout only
     if (lse_out) {
       hipLaunchKernelGGL((k_sparse_bf16<D, NW, PROJ, ELU, true>), dim3(D_.BH * D_.Nb), dim3(64 * NW), lbytes, s,
                          (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, mask, (const uint16_t*)w.Hx,

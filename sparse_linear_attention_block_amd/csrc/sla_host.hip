@@ -207,17 +207,23 @@ int sla_workspace_bytes(const sla_problem* p, size_t* bytes) {
 
 }  // extern "C"
 
+static int make_bwd_dims(const sla_problem* p, sla::Dims* D);
+
 namespace {
 
 // Both formulations: proj_o == NULL is SLA2 (O = alpha O_s + (1 - alpha) O_l),
-// otherwise SLA (O = O_s + O_l proj_o).
+// otherwise SLA (O = O_s + O_l proj_o). save: the workspace is the backward
+// pass's, and the pass leaves there what the backward would otherwise recompute
+// (h/z and H_i, Z_i in the forward regions; O_s and each query's log-sum-exp in
+// the backward regions).
 int run_forward(const sla_problem* p, const void* Q, const void* K, const void* V,
                 const float* proj_q, const float* proj_k, const float* alpha, const float* proj_o,
                 const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
-                size_t workspace_bytes, void* stream, const sla_debug* dbg) {
+                size_t workspace_bytes, void* stream, const sla_debug* dbg, bool save = false) {
   sla::Dims D;
-  int rc = make_dims(p, &D);
+  int rc = save ? make_bwd_dims(p, &D) : make_dims(p, &D);
   if (rc != SLA_OK) return rc;
+  if (save && !D.bf16) return fail(SLA_ERR_UNSUPPORTED, "the saving forward pass is built for bf16 inputs");
   const bool sla1 = proj_o != nullptr;
   if (!Q || !K || !V || !O) return fail(SLA_ERR_ARG, "Q, K, V and O must not be NULL");
   if (!sla1 && !alpha) return fail(SLA_ERR_ARG, "alpha must not be NULL");
@@ -235,12 +241,16 @@ int run_forward(const sla_problem* p, const void* Q, const void* K, const void* 
               (dbg->logits && !aligned(dbg->logits, 8)) || (dbg->o_s && !aligned(dbg->o_s, 16)) ||
               (dbg->o_l && !aligned(dbg->o_l, 16))))
     return fail(SLA_ERR_ARG, "debug buffers must be aligned (8 bytes float64, 16 bytes float32)");
-  const size_t need = sla::carve(D, nullptr, nullptr);
+  const size_t need = save ? sla::carve_bwd(D, sla1, nullptr, nullptr, nullptr) : sla::carve(D, nullptr, nullptr);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
     return fail(SLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu at %p)",
                 need, workspace_bytes, workspace);
   sla::Work w;
-  sla::carve(D, workspace, &w);
+  sla::BwdWork bw = {};
+  if (save)
+    sla::carve_bwd(D, sla1, workspace, &w, &bw);
+  else
+    sla::carve(D, workspace, &w);
   hipStream_t s = (hipStream_t)stream;
   const int proj_hs = p->proj_head_stride;
   (void)hipGetLastError();  // a stale error from earlier work is not ours to report
@@ -300,6 +310,9 @@ int run_forward(const sla_problem* p, const void* Q, const void* K, const void* 
   if (sla1 && D.bf16) SLA_LAUNCH(sla::launch_pack_proj(D, proj_o, w, s), "projection packing kernel");
   if (D.quant)
     SLA_LAUNCH(sla::launch_sparse_q8(D, Q, mask, alpha, w, O, dos, dol, s), "8-bit sparse kernel");
+  else if (D.bf16 && save)
+    SLA_LAUNCH(sla::launch_sparse(D, Q, K, V, mask, alpha, proj_o, w, O, bw.Os, nullptr, s, bw.lse),
+               "sparse kernel");
   else if (D.bf16)
     SLA_LAUNCH(sla::launch_sparse(D, Q, K, V, mask, alpha, proj_o, w, O, dos, dol, s), "sparse kernel");
   else
@@ -345,6 +358,23 @@ int sla1_forward(const sla_problem* p, const void* Q, const void* K, const void*
                  size_t workspace_bytes, void* stream) {
   return sla1_forward_debug(p, Q, K, V, proj_q, proj_k, proj_o, mask_in, O, mask_out, workspace,
                             workspace_bytes, stream, nullptr);
+}
+
+int sla_forward_train(const sla_problem* p, const void* Q, const void* K, const void* V,
+                      const float* proj_q, const float* proj_k, const float* alpha,
+                      const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return run_forward(p, Q, K, V, proj_q, proj_k, alpha, nullptr, mask_in, O, mask_out, workspace,
+                     workspace_bytes, stream, nullptr, true);
+}
+
+int sla1_forward_train(const sla_problem* p, const void* Q, const void* K, const void* V,
+                       const float* proj_q, const float* proj_k, const float* proj_o,
+                       const int8_t* mask_in, void* O, int8_t* mask_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!proj_o) return fail(SLA_ERR_ARG, "proj_o must not be NULL");
+  return run_forward(p, Q, K, V, proj_q, proj_k, nullptr, proj_o, mask_in, O, mask_out, workspace,
+                     workspace_bytes, stream, nullptr, true);
 }
 
 }  // extern "C"
@@ -470,12 +500,16 @@ int sla1_backward_workspace_bytes(const sla_problem* p, size_t* bytes) {
 namespace {
 
 // Both formulations: proj_o == NULL is SLA2 (dalpha), otherwise SLA (dproj_o).
+// saved: the workspace holds what the saving forward pass left there, so the
+// forward is not run again.
 int run_backward(const sla_problem* p, const void* Q, const void* K, const void* V, const float* alpha,
                  const float* proj_o, const int8_t* mask, const void* dO, float* dQ, float* dK, float* dV,
-                 float* dalpha, float* dproj_o, void* workspace, size_t workspace_bytes, void* stream) {
+                 float* dalpha, float* dproj_o, void* workspace, size_t workspace_bytes, void* stream,
+                 bool saved = false) {
   sla::Dims D;
   const int rc = make_bwd_dims(p, &D);
   if (rc != SLA_OK) return rc;
+  if (saved && !D.bf16) return fail(SLA_ERR_UNSUPPORTED, "the backward from saved state is built for bf16 inputs");
   const bool sla1 = proj_o != nullptr;
   if (!Q || !K || !V || !mask || !dO || !dQ || !dK || !dV)
     return fail(SLA_ERR_ARG, "Q, K, V, mask, dO, dQ, dK and dV must not be NULL");
@@ -499,16 +533,18 @@ int run_backward(const sla_problem* p, const void* Q, const void* K, const void*
     hipError_t e_ = (call);                                                               \
     if (e_ != hipSuccess) return fail(SLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e_)); \
   } while (0)
-  // the linear branch's per-query-block state H_i, Z_i, as in the forward pass
-  SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
-  if (D.chain) {
-    SLA_LAUNCH(sla::launch_chain(D, mask, w, s), "chain kernels");
-  } else {
-    if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
-    SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
+  if (!saved) {
+    // the linear branch's per-query-block state H_i, Z_i, as in the forward pass
+    SLA_LAUNCH(sla::launch_hz(D, K, V, w, s), "h/z kernel");
+    if (D.chain) {
+      SLA_LAUNCH(sla::launch_chain(D, mask, w, s), "chain kernels");
+    } else {
+      if (D.bf16) SLA_LAUNCH(sla::launch_indicator(D, mask, w, s), "indicator kernel");
+      SLA_LAUNCH(sla::launch_linear(D, mask, w, s), "linear kernel");
+    }
   }
   SLA_LAUNCH(sla::launch_backward(D, Q, K, V, mask, sla1 ? nullptr : alpha, proj_o, dO, w, bw, dQ, dK, dV,
-                                  dalpha, dproj_o, s),
+                                  dalpha, dproj_o, !saved, s),
              "backward kernels");
 #undef SLA_LAUNCH
   g_err[0] = 0;
@@ -532,6 +568,21 @@ int sla1_backward(const sla_problem* p, const void* Q, const void* K, const void
   if (!proj_o) return fail(SLA_ERR_ARG, "proj_o must not be NULL");
   return run_backward(p, Q, K, V, nullptr, proj_o, mask, dO, dQ, dK, dV, nullptr, dproj_o, workspace,
                       workspace_bytes, stream);
+}
+
+int sla_backward_saved(const sla_problem* p, const void* Q, const void* K, const void* V, const float* alpha,
+                       const int8_t* mask, const void* dO, float* dQ, float* dK, float* dV, float* dalpha,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return run_backward(p, Q, K, V, alpha, nullptr, mask, dO, dQ, dK, dV, dalpha, nullptr, workspace,
+                      workspace_bytes, stream, true);
+}
+
+int sla1_backward_saved(const sla_problem* p, const void* Q, const void* K, const void* V, const float* proj_o,
+                        const int8_t* mask, const void* dO, float* dQ, float* dK, float* dV, float* dproj_o,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!proj_o) return fail(SLA_ERR_ARG, "proj_o must not be NULL");
+  return run_backward(p, Q, K, V, nullptr, proj_o, mask, dO, dQ, dK, dV, nullptr, dproj_o, workspace,
+                      workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -112,14 +112,16 @@ hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const 
 // written, alpha and dalpha unused)
 // bf16 inputs: the MFMA kernels of k_backward_mfma.hip; writes dQ, dK, dV and the per-block
 // dalpha partials (bw.dal; SLA2) or dW parts (bw.dWp; proj_o given); uses bw.lse / bw.dt as
-// lse2 / D_t and bw.dHx as bf16 dH
+// lse2 / D_t and bw.dHx as bf16 dH. recompute: first run the sparse forward for bw.Os and
+// bw.lse; otherwise they hold what a saving forward pass left there (bf16 only)
 hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                                 const float* alpha, const float* proj_o, const void* dO, const Work& w,
-                                const BwdWork& bw, float* dQ, float* dK, float* dV, hipStream_t s);
+                                const BwdWork& bw, float* dQ, float* dK, float* dV, bool recompute,
+                                hipStream_t s);
 hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                            const float* alpha, const float* proj_o, const void* dO, const Work& w,
                            const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,
-                           hipStream_t s);
+                           bool recompute, hipStream_t s);
 // SoftTop-k rows of a float64 logit matrix (k_soft_topk.hip); cols <= 4096
 hipError_t launch_soft_topk(const double* logits, int rows, int cols, float k, float tau, float* out,
                             float* lambda, hipStream_t s);

@@ -237,6 +237,43 @@ def test_sla1_backward_workspace_adds_the_map_parts():
     assert b1.value == b2.value + 12 * 512 * 128 * 128 * 4 + 32 * 128 * 128 * 8 + 128 * 128 * 2
 
 
+def _train_call(name, p, ws=0x10000, wsb=0, **kw):
+    """One call of the training pair with dummy aligned pointers (no device work:
+    every case below fails its host checks first)."""
+    lib = sla.load_library()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    a = dict(Q=0x10000, K=0x10000, V=0x10000, x1=0x10000, x2=0x10000, x3=0x10000, x4=None, x5=0x10000,
+             x6=0x10000, x7=0x10000, x8=0x10000)
+    a.update(kw)
+    fn = getattr(lib, name)
+    if name.endswith("forward_train"):  # (p, Q, K, V, proj_q, proj_k, alpha | proj_o, mask_in, O, mask_out, ...)
+        args = [a["Q"], a["K"], a["V"], a["x1"], a["x2"], a["x3"], a["x4"], a["x5"], a["x6"]]
+    else:                               # (p, Q, K, V, alpha | proj_o, mask, dO, dQ, dK, dV, dalpha | dproj_o, ...)
+        args = [a["Q"], a["K"], a["V"], a["x3"], a["x5"], a["x6"], a["x7"], a["x8"], a["x1"], a["x2"]]
+    return fn(ctypes.byref(p), *[vp(x) for x in args], vp(ws), ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("name", ["sla_forward_train", "sla1_forward_train", "sla_backward_saved",
+                                  "sla1_backward_saved"])
+def test_training_pair_errors(name):
+    lib = sla.load_library()
+    p = good()
+    assert _train_call(name, p) == B.SLA_ERR_WORKSPACE  # valid up to the workspace
+    assert _train_call(name, p, x3=None) == B.SLA_ERR_ARG  # alpha / proj_o required
+    f32 = good()
+    f32.dtype = B.SLA_F32
+    assert _train_call(name, f32) == B.SLA_ERR_UNSUPPORTED  # the bf16 MFMA path only
+    q8 = good()
+    q8.quant = B.SLA_QUANT_I8QK_F8PV
+    assert _train_call(name, q8) == B.SLA_ERR_UNSUPPORTED
+    assert lib.sla_last_error()
+    if name.endswith("forward_train"):
+        # the saving forward needs the backward's workspace, not the forward's
+        fwd = ctypes.c_size_t()
+        assert lib.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(fwd)) == 0
+        assert _train_call(name, p, wsb=fwd.value) == B.SLA_ERR_WORKSPACE
+
+
 def test_backward_workspace_covers_the_forward():
     lib = sla.load_library()
     p = sla.make_problem(1, 12, 32760, 128, "bf16", 0.05, 0.10)
