@@ -336,17 +336,26 @@ def bench_backward(args, cfg, x, torch, sla, proj_o=None):
                 sla.forward_sla1_train(q, k, v, proj_o, x.kh, x.kl, proj_q=pq, proj_k=pk, workspace=ws_saved)
             else:
                 sla.forward_train(q, k, v, pq, pk, al, x.kh, x.kl, workspace=ws_saved)
-        for _ in range(3):
-            fwd_train()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            fwd_train()
-        e1.record()
-        torch.cuda.synchronize()
-        print(f"[bench] saving forward ({'sla1_' if sla1 else 'sla_'}forward_train): "
-              f"{e0.elapsed_time(e1) / 10:.4f} ms per call", file=sys.stderr, flush=True)
+        def fwd_plain():
+            if sla1:
+                sla.forward_sla1(q, k, v, proj_o, x.kh, x.kl, proj_q=pq, proj_k=pk)
+            else:
+                sla.forward(q, k, v, pq, pk, al, x.kh, x.kl)
+
+        def per_call(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / 10
+        print(f"[bench] saving forward ({'sla1_' if sla1 else 'sla_'}forward_train): {per_call(fwd_train):.4f} ms "
+              f"per call; the plain forward through the same binding call: {per_call(fwd_plain):.4f} ms",
+              file=sys.stderr, flush=True)
 
     def run():
         if saved:  # the state in ws_saved is only read, so every call sees the same inputs

@@ -214,7 +214,7 @@ template <int D, bool ELU, bool PROJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwdq_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const int8_t* __restrict__ mask, const uint16_t* __restrict__ Hx,
-    const float* __restrict__ Os, const float* __restrict__ lse2, const float* __restrict__ alpha,
+    const uint16_t* __restrict__ Os, const float* __restrict__ lse2, const float* __restrict__ alpha,
     const uint16_t* __restrict__ wq, int wq_hs, float* __restrict__ dQ, float* __restrict__ Dt,
     uint16_t* __restrict__ dH, float* __restrict__ dal, float* __restrict__ dWp, int H, int N, int Nb) {
   using Cf = BwCfg<D>;
@@ -245,13 +245,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     qr[ks] = *reinterpret_cast<const uint4*>(Q + qrow + 32 * ks + 8 * g);
     gr[ks] = *reinterpret_cast<const uint4*>(dO + qrow + 32 * ks + 8 * g);
   }
-  uint2 qa2[FT], ga2[FT];  // accumulator layout: features 16 ft + 4 g .. +3
-  float4 os[FT];
+  uint2 qa2[FT], ga2[FT], os2[FT], ol2[FT];  // accumulator layout: features 16 ft + 4 g .. +3
+  const size_t oplane = (size_t)(gridDim.x / Nb) * N * D;  // O_s lo after the hi plane
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
     qa2[ft] = *reinterpret_cast<const uint2*>(Q + qrow + 16 * ft + 4 * g);
     ga2[ft] = *reinterpret_cast<const uint2*>(dO + qrow + 16 * ft + 4 * g);
-    os[ft] = *reinterpret_cast<const float4*>(Os + qrow + 16 * ft + 4 * g);
+    os2[ft] = *reinterpret_cast<const uint2*>(Os + qrow + 16 * ft + 4 * g);
+    ol2[ft] = *reinterpret_cast<const uint2*>(Os + oplane + qrow + 16 * ft + 4 * g);
   }
   const float l2 = lse2[((size_t)bh * Nb + i) * kBlock + 16 * wave + l16];
   const float al = PROJ ? 1.0f : alpha[h];  // the SLA fusion weighs O_s by 1
@@ -264,8 +265,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   float dos = 0.f;  // dO . O_s
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft)
-    dos = fmaf(gf[ft][0], os[ft].x, fmaf(gf[ft][1], os[ft].y, fmaf(gf[ft][2], os[ft].z, fmaf(gf[ft][3], os[ft].w, dos))));
+  for (int ft = 0; ft < FT; ++ft) {
+    float of[4], lf[4];
+    unpack4(os2[ft], of);
+    unpack4(ol2[ft], lf);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) of[r] += lf[r];
+    dos = fmaf(gf[ft][0], of[0], fmaf(gf[ft][1], of[1], fmaf(gf[ft][2], of[2], fmaf(gf[ft][3], of[3], dos))));
+  }
   dos = qv ? group4_sum(dos) : 0.f;
   const float Dq = al * dos;
 
@@ -884,8 +891,8 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
   if (recompute) {
     // O_s and lse2 from the forward sparse kernel with this mask (O itself is not stored, so
     // the SLA2 mix runs with any alpha: the SLA fusion passes a workspace array in its place)
-    hipError_t e = launch_sparse(D, Q, K, V, mask, proj_o ? bw.dal : alpha, nullptr, w, nullptr, bw.Os, nullptr,
-                                 s, bw.lse);
+    hipError_t e = launch_sparse(D, Q, K, V, mask, proj_o ? bw.dal : alpha, nullptr, w, nullptr, nullptr, nullptr,
+                                 s, bw.lse, bw.Os);
     if (e != hipSuccess) return e;
   }
   const bool p = proj_o != nullptr;

@@ -92,8 +92,9 @@ struct FaCfg {
 // full-rate 16x16x32 MFMA (P.V contracts over the step's 32 keys) and the step
 // buffers are 16 KB. The critical list lives in dynamic LDS of
 // max(2 Nb, 2 D) bytes.
-// LSE: also write each query's log2 softmax normaliser (for the backward pass;
-// a separate instance so that the plain forward pays nothing for it).
+// LSE: also write each query's log2 softmax normaliser and O_s as two bf16 planes
+// hi + lo (for the backward pass; a separate instance so that the plain forward
+// pays nothing).
 template <int D, int NW, bool PROJ, bool ELU, bool LSE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 2 ? 2 : 3, NW == 2 ? 2 : 3)))
 void k_sparse_bf16(
@@ -101,7 +102,8 @@ void k_sparse_bf16(
     const uint16_t* __restrict__ V, const int8_t* __restrict__ mask,
     const uint16_t* __restrict__ Hx, const float* __restrict__ alpha,
     const uint16_t* __restrict__ wo, int wo_hs, uint16_t* __restrict__ O,
-    float* __restrict__ dbg_os, float* __restrict__ dbg_ol, float* __restrict__ lse_out, int H, int N, int Nb) {
+    float* __restrict__ dbg_os, float* __restrict__ dbg_ol, float* __restrict__ lse_out,
+    uint16_t* __restrict__ os_out, uint16_t* __restrict__ os_lo, int H, int N, int Nb) {
   using Cf = FaCfg<D, NW>;
   constexpr int NT = Cf::NT, QG = Cf::QG;
   constexpr int C = Cf::C, HT = Cf::HT, INSTR = Cf::INSTR, NN = Cf::NN;
@@ -533,6 +535,40 @@ void k_sparse_bf16(
       *reinterpret_cast<uint4*>(Ob + (size_t)row * D + ch * 8) =
           *reinterpret_cast<const uint4*>(ost + row * OS + ch * 8);
   }
+  if constexpr (LSE) {
+    // O_s of the same rows as hi = bf16(O_s) and lo = bf16(O_s - hi) (relative
+    // error 2^-17), each plane through the same stage and stored as full rows (a
+    // wave's LDS operations run in order, so each read above precedes the next writes)
+    const int nr = min(16 * QG, N - (i * kBlock + 16 * QG * wave));
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        const float il = inv_l[qg];
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = acc[qg][ft][r] * il;
+            v[r] = part == 0 ? x : x - bf_lo(pack_bf2(x, 0.f));
+          }
+          *reinterpret_cast<uint2*>(ost + (16 * qg + l16) * OS + 16 * ft + 4 * g) =
+              make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      uint16_t* Sb = (part == 0 ? os_out : os_lo) + ((size_t)bh * N + (size_t)i * kBlock + 16 * QG * wave) * D;
+#pragma unroll
+      for (int x0 = 0; x0 < 16 * QG * C; x0 += 64) {
+        const int x = x0 + lane;
+        const int row = x / C, ch = x % C;
+        if (row < nr)
+          *reinterpret_cast<uint4*>(Sb + (size_t)row * D + ch * 8) =
+              *reinterpret_cast<const uint4*>(ost + row * OS + ch * 8);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- f32 path
@@ -710,42 +746,44 @@ int sparse_waves() {
 template <int D, int NW, bool PROJ, bool ELU>
 hipError_t launch_bf16(const Dims& D_, const void* Q, const void* K, const void* V, const int8_t* mask,
                        const float* alpha, const Work& w, void* O, float* dbg_os, float* dbg_ol,
-                       float* lse_out, hipStream_t s) {
+                       float* lse_out, uint16_t* os_out, hipStream_t s) {
   // dynamic LDS: the critical list (2 Nb bytes), later Z_i (2 D bytes)
   const size_t lbytes = ((size_t)2 * (D_.Nb > D ? D_.Nb : D) + 15) / 16 * 16;
   if constexpr (!PROJ || NW == 2) {  // the SLA fusion's saving forward: two-wave layout only
     if (lse_out) {
+      if (!os_out) return hipErrorInvalidValue;
       hipLaunchKernelGGL((k_sparse_bf16<D, NW, PROJ, ELU, true>), dim3(D_.BH * D_.Nb), dim3(64 * NW), lbytes, s,
                          (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, mask, (const uint16_t*)w.Hx,
-                         alpha, w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, lse_out, D_.H, D_.N, D_.Nb);
+                         alpha, w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, lse_out, os_out,
+                         os_out + (size_t)D_.BH * D_.N * D, D_.H, D_.N, D_.Nb);
       return hipGetLastError();
     }
   }
-  if (lse_out) return hipErrorInvalidValue;
+  if (lse_out || os_out) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_sparse_bf16<D, NW, PROJ, ELU, false>), dim3(D_.BH * D_.Nb), dim3(64 * NW), lbytes, s,
                      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, mask, (const uint16_t*)w.Hx, alpha,
-                     w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, nullptr, D_.H, D_.N, D_.Nb);
+                     w.wo, D_.proj_hs, (uint16_t*)O, dbg_os, dbg_ol, nullptr, nullptr, nullptr, D_.H, D_.N, D_.Nb);
   return hipGetLastError();
 }
 
 template <int D, int NW>
 hipError_t launch_bf16_nw(const Dims& D_, const void* Q, const void* K, const void* V, const int8_t* mask,
                           const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
-                          float* dbg_ol, float* lse_out, hipStream_t s) {
+                          float* dbg_ol, float* lse_out, uint16_t* os_out, hipStream_t s) {
   if (proj)
-    return D_.elu ? launch_bf16<D, NW, true, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, s)
-                  : launch_bf16<D, NW, true, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, s);
-  return D_.elu ? launch_bf16<D, NW, false, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, s)
-                : launch_bf16<D, NW, false, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, s);
+    return D_.elu ? launch_bf16<D, NW, true, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, os_out, s)
+                  : launch_bf16<D, NW, true, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, os_out, s);
+  return D_.elu ? launch_bf16<D, NW, false, true>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, os_out, s)
+                : launch_bf16<D, NW, false, false>(D_, Q, K, V, mask, alpha, w, O, dbg_os, dbg_ol, lse_out, os_out, s);
 }
 
 template <int D>
 hipError_t launch_bf16_d(const Dims& D_, const void* Q, const void* K, const void* V, const int8_t* mask,
                          const float* alpha, bool proj, const Work& w, void* O, float* dbg_os,
-                         float* dbg_ol, float* lse_out, hipStream_t s) {
+                         float* dbg_ol, float* lse_out, uint16_t* os_out, hipStream_t s) {
   if (sparse_waves() == 4)
-    return launch_bf16_nw<D, 4>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, lse_out, s);
-  return launch_bf16_nw<D, 2>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, lse_out, s);
+    return launch_bf16_nw<D, 4>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, lse_out, os_out, s);
+  return launch_bf16_nw<D, 2>(D_, Q, K, V, mask, alpha, proj, w, O, dbg_os, dbg_ol, lse_out, os_out, s);
 }
 
 }  // namespace
@@ -762,11 +800,11 @@ hipError_t launch_pack_proj(const Dims& D, const float* proj_o, const Work& w, h
 
 hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                          const float* alpha, const float* proj_o, const Work& w, void* O,
-                         float* dbg_os, float* dbg_ol, hipStream_t s, float* lse_out) {
+                         float* dbg_os, float* dbg_ol, hipStream_t s, float* lse_out, uint16_t* os_out) {
   if (!D.bf16) return hipErrorInvalidValue;
   if (D.d == 128)
-    return launch_bf16_d<128>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, lse_out, s);
-  return launch_bf16_d<64>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, lse_out, s);
+    return launch_bf16_d<128>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, lse_out, os_out, s);
+  return launch_bf16_d<64>(D, Q, K, V, mask, alpha, proj_o != nullptr, w, O, dbg_os, dbg_ol, lse_out, os_out, s);
 }
 
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,

@@ -142,7 +142,7 @@ size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw) {
   x.dHtot = (float*)take(BH * D.NN * sizeof(float));
   x.dal = (float*)take(BH * D.Nb * sizeof(float));
   if (D.bf16) {  // the MFMA path (SLA2; carved for both formulations so that the SLA fusion only adds dW)
-    x.Os = (float*)take(BH * D.N * D.d * sizeof(float));
+    x.Os = (uint16_t*)take(2 * BH * D.N * D.d * sizeof(uint16_t));
     x.maskT = (int8_t*)take(BH * D.Nb * D.Nb);
     x.kvcnt = (int*)take(BH * D.Nb * sizeof(int));
     x.kvorder = (int*)take(BH * D.Nb * sizeof(int));
@@ -311,7 +311,7 @@ int run_forward(const sla_problem* p, const void* Q, const void* K, const void* 
   if (D.quant)
     SLA_LAUNCH(sla::launch_sparse_q8(D, Q, mask, alpha, w, O, dos, dol, s), "8-bit sparse kernel");
   else if (D.bf16 && save)
-    SLA_LAUNCH(sla::launch_sparse(D, Q, K, V, mask, alpha, proj_o, w, O, bw.Os, nullptr, s, bw.lse),
+    SLA_LAUNCH(sla::launch_sparse(D, Q, K, V, mask, alpha, proj_o, w, O, nullptr, nullptr, s, bw.lse, bw.Os),
                "sparse kernel");
   else if (D.bf16)
     SLA_LAUNCH(sla::launch_sparse(D, Q, K, V, mask, alpha, proj_o, w, O, dos, dol, s), "sparse kernel");

@@ -65,7 +65,8 @@ struct BwdWork {
   float* dal;    // [BH, Nb] partial dalpha of each query block
   float* dWp;    // SLA fusion only: [BH, Nb, d, d] each query block's part of dW = O_l^T dO
   double* dWs;   // SLA fusion only: [Hs, kDwSplit, d, d] sums of consecutive ranges of those parts
-  float* Os;     // bf16 only: [BH, N, d] O_s of the forward recompute (k_backward_mfma.hip)
+  uint16_t* Os;  // bf16 only: [2, BH, N, d] O_s as bf16 hi, then bf16 lo = O_s - hi (the sparse
+                 // kernel's LSE instance)
   int8_t* maskT; // bf16 only: [BH, Nb, Nb] the transposed mask
   uint16_t* wq;  // bf16 SLA fusion only: [Hs, d, d] the output map as bf16 A-operand fragments
   int* kvcnt;    // bf16 only: [BH * Nb] critical query blocks per key block
@@ -103,7 +104,8 @@ hipError_t launch_pack_proj(const Dims& D, const float* proj_o, const Work& w, h
 // critical key)
 hipError_t launch_sparse(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                          const float* alpha, const float* proj_o, const Work& w, void* O,
-                         float* dbg_os, float* dbg_ol, hipStream_t s, float* lse_out = nullptr);
+                         float* dbg_os, float* dbg_ol, hipStream_t s, float* lse_out = nullptr,
+                         uint16_t* os_out = nullptr);
 hipError_t launch_sparse_f32(const Dims& D, const void* Q, const void* K, const void* V,
                              const int8_t* mask, const float* alpha, const float* proj_o,
                              const Work& w, void* O, float* dbg_os, float* dbg_ol, hipStream_t s);
