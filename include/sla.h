@@ -251,8 +251,10 @@ int sla_backward(const sla_problem* p,
                  void* stream);
 
 /* Workspace that sla1_backward needs for `p` (host only, no device work): that
- * of sla_backward plus one d x d float32 part of dproj_o per query block (and,
- * with bf16 inputs, proj_o once in bf16). */
+ * of sla_backward plus the parts of dproj_o before their float64 sum (bf16
+ * inputs: O_l in bf16 and 512 d x d float32 parts, over consecutive row chunks,
+ * with proj_o once in bf16; float32 inputs: one d x d float32 part per query
+ * block) and 32 d x d float64 range sums per output map. */
 int sla1_backward_workspace_bytes(const sla_problem* p, size_t* bytes);
 
 /* The backward pass of the SLA formulation O = O_s + O_l proj_o (SLA paper

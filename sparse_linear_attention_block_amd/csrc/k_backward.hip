@@ -364,24 +364,28 @@ __global__ __launch_bounds__(kThreads) void k_bwd_q(
   }
 }
 
-// dW = sum of the per-block parts over batches and query blocks (and over the
-// heads when W is shared), in float64 and a fixed order: the parts, in the
-// order (batch, head, query block), are cut into kDwSplit consecutive ranges;
-// k_bwd_dw_part sums each range (a thread owns four consecutive entries of W,
-// read as 16-byte words, eight parts' words in flight before they are added in
-// part order; 1024 consecutive entries per workgroup, so every part is read as
-// whole rows), k_bwd_dw_fin the kDwSplit range sums in range order.
+// dW = sum of the parts, in float64 and a fixed order: the parts of each W
+// (float32 inputs: one per query block, in the order (batch, head, query
+// block), over the batches and blocks, and over the heads when W is shared;
+// bf16 inputs: the dW product's row chunks, in row order) are cut into
+// kDwSplit consecutive ranges; k_bwd_dw_part sums each range (a thread owns
+// four consecutive entries of W, read as 16-byte words, eight parts' words in
+// flight before they are added in part order; 1024 consecutive entries per
+// workgroup, so every part is read as whole rows), k_bwd_dw_fin the kDwSplit
+// range sums in range order.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_dw_part(const float* __restrict__ dWp, double* __restrict__ dWs,
-                                                     int B, int H, int Nb, int per_head) {
+                                                     int B, int H, int Nb, int per_head, int chunks) {
   const int x = 4 * (blockIdx.x * 256 + threadIdx.x), r = blockIdx.y, hw = blockIdx.z;
   if (x >= D * D) return;
-  const int P = per_head ? B * Nb : B * H * Nb;  // parts summed into this W
+  // parts summed into this W: `chunks` contiguous ones (bf16), else the query blocks'
+  const int P = chunks > 0 ? chunks : per_head ? B * Nb : B * H * Nb;
   const int per = (P + kDwSplit - 1) / kDwSplit;
   const int p0 = r * per, p1 = min(P, p0 + per);
-  // part q: (batch, head, block) = (q / (H Nb), q / Nb % H, q % Nb) for a shared W,
-  // (q / Nb, hw, q % Nb) for head hw's own
+  // part q: chunk q of W hw; or (batch, head, block) = (q / (H Nb), q / Nb % H, q % Nb)
+  // for a shared W, (q / Nb, hw, q % Nb) for head hw's own
   auto part = [&](int q) -> size_t {
+    if (chunks > 0) return (size_t)hw * chunks + q;
     return per_head ? ((size_t)(q / Nb) * H + hw) * Nb + q % Nb : (size_t)q;
   };
   double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
@@ -418,10 +422,15 @@ __global__ __launch_bounds__(256) void k_bwd_dw_fin(const double* __restrict__ d
 }
 
 template <int D>
-hipError_t launch_dw(const Dims& Dm, const BwdWork& bw, float* dW, hipStream_t s) {
+hipError_t launch_dw(const Dims& Dm, const BwdWork& bw, const void* dO, float* dW, hipStream_t s) {
   const int hs = Dm.proj_hs ? Dm.H : 1;
-  hipLaunchKernelGGL(k_bwd_dw_part<D>, dim3((D * D / 4 + 255) / 256, kDwSplit, hs), dim3(256), 0, s, bw.dWp, bw.dWs,
-                     Dm.B, Dm.H, Dm.Nb, Dm.proj_hs ? 1 : 0);
+  if (Dm.bf16) {  // the row-chunk parts of the dW product (k_backward_mfma.hip)
+    const hipError_t e = launch_dw_mfma(Dm, bw, dO, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_bwd_dw_part<D>, dim3((D * D / 4 + 255) / 256, kDwSplit, hs), dim3(256), 0, s,
+                     Dm.bf16 ? bw.dWg : bw.dWp, bw.dWs, Dm.B, Dm.H, Dm.Nb, Dm.proj_hs ? 1 : 0,
+                     Dm.bf16 ? dw_chunks(hs) : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_dw_fin<D>, dim3((D * D + 255) / 256, hs), dim3(256), 0, s, bw.dWs, dW);
@@ -589,7 +598,7 @@ hipError_t launch_bwd_t(const Dims& Dm, const void* Q, const void* K, const void
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (PROJ) {
-    e = launch_dw<D>(Dm, bw, dproj_o, s);
+    e = launch_dw<D>(Dm, bw, dO, dproj_o, s);
     if (e != hipSuccess) return e;
   } else {
     hipLaunchKernelGGL(k_bwd_alpha, dim3(Dm.H), dim3(64), 0, s, bw.dal, dalpha, Dm.B, Dm.H, Dm.Nb);
@@ -623,18 +632,13 @@ hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const vo
     hipError_t e = launch_backward_mfma(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, recompute, s);
     if (e != hipSuccess) return e;
     if (proj_o) {
-      e = D.d == 128 ? launch_dw<128>(D, bw, dproj_o, s) : launch_dw<64>(D, bw, dproj_o, s);
+      e = D.d == 128 ? launch_dw<128>(D, bw, dO, dproj_o, s) : launch_dw<64>(D, bw, dO, dproj_o, s);
       if (e != hipSuccess) return e;
     } else {
       hipLaunchKernelGGL(k_bwd_alpha, dim3(D.H), dim3(64), 0, s, bw.dal, dalpha, D.B, D.H, D.Nb);
     }
     return hipGetLastError();
   }
-  if (D.bf16)
-    return D.d == 128 ? launch_bwd_td<uint16_t, 128>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV,
-                                                      dalpha, dproj_o, s)
-                      : launch_bwd_td<uint16_t, 64>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV,
-                                                     dalpha, dproj_o, s);
   return D.d == 128 ? launch_bwd_td<float, 128>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, dalpha,
                                                 dproj_o, s)
                     : launch_bwd_td<float, 64>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, dalpha,

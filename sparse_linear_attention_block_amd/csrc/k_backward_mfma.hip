@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* __restrict__ dO, const int8_t* __restrict__ mask, const uint16_t* __restrict__ Hx,
     const uint16_t* __restrict__ Os, const float* __restrict__ lse2, const float* __restrict__ alpha,
     const uint16_t* __restrict__ wq, int wq_hs, float* __restrict__ dQ, float* __restrict__ Dt,
-    uint16_t* __restrict__ dH, float* __restrict__ dal, float* __restrict__ dWp, int H, int N, int Nb) {
+    uint16_t* __restrict__ dH, float* __restrict__ dal, uint16_t* __restrict__ Ol, int H, int N, int Nb) {
   using Cf = BwCfg<D>;
   constexpr int NT = Cf::NT, HT = Cf::HT, INSTR = Cf::INSTR, KS = Cf::KS, FT = Cf::FT;
   constexpr int HPARTS = Cf::HPARTS, NN = Cf::NN;
@@ -514,39 +514,128 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   if constexpr (PROJ) {
-    // the block's part of dW = O_l^T dO (W indexed [in c][out n]): O_l rows into
-    // bufA and dO rows into bufB (zero past N); D[n][c] = sum_q dO[q][n] O_l[q][c]
-    // with A = dO^T and B = O_l by transposed reads, so lane (l16 = c, g) holds
-    // n = 16 nt + 4 g .. +3 of row c of dW
+    // O_l of the block's rows in bf16 for dW = O_l^T dO (k_bwd_dw_mfma), staged in
+    // bufA and stored as whole rows; each wave reads back only its own 16 rows
     lds_barrier();  // every wave has read the u and dnum rows
-    {
-      const int row = 16 * wave + l16;
+    const int row = 16 * wave + l16;
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        const int o = swz<D>(row, 2 * ft + (g >> 1)) + 4 * (g & 1);
-        *reinterpret_cast<uint2*>(bufA + o) =
-            make_uint2(pack_bf2(olf[ft][0], olf[ft][1]), pack_bf2(olf[ft][2], olf[ft][3]));
-        *reinterpret_cast<uint2*>(bufB + o) = qv ? ga2[ft] : make_uint2(0u, 0u);
-      }
-    }
-    lds_barrier();
-    float* wout = dWp + ((size_t)bh * Nb + i) * D * D;
+    for (int ft = 0; ft < FT; ++ft)
+      *reinterpret_cast<uint2*>(bufA + swz<D>(row, 2 * ft + (g >> 1)) + 4 * (g & 1)) =
+          make_uint2(pack_bf2(olf[ft][0], olf[ft][1]), pack_bf2(olf[ft][2], olf[ft][3]));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    constexpr int C = D / 8;
+    uint16_t* orow = Ol + ((size_t)bh * N + (size_t)i * kBlock + 16 * wave) * D;
+    const int nr = min(16, N - (i * kBlock + 16 * wave));
 #pragma unroll
-    for (int x = 0; x < NTW; ++x) {
-      const int ct = NTW * wave + x;
-      uint4 ob[2];
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) ob[kq] = vt_frag<D>(bufA + 32 * kq * D, vxb, ct);
-#pragma unroll
-      for (int nt = 0; nt < FT; ++nt) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) a = mfma_bf16(vt_frag<D>(bufB + 32 * kq * D, vxb, nt), ob[kq], a);
-        *reinterpret_cast<float4*>(wout + (size_t)(16 * ct + l16) * D + 16 * nt + 4 * g) =
-            make_float4(a[0], a[1], a[2], a[3]);
-      }
+    for (int x0 = 0; x0 < 16 * C; x0 += 64) {
+      const int r = (x0 + lane) / C, ch = (x0 + lane) % C;
+      if (r < nr)
+        *reinterpret_cast<uint4*>(orow + (size_t)r * D + ch * 8) =
+            *reinterpret_cast<const uint4*>(bufA + swz<D>(16 * wave + r, ch));
     }
   }
+}
+
+// dW = O_l^T dO over one chunk of rows (SLA fusion, bf16 inputs): the rows of
+// the (batch, head) pairs whose output map is W hw (head hw's own, or every
+// pair when W is shared), in the order (pair, token), are cut into steps of 32
+// and the steps into `chunks` consecutive chunks; workgroup (chunk r, W hw)
+// writes its chunk's part of dW in float32 (bf16 products, float32
+// accumulation over at most a few thousand rows); the parts are summed in
+// float64 in a fixed order by k_bwd_dw_part / k_bwd_dw_fin. Each step's O_l and
+// dO rows go through LDS (row-major, chunks swizzled by the row), the next
+// step's rows loaded into registers meanwhile; D[n][c] = sum_t dO[t][n] O_l[t][c]
+// with A = dO^T and B = O_l by transposed reads, so lane (l16 = c, g) holds
+// n = 16 nt + 4 g .. +3 of row c of dW. Wave w owns the c tiles FT/4 w .. +FT/4-1.
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_dw_mfma(const uint16_t* __restrict__ Ol, const uint16_t* __restrict__ dO,
+                                                     float* __restrict__ part, int B, int H, int N, int per_head,
+                                                     int chunks) {
+  constexpr int C = D / 8, FT = D / 16, CTW = FT / 4, CPT = 32 * C / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t tl[2][32 * D];  // O_l rows of a step
+  __shared__ __attribute__((aligned(16))) uint16_t tg[2][32 * D];  // dO rows of a step
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int r = blockIdx.x, hw = blockIdx.y;
+  const int nseg = per_head ? B : B * H;  // (batch, head) pairs of W hw, N rows each
+  const long long R = (long long)nseg * N;
+  const int steps = (int)((R + 31) / 32);
+  const int per = (steps + chunks - 1) / chunks;
+  const int s0 = min(steps, r * per), s1 = min(steps, s0 + per);
+  // the current step's first row as (pair, token), advanced by 32 rows per step
+  int sg = (int)(32LL * s0 / N), tb = (int)(32LL * s0 % N);
+  uint4 rl[CPT], rg[CPT];
+  auto load = [&]() {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int G = 256 * u + tid, rw = G / C, ch = G % C;
+      int t = tb + rw, seg = sg;
+      while (t >= N) {  // at most once when N >= 32
+        t -= N;
+        ++seg;
+      }
+      if (seg < nseg) {
+        const size_t bh = per_head ? (size_t)seg * H + hw : (size_t)seg;
+        const size_t off = (bh * N + t) * D + ch * 8;
+        rl[u] = *reinterpret_cast<const uint4*>(Ol + off);
+        rg[u] = *reinterpret_cast<const uint4*>(dO + off);
+      } else {
+        rl[u] = make_uint4(0u, 0u, 0u, 0u);
+        rg[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  auto advance = [&]() {
+    tb += 32;
+    while (tb >= N) {
+      tb -= N;
+      ++sg;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int G = 256 * u + tid, rw = G / C, ch = G % C;
+      *reinterpret_cast<uint4*>(&tl[buf][swz<D>(rw, ch)]) = rl[u];
+      *reinterpret_cast<uint4*>(&tg[buf][swz<D>(rw, ch)]) = rg[u];
+    }
+  };
+  f32x4 acc[CTW][FT];
+#pragma unroll
+  for (int c = 0; c < CTW; ++c)
+#pragma unroll
+    for (int nt = 0; nt < FT; ++nt) acc[c][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int vxb = vt_base<D>(g, l16);
+  if (s0 < s1) {
+    load();
+    stash(0);
+  }
+  __syncthreads();
+  for (int s = s0; s < s1; ++s) {
+    const int buf = (s - s0) & 1;
+    if (s + 1 < s1) {
+      advance();
+      load();
+    }
+    uint4 ob[CTW];
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) ob[c] = vt_frag<D>(tl[buf], vxb, CTW * wave + c);
+#pragma unroll
+    for (int nt = 0; nt < FT; ++nt) {
+      const uint4 a = vt_frag<D>(tg[buf], vxb, nt);
+#pragma unroll
+      for (int c = 0; c < CTW; ++c) acc[c][nt] = mfma_bf16(a, ob[c], acc[c][nt]);
+    }
+    if (s + 1 < s1) stash(buf ^ 1);  // the other buffer was last read before the previous barrier
+    __syncthreads();
+  }
+  float* out = part + ((size_t)hw * chunks + r) * D * D;
+#pragma unroll
+  for (int c = 0; c < CTW; ++c)
+#pragma unroll
+    for (int nt = 0; nt < FT; ++nt)
+      *reinterpret_cast<float4*>(out + (size_t)(16 * (CTW * wave + c) + l16) * D + 16 * nt + 4 * g) =
+          make_float4(acc[c][nt][0], acc[c][nt][1], acc[c][nt][2], acc[c][nt][3]);
 }
 
 template <int D, bool ELU>
@@ -849,7 +938,7 @@ hipError_t launch_mfma_t(const Dims& Dm, const void* Q, const void* K, const voi
   }
   hipLaunchKernelGGL((k_bwdq_mfma<D, ELU, PROJ>), grid, dim3(256), lbytes, s, (const uint16_t*)Q,
                      (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)dO, mask, (const uint16_t*)w.Hx, bw.Os,
-                     bw.lse, alpha, (const uint16_t*)bw.wq, Dm.proj_hs, dQ, bw.dt, dH, bw.dal, bw.dWp, Dm.H, Dm.N,
+                     bw.lse, alpha, (const uint16_t*)bw.wq, Dm.proj_hs, dQ, bw.dt, dH, bw.dal, bw.Ol, Dm.H, Dm.N,
                      Dm.Nb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -908,6 +997,18 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
                  : launch_mfma_t<64, false, true>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s);
   return D.elu ? launch_mfma_t<64, true, false>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s)
                : launch_mfma_t<64, false, false>(D, Q, K, V, mask, alpha, proj_o, dO, w, bw, dQ, dK, dV, s);
+}
+
+hipError_t launch_dw_mfma(const Dims& D, const BwdWork& bw, const void* dO, hipStream_t s) {
+  const int hs = D.proj_hs ? D.H : 1;
+  const dim3 grid(dw_chunks(hs), hs);
+  if (D.d == 128)
+    hipLaunchKernelGGL(k_bwd_dw_mfma<128>, grid, dim3(256), 0, s, bw.Ol, (const uint16_t*)dO, bw.dWg, D.B, D.H, D.N,
+                       D.proj_hs ? 1 : 0, dw_chunks(hs));
+  else
+    hipLaunchKernelGGL(k_bwd_dw_mfma<64>, grid, dim3(256), 0, s, bw.Ol, (const uint16_t*)dO, bw.dWg, D.B, D.H, D.N,
+                       D.proj_hs ? 1 : 0, dw_chunks(hs));
+  return hipGetLastError();
 }
 
 }  // namespace sla

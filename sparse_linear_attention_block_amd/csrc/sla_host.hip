@@ -148,8 +148,14 @@ size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw) {
     x.kvorder = (int*)take(BH * D.Nb * sizeof(int));
   }
   if (proj) {
-    x.dWp = (float*)take(BH * D.Nb * D.d * D.d * sizeof(float));
-    x.dWs = (double*)take((size_t)(D.proj_hs ? D.H : 1) * kDwSplit * D.d * D.d * sizeof(double));
+    const int hs = D.proj_hs ? D.H : 1;
+    if (D.bf16) {
+      x.Ol = (uint16_t*)take(BH * D.N * D.d * sizeof(uint16_t));
+      x.dWg = (float*)take((size_t)hs * dw_chunks(hs) * D.d * D.d * sizeof(float));
+    } else {
+      x.dWp = (float*)take(BH * D.Nb * D.d * D.d * sizeof(float));
+    }
+    x.dWs = (double*)take((size_t)hs * kDwSplit * D.d * D.d * sizeof(double));
     if (D.bf16) x.wq = (uint16_t*)take((size_t)(D.proj_hs ? D.H : 1) * D.d * D.d * sizeof(uint16_t));
   }
   if (bw) *bw = x;

@@ -63,7 +63,9 @@ struct BwdWork {
   float* dHx;    // [BH, Nb, NN] dH_i (stored like H_i^T) then dZ_i, per query block
   float* dHtot;  // [BH, NN] their sum over the head's query blocks
   float* dal;    // [BH, Nb] partial dalpha of each query block
-  float* dWp;    // SLA fusion only: [BH, Nb, d, d] each query block's part of dW = O_l^T dO
+  float* dWp;    // SLA fusion, float32 inputs: [BH, Nb, d, d] each query block's part of dW = O_l^T dO
+  uint16_t* Ol;  // SLA fusion, bf16 inputs: [BH, N, d] O_l in bf16 (the dQ kernel's, for dW)
+  float* dWg;    // SLA fusion, bf16 inputs: [Hs, kDwChunks / Hs, d, d] dW over consecutive row chunks
   double* dWs;   // SLA fusion only: [Hs, kDwSplit, d, d] sums of consecutive ranges of those parts
   uint16_t* Os;  // bf16 only: [2, BH, N, d] O_s as bf16 hi, then bf16 lo = O_s - hi (the sparse
                  // kernel's LSE instance)
@@ -74,6 +76,9 @@ struct BwdWork {
 };
 // ranges the SLA fusion's dW parts are summed in before the ranges are added
 constexpr int kDwSplit = 32;
+// row chunks of the bf16 dW product (over all W matrices together)
+constexpr int kDwChunks = 512;
+inline int dw_chunks(int hs) { return kDwChunks / hs > 0 ? kDwChunks / hs : 1; }
 // forward + backward bytes; proj: the SLA fusion's dW parts are included
 size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw);
 
@@ -120,6 +125,8 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
                                 const float* alpha, const float* proj_o, const void* dO, const Work& w,
                                 const BwdWork& bw, float* dQ, float* dK, float* dV, bool recompute,
                                 hipStream_t s);
+// bf16 SLA fusion: dW over row chunks of O_l (bw.Ol) and dO into bw.dWg, one part per chunk
+hipError_t launch_dw_mfma(const Dims& D, const BwdWork& bw, const void* dO, hipStream_t s);
 hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V, const int8_t* mask,
                            const float* alpha, const float* proj_o, const void* dO, const Work& w,
                            const BwdWork& bw, float* dQ, float* dK, float* dV, float* dalpha, float* dproj_o,

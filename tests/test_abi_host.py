@@ -232,9 +232,21 @@ def test_sla1_backward_workspace_adds_the_map_parts():
     b2, b1 = ctypes.c_size_t(), ctypes.c_size_t()
     assert lib.sla_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(b2)) == 0
     assert lib.sla1_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(b1)) == 0
-    # dW's per-block parts (float32) and the map's bf16 fragments for the MFMA kernels
-    # dW parts of every query block, the range sums (32 ranges, float64) and W as bf16 fragments
-    assert b1.value == b2.value + 12 * 512 * 128 * 128 * 4 + 32 * 128 * 128 * 8 + 128 * 128 * 2
+    # bf16 inputs: O_l in bf16, the 512 row-chunk parts of dW (float32), the range sums
+    # (32 ranges, float64) and W as bf16 fragments for the MFMA kernels
+    assert b1.value == b2.value + 12 * 32760 * 128 * 2 + 512 * 128 * 128 * 4 + 32 * 128 * 128 * 8 + 128 * 128 * 2
+    # per-head maps: 512 // H chunk parts per head; float32 inputs: one part per query block
+    ph = sla.make_problem(1, 12, 32760, 128, "bf16", 0.05, 0.10, proj_head_stride=128 * 128)
+    bh2, bh1 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sla_backward_workspace_bytes(ctypes.byref(ph), ctypes.byref(bh2)) == 0
+    assert lib.sla1_backward_workspace_bytes(ctypes.byref(ph), ctypes.byref(bh1)) == 0
+    assert bh1.value == (bh2.value + 12 * 32760 * 128 * 2 + 12 * (512 // 12) * 128 * 128 * 4
+                         + 12 * 32 * 128 * 128 * 8 + 12 * 128 * 128 * 2)
+    f = sla.make_problem(1, 12, 32760, 128, "f32", 0.05, 0.10)
+    f2, f1 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sla_backward_workspace_bytes(ctypes.byref(f), ctypes.byref(f2)) == 0
+    assert lib.sla1_backward_workspace_bytes(ctypes.byref(f), ctypes.byref(f1)) == 0
+    assert f1.value == f2.value + 12 * 512 * 128 * 128 * 4 + 32 * 128 * 128 * 8
 
 
 def _train_call(name, p, ws=0x10000, wsb=0, **kw):
