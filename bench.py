@@ -497,6 +497,9 @@ def main():
                     help="before the warm-up, copy a buffer of this many MiB three times "
                          "(a plain copy kernel of known size, to scale HBM counters)")
     args = ap.parse_args()
+    if args.saved and args.op != "backward":
+        print("--saved applies to --op backward only", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the SLA2 forward pass is built and timed on a "
               "single MI355X (heads shard across GPUs with no exchange; see the design notes).",
