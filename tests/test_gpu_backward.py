@@ -210,6 +210,24 @@ def test_sla1_batch_of_two_injected_mask():
     _check_sla1(x, 1e-2, _proj(128), mask=mask)
 
 
+@pytest.mark.parametrize("N,per_head", [(20, True), (20, False), (37, True), (100, False)])
+def test_sla1_bf16_steps_across_pairs(N, per_head):
+    # the bf16 dW product walks the rows of every (batch, head) pair that shares a
+    # map in steps of 32: with N < 32 one step spans several pairs; B = 2
+    x = make_inputs(CONFIGS[4], H=3, N=N)
+    Nb = (N + 63) // 64
+    # one block per row: make it marginal, so that O_l and dW are not zero
+    mask = np.zeros((x.B, x.H, Nb, Nb), dtype=np.int8) if Nb == 1 else None
+    _check_sla1(x, 1e-2, _proj(128, H=3 if per_head else None), mask=mask)
+
+
+def test_sla1_bf16_d64_batch_of_two():
+    x = make_inputs(CONFIGS[1], B=2, N=700)
+    x.q, x.k, x.v = x.q.bfloat16(), x.k.bfloat16(), x.v.bfloat16()
+    _check_sla1(x, 1e-2, _proj(64, H=x.H))
+    _check_sla1(x, 1e-2, _proj(64), phi="elu1")
+
+
 def test_sla1_fp32_d128():
     x = make_inputs(CONFIGS[2], H=2, N=300)
     x.q, x.k, x.v = x.q.float(), x.k.float(), x.v.float()
