@@ -1,7 +1,7 @@
 """The C ABI from C: a C99 program includes include/sla.h, links libsla.so and
 makes the host-only calls (version, block counts, workspace sizes, status
 text and the error paths that return before any device work, including those
-of the SLA backward and the allocation-free forward)."""
+of the SLA backward, the training pair and the allocation-free forward)."""
 
 import os
 import shutil
@@ -43,6 +43,13 @@ int main(void) {
   if (sla1_forward(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != SLA_ERR_ARG) return 8;
   if (sla_soft_topk(0, 1, 1, 0.5, 1.0, 0, 0, 0) != SLA_ERR_ARG) return 9;
   if (!strstr(sla_status_str(SLA_ERR_WORKSPACE), "WORKSPACE")) return 10;
+  /* the training pair: bf16 only, and the backward's workspace for the saving forward */
+  p.dtype = SLA_F32;
+  if (sla_forward_train(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != SLA_ERR_UNSUPPORTED) return 14;
+  if (sla_backward_saved(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != SLA_ERR_UNSUPPORTED) return 15;
+  p.dtype = SLA_BF16;
+  if (sla1_forward_train(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != SLA_ERR_ARG) return 16;  /* no proj_o */
+  if (sla1_backward_saved(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != SLA_ERR_ARG) return 17;
   printf("ok\n");
   return 0;
 }
