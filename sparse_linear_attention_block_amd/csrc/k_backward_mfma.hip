@@ -30,8 +30,9 @@
 //    lse2 and D_t, dV^T += dO^T (alpha P), dK^T += Q^T dS / sqrt(d).
 // The SLA fusion O = O_s + O_l W (SLA paper summary, section 4, step 4) takes
 // the same kernels with alpha = 1 for the sparse side, dO_l = dO W^T on MFMA
-// (W packed once into A-operand fragments) and each query block's part of
-// dW = O_l^T dO (O_l and dO rows in LDS, both operands by transposed reads),
+// (W packed once into A-operand fragments), O_l of every row stored in bf16 by
+// k_bwdq_mfma, and dW = O_l^T dO formed by k_bwd_dw_mfma over chunks of rows
+// (O_l and dO rows in LDS, both operands by transposed reads), the chunk parts
 // summed in float64 by k_bwd_dw_part and k_bwd_dw_fin.
 // Every product takes bf16 operands and accumulates in float32.
 #include "sla_internal.h"
