@@ -644,7 +644,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const int8_t* __restrict__ maskT, const float* __restrict__ lse2,
     const float* __restrict__ Dt, const uint16_t* __restrict__ dh, const float* __restrict__ alpha,
-    const int* __restrict__ order, float* __restrict__ dK, float* __restrict__ dV, int H, int N, int Nb) {
+    const int* __restrict__ order, const int* __restrict__ hdr, const int2* __restrict__ info,
+    const int2* __restrict__ tab, float* __restrict__ part, int slots, float* __restrict__ dK,
+    float* __restrict__ dV, int H, int N, int Nb) {
   using Cf = BwCfg<D>;
   constexpr int NT = Cf::NT, HT = Cf::HT, INSTR = Cf::INSTR, KS = Cf::KS, FT = Cf::FT;
   constexpr int HPARTS = Cf::HPARTS, NN = Cf::NN;
@@ -659,8 +661,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  // key blocks in order of falling critical count (the longest first)
-  const int id = order[blockIdx.x];
+  // workgroups 0 .. slots-1: the extra chunks (chunk >= 1) of the key blocks cut
+  // into several; then chunk 0 of every key block, in order of falling critical
+  // count (the longest first)
+  int id, chunk;
+  if ((int)blockIdx.x < slots) {
+    if ((int)blockIdx.x >= hdr[1]) return;  // whole workgroup: no extra chunk here
+    const int2 t = tab[blockIdx.x];
+    id = t.x;
+    chunk = t.y;
+  } else {
+    id = order[blockIdx.x - slots];
+    chunk = 0;
+  }
+  const int2 inf = info[id];  // chunks of this key block, its first partial slot
   const int bh = id / Nb, j = id - bh * Nb, h = bh % H;
   const int8_t* mrow = maskT + ((size_t)bh * Nb + j) * Nb;
   int8_t mv[kMaskPre];
@@ -685,6 +699,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int ncol = compact_loaded<NT>(mv, mrow, Nb, (int8_t)1, list, wsum);
   const int vxb = vt_base<D>(g, l16);
 
+  f32x4 dv[FT], dk[FT];
+  if (chunk == 0) {  // uniform
   // ---- linear branch: dh_j^T (rows n) in parts of 64 rows into bufA / bufB, dz_j into zbuf
   const uint16_t* Hrow = dh + ((size_t)bh * Nb + j) * NN;
   copy_tile_part<D>(Hrow, 0, bufA, zbuf, wave, lane);
@@ -699,7 +715,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   lds_barrier();
   auto hpart = [&](int ks) -> const uint16_t* { return (ks < KS / HPARTS ? bufA : bufB) + 32 * (ks % (KS / HPARTS)) * D; };
   // dV^T = dh_j^T phi(K)^T (A: rows n of dh_j^T); dw^T = dh_j V^T (A by transposed reads) + dz_j
-  f32x4 dv[FT], dk[FT];
   float dw[FT][4];
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
@@ -722,6 +737,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ft = 0; ft < FT; ++ft) dk[ft] = f32x4{dkl[ft][0], dkl[ft][1], dkl[ft][2], dkl[ft][3]};
   }
   lds_barrier();  // every wave has read dh_j: the buffers take the query rows
+  } else {
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) dv[ft] = dk[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // ---- sparse branch over the query blocks that hold this key block as critical
   const uint16_t* Qb = Q + (size_t)bh * N * D;
@@ -733,9 +752,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float sc = kLog2e / sqrtf((float)D), isd = 1.0f / sqrtf((float)D);
   const float* Lh = lse2 + (size_t)bh * Nb * kBlock;
   const float* Dh = Dt + (size_t)bh * Nb * kBlock;
-  const int nstep = 2 * ncol;  // step s: queries 32 (s & 1) .. +31 of listed query block s >> 1
+  // this chunk's part of the critical list: entries c0 .. c1 - 1
+  const int c0 = (int)((long long)chunk * ncol / inf.x), c1 = (int)((long long)(chunk + 1) * ncol / inf.x);
+  const int nstep = 2 * (c1 - c0);  // step s: queries 32 (s & 1) .. +31 of listed query block c0 + s / 2
   auto copy = [&](int s, uint16_t* dst, float* ls) {
-    const int iq = __builtin_amdgcn_readfirstlane((int)list[s >> 1]);
+    const int iq = __builtin_amdgcn_readfirstlane((int)list[c0 + (s >> 1)]);
     const int q0 = iq * kBlock + 32 * (s & 1);
     copy_rows<D>(qrs, grs, koff, q0, N, dst, wave);
     if (wave == 0 && lane < 8) load_lds16(Lh + q0 + 4 * lane, ls);
@@ -810,13 +831,148 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     step(s + 1, bufB, bufA, lsB, lsA);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  if (kv) {
+  if (chunk == 0) {
+    if (kv) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        *reinterpret_cast<float4*>(dK + krow + 16 * ft + 4 * g) = make_float4(dk[ft][0], dk[ft][1], dk[ft][2], dk[ft][3]);
+        *reinterpret_cast<float4*>(dV + krow + 16 * ft + 4 * g) = make_float4(dv[ft][0], dv[ft][1], dv[ft][2], dv[ft][3]);
+      }
+    }
+  } else {  // this chunk's part, added to chunk 0's by k_kv_reduce in chunk order
+    float* pk = part + ((size_t)(inf.y + chunk - 1) * 2) * kBlock * D + (size_t)(16 * wave + l16) * D;
+    float* pv = pk + kBlock * D;
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      *reinterpret_cast<float4*>(dK + krow + 16 * ft + 4 * g) = make_float4(dk[ft][0], dk[ft][1], dk[ft][2], dk[ft][3]);
-      *reinterpret_cast<float4*>(dV + krow + 16 * ft + 4 * g) = make_float4(dv[ft][0], dv[ft][1], dv[ft][2], dv[ft][3]);
+      *reinterpret_cast<float4*>(pk + 16 * ft + 4 * g) = make_float4(dk[ft][0], dk[ft][1], dk[ft][2], dk[ft][3]);
+      *reinterpret_cast<float4*>(pv + 16 * ft + 4 * g) = make_float4(dv[ft][0], dv[ft][1], dv[ft][2], dv[ft][3]);
     }
   }
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads); returns the
+// exclusive prefix and leaves the total in *tot.
+__device__ int block_scan_1024(int v, int* sh, int* tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? sh[lane] : 0, wi = w;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int u = __shfl_up(wi, o);
+      if (lane >= o) wi += u;
+    }
+    if (lane < 16) sh[16 + lane] = wi - w;  // exclusive prefix of the wave sums
+    if (lane == 15) sh[32] = wi;
+  }
+  __syncthreads();
+  const int ex = sh[16 + wave] + incl - v;
+  *tot = sh[32];
+  __syncthreads();  // sh is reused by the next call
+  return ex;
+}
+
+// The dK/dV work of key block j (its c_j critical query blocks, two 32-query
+// steps each) cut into nch_j = ceil(c_j / ch) chunks of consecutive list
+// entries, ch = max(kKvChunk, ceil(sum_j c_j / slots)) so that the extra chunks
+// (nch_j - 1 per key block) fit the partial slots. Everything depends on the
+// counts only, not on the launch order, so the chunks and the order of their
+// sums are the same on every call. One workgroup: hdr = {ch, extra chunks,
+// split key blocks}; info[j] = {nch_j, first slot}; tab[slot] = {j, chunk};
+// list = the split key blocks in index order.
+__global__ __launch_bounds__(1024) void k_kv_split(const int* __restrict__ cnt, int rows, int slots,
+                                                   int* __restrict__ hdr, int2* __restrict__ info,
+                                                   int2* __restrict__ tab, int* __restrict__ list) {
+  __shared__ int sh[40];
+  __shared__ long long ssum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long t = 0;
+  for (int r = tid; r < rows; r += 1024) t += cnt[r];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+  if (lane == 0) ssum[wave] = t;
+  __syncthreads();
+  long long S = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) S += ssum[w];
+  const long long need = (S + slots - 1) / slots;
+  const int ch = (int)(need > kKvChunk ? need : kKvChunk);
+  // each thread a contiguous range of key blocks, so the scans follow the index order
+  const int per = (rows + 1023) / 1024, r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
+  int ext = 0, nsp = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int n = max(1, (cnt[r] + ch - 1) / ch);
+    ext += n - 1;
+    nsp += n > 1;
+  }
+  int text, tsp;
+  int slot = block_scan_1024(ext, sh, &text);
+  int pos = block_scan_1024(nsp, sh, &tsp);
+  for (int r = r0; r < r1; ++r) {
+    const int n = max(1, (cnt[r] + ch - 1) / ch);
+    info[r] = make_int2(n, slot);
+    for (int k = 1; k < n; ++k) tab[slot + k - 1] = make_int2(r, k);
+    if (n > 1) list[pos++] = r;
+    slot += n - 1;
+  }
+  if (tid == 0) {
+    hdr[0] = ch;
+    hdr[1] = text;
+    hdr[2] = tsp;
+  }
+}
+
+// dK, dV of the key blocks cut into several chunks: chunk 0's values (written by
+// k_bwdkv_mfma) plus the parts of chunks 1 .. nch - 1, added in chunk order.
+// Workgroup (m, y) takes slice y of kKvRedY of split key block list[m]; rows past
+// N are not touched; each thread's words are loaded chunk by chunk, all of them
+// in flight before the adds.
+template <int D>
+__global__ __launch_bounds__(256) void k_kv_reduce(const int* __restrict__ hdr, const int2* __restrict__ info,
+                                                   const int* __restrict__ list, const float* __restrict__ part,
+                                                   float* __restrict__ dK, float* __restrict__ dV, int N, int Nb) {
+  if ((int)blockIdx.x >= hdr[2]) return;
+  const int id = list[blockIdx.x];
+  const int2 inf = info[id];
+  const int bh = id / Nb, j = id - bh * Nb;
+  constexpr int Q4 = kBlock * D / 4;        // float4 words of one key block's dK (or dV)
+  constexpr int PER = 2 * Q4 / kKvRedY / 256;  // words per thread
+  float4 acc[PER];
+  float* out[PER];
+  bool live[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int x = (blockIdx.y * PER + u) * 256 + threadIdx.x;
+    const int which = x / Q4, e = x % Q4, key = j * kBlock + (4 * e) / D;
+    live[u] = key < N;
+    out[u] = (which ? dV : dK) + ((size_t)bh * N + min(key, N - 1)) * D + (4 * e) % D;
+    acc[u] = live[u] ? *reinterpret_cast<const float4*>(out[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int k = 1; k < inf.x; ++k) {
+    float4 p[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int x = (blockIdx.y * PER + u) * 256 + threadIdx.x;
+      p[u] = *reinterpret_cast<const float4*>(part + ((size_t)(inf.y + k - 1) * 2) * kBlock * D + 4 * x);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      acc[u].x += p[u].x;
+      acc[u].y += p[u].y;
+      acc[u].z += p[u].z;
+      acc[u].w += p[u].w;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (live[u]) *reinterpret_cast<float4*>(out[u]) = acc[u];
 }
 
 // maskT[bh][j][i] = mask[bh][i][j], 64 x 64 tiles through LDS
@@ -965,9 +1121,20 @@ hipError_t launch_mfma_t(const Dims& Dm, const void* Q, const void* K, const voi
   hipLaunchKernelGGL(k_lpt_order, dim3(1), dim3(1024), 0, s, bw.kvcnt, bw.kvorder, Dm.Nb, rows);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwdkv_mfma<D, ELU>), grid, dim3(256), lbytes, s, (const uint16_t*)Q, (const uint16_t*)K,
-                     (const uint16_t*)V, (const uint16_t*)dO, bw.maskT, bw.lse, bw.dt, (const uint16_t*)w.Hx,
-                     PROJ ? nullptr : alpha, bw.kvorder, dK, dV, Dm.H, Dm.N, Dm.Nb);
+  const int slots = kv_slots(rows);
+  hipLaunchKernelGGL(k_kv_split, dim3(1), dim3(1024), 0, s, bw.kvcnt, rows, slots, bw.kvhdr,
+                     reinterpret_cast<int2*>(bw.kvinfo), reinterpret_cast<int2*>(bw.kvtab), bw.kvlist);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bwdkv_mfma<D, ELU>), dim3(slots + rows), dim3(256), lbytes, s, (const uint16_t*)Q,
+                     (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)dO, bw.maskT, bw.lse, bw.dt,
+                     (const uint16_t*)w.Hx, PROJ ? nullptr : alpha, bw.kvorder, bw.kvhdr,
+                     reinterpret_cast<const int2*>(bw.kvinfo), reinterpret_cast<const int2*>(bw.kvtab), bw.kvpart,
+                     slots, dK, dV, Dm.H, Dm.N, Dm.Nb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_kv_reduce<D>, dim3(slots, kKvRedY), dim3(256), 0, s, bw.kvhdr,
+                     reinterpret_cast<const int2*>(bw.kvinfo), bw.kvlist, bw.kvpart, dK, dV, Dm.N, Dm.Nb);
   return hipGetLastError();
 }
 

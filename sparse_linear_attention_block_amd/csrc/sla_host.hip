@@ -146,6 +146,12 @@ size_t carve_bwd(const Dims& D, bool proj, void* base, Work* w, BwdWork* bw) {
     x.maskT = (int8_t*)take(BH * D.Nb * D.Nb);
     x.kvcnt = (int*)take(BH * D.Nb * sizeof(int));
     x.kvorder = (int*)take(BH * D.Nb * sizeof(int));
+    const int slots = kv_slots((int)(BH * D.Nb));
+    x.kvhdr = (int*)take(4 * sizeof(int));
+    x.kvinfo = (int*)take(2 * BH * D.Nb * sizeof(int));
+    x.kvtab = (int*)take(2 * (size_t)slots * sizeof(int));
+    x.kvlist = (int*)take((size_t)slots * sizeof(int));
+    x.kvpart = (float*)take((size_t)slots * 2 * kBlock * D.d * sizeof(float));
   }
   if (proj) {
     const int hs = D.proj_hs ? D.H : 1;

@@ -73,9 +73,19 @@ struct BwdWork {
   uint16_t* wq;  // bf16 SLA fusion only: [Hs, d, d] the output map as bf16 A-operand fragments
   int* kvcnt;    // bf16 only: [BH * Nb] critical query blocks per key block
   int* kvorder;  // bf16 only: [BH * Nb] key blocks by falling count (the dK/dV launch order)
+  // bf16 only: the dK/dV work of a key block cut into chunks of its critical list (k_kv_split)
+  int* kvhdr;    // [4]: chunk length, extra chunks, split key blocks
+  int* kvinfo;   // [BH * Nb][2]: chunks of the key block, its first partial slot
+  int* kvtab;    // [kv_slots][2]: key block and chunk (>= 1) of each extra chunk
+  int* kvlist;   // [kv_slots]: the key blocks cut into more than one chunk
+  float* kvpart; // [kv_slots][2][64][d]: dK and dV of each extra chunk
 };
 // ranges the SLA fusion's dW parts are summed in before the ranges are added
 constexpr int kDwSplit = 32;
+// partial slots of the chunked dK/dV work (one per extra chunk) and the shortest chunk
+inline int kv_slots(int rows) { return rows / 4 > 0 ? rows / 4 : 1; }
+constexpr int kKvChunk = 64;
+constexpr int kKvRedY = 8;  // slices of a key block in the ordered sum of its chunk parts
 // row chunks of the bf16 dW product (over all W matrices together)
 constexpr int kDwChunks = 512;
 inline int dw_chunks(int hs) { return kDwChunks / hs > 0 ? kDwChunks / hs : 1; }
