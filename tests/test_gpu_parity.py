@@ -224,3 +224,34 @@ def test_long_rows_past_the_prefetched_mask():
         m = float(np.abs(gg - r).max())
         _flush(f"long rows {name}: rel-L1 {e:.2e} max-abs {m:.2e}")
         assert e <= BF16_REL_L1 and m <= BF16_MAX_ABS, (name, e, m)
+
+
+def test_largest_supported_block_count():
+    """Nb = 4096, the largest block count the library takes (N = 262107, a
+    ragged last block of 27 tokens), one head at d = 128 with a learned router:
+    every per-row loop at its largest instance (classify with 64 keys per lane,
+    128 k steps of the linear product, compaction of the mask row past the 2048
+    entries the sparse kernel prefetches). The mask is checked on every row;
+    O, O_s and O_l on query blocks at both ends and on both sides of index 2048."""
+    from workloads.configs import WorkloadConfig
+    N = 4096 * 64 - 37
+    cfg = WorkloadConfig(12, "max_nb", 1, 1, N, 128, None, "bf16", 0.01, 0.05, "learned",
+                         ("const", 0.6), False, 83, qk="normal")
+    x = make_inputs(cfg)
+    assert cfg.Nb == 4096
+    qb = [0, 1, 2047, 2048, 4095]
+    ref = orc.forward(x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha, x.kh, x.kl,
+                      query_blocks={(0, 0): qb})
+    _flush(f"max Nb: oracle done, n_h={ref.n_h} n_l={ref.n_l}")
+    g = run_gpu(x, debug=True)
+    exact, excused, bad = compare_masks(g["mask"], ref.mask, ref.logits, ref.n_h, ref.n_l)
+    _flush(f"max Nb: mask rows exact={exact} near-tie={excused} bad={len(bad)}")
+    assert not bad, bad[:10]
+    rows = orc.token_rows(qb, N)
+    for name, key in (("O", "O"), ("O_s", "o_s"), ("O_l", "o_l")):
+        r = getattr(ref, name)[(0, 0)]
+        gg = g[key][0, 0][rows]
+        e = rel_l1(gg, r)
+        m = float(np.abs(gg - r).max())
+        _flush(f"max Nb {name}: rel-L1 {e:.2e} max-abs {m:.2e}")
+        assert e <= BF16_REL_L1 and m <= BF16_MAX_ABS, (name, e, m)
