@@ -143,3 +143,17 @@ def test_q8_long_rows_past_the_prefetched_mask():
     mask[0, 0, Nb - 1, :] = -1
     mask[0, 0, Nb - 1, [3, 2050, Nb - 1]] = 1
     _check(x, heads=[(0, 0)], qblocks={(0, 0): [0, 1, 2, 1500, Nb - 1]}, mask=mask)
+
+
+def test_q8_largest_supported_block_count():
+    """Nb = 4096, the largest block count the library takes, in 8-bit mode at
+    d = 128 (N = 262107, a ragged last block of 27 tokens): the mask on every
+    row, then O, O_s and O_l on query blocks at both ends and on both sides of
+    index 2048."""
+    from workloads.configs import WorkloadConfig
+    N = 4096 * 64 - 37
+    cfg = WorkloadConfig(13, "max_nb_q8", 1, 1, N, 128, None, "bf16", 0.01, 0.05, "learned",
+                         ("const", 0.6), True, 84, qk="normal")
+    x = make_inputs(cfg)
+    assert cfg.Nb == 4096
+    _check(x, heads=[(0, 0)], qblocks={(0, 0): [0, 1, 2047, 2048, 4095]})
