@@ -132,6 +132,40 @@ def test_full_size_sampled():
     _flush(f"sum of dV over the keys matches its closed form on all {cfg.H} heads (worst {worst:.2e})")
 
 
+def test_largest_supported_block_count():
+    """Nb = 4096, the largest block count the library takes (N = 262107, a
+    ragged last block of 27 tokens), one head at d = 128: dQ on query blocks at
+    both ends and on both sides of index 2048 against the oracle's per-block
+    gradient, and the sum of dV over the keys against its closed form (as in
+    the full-size test above); the chunked dK/dV work runs over 4096 key blocks
+    with 1024 partial slots."""
+    from workloads.configs import WorkloadConfig
+    N = 4096 * 64 - 37
+    cfg = WorkloadConfig(14, "max_nb_bwd", 1, 1, N, 128, None, "bf16", 0.01, 0.05, "learned",
+                         ("const", 0.6), False, 85, qk="normal")
+    x = make_inputs(cfg)
+    assert cfg.Nb == 4096
+    mask = run_gpu(x, debug=False)["mask"]
+    dO = _grad_out(x, 13)
+    dQ, dK, dV, da = sla.backward(x.q.cuda(), x.k.cuda(), x.v.cuda(), x.alpha.cuda(),
+                                  torch.from_numpy(mask).cuda(), dO.cuda())
+    torch.cuda.synchronize()
+    dQ, dV = dQ.cpu().numpy(), dV.cpu().numpy().astype(np.float64)
+    assert np.isfinite(dK.cpu().numpy()).all()
+    ref = ob.dq_rows(x.q, x.k, x.v, x.alpha, mask, dO, 0, 0, [0, 1, 2047, 2048, 4095])
+    for i, r in ref.items():
+        e = rel_l1(dQ[0, 0, 64 * i:64 * i + r.shape[0]], r)
+        _flush(f"max Nb block {i}: dQ rel-L1 {e:.2e}")
+        assert e <= 1e-2, (i, e)
+    al = float(x.alpha.double()[0])
+    c = np.repeat((mask[0, 0] == 1).any(axis=1), 64)[:N].astype(float)
+    m = np.repeat((mask[0, 0] == 0).any(axis=1), 64)[:N].astype(float)
+    expect = ((al * c + (1 - al) * m)[:, None] * dO.double().numpy()[0, 0]).sum(axis=0)
+    e = rel_l1(dV[0, 0].sum(axis=0), expect)
+    _flush(f"max Nb: sum of dV over the keys against its closed form {e:.2e}")
+    assert e <= 3e-3, e
+
+
 def test_bf16_batch_of_two():
     # the CFG-batch recipe (B = 2, per-head alpha): dalpha sums over the batch
     _check(make_inputs(CONFIGS[4], H=3, N=500), 1e-2)
